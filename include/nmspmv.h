@@ -1,0 +1,122 @@
+/*
+ * nmspmv.h -- C ABI of libnmspmv, N:M semi-structured sparse matrix-vector
+ * products for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one that SparseDecoding names as the decode-time hot
+ * path: "SparseDecoding: Decoding-Aware Pruning for Accurate and Efficient
+ * LLM Inference" (humanity-list story page, section "Abstract") -- decoding
+ * is memory-bound and dominated by sparse matrix-vector products, and the
+ * paper's system contribution is an N:M sparse matrix-vector kernel that
+ * indexes kept weights with a bitmask and walks them with a fixed step.  The
+ * bedrocknews arXiv 2610.12327v1 article adds that N:M means a fixed count
+ * kept in every small block, and that the product is a sparse matrix times a
+ * single vector rather than a batch.
+ *
+ * ---- Storage format (the readings this library fixes) --------------------
+ * W is R x K, row-major, [out][in] (a PyTorch Linear weight); K is the
+ * reduction axis.  Every M-wide group of columns [g*M, g*M + M) of a row keeps
+ * exactly N entries (stored values may be zero).
+ *   values [R][K*N/M]  16-bit words; group g of a row starts at value g*N
+ *                      (fixed step) and holds its kept entries in ascending
+ *                      column order.  No column-index or row-pointer arrays.
+ *   masks  [R][K/8]    uint8 keep bitmap, one bit per dense column, least
+ *                      significant bit first: bit (c % 8) of byte c/8 of a row
+ *                      is set iff column c is kept.  (For M = 4 a byte holds
+ *                      two groups, the even group in the low nibble.)
+ *
+ * ---- Conventions shared by every call -------------------------------------
+ * - All pointers are device pointers (hipMalloc or a torch CUDA tensor).  The
+ *   caller allocates and frees every buffer; the library keeps no
+ *   allocations and no per-call state except one device word per GPU that
+ *   nm_pack uses to report errors.  Calls are thread-safe.
+ * - dtype is NM_FP16 (IEEE binary16) or NM_BF16 (bfloat16); W, values, x and y
+ *   all use it.
+ * - Shapes: R >= 0, K >= 0, K % 8 == 0, M in {4, 8}, 1 <= N < M, K % M == 0,
+ *   1 <= B <= 8, and R, K below 2^31.  Anything else returns NM_ERR_BAD_SHAPE
+ *   (or NM_ERR_UNSUPPORTED for a dtype that is not one of the two) before
+ *   any work is queued; outputs are then untouched.
+ * - Alignment: W, values, masks and x must be 16-byte aligned; y 2-byte
+ *   aligned; keep needs none.  Rows are contiguous, no strides.  y must not
+ *   overlap any input.  Violations return NM_ERR_INVALID_ARG.
+ * - stream is a hipStream_t (NULL = the null stream).  nm_spmv and
+ *   nm_gemv_dense only enqueue work and return; nm_pack waits for its own
+ *   work to finish.
+ * - x must be finite.  With Inf or NaN in x the outputs are unspecified
+ *   (a pruned column may or may not contribute 0 * Inf).
+ */
+#ifndef NMSPMV_H
+#define NMSPMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NM_OK = 0,
+    NM_ERR_INVALID_ARG = 1, /* null pointer, misalignment, overlapping output */
+    NM_ERR_BAD_SHAPE = 2,   /* R, K, N, M or B outside the accepted set */
+    NM_ERR_UNSUPPORTED = 3, /* dtype not NM_FP16 / NM_BF16 */
+    NM_ERR_BAD_MASK = 4,    /* nm_pack: a keep-mask group without exactly N kept */
+    NM_ERR_NONFINITE = 5,   /* nm_pack top-N: a NaN weight */
+    NM_ERR_HIP = 6          /* the HIP runtime reported an error */
+} nm_status;
+
+typedef enum { NM_FP16 = 0, NM_BF16 = 1 } nm_dtype;
+
+/*
+ * nm_pack -- prune a dense W to N:M and pack it (the offline step that turns
+ * a pruned weight into the bitmask-indexed form of the SparseDecoding
+ * abstract; the pruning choice itself is the caller's, or top-N here).
+ *   W      [R][K] 16-bit weights (dtype).
+ *   keep   [R][K] bytes, nonzero = keep, or NULL.  With a keep-mask every
+ *          group must have exactly N nonzero bytes, else NM_ERR_BAD_MASK;
+ *          kept words (NaN included) are copied bit for bit.  With NULL the N
+ *          entries of largest |w| are kept per group, the lower column
+ *          winning a tie (-0 and +0 tie); a NaN anywhere gives
+ *          NM_ERR_NONFINITE.
+ *   values [R][K*N/M] 16-bit, masks [R][K/8] bytes: outputs, fully written.
+ * Every group is checked before anything is written: on NM_ERR_BAD_MASK or
+ * NM_ERR_NONFINITE the outputs are untouched.  The call returns when the
+ * packed outputs are complete on the device.
+ */
+int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int M, int dtype,
+            void* values, uint8_t* masks, void* stream);
+
+/*
+ * nm_spmv -- y = W_sparse * x for 1..8 activation vectors: the decode-time
+ * N:M sparse matrix-vector product of the SparseDecoding abstract and of the
+ * "Key points" of "SparseDecoding Makes LLM Pruning Aware of Generation".
+ *   values, masks  packed as nm_pack writes them (R rows, K dense columns).
+ *                  The mask contents are not validated; a bitmap whose groups
+ *                  do not hold exactly N bits gives unspecified y but never
+ *                  an out-of-bounds access.
+ *   x [B][K] 16-bit, y [B][R] 16-bit (output).
+ *   y[b][r] = sum over kept columns c of W[r][c] * x[b][c]; every product and
+ *   sum is formed in fp32 (in an unspecified order) and the sum is rounded
+ *   once to the output dtype, to nearest even.
+ * Enqueues on stream and returns; y is complete when the stream reaches it.
+ */
+int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int N, int M, int dtype,
+            const void* x, int B, void* y, void* stream);
+
+/*
+ * nm_gemv_dense -- the dense baseline y = W * x (the unpruned decode
+ * projection the SparseDecoding speedup is measured against).
+ *   W [R][K], x [B][K], y [B][R], all dtype; fp32 accumulation, one rounding.
+ * Same shape rules as nm_spmv without N and M (K % 8 == 0).
+ */
+int nm_gemv_dense(const void* W, int64_t R, int64_t K, int dtype, const void* x, int B, void* y, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* nm_status_string(int status);
+
+/* Library ABI version: 100 * major + minor. */
+int nm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NMSPMV_H */

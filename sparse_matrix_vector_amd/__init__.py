@@ -1,0 +1,97 @@
+"""libnmspmv for MI355X: N:M semi-structured sparse matrix-vector products.
+
+Python face of the C ABI in ``include/nmspmv.h``.  Tensors are torch CUDA
+(HIP) tensors; torch supplies device memory and the current stream, and every
+step of the computation runs in the HIP kernels of ``libnmspmv.so``.
+
+    values, masks = pack(W, keep=None, n=2, m=4)   # offline: prune + pack
+    y = spmv(values, masks, x, n=2, m=4)           # per token: y = W_sparse x
+    y = gemv_dense(W, x)                           # dense baseline
+"""
+import ctypes
+
+import torch
+
+from ._lib import (NM_BF16, NM_ERR_BAD_MASK, NM_ERR_BAD_SHAPE, NM_ERR_HIP, NM_ERR_INVALID_ARG,  # noqa: F401
+                   NM_ERR_NONFINITE, NM_ERR_UNSUPPORTED, NM_FP16, NM_OK, NmError, call, lib)
+
+__all__ = ["pack", "spmv", "gemv_dense", "NmError", "dtype_code", "stream_handle"]
+
+_DT = {torch.float16: NM_FP16, torch.bfloat16: NM_BF16}
+
+
+def dtype_code(dtype):
+    if dtype not in _DT:
+        raise TypeError(f"libnmspmv supports float16 and bfloat16, not {dtype}")
+    return _DT[dtype]
+
+
+def stream_handle(stream=None):
+    """hipStream_t of ``stream`` (default: torch's current stream) for the C ABI."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def pack(W, keep=None, n=2, m=4, stream=None):
+    """Prune W [R][K] to n:m and pack it.  ``keep`` is a bool/uint8 tensor of
+    W's shape (nonzero = keep, exactly n per group) or None for top-n by
+    magnitude (lower column wins ties).  Returns (values [R][K*n/m] in W's
+    dtype, masks [R][K/8] uint8)."""
+    _dev(W, "W")
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [R][K]")
+    R, K = W.shape
+    kp = None
+    if keep is not None:
+        _dev(keep, "keep")
+        if keep.shape != W.shape or keep.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("keep must be a bool/uint8 tensor shaped like W")
+        kp = keep.data_ptr()
+    if m <= 0 or K % m:
+        raise ValueError("K must be a multiple of m")
+    values = torch.empty((R, K // m * n), dtype=W.dtype, device=W.device)
+    masks = torch.empty((R, K // 8), dtype=torch.uint8, device=W.device)
+    call("nm_pack", W.data_ptr(), kp, R, K, n, m, dtype_code(W.dtype), values.data_ptr(), masks.data_ptr(),
+         stream_handle(stream))
+    return values, masks
+
+
+def spmv(values, masks, x, n=2, m=4, out=None, stream=None):
+    """y = W_sparse x.  x is [K] or [B][K] (B <= 8); returns [R] or [B][R]."""
+    _dev(values, "values"), _dev(masks, "masks"), _dev(x, "x")
+    R = masks.shape[0]
+    K = masks.shape[1] * 8
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    B = x2.shape[0]
+    if x2.shape[1] != K or x.dtype != values.dtype:
+        raise ValueError("x must be [B][K] in the values' dtype")
+    if values.shape != (R, K // m * n):
+        raise ValueError("values shape does not match masks and n:m")
+    y = torch.empty((B, R), dtype=values.dtype, device=values.device) if out is None else _dev(out, "out")
+    call("nm_spmv", values.data_ptr(), masks.data_ptr(), R, K, n, m, dtype_code(values.dtype), x2.data_ptr(), B,
+         y.data_ptr(), stream_handle(stream))
+    return y[0] if squeeze else y
+
+
+def gemv_dense(W, x, out=None, stream=None):
+    """Dense baseline y = W x.  x is [K] or [B][K]; returns [R] or [B][R]."""
+    _dev(W, "W"), _dev(x, "x")
+    R, K = W.shape
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    B = x2.shape[0]
+    if x2.shape[1] != K or x.dtype != W.dtype:
+        raise ValueError("x must be [B][K] in W's dtype")
+    y = torch.empty((B, R), dtype=W.dtype, device=W.device) if out is None else _dev(out, "out")
+    call("nm_gemv_dense", W.data_ptr(), R, K, dtype_code(W.dtype), x2.data_ptr(), B, y.data_ptr(),
+         stream_handle(stream))
+    return y[0] if squeeze else y

@@ -1,0 +1,118 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/nmspmv.h declares, and rejects bad arguments before touching the GPU
+(argument validation is host code; no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_matrix_vector_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nmspmv.h")
+
+FAKE = 0x10000          # a 16-byte aligned address that is never dereferenced: every call below fails validation first
+FAKE2 = 0x900000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for f in ("nm_pack", "nm_spmv", "nm_gemv_dense"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in L.SIGNATURES, f"binding has no signature for {name}"
+
+
+def test_version_and_status_strings():
+    lib = L.lib()
+    assert lib.nm_version() == 100
+    for code, name in [(0, b"NM_OK"), (1, b"NM_ERR_INVALID_ARG"), (2, b"NM_ERR_BAD_SHAPE"), (3, b"NM_ERR_UNSUPPORTED"),
+                       (4, b"NM_ERR_BAD_MASK"), (5, b"NM_ERR_NONFINITE"), (6, b"NM_ERR_HIP")]:
+        assert lib.nm_status_string(code) == name
+    assert lib.nm_status_string(99) == b"NM_ERR_UNKNOWN"
+
+
+def spmv(values=FAKE, masks=FAKE, R=16, K=64, N=2, M=4, dt=0, x=FAKE2, B=1, y=FAKE2 + 0x100000):
+    return L.lib().nm_spmv(values, masks, R, K, N, M, dt, x, B, y, None)
+
+
+def gemv(W=FAKE, R=16, K=64, dt=0, x=FAKE2, B=1, y=FAKE2 + 0x100000):
+    return L.lib().nm_gemv_dense(W, R, K, dt, x, B, y, None)
+
+
+def pack(W=FAKE, keep=None, R=16, K=64, N=2, M=4, dt=0, values=FAKE2, masks=FAKE2 + 0x100000):
+    return L.lib().nm_pack(W, keep, R, K, N, M, dt, values, masks, None)
+
+
+@pytest.mark.parametrize("kw", [dict(K=12), dict(K=-8), dict(R=-1), dict(M=3), dict(M=16), dict(N=0), dict(N=4),
+                                dict(N=8, M=8), dict(K=8 * 3, M=8, N=4) | dict(K=20), dict(B=0), dict(B=9),
+                                dict(R=2 ** 31), dict(K=2 ** 31 + 8)])
+def test_spmv_bad_shape(kw):
+    assert spmv(**kw) == L.NM_ERR_BAD_SHAPE
+
+
+def test_spmv_unsupported_dtype():
+    assert spmv(dt=2) == L.NM_ERR_UNSUPPORTED
+    assert spmv(dt=-1) == L.NM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(values=None), dict(masks=None), dict(x=None), dict(y=None),
+                                dict(values=FAKE + 8), dict(masks=FAKE + 2), dict(x=FAKE2 + 4), dict(y=FAKE2 + 1),
+                                dict(y=FAKE), dict(y=FAKE2 + 64)])
+def test_spmv_invalid_pointer(kw):
+    assert spmv(**kw) == L.NM_ERR_INVALID_ARG
+
+
+def test_spmv_empty_is_ok_without_gpu():
+    # R == 0: nothing to compute, no launch, pointers may be NULL.
+    assert L.lib().nm_spmv(None, None, 0, 64, 2, 4, 0, FAKE2, 1, None, None) == L.NM_OK
+
+
+@pytest.mark.parametrize("kw", [dict(K=12), dict(R=-1), dict(B=0), dict(B=9)])
+def test_gemv_bad_shape(kw):
+    assert gemv(**kw) == L.NM_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(W=None), dict(W=FAKE + 2), dict(x=FAKE2 + 8), dict(y=None), dict(y=FAKE + 16)])
+def test_gemv_invalid_pointer(kw):
+    assert gemv(**kw) == L.NM_ERR_INVALID_ARG
+
+
+def test_gemv_unsupported_dtype():
+    assert gemv(dt=7) == L.NM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(K=12), dict(M=2), dict(N=4), dict(N=0), dict(R=-3)])
+def test_pack_bad_shape(kw):
+    assert pack(**kw) == L.NM_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(W=None), dict(values=None), dict(masks=None), dict(W=FAKE + 4),
+                                dict(values=FAKE2 + 2), dict(values=FAKE), dict(masks=FAKE + 32),
+                                dict(keep=FAKE2 + 8)])
+def test_pack_invalid_pointer(kw):
+    assert pack(**kw) == L.NM_ERR_INVALID_ARG
+
+
+def test_pack_empty_is_ok_without_gpu():
+    assert L.lib().nm_pack(None, None, 0, 64, 2, 4, 0, None, None, None) == L.NM_OK
+    assert L.lib().nm_pack(None, None, 5, 0, 2, 4, 0, None, None, None) == L.NM_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        L.lib()
