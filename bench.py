@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark: N:M SpMV achieved HBM GB/s (% of peak) and speedup over the
+dense GEMV, batch 1, on one MI355X.
+
+A step is one decode token's worth of weight projections of Llama-3.1-8B
+(32 layers x q, k, v, o, gate, up, down; 2:4, fp16, B = 1).  Each layer is
+four launches, as a decoder issues them: q/k/v fused (one x), o, gate/up
+fused (one x), down -- every one on its own layer's packed weights, so a step
+streams 7.86 GB of distinct packed bytes, far beyond the 256 MB last-level
+cache.  The dense baseline runs the same step on the unpruned weights with the
+same fusion.  Weights are synthetic, W ~ N(0, 0.02); activations x ~ N(0, 1)
+with ceil(1% K) channels x10; all seeded.  The step is captured once into a
+HIP graph and replayed.
+
+One JSON line is printed.  ``value`` = algorithmic bytes per step / step time
+(bytes = packed values + bitmaps + x + y of every launch).  ``roofline`` is for
+the sparse kernel instantiation that carries q/k/v, o and gate/up (all rows of
+4096 columns): its launches timed in back-to-back bursts with HIP events on
+the launch stream.  ``mlp_shapes`` times the Llama-3.1-8B MLP projections as
+single launches.  ``cpu_baseline`` times the CPU oracle on one layer.
+"""
+import argparse
+import ctypes
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "N:M SpMV achieved HBM GB/s (% of peak) + speedup vs dense GEMV, batch 1"
+PEAK_GBS = 8000.0
+P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a graph")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+class Launch:
+    """One launch of the step: 1-3 projections of one layer sharing one x."""
+
+    def __init__(self, torch, nm, I, layer, names, K):
+        dt = torch.float16
+        self.layer, self.names, self.K = layer, names, K
+        self.x = I.activation_normal(1, K, dt, I.seed_of("llama31_8b", layer, names[0], "x"), device="cuda",
+                                     outlier_frac=0.01)
+        self.R, self.W, self.values, self.masks, self.y, self.yd = [], [], [], [], [], []
+        for nme in names:
+            R, K2 = I.LLAMA31_8B[nme]
+            assert K2 == K
+            W = I.weight(R, K, dt, I.seed_of("llama31_8b", layer, nme, "W"), device="cuda")
+            v, m = nm.pack(W, None, 2, 4)
+            self.R.append(R)
+            self.W.append(W)
+            self.values.append(v)
+            self.masks.append(m)
+            self.y.append(torch.empty((1, R), dtype=dt, device="cuda"))
+            self.yd.append(torch.empty((1, R), dtype=dt, device="cuda"))
+
+    @property
+    def kind(self):
+        return "+".join(self.names)
+
+    def sparse_args(self, stream):
+        c = len(self.names)
+        return (I32(c), (P * c)(*[v.data_ptr() for v in self.values]), (P * c)(*[m.data_ptr() for m in self.masks]),
+                (I64 * c)(*self.R), I64(self.K), I32(2), I32(4), I32(0), P(self.x.data_ptr()), I32(1),
+                (P * c)(*[y.data_ptr() for y in self.y]), P(stream))
+
+    def dense_args(self, stream):
+        c = len(self.names)
+        return (I32(c), (P * c)(*[W.data_ptr() for W in self.W]), (I64 * c)(*self.R), I64(self.K), I32(0),
+                P(self.x.data_ptr()), I32(1), (P * c)(*[y.data_ptr() for y in self.yd]), P(stream))
+
+    def sparse_bytes(self):
+        return sum(R * self.K // 2 * 2 + R * self.K // 8 + R * 2 for R in self.R) + self.K * 2
+
+    def dense_bytes(self):
+        return sum(R * self.K * 2 + R * 2 for R in self.R) + self.K * 2
+
+
+def build_step(layers, torch, nm, I):
+    launches = []
+    for l in range(layers):
+        launches.append(Launch(torch, nm, I, l, ("q", "k", "v"), 4096))
+        launches.append(Launch(torch, nm, I, l, ("o",), 4096))
+        launches.append(Launch(torch, nm, I, l, ("gate", "up"), 4096))
+        launches.append(Launch(torch, nm, I, l, ("down",), 14336))
+    torch.cuda.synchronize()
+    return launches
+
+
+def run(fn, arg_lists):
+    for a in arg_lists:
+        st = fn(*a)
+        if st != 0:
+            raise RuntimeError(f"launch failed with status {st}")
+
+
+def time_ms(torch, body, reps):
+    """HIP events on torch's current stream around `reps` calls of body()."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(reps):
+        body()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def capture(torch, fn, args_for_stream):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        args = args_for_stream(s.cuda_stream)
+        run(fn, args)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            run(fn, args)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def read_ceiling(torch, cur):
+    """Plain 16-byte streaming read of 1 GB regions rotated over 4 GB."""
+    from sparse_matrix_vector_amd import probe
+    lib = probe.lib()
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    nb = 1 << 30
+    best = 0.0
+    for blocks in (512, 1024, 2048):
+        def body():
+            for i in range(4):
+                if lib.nmp_read(P(buf.data_ptr() + i * nb), nb, P(sink.data_ptr()), blocks, P(cur)) != 0:
+                    raise RuntimeError("probe launch failed")
+        body()
+        ms = time_ms(torch, body, 3) / 4
+        best = max(best, nb / (ms * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
+def mlp_single(torch, nm, I, lib, launches, cur):
+    """Llama-3.1-8B MLP shapes as single nm_spmv / nm_gemv_dense launches,
+    back to back over the 32 layers' weights."""
+    out = {}
+    for name in ("gate", "up", "down"):
+        sargs, dargs, nbytes, dbytes = [], [], 0, 0
+        for L in launches:
+            if name not in L.names:
+                continue
+            i = L.names.index(name)
+            R, K = L.R[i], L.K
+            sargs.append((P(L.values[i].data_ptr()), P(L.masks[i].data_ptr()), I64(R), I64(K), I32(2), I32(4),
+                          I32(0), P(L.x.data_ptr()), I32(1), P(L.y[i].data_ptr()), P(cur)))
+            dargs.append((P(L.W[i].data_ptr()), I64(R), I64(K), I32(0), P(L.x.data_ptr()), I32(1),
+                          P(L.yd[i].data_ptr()), P(cur)))
+            nbytes = R * K // 2 * 2 + R * K // 8 + K * 2 + R * 2
+            dbytes = R * K * 2 + K * 2 + R * 2
+        run(lib.nm_spmv, sargs)
+        us = time_ms(torch, lambda: run(lib.nm_spmv, sargs), 10) / len(sargs) * 1e3
+        run(lib.nm_gemv_dense, dargs)
+        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense, dargs), 10) / len(dargs) * 1e3
+        out[name] = {"shape": [R, K], "us": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
+                     "pct_of_peak": round(100 * nbytes / us / 1e3 / PEAK_GBS, 2),
+                     "dense_us": round(usd, 3), "dense_gbs": round(dbytes / usd / 1e3, 1),
+                     "speedup": round(usd / us, 4)}
+    return out
+
+
+def cpu_baseline(launches, budget_s, torch):
+    """CPU oracle (plain C, fp64, one thread) on layer 0's seven projections,
+    packed by the oracle itself from the same weights; repeated until about
+    budget_s seconds of oracle time."""
+    import numpy as np
+
+    import oracle
+    work = []
+    for L in launches:
+        if L.layer != 0:
+            continue
+        xb = L.x.cpu().view(torch.int16).numpy().view(np.uint16)
+        for i, R in enumerate(L.R):
+            Wb = L.W[i].cpu().view(torch.int16).numpy().view(np.uint16)
+            v, m = oracle.pack(Wb, None, 2, 4, "fp16")
+            nbytes = R * L.K // 2 * 2 + R * L.K // 8 + L.K * 2 + R * 2
+            work.append((v, m, L.K, xb, nbytes))
+    done, elapsed, reps = 0, 0.0, 0
+    while elapsed < budget_s or reps == 0:
+        for v, m, K, xb, nbytes in work:
+            t0 = time.perf_counter()
+            oracle.spmv(v, m, K, 2, 4, "fp16", xb)
+            elapsed += time.perf_counter() - t0
+            done += nbytes
+        reps += 1
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(done / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"Llama-3.1-8B decoder layer 0 (q,k,v,o,gate,up,down; 2:4 fp16, B=1) x {reps}: "
+                      f"fp64 scalar C oracle, 1 thread, {elapsed:.1f} s, {elapsed / reps * 1e3:.0f} ms per layer "
+                      f"(GPU step has 32 layers); host {cpu}, {os.cpu_count()} logical CPUs"}
+
+
+def sampled_parity(launches, torch):
+    """First 64 rows of layer 0's q, gate and down against the oracle."""
+    import numpy as np
+
+    import oracle
+    worst = 0.0
+    for L in launches:
+        if L.layer != 0:
+            continue
+        xb = L.x.cpu().view(torch.int16).numpy().view(np.uint16)
+        for i, nme in enumerate(L.names):
+            if nme not in ("q", "gate", "down"):
+                continue
+            Wb = L.W[i][:64].cpu().view(torch.int16).numpy().view(np.uint16)
+            v, m = oracle.pack(Wb, None, 2, 4, "fp16")
+            assert np.array_equal(v, L.values[i][:64].cpu().view(torch.int16).numpy().view(np.uint16)), "pack"
+            assert np.array_equal(m, L.masks[i][:64].cpu().numpy()), "masks"
+            yref, A = oracle.spmv(v, m, L.K, 2, 4, "fp16", xb)
+            got = L.y[i][:, :64].cpu().view(torch.int16).numpy().view(np.uint16)
+            ok, w, _ = oracle.check(got, yref, A, "fp16")
+            assert ok, f"{nme}: outside tolerance ({w})"
+            worst = max(worst, w)
+    return worst
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (multi-GPU sharding of this kernel "
+              f"is design-only).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_matrix_vector_amd as nm
+    from sparse_matrix_vector_amd import inputs as I
+    lib = nm.lib()
+    torch.cuda.set_device(0)
+    cur = torch.cuda.current_stream().cuda_stream
+
+    launches = build_step(a.layers, torch, nm, I)
+    sparse_bytes = sum(L.sparse_bytes() for L in launches)
+    dense_bytes = sum(L.dense_bytes() for L in launches)
+
+    if a.eager:
+        sl = [L.sparse_args(cur) for L in launches]
+        dl = [L.dense_args(cur) for L in launches]
+        step_sparse = lambda: run(lib.nm_spmv_multi, sl)          # noqa: E731
+        step_dense = lambda: run(lib.nm_gemv_dense_multi, dl)     # noqa: E731
+    else:
+        gs = capture(torch, lib.nm_spmv_multi, lambda s: [L.sparse_args(s) for L in launches])
+        gd = capture(torch, lib.nm_gemv_dense_multi, lambda s: [L.dense_args(s) for L in launches])
+        step_sparse, step_dense = gs.replay, gd.replay
+
+    # ---- the timed region: K sparse steps ----
+    for _ in range(a.warmup):
+        step_sparse()
+    torch.cuda.synchronize()
+    ms_step = time_ms(torch, step_sparse, a.steps)
+    # ---- dense baseline, same step structure ----
+    for _ in range(max(1, a.warmup)):
+        step_dense()
+    ms_dense = time_ms(torch, step_dense, max(5, a.steps // 2))
+
+    # ---- per launch type: back-to-back bursts over the layers' weights ----
+    per = {}
+    for kind in ("q+k+v", "o", "gate+up", "down"):
+        group = [L for L in launches if L.kind == kind]
+        sl = [L.sparse_args(cur) for L in group]
+        dl = [L.dense_args(cur) for L in group]
+        run(lib.nm_spmv_multi, sl)
+        us = time_ms(torch, lambda: run(lib.nm_spmv_multi, sl), 10) / len(sl) * 1e3
+        run(lib.nm_gemv_dense_multi, dl)
+        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense_multi, dl), 10) / len(dl) * 1e3
+        sb, db = group[0].sparse_bytes(), group[0].dense_bytes()
+        per[kind] = {"rows": sum(group[0].R), "K": group[0].K, "us": round(us, 3), "gbs": round(sb / us / 1e3, 1),
+                     "dense_us": round(usd, 3), "dense_gbs": round(db / usd / 1e3, 1), "speedup": round(usd / us, 4),
+                     "bytes": sb}
+    # roofline kernel: the instantiation shared by the K = 4096 launches (3 per layer)
+    rk = ("q+k+v", "o", "gate+up")
+    rbytes = sum(per[k]["bytes"] for k in rk) / len(rk)
+    rus = sum(per[k]["us"] for k in rk) / len(rk)
+    achieved = rbytes / rus / 1e3
+
+    mlp = mlp_single(torch, nm, I, lib, launches, cur)
+    ceiling = read_ceiling(torch, cur)
+    worst = sampled_parity(launches, torch)
+    cpu = None if a.no_cpu else cpu_baseline(launches, a.cpu_seconds, torch)
+
+    gbs = sparse_bytes / (ms_step * 1e-3) / 1e9
+    props = torch.cuda.get_device_properties(0)
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B decode-step projections: 32 layers x (q+k+v fused, o, gate+up fused, "
+                               "down), 2:4 sparse, fp16, batch 1",
+                   "layers": a.layers, "n_m": "2:4", "batch": 1, "launches_per_step": len(launches),
+                   "mode": "eager" if a.eager else "hip_graph",
+                   "packed_bytes_per_step": sparse_bytes, "dense_bytes_per_step": dense_bytes},
+        "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
+        "speedup_vs_dense": round(ms_dense / ms_step, 4),
+        "dense_ms_per_step": round(ms_dense, 4),
+        "dense_gbs": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
+        "us_per_layer": round(ms_step * 1e3 / a.layers, 2),
+        "per_launch": per,
+        "mlp_shapes": mlp,
+        "read_ceiling_gbs": round(ceiling, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "kernel": "rowslice_kernel<2:4, fp16, B=1, 4 chunks/lane> (q+k+v, o, gate+up launches)",
+                     "avg_launch_us": round(rus, 3), "algorithmic_bytes_per_launch": round(rbytes)},
+        "cpu_baseline": cpu,
+        "parity_sampled_worst_ratio": round(worst, 4),
+        "env": {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+                "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                "python": platform.python_version()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

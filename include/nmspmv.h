@@ -109,6 +109,27 @@ int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int 
  */
 int nm_gemv_dense(const void* W, int64_t R, int64_t K, int dtype, const void* x, int B, void* y, void* stream);
 
+/*
+ * nm_spmv_multi -- count (1..4) packed matrices with the same K, N:M and dtype
+ * multiplied by the same x in one launch: y_i = W_i x for every i.  This is
+ * the decode-layer fusion of projections that read one activation (q, k and
+ * v; gate and up), so the per-launch start-up and drain are paid once.
+ *   values[i], masks[i]  part i packed as nm_pack writes it, R[i] rows.
+ *   y[i]                 [B][R[i]] output of part i.
+ * Each y[i] equals what nm_spmv would give for part i alone up to fp32
+ * summation order (the row split across lanes may differ); rules as for
+ * nm_spmv, applied per part, plus: no y[i] may overlap another y[j], and the
+ * total row count must stay below 2^31.  count outside 1..4 is
+ * NM_ERR_BAD_SHAPE; NULL array arguments are NM_ERR_INVALID_ARG.
+ */
+int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
+                  int N, int M, int dtype, const void* x, int B, void* const* y, void* stream);
+
+/* nm_gemv_dense_multi -- the dense baseline of nm_spmv_multi: y_i = W_i x for
+ * count (1..4) dense [R[i]][K] matrices sharing x, in one launch. */
+int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t K, int dtype, const void* x, int B,
+                        void* const* y, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* nm_status_string(int status);
 

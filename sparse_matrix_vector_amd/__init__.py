@@ -15,7 +15,7 @@ import torch
 from ._lib import (NM_BF16, NM_ERR_BAD_MASK, NM_ERR_BAD_SHAPE, NM_ERR_HIP, NM_ERR_INVALID_ARG,  # noqa: F401
                    NM_ERR_NONFINITE, NM_ERR_UNSUPPORTED, NM_FP16, NM_OK, NmError, call, lib)
 
-__all__ = ["pack", "spmv", "gemv_dense", "NmError", "dtype_code", "stream_handle"]
+__all__ = ["pack", "spmv", "spmv_multi", "gemv_dense", "gemv_dense_multi", "NmError", "dtype_code", "stream_handle"]
 
 _DT = {torch.float16: NM_FP16, torch.bfloat16: NM_BF16}
 
@@ -95,3 +95,52 @@ def gemv_dense(W, x, out=None, stream=None):
     call("nm_gemv_dense", W.data_ptr(), R, K, dtype_code(W.dtype), x2.data_ptr(), B, y.data_ptr(),
          stream_handle(stream))
     return y[0] if squeeze else y
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return arr
+
+
+def spmv_multi(parts, x, n=2, m=4, stream=None):
+    """One launch for several packed matrices sharing x (e.g. q, k, v).
+    ``parts`` is a list of (values, masks); returns a list of y [B][R_i]
+    (or [R_i] for a 1-D x)."""
+    if not 1 <= len(parts) <= 4:
+        raise ValueError("1 to 4 parts")
+    _dev(x, "x")
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    B, K = x2.shape
+    ys, Rs = [], []
+    for values, masks in parts:
+        _dev(values, "values"), _dev(masks, "masks")
+        R = masks.shape[0]
+        if masks.shape[1] * 8 != K or values.shape != (R, K // m * n) or values.dtype != x.dtype:
+            raise ValueError("part shapes do not match x and n:m")
+        ys.append(torch.empty((B, R), dtype=x.dtype, device=x.device))
+        Rs.append(R)
+    call("nm_spmv_multi", len(parts), _ptr_array([v.data_ptr() for v, _ in parts]),
+         _ptr_array([mk.data_ptr() for _, mk in parts]), (ctypes.c_int64 * len(parts))(*Rs), K, n, m,
+         dtype_code(x.dtype), x2.data_ptr(), B, _ptr_array([y.data_ptr() for y in ys]), stream_handle(stream))
+    return [y[0] for y in ys] if squeeze else ys
+
+
+def gemv_dense_multi(Ws, x, stream=None):
+    """Dense baseline of spmv_multi: one launch for several W sharing x."""
+    if not 1 <= len(Ws) <= 4:
+        raise ValueError("1 to 4 matrices")
+    _dev(x, "x")
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    B, K = x2.shape
+    ys = []
+    for W in Ws:
+        _dev(W, "W")
+        if W.shape[1] != K or W.dtype != x.dtype:
+            raise ValueError("W shapes do not match x")
+        ys.append(torch.empty((B, W.shape[0]), dtype=x.dtype, device=x.device))
+    call("nm_gemv_dense_multi", len(Ws), _ptr_array([W.data_ptr() for W in Ws]),
+         (ctypes.c_int64 * len(Ws))(*[W.shape[0] for W in Ws]), K, dtype_code(x.dtype), x2.data_ptr(), B,
+         _ptr_array([y.data_ptr() for y in ys]), stream_handle(stream))
+    return [y[0] for y in ys] if squeeze else ys

@@ -11,6 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "nmspmv.hip")
 LIB = os.path.join(HERE, "libnmspmv.so")
+# (source, library): the product library and the measurement probes beside it
+TARGETS = [(SRC, LIB), (os.path.join(HERE, "csrc", "nmprobe.hip"), os.path.join(HERE, "libnmprobe.so"))]
 ARCH = "gfx950"
 
 
@@ -22,11 +24,17 @@ def hipcc():
 
 
 def build(verbose: bool = False) -> str:
+    for src, lib in TARGETS:
+        build_one(src, lib, verbose)
+    return LIB
+
+
+def build_one(src, lib, verbose=False):
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed-fp32 instructions stay off (the compiler would otherwise form them from float code)
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-fno-gpu-rdc", "-Wall", "-Wno-unused-result",
-           "-I", os.path.join(ROOT, "include"), SRC, "-o", LIB + ".tmp"]
+           "-I", os.path.join(ROOT, "include"), src, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,8 +43,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

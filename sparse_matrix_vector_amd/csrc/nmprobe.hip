@@ -1,0 +1,79 @@
+// nmprobe.hip -- libnmprobe: measurement probes used beside libnmspmv.
+//
+// Not part of the product path.  The benchmark uses these to learn what the
+// GPU can do at all:
+//   nmp_read   streams a buffer with 16-byte loads (the same load width and
+//              cache hints as the product kernels) and folds it into one word
+//              per block, so its time is the achievable read-bandwidth ceiling
+//              for a given size;
+//   nmp_copy   a plain 16-byte copy of known size, whose FETCH_SIZE and
+//              WRITE_SIZE counter readings calibrate the counters' units;
+//   nmp_empty  an empty kernel, to time launch cost alone.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n16, uint32_t* __restrict__ sink)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    uint32_t acc = 0;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(src + i);
+        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 a = __builtin_nontemporal_load(src + i);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    // A value-dependent store keeps the loads alive; it almost never fires.
+    if (acc == 0x9E3779B9u)
+        sink[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n16)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+}
+
+__global__ void empty_kernel() {}
+
+}  // namespace
+
+extern "C" {
+
+// bytes must be a multiple of 16 and src 16-byte aligned; sink holds `blocks` words.
+int nmp_read(const void* src, int64_t bytes, void* sink, int blocks, void* stream)
+{
+    if (!src || !sink || bytes < 0 || bytes % 16 || blocks < 1 || (reinterpret_cast<uintptr_t>(src) & 15))
+        return 1;
+    hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, bytes / 16,
+                       (uint32_t*)sink);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int nmp_copy(const void* src, void* dst, int64_t bytes, int blocks, void* stream)
+{
+    if (!src || !dst || bytes < 0 || bytes % 16 || blocks < 1 || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15))
+        return 1;
+    hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, (u32x4*)dst,
+                       bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int nmp_empty(void* stream)
+{
+    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+}  // extern "C"

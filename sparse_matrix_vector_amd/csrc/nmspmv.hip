@@ -8,27 +8,36 @@
 // this one is designed for CDNA4 (wave64, 160 KB LDS per CU, HBM3E) and shares
 // nothing with the CPU checker.
 //
-// Format (see include/nmspmv.h): values [R][K*N/M] 16-bit, group g of a row at
-// value g*N; masks [R][K/8] one bit per dense column, LSB first.
+// Format (include/nmspmv.h): values [R][K*N/M] 16-bit, group g of a row at
+// value g*N; masks [R][K/8], one bit per dense column, LSB first.
 //
-// Kernels
-//   rowdot_kernel<SPARSE=true>   N/M = 1/2 (2:4, 4:8), K % 16 == 0.  Each lane
-//       streams 16-byte chunks of a row's values (8 values = 16 dense columns)
-//       plus the 16 mask bits of those columns, expands the 8 values into the
-//       16 dense columns with 8 byte-permutes whose selectors come from a
-//       256-entry LDS table indexed by mask byte, and multiplies against x
-//       staged in LDS with packed dot2 (fp32 accumulate).
-//   rowdot_kernel<SPARSE=false>  dense GEMV baseline, same skeleton, 16-byte
-//       chunks of W (8 columns).
-//   generic_spmv_kernel          any N:M (M = 4 or 8) and K % 8 == 0: one mask
-//       byte per lane step, values read word by word.  Correct, not tuned.
-//   pack_check_kernel / pack_kernel   nm_pack's validation and packing passes.
-// Rows are owned by wavefronts; each row's partial sums are reduced across the
-// 64 lanes with DPP row permutes and four lane reads (fixed order, so results
-// are deterministic run to run).
+// Work unit: a 16-byte chunk of a row -- 8 weights (dense) or, at N/M = 1/2,
+// 8 kept values covering 16 dense columns with their 16 mask bits (2 bytes,
+// at the same chunk index in the mask row: fixed step, no index arrays).
+// Lanes stream chunks with 128-bit non-temporal loads; x sits in LDS.
+//   2:4  each mask nibble is one group: a 16-entry LDS table turns it into a
+//        byte-permute selector that gathers the group's two x halves next to
+//        each other, and one packed dot2 multiplies them with the group's two
+//        values (x-select).
+//   4:8  each mask byte is one group: a 256-entry LDS table gives four
+//        selectors that spread the group's four values over its eight dense
+//        columns, then four dot2 with contiguous x (value expansion).
+//   dense  four dot2 per chunk.
+// Products of two 16-bit floats are exact in fp32; sums are fp32; each row is
+// reduced across the 64 lanes with DPP row permutes and four lane reads in a
+// fixed order (deterministic), then rounded once to fp16/bf16.
+//
+// Kernel shapes (chosen per matrix shape on the host):
+//   rowslice_kernel  a wave owns one (row, K-slice) item and issues all of its
+//                    loads before anything else; many short-lived waves.
+//   stream_kernel    waves walk rows g, g+G, ... with the next group of loads
+//                    in flight while computing (long rows, few blocks).
+//   tiled_kernel     x staged in K-tiles when B*K*2 bytes exceed the LDS tile.
+//   generic_spmv_kernel  any N:M with M in {4, 8} and K % 8 == 0 (untuned).
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <mutex>
@@ -42,15 +51,26 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kBlock = 256;
-constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kUnroll = 4;                       // 16-byte chunks in flight per lane per row step
-constexpr int kXTileBudget = 56 * 1024;          // bytes of LDS for the staged x tile
+constexpr int kXTileBudget = 56 * 1024;   // LDS bytes for x in the row-slice / stream kernels
+constexpr int kTiledBlock = 256;
 
-// ---- arithmetic helpers --------------------------------------------------
+enum Fmt { kDense = 0, kNM24 = 1, kNM48 = 2 };
 
-// fp32 += a.lo * b.lo + a.hi * b.hi for two packed 16-bit pairs.  Products of
-// two 16-bit floats are exact in fp32.
+// 16-byte units of the selector table each format keeps in LDS.
+template <int F>
+constexpr int table_units()
+{
+    return F == kNM24 ? 4 : (F == kNM48 ? 256 : 0);
+}
+
+template <int F>
+constexpr int chunk_cols()
+{
+    return F == kDense ? 8 : 16;
+}
+
+// ---- arithmetic helpers ----------------------------------------------------
+
 template <int DT>
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c);
 
@@ -100,29 +120,43 @@ __device__ __forceinline__ float wave_sum(float v)
     v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
     v += dpp_mov<0x141>(v);   // row_half_mirror
     v += dpp_mov<0x140>(v);   // row_mirror
-    float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-    float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
     return (a + b) + (c + d);
 }
 
-// Byte-permute selectors that expand the four 16-bit values of one mask byte
-// (8 dense columns) into four dense dwords.  Value k (in column order) sits in
-// bytes 2k, 2k+1 of the 8-byte source {hi dword : lo dword}; an unkept column
-// gets selector 0x0C, which v_perm_b32 turns into a zero byte.  With more than
-// four bits set (a malformed mask) selectors run past 7 and produce junk
-// bytes, never an out-of-range access.
-__device__ u32x4 expand_selectors(uint32_t mb)
+// ---- selector tables ---------------------------------------------------------
+
+// 2:4.  Nibble n marks the kept columns j0 < j1 of a 4-column group whose x
+// halves sit in the 8-byte source {x23 : x01} (half j in bytes 2j, 2j+1).  The
+// selector moves x[j0] to the low half and x[j1] to the high half, matching
+// the order of the group's two stored values.  Nibbles without exactly two
+// bits are malformed; their selector yields zeros (0x0C = zero byte).
+__device__ uint32_t select24(uint32_t n)
+{
+    if (__builtin_popcount(n) != 2)
+        return 0x0C0C0C0Cu;
+    const uint32_t j0 = __builtin_ctz(n);
+    const uint32_t j1 = 31 - __builtin_clz(n);
+    return (2 * j0) | ((2 * j0 + 1) << 8) | ((2 * j1) << 16) | ((2 * j1 + 1) << 24);
+}
+
+// 4:8.  Byte m marks the kept columns of an 8-column group; its four values
+// (in column order) sit in bytes 2k, 2k+1 of {hi dword : lo dword}.  Dense
+// dword d (columns 2d, 2d+1) gets selector bytes that copy value k into the
+// kept column and zero bytes (0x0C) elsewhere.  With more than four bits set
+// the selectors run past 7 and give junk bytes, never an out-of-range access.
+__device__ u32x4 select48(uint32_t m)
 {
     uint32_t s[4];
     uint32_t k = 0;
     for (int d = 0; d < 4; ++d) {
         uint32_t sel = 0;
         for (int h = 0; h < 2; ++h) {
-            int j = 2 * d + h;
             uint32_t pair = 0x0C0Cu;
-            if ((mb >> j) & 1u) {
+            if ((m >> (2 * d + h)) & 1u) {
                 pair = (2 * k) | ((2 * k + 1) << 8);
                 ++k;
             }
@@ -133,145 +167,379 @@ __device__ u32x4 expand_selectors(uint32_t mb)
     return u32x4{s[0], s[1], s[2], s[3]};
 }
 
-// ---- row-dot kernels (sparse N/M = 1/2 and dense) -------------------------
+template <int F>
+__device__ __forceinline__ void build_table(u32x4* tab)
+{
+    if constexpr (F == kNM24) {
+        if (threadIdx.x < 4)
+            tab[threadIdx.x] = u32x4{select24(4 * threadIdx.x), select24(4 * threadIdx.x + 1),
+                                     select24(4 * threadIdx.x + 2), select24(4 * threadIdx.x + 3)};
+    } else if constexpr (F == kNM48) {
+        for (unsigned i = threadIdx.x; i < 256; i += blockDim.x)
+            tab[i] = select48(i);
+    }
+}
 
-// One block owns rows [blockIdx.x * rows_per_block, +rows_per_block); its
-// waves take those rows round-robin.  x is staged into LDS in tiles of
-// tile_cols columns (one tile when B*K*2 bytes fit); with several tiles the
-// per-row partial sums wait in LDS between tiles.
-template <bool SPARSE, int DT, int NB>
-__global__ __launch_bounds__(kBlock) void rowdot_kernel(const u32x4* __restrict__ w4, const uint16_t* __restrict__ m2,
-                                                        const u32x4* __restrict__ x4, uint16_t* __restrict__ y, int R,
-                                                        int K, int rows_per_block, int tile_cols)
+// x in LDS: [NB][bstride] 16-byte units.  Sparse formats split each 32-byte
+// column range of a chunk into two planes (first 16 bytes at unit c, second
+// at unit bstride/2 + c) so that lanes reading consecutive chunks touch
+// consecutive LDS addresses.  `cols` columns starting at global column c0 are
+// staged from x [NB][K].
+template <int F, int NB>
+__device__ __forceinline__ void stage_x(u32x4* xs, const u32x4* __restrict__ x4, int K, int c0, int cols, int bstride)
+{
+    const int q = cols / 8;
+    for (int i = threadIdx.x; i < NB * q; i += blockDim.x) {
+        const int b = i / q, j = i - b * q;
+        const u32x4 val = x4[(size_t)b * (K / 8) + c0 / 8 + j];
+        if constexpr (F == kDense)
+            xs[b * bstride + j] = val;
+        else
+            xs[b * bstride + (j & 1) * (bstride / 2) + (j >> 1)] = val;
+    }
+}
+
+// ---- one 16-byte chunk -------------------------------------------------------
+
+// acc[b] += (chunk . x[b][chunk columns]).  xs: staged x, c: the chunk's index
+// within the staged columns, bstride: units per batch row.
+template <int F, int DT, int NB>
+__device__ __forceinline__ void chunk_dot(const u32x4 v, const uint32_t mk, const u32x4* __restrict__ tab,
+                                          const u32x4* __restrict__ xs, const int c, const int bstride, float* acc)
+{
+    if constexpr (F == kDense) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const u32x4 xa = xs[b * bstride + c];
+            float a = acc[b];
+            a = dot2<DT>(v.x, xa.x, a);
+            a = dot2<DT>(v.y, xa.y, a);
+            a = dot2<DT>(v.z, xa.z, a);
+            a = dot2<DT>(v.w, xa.w, a);
+            acc[b] = a;
+        }
+    } else if constexpr (F == kNM24) {
+        const uint32_t* t = reinterpret_cast<const uint32_t*>(tab);
+        const uint32_t s0 = t[mk & 0xF], s1 = t[(mk >> 4) & 0xF], s2 = t[(mk >> 8) & 0xF], s3 = t[(mk >> 12) & 0xF];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const u32x4 xa = xs[b * bstride + c];
+            const u32x4 xb = xs[b * bstride + bstride / 2 + c];
+            float a = acc[b];
+            a = dot2<DT>(v.x, __builtin_amdgcn_perm(xa.y, xa.x, s0), a);
+            a = dot2<DT>(v.y, __builtin_amdgcn_perm(xa.w, xa.z, s1), a);
+            a = dot2<DT>(v.z, __builtin_amdgcn_perm(xb.y, xb.x, s2), a);
+            a = dot2<DT>(v.w, __builtin_amdgcn_perm(xb.w, xb.z, s3), a);
+            acc[b] = a;
+        }
+    } else {
+        const u32x4 s0 = tab[mk & 0xFF];
+        const u32x4 s1 = tab[(mk >> 8) & 0xFF];
+        uint32_t w[8];
+        w[0] = __builtin_amdgcn_perm(v.y, v.x, s0.x);
+        w[1] = __builtin_amdgcn_perm(v.y, v.x, s0.y);
+        w[2] = __builtin_amdgcn_perm(v.y, v.x, s0.z);
+        w[3] = __builtin_amdgcn_perm(v.y, v.x, s0.w);
+        w[4] = __builtin_amdgcn_perm(v.w, v.z, s1.x);
+        w[5] = __builtin_amdgcn_perm(v.w, v.z, s1.y);
+        w[6] = __builtin_amdgcn_perm(v.w, v.z, s1.z);
+        w[7] = __builtin_amdgcn_perm(v.w, v.z, s1.w);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const u32x4 xa = xs[b * bstride + c];
+            const u32x4 xb = xs[b * bstride + bstride / 2 + c];
+            float a = acc[b];
+            a = dot2<DT>(w[0], xa.x, a);
+            a = dot2<DT>(w[1], xa.y, a);
+            a = dot2<DT>(w[2], xa.z, a);
+            a = dot2<DT>(w[3], xa.w, a);
+            a = dot2<DT>(w[4], xb.x, a);
+            a = dot2<DT>(w[5], xb.y, a);
+            a = dot2<DT>(w[6], xb.z, a);
+            a = dot2<DT>(w[7], xb.w, a);
+            acc[b] = a;
+        }
+    }
+}
+
+// Up to kMaxParts matrices with the same K (and format) multiplied by the
+// same x in one launch, their rows concatenated: part p owns rows
+// [begin[p], begin[p+1]) of the launch.  A single matrix is one part.
+constexpr int kMaxParts = 4;
+
+struct Parts {
+    const u32x4* w[kMaxParts];
+    const uint16_t* m[kMaxParts];
+    uint16_t* y[kMaxParts];
+    int begin[kMaxParts + 1];
+    int count;
+};
+
+struct RowRef {
+    const u32x4* w;      // the row's chunks
+    const uint16_t* m;   // the row's mask words (sparse)
+    uint16_t* y;         // y[0][row] of its part; batch b at y + b * R
+    int R;               // rows of its part
+};
+
+__device__ __forceinline__ RowRef locate(const Parts& P, int r, int C)
+{
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxParts; ++i)
+        if (i < P.count && r >= P.begin[i])
+            p = i;
+    const int rl = r - P.begin[p];
+    RowRef o;
+    o.w = P.w[p] + (size_t)rl * C;
+    o.m = P.m[p] + (size_t)rl * C;
+    o.y = P.y[p] + rl;
+    o.R = P.begin[p + 1] - P.begin[p];
+    return o;
+}
+
+// Loads chunks [c0 + lane + 64 u] (u < U, below cend) of a row.
+template <int F, int U>
+__device__ __forceinline__ void load_chunks(const u32x4* __restrict__ wrow, const uint16_t* __restrict__ mrow,
+                                            int c0, int cend, int lane, u32x4* v, uint32_t* mk)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = c0 + lane + u * kWave;
+        v[u] = u32x4{0, 0, 0, 0};
+        mk[u] = 0;
+        if (c < cend) {
+            v[u] = __builtin_nontemporal_load(wrow + c);
+            if constexpr (F != kDense)
+                mk[u] = __builtin_nontemporal_load(mrow + c);
+        }
+    }
+}
+
+// ---- row-slice kernel ------------------------------------------------------
+
+// A block holds rows_per_block rows x S K-slices, one wave per (row, slice).
+// A lane issues all of its chunk loads (at most CPL) first, then the block
+// stages the selector table and x in LDS, computes, reduces each wave across
+// lanes, and adds a row's S slice sums in slice order.
+template <int F, int DT, int NB, int CPL>
+__global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K, int S,
+                                                        int rows_per_block)
 {
     extern __shared__ u32x4 smem[];
-    constexpr int COLS = SPARSE ? 16 : 8;        // dense columns per 16-byte chunk
+    constexpr int COLS = chunk_cols<F>();
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    const int lr = wave / S, sl = wave - lr * S;
+    const int r = blockIdx.x * rows_per_block + lr;
+    const bool active = r < R;
+    const int C = K / COLS;
+    const int cps = (C + S - 1) / S;
+    const int cbeg = sl * cps, cend = active ? min(C, cbeg + cps) : cbeg;
+    const RowRef row = locate(P, active ? r : 0, C);
+
+    u32x4 v[CPL];
+    uint32_t mk[CPL];
+    load_chunks<F, CPL>(row.w, row.m, cbeg, cend, lane, v, mk);
+
+    u32x4* tab = smem;
+    u32x4* xs = smem + table_units<F>();
+    const int bstride = K / 8;
+    float* part = reinterpret_cast<float*>(xs + NB * bstride);
+    build_table<F>(tab);
+    stage_x<F, NB>(xs, x4, K, 0, K, bstride);
+    __syncthreads();
+
+    float acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        acc[b] = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+        const int c = cbeg + lane + u * kWave;
+        if (c < cend)
+            chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, c, bstride, acc);
+    }
+    float sum[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        sum[b] = wave_sum(acc[b]);
+    if (S == 1) {
+        if (active && lane == 0)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                row.y[(size_t)b * row.R] = from_f32<DT>(sum[b]);
+        return;
+    }
+    if (lane == 0)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            part[wave * NB + b] = sum[b];
+    __syncthreads();
+    if (active && sl == 0 && lane == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float t = part[wave * NB + b];
+            for (int j = 1; j < S; ++j)
+                t += part[(wave + j) * NB + b];
+            row.y[(size_t)b * row.R] = from_f32<DT>(t);
+        }
+    }
+}
+
+// ---- streaming kernel --------------------------------------------------------
+
+// Wave g of G handles rows g, g + G, g + 2G, ..., so at any moment the grid
+// reads one compact band of rows (DRAM-page friendly).  A row is cut into
+// groups of U chunks per lane; the wave walks its (row, group) sequence with
+// the next group's loads in flight while it multiplies the current one (two
+// register buffers), and reduces and stores a row after its last group.
+template <int F, int DT, int NB, int U>
+__global__ __launch_bounds__(512) void stream_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K)
+{
+    extern __shared__ u32x4 smem[];
+    constexpr int COLS = chunk_cols<F>();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nw = blockDim.x / kWave;
+    const int g = blockIdx.x * nw + threadIdx.x / kWave;
+    const int G = gridDim.x * nw;
+    const int C = K / COLS;
+    const int gpr = (C + kWave * U - 1) / (kWave * U);
+    const int nrows = g < R ? (R - g + G - 1) / G : 0;
+    const int ng = nrows * gpr;
+
+    u32x4 va[U], vb[U];
+    uint32_t ma[U], mb[U];
+    if (ng > 0) {
+        const RowRef row = locate(P, g, C);
+        load_chunks<F, U>(row.w, row.m, 0, C, lane, va, ma);
+    }
+
+    u32x4* tab = smem;
+    u32x4* xs = smem + table_units<F>();
+    const int bstride = K / 8;
+    build_table<F>(tab);
+    stage_x<F, NB>(xs, x4, K, 0, K, bstride);
+    __syncthreads();
+
+    float acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        acc[b] = 0.f;
+
+    auto consume = [&](int j, const u32x4* v, const uint32_t* mk) {
+        const int t = j / gpr, q = j - t * gpr;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = q * kWave * U + lane + u * kWave;
+            if (c < C)
+                chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, c, bstride, acc);
+        }
+        if (q == gpr - 1) {
+            const RowRef row = locate(P, g + t * G, C);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const float sum = wave_sum(acc[b]);
+                if (lane == 0)
+                    row.y[(size_t)b * row.R] = from_f32<DT>(sum);
+                acc[b] = 0.f;
+            }
+        }
+    };
+    auto fetch = [&](int j, u32x4* v, uint32_t* mk) {
+        const int t = j / gpr, q = j - t * gpr;
+        const RowRef row = locate(P, g + t * G, C);
+        load_chunks<F, U>(row.w, row.m, q * kWave * U, C, lane, v, mk);
+    };
+
+    for (int j = 0; j < ng; j += 2) {
+        if (j + 1 < ng)
+            fetch(j + 1, vb, mb);
+        consume(j, va, ma);
+        if (j + 1 < ng) {
+            if (j + 2 < ng)
+                fetch(j + 2, va, ma);
+            consume(j + 1, vb, mb);
+        }
+    }
+}
+
+// ---- tiled kernel (x larger than one LDS tile) --------------------------------
+
+// One block owns rows_per_block consecutive rows, taken by its waves
+// round-robin.  x is staged in tiles of tile_cols columns; per-row partial
+// sums wait in LDS between tiles.
+template <int F, int DT, int NB>
+__global__ __launch_bounds__(kTiledBlock) void tiled_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
+                                                            int rows_per_block, int tile_cols)
+{
+    extern __shared__ u32x4 smem[];
+    constexpr int COLS = chunk_cols<F>();
+    constexpr int U = 4;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = kTiledBlock / kWave;
     const int r0 = blockIdx.x * rows_per_block;
     const int r1 = min(R, r0 + rows_per_block);
-    const int tq = tile_cols / 8;                // 16-byte x chunks per batch row of the tile
-    u32x4* lut = smem;
-    u32x4* xs = smem + (SPARSE ? 256 : 0);
-    float* part = reinterpret_cast<float*>(xs + NB * tq);
-    const bool multi = tile_cols < K;
-    const int cpr = K / COLS;
+    const int bstride = tile_cols / 8;
+    u32x4* tab = smem;
+    u32x4* xs = smem + table_units<F>();
+    float* part = reinterpret_cast<float*>(xs + NB * bstride);
+    const int C = K / COLS;
 
-    if constexpr (SPARSE)
-        lut[threadIdx.x] = expand_selectors(threadIdx.x);
-    if (multi)
-        for (int i = threadIdx.x; i < rows_per_block * NB; i += kBlock)
-            part[i] = 0.f;
+    build_table<F>(tab);
+    for (int i = threadIdx.x; i < rows_per_block * NB; i += kTiledBlock)
+        part[i] = 0.f;
 
     for (int t0 = 0; t0 < K; t0 += tile_cols) {
         const int tc = min(tile_cols, K - t0);
         __syncthreads();
-        const int q = tc / 8;
-        for (int i = threadIdx.x; i < NB * q; i += kBlock) {
-            int b = i / q, j = i - b * q;
-            xs[b * tq + j] = x4[(size_t)b * (K / 8) + t0 / 8 + j];
-        }
+        stage_x<F, NB>(xs, x4, K, t0, tc, bstride);
         __syncthreads();
         const int cb = t0 / COLS, ce = (t0 + tc) / COLS;
-        for (int r = r0 + wave; r < r1; r += kWavesPerBlock) {
+        for (int r = r0 + wave; r < r1; r += nw) {
+            const RowRef row = locate(P, r, C);
             float acc[NB];
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 acc[b] = 0.f;
-            const u32x4* wrow = w4 + (size_t)r * cpr;
-            const uint16_t* mrow = m2 + (size_t)r * cpr;
-            for (int c0 = cb; c0 < ce; c0 += kWave * kUnroll) {
-                u32x4 v[kUnroll];
-                uint32_t mk[kUnroll];
+            for (int c0 = cb; c0 < ce; c0 += kWave * U) {
+                u32x4 v[U];
+                uint32_t mk[U];
+                load_chunks<F, U>(row.w, row.m, c0, ce, lane, v, mk);
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int c = c0 + u * kWave + lane;
-                    v[u] = u32x4{0, 0, 0, 0};
-                    mk[u] = 0;
-                    if (c < ce) {
-                        v[u] = __builtin_nontemporal_load(wrow + c);
-                        if constexpr (SPARSE)
-                            mk[u] = __builtin_nontemporal_load(mrow + c);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int c = c0 + u * kWave + lane;
-                    if (c >= ce)
-                        continue;
-                    const int xi = (c * COLS - t0) / 8;      // first 16-byte x chunk of this column range
-                    if constexpr (SPARSE) {
-                        const u32x4 s0 = lut[mk[u] & 0xFF];
-                        const u32x4 s1 = lut[mk[u] >> 8];
-                        uint32_t w[8];
-                        w[0] = __builtin_amdgcn_perm(v[u].y, v[u].x, s0.x);
-                        w[1] = __builtin_amdgcn_perm(v[u].y, v[u].x, s0.y);
-                        w[2] = __builtin_amdgcn_perm(v[u].y, v[u].x, s0.z);
-                        w[3] = __builtin_amdgcn_perm(v[u].y, v[u].x, s0.w);
-                        w[4] = __builtin_amdgcn_perm(v[u].w, v[u].z, s1.x);
-                        w[5] = __builtin_amdgcn_perm(v[u].w, v[u].z, s1.y);
-                        w[6] = __builtin_amdgcn_perm(v[u].w, v[u].z, s1.z);
-                        w[7] = __builtin_amdgcn_perm(v[u].w, v[u].z, s1.w);
-#pragma unroll
-                        for (int b = 0; b < NB; ++b) {
-                            const u32x4 xa = xs[b * tq + xi];
-                            const u32x4 xb = xs[b * tq + xi + 1];
-                            float a = acc[b];
-                            a = dot2<DT>(w[0], xa.x, a);
-                            a = dot2<DT>(w[1], xa.y, a);
-                            a = dot2<DT>(w[2], xa.z, a);
-                            a = dot2<DT>(w[3], xa.w, a);
-                            a = dot2<DT>(w[4], xb.x, a);
-                            a = dot2<DT>(w[5], xb.y, a);
-                            a = dot2<DT>(w[6], xb.z, a);
-                            a = dot2<DT>(w[7], xb.w, a);
-                            acc[b] = a;
-                        }
-                    } else {
-#pragma unroll
-                        for (int b = 0; b < NB; ++b) {
-                            const u32x4 xa = xs[b * tq + xi];
-                            float a = acc[b];
-                            a = dot2<DT>(v[u].x, xa.x, a);
-                            a = dot2<DT>(v[u].y, xa.y, a);
-                            a = dot2<DT>(v[u].z, xa.z, a);
-                            a = dot2<DT>(v[u].w, xa.w, a);
-                            acc[b] = a;
-                        }
-                    }
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + lane + u * kWave;
+                    if (c < ce)
+                        chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, c - cb, bstride, acc);
                 }
             }
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const float s = wave_sum(acc[b]);
-                if (lane == 0) {
-                    if (multi)
-                        part[(r - r0) * NB + b] += s;
-                    else
-                        y[(size_t)b * R + r] = from_f32<DT>(s);
-                }
+                if (lane == 0)
+                    part[(r - r0) * NB + b] += s;
             }
         }
     }
-    if (multi) {
-        __syncthreads();
-        for (int i = threadIdx.x; i < (r1 - r0) * NB; i += kBlock) {
-            const int row = i / NB, b = i - row * NB;
-            y[(size_t)b * R + r0 + row] = from_f32<DT>(part[i]);
-        }
+    __syncthreads();
+    for (int i = threadIdx.x; i < (r1 - r0) * NB; i += kTiledBlock) {
+        const int lr = i / NB, b = i - lr * NB;
+        const RowRef row = locate(P, r0 + lr, C);
+        row.y[(size_t)b * row.R] = from_f32<DT>(part[i]);
     }
 }
 
-// ---- generic N:M (any N < M, M in {4, 8}, K % 8 == 0) --------------------
+// ---- generic N:M (any N < M, M in {4, 8}, K % 8 == 0) --------------------------
 
 template <int DT, int NB>
-__global__ __launch_bounds__(kBlock) void generic_spmv_kernel(const uint16_t* __restrict__ values,
-                                                              const uint8_t* __restrict__ masks,
-                                                              const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-                                                              int R, int K, int N, int M)
+__global__ __launch_bounds__(256) void generic_spmv_kernel(const uint16_t* __restrict__ values,
+                                                           const uint8_t* __restrict__ masks,
+                                                           const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+                                                           int R, int K, int N, int M)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int row = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (row >= R)                                // whole wave leaves together
         return;
     const int vpb = 8 / M * N;                   // values per mask byte (fixed step)
@@ -309,23 +577,23 @@ __global__ void fill_zero_kernel(uint16_t* __restrict__ y, int64_t n)
         y[i] = 0;
 }
 
-// ---- pack -------------------------------------------------------------------
+// ---- pack ---------------------------------------------------------------------
 
 constexpr uint32_t kStatusBadMask = 1u << 0;
 constexpr uint32_t kStatusNaN = 1u << 1;
 
-// One thread per (row, mask byte): 8 columns, two 4-groups or one 8-group.
 template <int DT>
 __device__ __forceinline__ uint32_t inf_code()
 {
     return DT == NM_FP16 ? 0x7C00u : 0x7F80u;
 }
 
+// One thread per (row, mask byte) = 8 columns: two 4-groups or one 8-group.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void pack_check_kernel(const u32x4* __restrict__ W, const uint8_t* __restrict__ keep,
-                                                            int64_t nbytes, int N, int M, uint32_t* __restrict__ status)
+__global__ __launch_bounds__(256) void pack_check_kernel(const u32x4* __restrict__ W, const uint8_t* __restrict__ keep,
+                                                         int64_t nbytes, int N, int M, uint32_t* __restrict__ status)
 {
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nbytes)
         return;
     uint32_t bad = 0;
@@ -341,21 +609,20 @@ __global__ __launch_bounds__(kBlock) void pack_check_kernel(const u32x4* __restr
     } else {
         const u32x4 w = W[i];
         const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-        for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < 4; ++d)
             if ((words[d] & 0x7FFFu) > inf_code<DT>() || ((words[d] >> 16) & 0x7FFFu) > inf_code<DT>())
                 bad |= kStatusNaN;
-        }
     }
     if (bad)
         atomicOr(status, bad);
 }
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void pack_kernel(const u32x4* __restrict__ W, const uint8_t* __restrict__ keep,
-                                                      int64_t nbytes, int N, int M, uint16_t* __restrict__ values,
-                                                      uint8_t* __restrict__ masks)
+__global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, const uint8_t* __restrict__ keep,
+                                                   int64_t nbytes, int N, int M, uint16_t* __restrict__ values,
+                                                   uint8_t* __restrict__ masks)
 {
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nbytes)
         return;
     const u32x4 wv = W[i];
@@ -387,21 +654,166 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(const u32x4* __restrict__ 
     uint16_t* out = values + i * vpb;            // rows are whole bytes, so i * vpb is the fixed-step offset
     int k = 0;
     for (int j = 0; j < 8; ++j)
-        if (((kb >> j) & 1u) && k < vpb)           // the check pass guarantees k < vpb; the guard keeps writes in bounds regardless
+        if (((kb >> j) & 1u) && k < vpb)         // the check pass guarantees k < vpb; the guard keeps writes in bounds
             out[k++] = w[j];
     masks[i] = (uint8_t)kb;
 }
 
-// ---- host side --------------------------------------------------------------
+// ---- host: launch planning -------------------------------------------------------
 
-int g_rows_per_block_sparse = 0;   // 0 = built-in heuristic; NMSPMV_ROWS_PER_BLOCK overrides
+// Launch-shape overrides, read once, for tuning sweeps (0 = built-in choice):
+// NMSPMV_KERNEL 1 = row-slice, 2 = tiled, 3 = stream; NMSPMV_SLICES,
+// NMSPMV_ROWS_PER_BLOCK (row-slice); NMSPMV_BLOCKS, NMSPMV_THREADS (stream).
+struct Env {
+    int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0;
+};
+Env g_env;
 std::once_flag g_env_once;
 
 void read_env()
 {
-    if (const char* s = std::getenv("NMSPMV_ROWS_PER_BLOCK"))
-        g_rows_per_block_sparse = std::atoi(s);
+    auto get = [](const char* name) {
+        const char* e = std::getenv(name);
+        return e ? std::atoi(e) : 0;
+    };
+    g_env.kernel = get("NMSPMV_KERNEL");
+    g_env.slices = get("NMSPMV_SLICES");
+    g_env.rpb = get("NMSPMV_ROWS_PER_BLOCK");
+    g_env.blocks = get("NMSPMV_BLOCKS");
+    g_env.threads = get("NMSPMV_THREADS");
 }
+
+int g_cu_count[64] = {};
+
+int cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!g_cu_count[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        g_cu_count[dev] = n;
+    }
+    return g_cu_count[dev];
+}
+
+struct Plan {
+    int kind = 0;            // 1 row-slice, 2 tiled, 3 stream
+    int S = 1, rpb = 1, cpl = 1, threads = 256, tile_cols = 0;
+    size_t lds = 0;
+    unsigned grid = 1;
+};
+
+// Row-slice: S slices per row keep each lane at <= 8 chunks (all loads in
+// flight at once), and rows longer than 256 chunks get at least two slices
+// (measured faster at 512-1024 chunks); more slices while the matrix has
+// fewer than ~16 waves per CU of rows; rows per block fill at most 8 waves
+// and leave at least two blocks per CU.
+bool plan_rowslice(int64_t R, int64_t C, Plan* P)
+{
+    const int cus = cu_count();
+    int S = C > 4 * kWave ? 2 : 1;
+    while (S < 16 && (C + S - 1) / S > 8 * kWave)
+        S *= 2;
+    while (S < 16 && R * S < 16LL * cus && (C + 2 * S - 1) / (2 * S) >= kWave)
+        S *= 2;
+    if (g_env.slices > 0)
+        S = g_env.slices;
+    const int64_t cps = (C + S - 1) / S;
+    int cpl = 1;
+    while ((int64_t)cpl * kWave < cps)
+        cpl *= 2;
+    if (cpl > 8)
+        return false;
+    int rpb = std::max(1, 8 / S);
+    while (rpb > 1 && (R + rpb - 1) / rpb < 2 * cus)
+        rpb /= 2;
+    if (g_env.rpb > 0)
+        rpb = g_env.rpb;
+    if (rpb * S > 16)
+        return false;
+    P->kind = 1;
+    P->S = S;
+    P->rpb = rpb;
+    P->cpl = cpl;
+    P->threads = rpb * S * kWave;
+    P->grid = (unsigned)((R + rpb - 1) / rpb);
+    return true;
+}
+
+// Chooses the kernel for a matrix shape.  Rows of up to 1024 chunks (2048
+// for dense rows) go to the row-slice kernel; longer rows to the stream
+// kernel, whose few blocks stage x once for many rows; x larger than the LDS
+// budget to the tiled one.  (Thresholds from timing sweeps on MI355X.)
+template <int F>
+Plan plan_for(int64_t R, int64_t K, int B)
+{
+    std::call_once(g_env_once, read_env);
+    constexpr int COLS = chunk_cols<F>();
+    const int64_t C = K / COLS;
+    const size_t tab = (size_t)table_units<F>() * sizeof(u32x4);
+    const size_t xbytes = (size_t)B * (size_t)K * 2;
+    Plan P;
+    const bool fits = xbytes <= (size_t)kXTileBudget;
+    int kind = g_env.kernel;
+    if (kind == 0)
+        kind = !fits ? 2 : (C <= (F == kDense ? 32 : 16) * kWave ? 1 : 3);
+    if (kind == 1 && fits && plan_rowslice(R, C, &P)) {
+        P.lds = tab + xbytes + (P.S > 1 ? (size_t)P.rpb * P.S * B * 4 : 0);
+        return P;
+    }
+    if ((kind == 3 || kind == 1) && fits) {
+        const int cus = cu_count();
+        P.kind = 3;
+        P.threads = (g_env.threads > 0 && g_env.threads <= 512 && g_env.threads % kWave == 0) ? g_env.threads : 512;
+        int64_t blocks = g_env.blocks > 0 ? g_env.blocks : 2LL * cus;
+        const int nw = P.threads / kWave;
+        while (blocks > 1 && (blocks - 1) * nw >= R)
+            --blocks;
+        P.grid = (unsigned)blocks;
+        P.lds = tab + xbytes;
+        return P;
+    }
+    P.kind = 2;
+    P.threads = kTiledBlock;
+    int64_t tile = ((int64_t)kXTileBudget / (2 * B)) / 1024 * 1024;
+    if (tile >= K)
+        tile = K;
+    P.tile_cols = (int)tile;
+    P.rpb = 16;
+    P.lds = tab + (size_t)B * (size_t)tile * 2 + (size_t)P.rpb * B * 4;
+    P.grid = (unsigned)((R + P.rpb - 1) / P.rpb);
+    return P;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
+
+// Launches the chosen kernel over the concatenated rows of `parts` (R in total).
+template <int F, int DT, int NB>
+int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
+{
+    const Plan P = plan_for<F>(R, K, NB);
+    const u32x4* x4 = static_cast<const u32x4*>(x);
+    (void)hipGetLastError();
+    if (P.kind == 1) {
+        switch (P.cpl) {
+        case 1: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 1>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
+        case 2: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 2>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
+        case 4: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 4>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
+        default: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 8>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
+        }
+    } else if (P.kind == 3) {
+        hipLaunchKernelGGL((stream_kernel<F, DT, NB, 4>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K);
+    } else {
+        hipLaunchKernelGGL((tiled_kernel<F, DT, NB>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.rpb,
+                           P.tile_cols);
+    }
+    return hip_status(hipGetLastError());
+}
+
+// ---- host: argument rules ------------------------------------------------------
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -409,7 +821,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 {
     if (na == 0 || nb == 0)
         return false;
-    uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
@@ -437,99 +849,54 @@ int check_nm(int64_t K, int N, int M)
     return NM_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
-
 int launch_zero(void* y, int64_t n, hipStream_t s)
 {
     if (n == 0)
         return NM_OK;
     (void)hipGetLastError();
-    const int64_t blocks = (n + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, (uint16_t*)y, n);
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint16_t*)y, n);
     return hip_status(hipGetLastError());
 }
 
-struct RowdotLaunch {
-    int rows_per_block;
-    int tile_cols;
-    size_t lds_bytes;
-    unsigned grid;
-};
+// ---- host: dtype x batch dispatch ------------------------------------------------
 
-RowdotLaunch plan_rowdot(bool sparse, int64_t R, int64_t K, int B)
-{
-    std::call_once(g_env_once, read_env);
-    RowdotLaunch L;
-    // x tile: all of K when it fits, else the largest multiple of 1024 columns.
-    int64_t tile = K;
-    if ((int64_t)B * K * 2 > kXTileBudget)
-        tile = ((int64_t)kXTileBudget / (2 * B)) / 1024 * 1024;
-    L.tile_cols = (int)tile;
-    int rpb = sparse ? g_rows_per_block_sparse : 0;
-    if (rpb <= 0)
-        rpb = 16;
-    L.rows_per_block = rpb;
-    const bool multi = tile < K;
-    L.lds_bytes = (sparse ? 256 * sizeof(u32x4) : 0) + (size_t)B * tile * 2 + (multi ? (size_t)rpb * B * 4 : 0);
-    L.grid = (unsigned)((R + rpb - 1) / rpb);
-    return L;
-}
-
-template <bool SPARSE, int DT, int NB>
-int launch_rowdot(const void* w, const void* m, const void* x, void* y, int R, int K, hipStream_t s)
-{
-    const RowdotLaunch L = plan_rowdot(SPARSE, R, K, NB);
-    (void)hipGetLastError();
-    hipLaunchKernelGGL((rowdot_kernel<SPARSE, DT, NB>), dim3(L.grid), dim3(kBlock), L.lds_bytes, s,
-                       (const u32x4*)w, (const uint16_t*)m, (const u32x4*)x, (uint16_t*)y, R, K, L.rows_per_block,
-                       L.tile_cols);
-    return hip_status(hipGetLastError());
-}
-
-template <int DT, int NB>
-int launch_generic(const void* v, const uint8_t* m, const void* x, void* y, int R, int K, int N, int M, hipStream_t s)
-{
-    (void)hipGetLastError();
-    const unsigned grid = (unsigned)((R + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((generic_spmv_kernel<DT, NB>), dim3(grid), dim3(kBlock), 0, s, (const uint16_t*)v, m,
-                       (const uint16_t*)x, (uint16_t*)y, R, K, N, M);
-    return hip_status(hipGetLastError());
-}
-
-template <template <int, int> class F, typename... A>
+template <template <int, int> class Fn, typename... A>
 int dispatch(int dtype, int B, A... a)
 {
-    if (dtype == NM_FP16) {
-        switch (B) {
-        case 1: return F<NM_FP16, 1>::run(a...);
-        case 2: return F<NM_FP16, 2>::run(a...);
-        case 3: return F<NM_FP16, 3>::run(a...);
-        case 4: return F<NM_FP16, 4>::run(a...);
-        case 5: return F<NM_FP16, 5>::run(a...);
-        case 6: return F<NM_FP16, 6>::run(a...);
-        case 7: return F<NM_FP16, 7>::run(a...);
-        case 8: return F<NM_FP16, 8>::run(a...);
-        }
-    } else {
-        switch (B) {
-        case 1: return F<NM_BF16, 1>::run(a...);
-        case 2: return F<NM_BF16, 2>::run(a...);
-        case 3: return F<NM_BF16, 3>::run(a...);
-        case 4: return F<NM_BF16, 4>::run(a...);
-        case 5: return F<NM_BF16, 5>::run(a...);
-        case 6: return F<NM_BF16, 6>::run(a...);
-        case 7: return F<NM_BF16, 7>::run(a...);
-        case 8: return F<NM_BF16, 8>::run(a...);
-        }
+#define NM_CASES(DT)                            \
+    switch (B) {                                \
+    case 1: return Fn<DT, 1>::run(a...);        \
+    case 2: return Fn<DT, 2>::run(a...);        \
+    case 3: return Fn<DT, 3>::run(a...);        \
+    case 4: return Fn<DT, 4>::run(a...);        \
+    case 5: return Fn<DT, 5>::run(a...);        \
+    case 6: return Fn<DT, 6>::run(a...);        \
+    case 7: return Fn<DT, 7>::run(a...);        \
+    case 8: return Fn<DT, 8>::run(a...);        \
     }
+    if (dtype == NM_FP16) {
+        NM_CASES(NM_FP16)
+    } else {
+        NM_CASES(NM_BF16)
+    }
+#undef NM_CASES
     return NM_ERR_BAD_SHAPE;
 }
 
 template <int DT, int NB>
-struct SparseFast {
-    static int run(const void* v, const uint8_t* m, const void* x, void* y, int R, int K, hipStream_t s)
+struct Sparse24 {
+    static int run(const Parts* p, const void* x, int R, int K, hipStream_t s)
     {
-        return launch_rowdot<true, DT, NB>(v, m, x, y, R, K, s);
+        return launch_rows<kNM24, DT, NB>(*p, x, R, K, s);
+    }
+};
+
+template <int DT, int NB>
+struct Sparse48 {
+    static int run(const Parts* p, const void* x, int R, int K, hipStream_t s)
+    {
+        return launch_rows<kNM48, DT, NB>(*p, x, R, K, s);
     }
 };
 
@@ -537,15 +904,19 @@ template <int DT, int NB>
 struct SparseGeneric {
     static int run(const void* v, const uint8_t* m, const void* x, void* y, int R, int K, int N, int M, hipStream_t s)
     {
-        return launch_generic<DT, NB>(v, m, x, y, R, K, N, M, s);
+        (void)hipGetLastError();
+        const unsigned grid = (unsigned)((R + 3) / 4);
+        hipLaunchKernelGGL((generic_spmv_kernel<DT, NB>), dim3(grid), dim3(256), 0, s, (const uint16_t*)v, m,
+                           (const uint16_t*)x, (uint16_t*)y, R, K, N, M);
+        return hip_status(hipGetLastError());
     }
 };
 
 template <int DT, int NB>
 struct Dense {
-    static int run(const void* w, const void* x, void* y, int R, int K, hipStream_t s)
+    static int run(const Parts* p, const void* x, int R, int K, hipStream_t s)
     {
-        return launch_rowdot<false, DT, NB>(w, nullptr, x, y, R, K, s);
+        return launch_rows<kDense, DT, NB>(*p, x, R, K, s);
     }
 };
 
@@ -590,52 +961,149 @@ const char* nm_status_string(int status)
     }
 }
 
-int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int N, int M, int dtype, const void* x,
-            int B, void* y, void* stream)
+int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
+                  int N, int M, int dtype, const void* x, int B, void* const* y, void* stream)
 {
     int st = check_dtype(dtype);
     if (st != NM_OK)
         return st;
-    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
+    if (count < 1 || count > kMaxParts || !R)
+        return count < 1 || count > kMaxParts ? NM_ERR_BAD_SHAPE : NM_ERR_INVALID_ARG;
+    if ((st = check_rk(0, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
         return st;
     if (B < 1 || B > 8)
         return NM_ERR_BAD_SHAPE;
-    const size_t vbytes = (size_t)R * (size_t)(K / M * N) * 2, mbytes = (size_t)R * (size_t)(K / 8);
-    const size_t xbytes = (size_t)B * (size_t)K * 2, ybytes = (size_t)B * (size_t)R * 2;
-    if (!ptr_ok(values, vbytes, 16) || !ptr_ok(masks, mbytes, 16) || !ptr_ok(x, xbytes, 16) || !ptr_ok(y, ybytes, 2))
+    int64_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        if ((st = check_rk(R[i], K)) != NM_OK)
+            return st;
+        total += R[i];
+    }
+    if (total > INT32_MAX)
+        return NM_ERR_BAD_SHAPE;
+    if (!values || !masks || !y)
         return NM_ERR_INVALID_ARG;
-    if (overlaps(y, ybytes, values, vbytes) || overlaps(y, ybytes, masks, mbytes) || overlaps(y, ybytes, x, xbytes))
+    const size_t xbytes = (size_t)B * (size_t)K * 2;
+    if (!ptr_ok(x, xbytes, 16))
         return NM_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i) {
+        const size_t vb = (size_t)R[i] * (size_t)(K / M * N) * 2, mb = (size_t)R[i] * (size_t)(K / 8);
+        const size_t yb = (size_t)B * (size_t)R[i] * 2;
+        if (!ptr_ok(values[i], vb, 16) || !ptr_ok(masks[i], mb, 16) || !ptr_ok(y[i], yb, 2))
+            return NM_ERR_INVALID_ARG;
+        if (overlaps(y[i], yb, x, xbytes))
+            return NM_ERR_INVALID_ARG;
+        for (int j = 0; j < count; ++j) {
+            const size_t vbj = (size_t)R[j] * (size_t)(K / M * N) * 2, mbj = (size_t)R[j] * (size_t)(K / 8);
+            if (overlaps(y[i], yb, values[j], vbj) || overlaps(y[i], yb, masks[j], mbj) ||
+                (j != i && overlaps(y[i], yb, y[j], (size_t)B * (size_t)R[j] * 2)))
+                return NM_ERR_INVALID_ARG;
+        }
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (R == 0)
+    if (total == 0)
         return NM_OK;
-    if (K == 0)
-        return launch_zero(y, (int64_t)B * R, s);
-    if (2 * N == M && K % 16 == 0)
-        return dispatch<SparseFast>(dtype, B, values, masks, x, y, (int)R, (int)K, s);
-    return dispatch<SparseGeneric>(dtype, B, values, masks, x, y, (int)R, (int)K, N, M, s);
+    if (K == 0) {
+        for (int i = 0; i < count; ++i)
+            if ((st = launch_zero(y[i], (int64_t)B * R[i], s)) != NM_OK)
+                return st;
+        return NM_OK;
+    }
+    if (K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8))) {
+        Parts P = {};
+        P.begin[0] = 0;
+        for (int i = 0; i < count; ++i) {
+            if (R[i] == 0)
+                continue;
+            P.w[P.count] = static_cast<const u32x4*>(values[i]);
+            P.m[P.count] = reinterpret_cast<const uint16_t*>(masks[i]);
+            P.y[P.count] = static_cast<uint16_t*>(y[i]);
+            P.begin[P.count + 1] = P.begin[P.count] + (int)R[i];
+            ++P.count;
+        }
+        for (int i = P.count + 1; i <= kMaxParts; ++i)
+            P.begin[i] = P.begin[P.count];
+        return M == 4 ? dispatch<Sparse24>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s)
+                      : dispatch<Sparse48>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s);
+    }
+    for (int i = 0; i < count; ++i) {
+        if (R[i] == 0)
+            continue;
+        if ((st = dispatch<SparseGeneric>(dtype, B, values[i], masks[i], x, y[i], (int)R[i], (int)K, N, M, s)) != NM_OK)
+            return st;
+    }
+    return NM_OK;
+}
+
+int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int N, int M, int dtype, const void* x,
+            int B, void* y, void* stream)
+{
+    return nm_spmv_multi(1, &values, &masks, &R, K, N, M, dtype, x, B, &y, stream);
+}
+
+int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t K, int dtype, const void* x, int B,
+                        void* const* y, void* stream)
+{
+    int st = check_dtype(dtype);
+    if (st != NM_OK)
+        return st;
+    if (count < 1 || count > kMaxParts || !R)
+        return count < 1 || count > kMaxParts ? NM_ERR_BAD_SHAPE : NM_ERR_INVALID_ARG;
+    if ((st = check_rk(0, K)) != NM_OK)
+        return st;
+    if (B < 1 || B > 8)
+        return NM_ERR_BAD_SHAPE;
+    int64_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        if ((st = check_rk(R[i], K)) != NM_OK)
+            return st;
+        total += R[i];
+    }
+    if (total > INT32_MAX)
+        return NM_ERR_BAD_SHAPE;
+    if (!W || !y)
+        return NM_ERR_INVALID_ARG;
+    const size_t xbytes = (size_t)B * (size_t)K * 2;
+    if (!ptr_ok(x, xbytes, 16))
+        return NM_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i) {
+        const size_t wb = (size_t)R[i] * (size_t)K * 2, yb = (size_t)B * (size_t)R[i] * 2;
+        if (!ptr_ok(W[i], wb, 16) || !ptr_ok(y[i], yb, 2))
+            return NM_ERR_INVALID_ARG;
+        if (overlaps(y[i], yb, x, xbytes))
+            return NM_ERR_INVALID_ARG;
+        for (int j = 0; j < count; ++j)
+            if (overlaps(y[i], yb, W[j], (size_t)R[j] * (size_t)K * 2) ||
+                (j != i && overlaps(y[i], yb, y[j], (size_t)B * (size_t)R[j] * 2)))
+                return NM_ERR_INVALID_ARG;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (total == 0)
+        return NM_OK;
+    if (K == 0) {
+        for (int i = 0; i < count; ++i)
+            if ((st = launch_zero(y[i], (int64_t)B * R[i], s)) != NM_OK)
+                return st;
+        return NM_OK;
+    }
+    Parts P = {};
+    for (int i = 0; i < count; ++i) {
+        if (R[i] == 0)
+            continue;
+        P.w[P.count] = static_cast<const u32x4*>(W[i]);
+        P.m[P.count] = nullptr;
+        P.y[P.count] = static_cast<uint16_t*>(y[i]);
+        P.begin[P.count + 1] = P.begin[P.count] + (int)R[i];
+        ++P.count;
+    }
+    for (int i = P.count + 1; i <= kMaxParts; ++i)
+        P.begin[i] = P.begin[P.count];
+    return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s);
 }
 
 int nm_gemv_dense(const void* W, int64_t R, int64_t K, int dtype, const void* x, int B, void* y, void* stream)
 {
-    int st = check_dtype(dtype);
-    if (st != NM_OK)
-        return st;
-    if ((st = check_rk(R, K)) != NM_OK)
-        return st;
-    if (B < 1 || B > 8)
-        return NM_ERR_BAD_SHAPE;
-    const size_t wbytes = (size_t)R * (size_t)K * 2, xbytes = (size_t)B * (size_t)K * 2, ybytes = (size_t)B * (size_t)R * 2;
-    if (!ptr_ok(W, wbytes, 16) || !ptr_ok(x, xbytes, 16) || !ptr_ok(y, ybytes, 2))
-        return NM_ERR_INVALID_ARG;
-    if (overlaps(y, ybytes, W, wbytes) || overlaps(y, ybytes, x, xbytes))
-        return NM_ERR_INVALID_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (R == 0)
-        return NM_OK;
-    if (K == 0)
-        return launch_zero(y, (int64_t)B * R, s);
-    return dispatch<Dense>(dtype, B, W, x, y, (int)R, (int)K, s);
+    return nm_gemv_dense_multi(1, &W, &R, K, dtype, x, B, &y, stream);
 }
 
 int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int M, int dtype, void* values,
@@ -662,16 +1130,16 @@ int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int
     uint32_t* status = nullptr;
     if ((st = status_word(&status)) != NM_OK)
         return st;
-    const unsigned grid = (unsigned)((nbytes + kBlock - 1) / kBlock);
+    const unsigned grid = (unsigned)((nbytes + 255) / 256);
     (void)hipGetLastError();
     if (hipMemsetAsync(status, 0, sizeof(uint32_t), s) != hipSuccess)
         return NM_ERR_HIP;
     if (dtype == NM_FP16)
-        hipLaunchKernelGGL(pack_check_kernel<NM_FP16>, dim3(grid), dim3(kBlock), 0, s, (const u32x4*)W, keep, nbytes,
-                           N, M, status);
+        hipLaunchKernelGGL(pack_check_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
+                           status);
     else
-        hipLaunchKernelGGL(pack_check_kernel<NM_BF16>, dim3(grid), dim3(kBlock), 0, s, (const u32x4*)W, keep, nbytes,
-                           N, M, status);
+        hipLaunchKernelGGL(pack_check_kernel<NM_BF16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
+                           status);
     if (hipGetLastError() != hipSuccess)
         return NM_ERR_HIP;
     uint32_t host_status = 0;
@@ -683,10 +1151,10 @@ int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int
     if (host_status & kStatusNaN)
         return NM_ERR_NONFINITE;
     if (dtype == NM_FP16)
-        hipLaunchKernelGGL(pack_kernel<NM_FP16>, dim3(grid), dim3(kBlock), 0, s, (const u32x4*)W, keep, nbytes, N, M,
+        hipLaunchKernelGGL(pack_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
                            (uint16_t*)values, masks);
     else
-        hipLaunchKernelGGL(pack_kernel<NM_BF16>, dim3(grid), dim3(kBlock), 0, s, (const u32x4*)W, keep, nbytes, N, M,
+        hipLaunchKernelGGL(pack_kernel<NM_BF16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
                            (uint16_t*)values, masks);
     if (hipGetLastError() != hipSuccess)
         return NM_ERR_HIP;

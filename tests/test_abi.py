@@ -116,3 +116,47 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         L.lib()
+
+
+def _arr(T, vals):
+    return (T * len(vals))(*vals)
+
+
+def test_multi_rejects_bad_count_and_null_arrays():
+    lib = L.lib()
+    P = ctypes.c_void_p
+    v = _arr(P, [FAKE, FAKE + 0x1000])
+    m = _arr(P, [FAKE + 0x2000, FAKE + 0x3000])
+    R = _arr(ctypes.c_int64, [4, 4])
+    y = _arr(P, [FAKE2 + 0x100000, FAKE2 + 0x200000])
+    assert lib.nm_spmv_multi(0, v, m, R, 64, 2, 4, 0, FAKE2, 1, y, None) == L.NM_ERR_BAD_SHAPE
+    assert lib.nm_spmv_multi(5, v, m, R, 64, 2, 4, 0, FAKE2, 1, y, None) == L.NM_ERR_BAD_SHAPE
+    assert lib.nm_spmv_multi(2, None, m, R, 64, 2, 4, 0, FAKE2, 1, y, None) == L.NM_ERR_INVALID_ARG
+    assert lib.nm_spmv_multi(2, v, m, None, 64, 2, 4, 0, FAKE2, 1, y, None) == L.NM_ERR_INVALID_ARG
+    assert lib.nm_spmv_multi(2, v, m, R, 64, 2, 4, 0, FAKE2, 1, None, None) == L.NM_ERR_INVALID_ARG
+    assert lib.nm_spmv_multi(2, v, m, R, 60, 2, 4, 0, FAKE2, 1, y, None) == L.NM_ERR_BAD_SHAPE
+    assert lib.nm_spmv_multi(2, v, m, R, 64, 2, 4, 5, FAKE2, 1, y, None) == L.NM_ERR_UNSUPPORTED
+    # two outputs that overlap each other
+    y_bad = _arr(P, [FAKE2 + 0x100000, FAKE2 + 0x100004])
+    assert lib.nm_spmv_multi(2, v, m, R, 64, 2, 4, 0, FAKE2, 1, y_bad, None) == L.NM_ERR_INVALID_ARG
+    # an output over another part's values
+    y_bad = _arr(P, [FAKE2 + 0x100000, FAKE + 0x1000])
+    assert lib.nm_spmv_multi(2, v, m, R, 64, 2, 4, 0, FAKE2, 1, y_bad, None) == L.NM_ERR_INVALID_ARG
+    # all parts empty: nothing to do
+    R0 = _arr(ctypes.c_int64, [0, 0])
+    assert lib.nm_spmv_multi(2, v, m, R0, 64, 2, 4, 0, FAKE2, 1, y, None) == L.NM_OK
+    Rbig = _arr(ctypes.c_int64, [2 ** 30, 2 ** 30])
+    assert lib.nm_spmv_multi(2, v, m, Rbig, 64, 2, 4, 0, FAKE2, 1, y, None) == L.NM_ERR_BAD_SHAPE
+
+
+def test_dense_multi_rejects_bad_arguments():
+    lib = L.lib()
+    P = ctypes.c_void_p
+    W = _arr(P, [FAKE, FAKE + 0x10000])
+    R = _arr(ctypes.c_int64, [4, 4])
+    y = _arr(P, [FAKE2 + 0x100000, FAKE2 + 0x200000])
+    assert lib.nm_gemv_dense_multi(0, W, R, 64, 0, FAKE2, 1, y, None) == L.NM_ERR_BAD_SHAPE
+    assert lib.nm_gemv_dense_multi(2, None, R, 64, 0, FAKE2, 1, y, None) == L.NM_ERR_INVALID_ARG
+    assert lib.nm_gemv_dense_multi(2, W, R, 64, 0, FAKE2, 9, y, None) == L.NM_ERR_BAD_SHAPE
+    Wm = _arr(P, [FAKE, FAKE + 0x10002])
+    assert lib.nm_gemv_dense_multi(2, Wm, R, 64, 0, FAKE2, 1, y, None) == L.NM_ERR_INVALID_ARG

@@ -281,3 +281,52 @@ def test_gemv_dense_integer_exact(nm, dt):
     yref, _ = oracle.gemv(bits(W), dt, bits(x))
     y = nm.gemv_dense(gpu(W), gpu(x))
     assert np.array_equal(bits(y), oracle.round_to(yref, dt))
+
+
+# ---- several matrices sharing x in one launch -----------------------------------
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (1, 4)])
+@pytest.mark.parametrize("Rs,K,B", [((96, 32, 32), 1024, 1), ((40, 0, 77, 13), 2048 + 16 * 3, 2),
+                                     ((300, 300), 14336, 1), ((5,), 64, 8)])
+def test_spmv_multi(nm, dt, n, m, Rs, K, B):
+    tdt = TD[dt]
+    x = I.activation_normal(B, K, tdt, I.seed_of("mx", K, B, dt), outlier_frac=0.01)
+    parts, ref = [], []
+    for i, R in enumerate(Rs):
+        W = I.weight(R, K, tdt, I.seed_of("mW", i, R, K, dt, n, m))
+        ov, om = oracle.pack(bits(W), None, n, m, dt)
+        ref.append(oracle.spmv(ov, om, K, n, m, dt, bits(x)))
+        parts.append(nm.pack(gpu(W), None, n, m))
+    ys = nm.spmv_multi(parts, gpu(x), n, m)
+    torch.cuda.synchronize()
+    for i, (y, (yref, A)) in enumerate(zip(ys, ref)):
+        assert y.shape == (B, Rs[i])
+        ok, worst, idx = oracle.check(bits(y), yref, A, dt)
+        assert ok, (i, worst, idx)
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_spmv_multi_integer_exact_matches_single(nm, dt):
+    """Integer-valued inputs: every summation order is exact, so the fused
+    launch must reproduce the single launches bit for bit."""
+    tdt = TD[dt]
+    K = 4096
+    x = gpu(I.integer_valued(1, K, tdt, 51))
+    parts = [nm.pack(gpu(I.integer_valued(R, K, tdt, 52 + R, scale=1 / 16)), None, 2, 4) for R in (256, 64, 64)]
+    ys = nm.spmv_multi(parts, x, 2, 4)
+    for (v, mk), y in zip(parts, ys):
+        assert torch.equal(y.view(torch.int16), nm.spmv(v, mk, x, 2, 4).view(torch.int16))
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("Rs,K,B", [((64, 16, 16), 4096, 1), ((33, 70), 1000, 3)])
+def test_gemv_dense_multi(nm, dt, Rs, K, B):
+    tdt = TD[dt]
+    x = I.activation_normal(B, K, tdt, I.seed_of("dmx", K, B, dt))
+    Ws = [I.weight(R, K, tdt, I.seed_of("dmW", i, R, K, dt)) for i, R in enumerate(Rs)]
+    ys = nm.gemv_dense_multi([gpu(W) for W in Ws], gpu(x))
+    for W, y in zip(Ws, ys):
+        yref, A = oracle.gemv(bits(W), dt, bits(x))
+        ok, worst, idx = oracle.check(bits(y), yref, A, dt)
+        assert ok, (worst, idx)
