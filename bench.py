@@ -157,6 +157,19 @@ def read_ceiling(torch, cur):
     return best
 
 
+def copy_calibration(torch, cur, nbytes=256 << 20):
+    """One plain 16-byte copy of known size: its FETCH_SIZE / WRITE_SIZE
+    counter readings calibrate the counters' units in profiling runs."""
+    from sparse_matrix_vector_amd import probe
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    if probe.lib().nmp_copy(P(src.data_ptr()), P(dst.data_ptr()), nbytes, 1024, P(cur)) != 0:
+        raise RuntimeError("probe copy failed")
+    torch.cuda.synchronize()
+    del src, dst
+    return nbytes
+
+
 def mlp_single(torch, nm, I, lib, launches, cur):
     """Llama-3.1-8B MLP shapes as single nm_spmv / nm_gemv_dense launches,
     back to back over the 32 layers' weights."""
@@ -250,6 +263,22 @@ def sampled_parity(launches, torch):
     return worst
 
 
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "nm_spmv_llama31_8b_decode_traffic.json")
+    src = os.path.join(ROOT, "sparse_matrix_vector_amd", "csrc", "nmspmv.hip")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+        with open(src, "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+    except OSError:
+        return None
+    return rec["traffic_bytes_per_launch"] if rec.get("source_sha256") == sha else None
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -310,6 +339,7 @@ def main():
 
     mlp = mlp_single(torch, nm, I, lib, launches, cur)
     ceiling = read_ceiling(torch, cur)
+    copy_bytes = copy_calibration(torch, cur)
     worst = sampled_parity(launches, torch)
     cpu = None if a.no_cpu else cpu_baseline(launches, a.cpu_seconds, torch)
 
@@ -341,8 +371,9 @@ def main():
         "per_launch": per,
         "mlp_shapes": mlp,
         "read_ceiling_gbs": round(ceiling, 1),
+        "copy_calibration_bytes": copy_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "rowslice_kernel<2:4, fp16, B=1, 4 chunks/lane> (q+k+v, o, gate+up launches)",
                      "avg_launch_us": round(rus, 3), "algorithmic_bytes_per_launch": round(rbytes)},
         "cpu_baseline": cpu,

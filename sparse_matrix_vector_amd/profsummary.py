@@ -1,0 +1,71 @@
+"""Summarise rocprofv3 CSV output (kernel trace and counter collection).
+
+    python -m sparse_matrix_vector_amd.profsummary trace <run>_kernel_trace.csv
+    python -m sparse_matrix_vector_amd.profsummary pmc <run>_counter_collection.csv COUNTER [calib_kernel calib_bytes]
+
+`trace` prints, per kernel name and grid size, the dispatch count and the
+mean / min / max duration in microseconds.  `pmc` prints, per kernel name and
+grid size, the mean of COUNTER per dispatch (nominally KiB for FETCH_SIZE and
+WRITE_SIZE) and, given a calibration kernel (a name prefix) of known byte
+count per dispatch, the factor that turns the counter into bytes and the
+scaled bytes per dispatch.  The grid size (work-items) tells the shapes of one
+kernel apart.
+"""
+import collections
+import csv
+import sys
+
+
+def short(name, width=110):
+    name = name.replace("(anonymous namespace)::", "")
+    return name if len(name) <= width else name[:width] + "..."
+
+
+def _grid(r):
+    for k in ("Grid_Size", "Grid_Size_X"):
+        if k in r:
+            return int(r[k])
+    return 0
+
+
+def trace(path):
+    dur = collections.defaultdict(list)
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            dur[(r["Kernel_Name"], _grid(r))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rows = sorted(dur.items(), key=lambda kv: -sum(kv[1]))
+    total = sum(sum(v) for v in dur.values())
+    print(f"{'calls':>7} {'grid':>9} {'mean_us':>9} {'min_us':>9} {'max_us':>9} {'share':>6}  kernel")
+    for (name, grid), v in rows:
+        print(f"{len(v):7d} {grid:9d} {sum(v) / len(v):9.3f} {min(v):9.3f} {max(v):9.3f} "
+              f"{100 * sum(v) / total:5.1f}%  {short(name)}")
+
+
+def pmc(path, counter, calib_kernel=None, calib_bytes=None):
+    vals = collections.defaultdict(list)
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                vals[(r["Kernel_Name"], _grid(r))].append(float(r["Counter_Value"]))
+    factor = None
+    if calib_kernel:
+        cal = [v for (k, _), vs in vals.items() if short(k, 1 << 20).startswith(calib_kernel) for v in vs]
+        if cal:
+            factor = float(calib_bytes) / (sum(cal) / len(cal))
+            print(f"calibration: {calib_kernel} reads {sum(cal) / len(cal):.1f} {counter} units per dispatch "
+                  f"for {int(calib_bytes)} bytes -> {factor:.3f} bytes per unit")
+    print(f"{'calls':>7} {'grid':>9} {'mean_' + counter:>16} {'bytes/dispatch':>16}  kernel")
+    for (name, grid), v in sorted(vals.items(), key=lambda kv: -sum(kv[1])):
+        mean = sum(v) / len(v)
+        scaled = f"{mean * factor:16.0f}" if factor else f"{'':>16}"
+        print(f"{len(v):7d} {grid:9d} {mean:16.1f} {scaled}  {short(name)}")
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 3 and sys.argv[1] == "trace":
+        trace(sys.argv[2])
+    elif len(sys.argv) >= 4 and sys.argv[1] == "pmc":
+        pmc(sys.argv[2], sys.argv[3], *(sys.argv[4:6]))
+    else:
+        print(__doc__)
+        sys.exit(2)
