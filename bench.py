@@ -35,12 +35,38 @@ PEAK_GBS = 8000.0
 P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 
 
+# name -> (description, model shapes, layers, dtype, n, m, batch, launch groups, x kind)
+ATTN_MLP = [(("q", "k", "v"), "attn"), (("o",), "o"), (("gate", "up"), "mlp"), (("down",), "down")]
+MLP_ONLY = [(("gate", "up"), "mlp"), (("down",), "down")]
+
+
+def workloads(I):
+    w = {
+        "llama31_8b": ("Llama-3.1-8B decode-step projections: 32 layers x (q+k+v fused, o, gate+up fused, down), "
+                       "2:4 sparse, fp16, batch 1", I.LLAMA31_8B, 32, "fp16", 2, 4, 1, ATTN_MLP, "outliers"),
+        "llama33_70b": ("Llama-3.3-70B full decode-step weight sweep: 80 layers x (q+k+v fused, o, gate+up fused, "
+                        "down), 2:4 sparse, bf16, batch 1", I.LLAMA33_70B, 80, "bf16", 2, 4, 1, ATTN_MLP, "normal"),
+    }
+    for nmk, (n, m) in (("4of8", (4, 8)), ("2of4", (2, 4))):
+        w[f"qwen3_14b_{nmk}"] = (f"Qwen3-14B MLP projections: 40 layers x (gate+up fused, down), {n}:{m} sparse, "
+                                 f"bf16, batch 1, Laplace x", I.QWEN3_14B_MLP, 40, "bf16", n, m, 1, MLP_ONLY, "laplace")
+        w[f"qwen3_32b_{nmk}"] = (f"Qwen3-32B MLP projections: 64 layers x (gate+up fused, down), {n}:{m} sparse, "
+                                 f"bf16, batch 1, Laplace x", I.QWEN3_32B_MLP, 64, "bf16", n, m, 1, MLP_ONLY, "laplace")
+    for B in (1, 2, 4, 8):
+        w[f"qwen3_32b_b{B}"] = (f"Qwen3-32B MLP projections: 64 layers x (gate+up fused, down), 2:4 sparse, bf16, "
+                                f"batch {B}", I.QWEN3_32B_MLP, 64, "bf16", 2, 4, B, MLP_ONLY, "normal")
+    return w
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--workload", default="llama31_8b",
+                   help="llama31_8b (default), llama33_70b, qwen3_14b_4of8, qwen3_14b_2of4, qwen3_32b_4of8, "
+                        "qwen3_32b_2of4, qwen3_32b_b1/b2/b4/b8")
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
     p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a graph")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -50,23 +76,30 @@ def parse():
 class Launch:
     """One launch of the step: 1-3 projections of one layer sharing one x."""
 
-    def __init__(self, torch, nm, I, layer, names, K):
-        dt = torch.float16
-        self.layer, self.names, self.K = layer, names, K
-        self.x = I.activation_normal(1, K, dt, I.seed_of("llama31_8b", layer, names[0], "x"), device="cuda",
-                                     outlier_frac=0.01)
+    def __init__(self, torch, nm, I, spec, tag, layer, names):
+        _, shapes, _, dts, n, m, B, _, xkind = spec
+        dt = {"fp16": torch.float16, "bf16": torch.bfloat16}[dts]
+        self.layer, self.names, self.n, self.m, self.B = layer, names, n, m, B
+        self.dtc = 0 if dts == "fp16" else 1
+        self.K = K = shapes[names[0]][1]
+        xseed = I.seed_of(tag, layer, names[0], "x")
+        if xkind == "laplace":
+            self.x = I.activation_laplace(B, K, dt, xseed, device="cuda")
+        else:
+            self.x = I.activation_normal(B, K, dt, xseed, device="cuda",
+                                         outlier_frac=0.01 if xkind == "outliers" else 0.0)
         self.R, self.W, self.values, self.masks, self.y, self.yd = [], [], [], [], [], []
         for nme in names:
-            R, K2 = I.LLAMA31_8B[nme]
+            R, K2 = shapes[nme]
             assert K2 == K
-            W = I.weight(R, K, dt, I.seed_of("llama31_8b", layer, nme, "W"), device="cuda")
-            v, m = nm.pack(W, None, 2, 4)
+            W = I.weight(R, K, dt, I.seed_of(tag, layer, nme, "W"), device="cuda")
+            v, mk = nm.pack(W, None, n, m)
             self.R.append(R)
             self.W.append(W)
             self.values.append(v)
-            self.masks.append(m)
-            self.y.append(torch.empty((1, R), dtype=dt, device="cuda"))
-            self.yd.append(torch.empty((1, R), dtype=dt, device="cuda"))
+            self.masks.append(mk)
+            self.y.append(torch.empty((B, R), dtype=dt, device="cuda"))
+            self.yd.append(torch.empty((B, R), dtype=dt, device="cuda"))
 
     @property
     def kind(self):
@@ -75,28 +108,30 @@ class Launch:
     def sparse_args(self, stream):
         c = len(self.names)
         return (I32(c), (P * c)(*[v.data_ptr() for v in self.values]), (P * c)(*[m.data_ptr() for m in self.masks]),
-                (I64 * c)(*self.R), I64(self.K), I32(2), I32(4), I32(0), P(self.x.data_ptr()), I32(1),
-                (P * c)(*[y.data_ptr() for y in self.y]), P(stream))
+                (I64 * c)(*self.R), I64(self.K), I32(self.n), I32(self.m), I32(self.dtc), P(self.x.data_ptr()),
+                I32(self.B), (P * c)(*[y.data_ptr() for y in self.y]), P(stream))
 
     def dense_args(self, stream):
         c = len(self.names)
-        return (I32(c), (P * c)(*[W.data_ptr() for W in self.W]), (I64 * c)(*self.R), I64(self.K), I32(0),
-                P(self.x.data_ptr()), I32(1), (P * c)(*[y.data_ptr() for y in self.yd]), P(stream))
+        return (I32(c), (P * c)(*[W.data_ptr() for W in self.W]), (I64 * c)(*self.R), I64(self.K), I32(self.dtc),
+                P(self.x.data_ptr()), I32(self.B), (P * c)(*[y.data_ptr() for y in self.yd]), P(stream))
+
+    def part_bytes(self, i):
+        R, K = self.R[i], self.K
+        return R * K * self.n // self.m * 2 + R * K // 8 + self.B * R * 2
 
     def sparse_bytes(self):
-        return sum(R * self.K // 2 * 2 + R * self.K // 8 + R * 2 for R in self.R) + self.K * 2
+        return sum(self.part_bytes(i) for i in range(len(self.R))) + self.B * self.K * 2
 
     def dense_bytes(self):
-        return sum(R * self.K * 2 + R * 2 for R in self.R) + self.K * 2
+        return sum(R * self.K * 2 + self.B * R * 2 for R in self.R) + self.B * self.K * 2
 
 
-def build_step(layers, torch, nm, I):
+def build_step(spec, tag, layers, torch, nm, I):
     launches = []
     for l in range(layers):
-        launches.append(Launch(torch, nm, I, l, ("q", "k", "v"), 4096))
-        launches.append(Launch(torch, nm, I, l, ("o",), 4096))
-        launches.append(Launch(torch, nm, I, l, ("gate", "up"), 4096))
-        launches.append(Launch(torch, nm, I, l, ("down",), 14336))
+        for names, _ in spec[7]:
+            launches.append(Launch(torch, nm, I, spec, tag, l, names))
     torch.cuda.synchronize()
     return launches
 
@@ -170,9 +205,9 @@ def copy_calibration(torch, cur, nbytes=256 << 20):
     return nbytes
 
 
-def mlp_single(torch, nm, I, lib, launches, cur):
-    """Llama-3.1-8B MLP shapes as single nm_spmv / nm_gemv_dense launches,
-    back to back over the 32 layers' weights."""
+def mlp_single(torch, lib, launches, cur, reps=10):
+    """MLP projections (gate, up, down) as single nm_spmv / nm_gemv_dense
+    launches, back to back over every layer's weights."""
     out = {}
     for name in ("gate", "up", "down"):
         sargs, dargs, nbytes, dbytes = [], [], 0, 0
@@ -181,16 +216,18 @@ def mlp_single(torch, nm, I, lib, launches, cur):
                 continue
             i = L.names.index(name)
             R, K = L.R[i], L.K
-            sargs.append((P(L.values[i].data_ptr()), P(L.masks[i].data_ptr()), I64(R), I64(K), I32(2), I32(4),
-                          I32(0), P(L.x.data_ptr()), I32(1), P(L.y[i].data_ptr()), P(cur)))
-            dargs.append((P(L.W[i].data_ptr()), I64(R), I64(K), I32(0), P(L.x.data_ptr()), I32(1),
+            sargs.append((P(L.values[i].data_ptr()), P(L.masks[i].data_ptr()), I64(R), I64(K), I32(L.n), I32(L.m),
+                          I32(L.dtc), P(L.x.data_ptr()), I32(L.B), P(L.y[i].data_ptr()), P(cur)))
+            dargs.append((P(L.W[i].data_ptr()), I64(R), I64(K), I32(L.dtc), P(L.x.data_ptr()), I32(L.B),
                           P(L.yd[i].data_ptr()), P(cur)))
-            nbytes = R * K // 2 * 2 + R * K // 8 + K * 2 + R * 2
-            dbytes = R * K * 2 + K * 2 + R * 2
+            nbytes = L.part_bytes(i) + L.B * K * 2
+            dbytes = R * K * 2 + L.B * (K + R) * 2
+        if not sargs:
+            continue
         run(lib.nm_spmv, sargs)
-        us = time_ms(torch, lambda: run(lib.nm_spmv, sargs), 10) / len(sargs) * 1e3
+        us = time_ms(torch, lambda: run(lib.nm_spmv, sargs), reps) / len(sargs) * 1e3
         run(lib.nm_gemv_dense, dargs)
-        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense, dargs), 10) / len(dargs) * 1e3
+        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense, dargs), reps) / len(dargs) * 1e3
         out[name] = {"shape": [R, K], "us": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
                      "pct_of_peak": round(100 * nbytes / us / 1e3 / PEAK_GBS, 2),
                      "dense_us": round(usd, 3), "dense_gbs": round(dbytes / usd / 1e3, 1),
@@ -198,10 +235,10 @@ def mlp_single(torch, nm, I, lib, launches, cur):
     return out
 
 
-def cpu_baseline(launches, budget_s, torch):
-    """CPU oracle (plain C, fp64, one thread) on layer 0's seven projections,
-    packed by the oracle itself from the same weights; repeated until about
-    budget_s seconds of oracle time."""
+def cpu_baseline(launches, budget_s, torch, label):
+    """CPU oracle (plain C, fp64, one thread) on layer 0's projections, packed
+    by the oracle itself from the same weights; repeated until about budget_s
+    seconds of oracle time."""
     import numpy as np
 
     import oracle
@@ -210,16 +247,16 @@ def cpu_baseline(launches, budget_s, torch):
         if L.layer != 0:
             continue
         xb = L.x.cpu().view(torch.int16).numpy().view(np.uint16)
+        dts = "fp16" if L.dtc == 0 else "bf16"
         for i, R in enumerate(L.R):
             Wb = L.W[i].cpu().view(torch.int16).numpy().view(np.uint16)
-            v, m = oracle.pack(Wb, None, 2, 4, "fp16")
-            nbytes = R * L.K // 2 * 2 + R * L.K // 8 + L.K * 2 + R * 2
-            work.append((v, m, L.K, xb, nbytes))
+            v, m = oracle.pack(Wb, None, L.n, L.m, dts)
+            work.append((v, m, L, xb, L.part_bytes(i) + L.B * L.K * 2, dts))
     done, elapsed, reps = 0, 0.0, 0
     while elapsed < budget_s or reps == 0:
-        for v, m, K, xb, nbytes in work:
+        for v, m, L, xb, nbytes, dts in work:
             t0 = time.perf_counter()
-            oracle.spmv(v, m, K, 2, 4, "fp16", xb)
+            oracle.spmv(v, m, L.K, L.n, L.m, dts, xb)
             elapsed += time.perf_counter() - t0
             done += nbytes
         reps += 1
@@ -233,13 +270,12 @@ def cpu_baseline(launches, budget_s, torch):
     except OSError:
         pass
     return {"value": round(done / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"Llama-3.1-8B decoder layer 0 (q,k,v,o,gate,up,down; 2:4 fp16, B=1) x {reps}: "
-                      f"fp64 scalar C oracle, 1 thread, {elapsed:.1f} s, {elapsed / reps * 1e3:.0f} ms per layer "
-                      f"(GPU step has 32 layers); host {cpu}, {os.cpu_count()} logical CPUs"}
+            "sample": f"{label}: layer 0's projections x {reps}, fp64 scalar C oracle, 1 thread, {elapsed:.1f} s, "
+                      f"{elapsed / reps * 1e3:.0f} ms per layer; host {cpu}, {os.cpu_count()} logical CPUs"}
 
 
 def sampled_parity(launches, torch):
-    """First 64 rows of layer 0's q, gate and down against the oracle."""
+    """First 64 rows of every layer-0 projection against the oracle."""
     import numpy as np
 
     import oracle
@@ -248,16 +284,15 @@ def sampled_parity(launches, torch):
         if L.layer != 0:
             continue
         xb = L.x.cpu().view(torch.int16).numpy().view(np.uint16)
+        dts = "fp16" if L.dtc == 0 else "bf16"
         for i, nme in enumerate(L.names):
-            if nme not in ("q", "gate", "down"):
-                continue
             Wb = L.W[i][:64].cpu().view(torch.int16).numpy().view(np.uint16)
-            v, m = oracle.pack(Wb, None, 2, 4, "fp16")
+            v, m = oracle.pack(Wb, None, L.n, L.m, dts)
             assert np.array_equal(v, L.values[i][:64].cpu().view(torch.int16).numpy().view(np.uint16)), "pack"
             assert np.array_equal(m, L.masks[i][:64].cpu().numpy()), "masks"
-            yref, A = oracle.spmv(v, m, L.K, 2, 4, "fp16", xb)
+            yref, A = oracle.spmv(v, m, L.K, L.n, L.m, dts, xb)
             got = L.y[i][:, :64].cpu().view(torch.int16).numpy().view(np.uint16)
-            ok, w, _ = oracle.check(got, yref, A, "fp16")
+            ok, w, _ = oracle.check(got, yref, A, dts)
             assert ok, f"{nme}: outside tolerance ({w})"
             worst = max(worst, w)
     return worst
@@ -289,11 +324,18 @@ def main():
 
     import sparse_matrix_vector_amd as nm
     from sparse_matrix_vector_amd import inputs as I
+    specs = workloads(I)
+    if a.workload not in specs:
+        print(f"unknown workload {a.workload}; one of {sorted(specs)}", file=sys.stderr)
+        sys.exit(2)
+    spec = specs[a.workload]
+    desc, _, layers, dts, n, m, B = spec[:7]
+    layers = a.layers or layers
     lib = nm.lib()
     torch.cuda.set_device(0)
     cur = torch.cuda.current_stream().cuda_stream
 
-    launches = build_step(a.layers, torch, nm, I)
+    launches = build_step(spec, a.workload, layers, torch, nm, I)
     sparse_bytes = sum(L.sparse_bytes() for L in launches)
     dense_bytes = sum(L.dense_bytes() for L in launches)
 
@@ -317,31 +359,41 @@ def main():
         step_dense()
     ms_dense = time_ms(torch, step_dense, max(5, a.steps // 2))
 
-    # ---- per launch type: back-to-back bursts over the layers' weights ----
+    # ---- per launch kind: back-to-back bursts over the layers' weights ----
     per = {}
-    for kind in ("q+k+v", "o", "gate+up", "down"):
+    for names, _ in spec[7]:
+        kind = "+".join(names)
         group = [L for L in launches if L.kind == kind]
         sl = [L.sparse_args(cur) for L in group]
         dl = [L.dense_args(cur) for L in group]
         run(lib.nm_spmv_multi, sl)
-        us = time_ms(torch, lambda: run(lib.nm_spmv_multi, sl), 10) / len(sl) * 1e3
+        us = time_ms(torch, lambda: run(lib.nm_spmv_multi, sl), 5) / len(sl) * 1e3
         run(lib.nm_gemv_dense_multi, dl)
-        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense_multi, dl), 10) / len(dl) * 1e3
+        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense_multi, dl), 5) / len(dl) * 1e3
         sb, db = group[0].sparse_bytes(), group[0].dense_bytes()
         per[kind] = {"rows": sum(group[0].R), "K": group[0].K, "us": round(us, 3), "gbs": round(sb / us / 1e3, 1),
                      "dense_us": round(usd, 3), "dense_gbs": round(db / usd / 1e3, 1), "speedup": round(usd / us, 4),
                      "bytes": sb}
-    # roofline kernel: the instantiation shared by the K = 4096 launches (3 per layer)
-    rk = ("q+k+v", "o", "gate+up")
+
+    if a.workload == "llama31_8b":
+        # roofline kernel: the instantiation shared by the K = 4096 launches (3 per layer)
+        rk = ("q+k+v", "o", "gate+up")
+        kernel = "rowslice_kernel<2:4, fp16, B=1, 4 chunks/lane> (q+k+v, o, gate+up launches)"
+        traffic = measured_traffic()
+    else:
+        rk = ("gate+up",)
+        kernel = f"nm_spmv_multi gate+up launch ({n}:{m}, {dts}, B={B})"
+        traffic = None
     rbytes = sum(per[k]["bytes"] for k in rk) / len(rk)
     rus = sum(per[k]["us"] for k in rk) / len(rk)
     achieved = rbytes / rus / 1e3
 
-    mlp = mlp_single(torch, nm, I, lib, launches, cur)
+    mlp = mlp_single(torch, lib, launches, cur, reps=10 if layers <= 64 else 3)
     ceiling = read_ceiling(torch, cur)
     copy_bytes = copy_calibration(torch, cur)
     worst = sampled_parity(launches, torch)
-    cpu = None if a.no_cpu else cpu_baseline(launches, a.cpu_seconds, torch)
+    default_workload = a.workload == "llama31_8b"
+    cpu = None if (a.no_cpu or not default_workload) else cpu_baseline(launches, a.cpu_seconds, torch, desc)
 
     gbs = sparse_bytes / (ms_step * 1e-3) / 1e9
     props = torch.cuda.get_device_properties(0)
@@ -356,25 +408,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f16" if dts == "fp16" else "bf16",
         "data": "synthetic",
-        "config": {"workload": "Llama-3.1-8B decode-step projections: 32 layers x (q+k+v fused, o, gate+up fused, "
-                               "down), 2:4 sparse, fp16, batch 1",
-                   "layers": a.layers, "n_m": "2:4", "batch": 1, "launches_per_step": len(launches),
-                   "mode": "eager" if a.eager else "hip_graph",
+        "config": {"workload": desc, "name": a.workload, "layers": layers, "n_m": f"{n}:{m}", "batch": B,
+                   "launches_per_step": len(launches), "mode": "eager" if a.eager else "hip_graph",
                    "packed_bytes_per_step": sparse_bytes, "dense_bytes_per_step": dense_bytes},
         "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
         "speedup_vs_dense": round(ms_dense / ms_step, 4),
         "dense_ms_per_step": round(ms_dense, 4),
         "dense_gbs": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
-        "us_per_layer": round(ms_step * 1e3 / a.layers, 2),
+        "us_per_layer": round(ms_step * 1e3 / layers, 2),
         "per_launch": per,
         "mlp_shapes": mlp,
         "read_ceiling_gbs": round(ceiling, 1),
         "copy_calibration_bytes": copy_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "rowslice_kernel<2:4, fp16, B=1, 4 chunks/lane> (q+k+v, o, gate+up launches)",
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
                      "avg_launch_us": round(rus, 3), "algorithmic_bytes_per_launch": round(rbytes)},
         "cpu_baseline": cpu,
         "parity_sampled_worst_ratio": round(worst, 4),

@@ -31,8 +31,8 @@
 //   rowslice_kernel  a wave owns one (row, K-slice) item and issues all of its
 //                    loads before anything else; many short-lived waves.
 //   stream_kernel    waves walk rows g, g+G, ... with the next group of loads
-//                    in flight while computing (long rows, few blocks).
-//   tiled_kernel     x staged in K-tiles when B*K*2 bytes exceed the LDS tile.
+//                    in flight while computing (long rows, few blocks); x in
+//                    K-tiles when B*K*2 bytes exceed the LDS tile.
 //   generic_spmv_kernel  any N:M with M in {4, 8} and K % 8 == 0 (untuned).
 
 #include <hip/hip_runtime.h>
@@ -52,7 +52,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kXTileBudget = 56 * 1024;   // LDS bytes for x in the row-slice / stream kernels
-constexpr int kTiledBlock = 256;
 
 enum Fmt { kDense = 0, kNM24 = 1, kNM48 = 2 };
 
@@ -393,140 +392,100 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
 // reads one compact band of rows (DRAM-page friendly).  A row is cut into
 // groups of U chunks per lane; the wave walks its (row, group) sequence with
 // the next group's loads in flight while it multiplies the current one (two
-// register buffers), and reduces and stores a row after its last group.
+// register buffers).  x is staged in LDS in tiles of tile_cols columns; with
+// one tile a row's sum goes straight to y, with several the wave keeps each
+// of its rows' partial sums in LDS between tiles (slot = wave * rpw + t).
 template <int F, int DT, int NB, int U>
-__global__ __launch_bounds__(512) void stream_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K)
+__global__ __launch_bounds__(512) void stream_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
+                                                     int tile_cols)
 {
     extern __shared__ u32x4 smem[];
     constexpr int COLS = chunk_cols<F>();
     const int lane = threadIdx.x & (kWave - 1);
     const int nw = blockDim.x / kWave;
-    const int g = blockIdx.x * nw + threadIdx.x / kWave;
+    const int wave = threadIdx.x / kWave;
+    const int g = blockIdx.x * nw + wave;
     const int G = gridDim.x * nw;
     const int C = K / COLS;
-    const int gpr = (C + kWave * U - 1) / (kWave * U);
+    const int rpw = (R + G - 1) / G;                       // rows per wave, at most
     const int nrows = g < R ? (R - g + G - 1) / G : 0;
-    const int ng = nrows * gpr;
-
-    u32x4 va[U], vb[U];
-    uint32_t ma[U], mb[U];
-    if (ng > 0) {
-        const RowRef row = locate(P, g, C);
-        load_chunks<F, U>(row.w, row.m, 0, C, lane, va, ma);
-    }
-
-    u32x4* tab = smem;
-    u32x4* xs = smem + table_units<F>();
-    const int bstride = K / 8;
-    build_table<F>(tab);
-    stage_x<F, NB>(xs, x4, K, 0, K, bstride);
-    __syncthreads();
-
-    float acc[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-        acc[b] = 0.f;
-
-    auto consume = [&](int j, const u32x4* v, const uint32_t* mk) {
-        const int t = j / gpr, q = j - t * gpr;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = q * kWave * U + lane + u * kWave;
-            if (c < C)
-                chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, c, bstride, acc);
-        }
-        if (q == gpr - 1) {
-            const RowRef row = locate(P, g + t * G, C);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const float sum = wave_sum(acc[b]);
-                if (lane == 0)
-                    row.y[(size_t)b * row.R] = from_f32<DT>(sum);
-                acc[b] = 0.f;
-            }
-        }
-    };
-    auto fetch = [&](int j, u32x4* v, uint32_t* mk) {
-        const int t = j / gpr, q = j - t * gpr;
-        const RowRef row = locate(P, g + t * G, C);
-        load_chunks<F, U>(row.w, row.m, q * kWave * U, C, lane, v, mk);
-    };
-
-    for (int j = 0; j < ng; j += 2) {
-        if (j + 1 < ng)
-            fetch(j + 1, vb, mb);
-        consume(j, va, ma);
-        if (j + 1 < ng) {
-            if (j + 2 < ng)
-                fetch(j + 2, va, ma);
-            consume(j + 1, vb, mb);
-        }
-    }
-}
-
-// ---- tiled kernel (x larger than one LDS tile) --------------------------------
-
-// One block owns rows_per_block consecutive rows, taken by its waves
-// round-robin.  x is staged in tiles of tile_cols columns; per-row partial
-// sums wait in LDS between tiles.
-template <int F, int DT, int NB>
-__global__ __launch_bounds__(kTiledBlock) void tiled_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
-                                                            int rows_per_block, int tile_cols)
-{
-    extern __shared__ u32x4 smem[];
-    constexpr int COLS = chunk_cols<F>();
-    constexpr int U = 4;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int nw = kTiledBlock / kWave;
-    const int r0 = blockIdx.x * rows_per_block;
-    const int r1 = min(R, r0 + rows_per_block);
+    const bool multi = tile_cols < K;
     const int bstride = tile_cols / 8;
+
     u32x4* tab = smem;
     u32x4* xs = smem + table_units<F>();
     float* part = reinterpret_cast<float*>(xs + NB * bstride);
-    const int C = K / COLS;
-
     build_table<F>(tab);
-    for (int i = threadIdx.x; i < rows_per_block * NB; i += kTiledBlock)
-        part[i] = 0.f;
+    if (multi)
+        for (int i = threadIdx.x; i < nw * rpw * NB; i += blockDim.x)
+            part[i] = 0.f;
 
     for (int t0 = 0; t0 < K; t0 += tile_cols) {
         const int tc = min(tile_cols, K - t0);
+        const int cb = t0 / COLS, ce = (t0 + tc) / COLS;
+        const int gpr = (ce - cb + kWave * U - 1) / (kWave * U);   // groups per row in this tile
+        const int ng = nrows * gpr;
+        u32x4 va[U], vb[U];
+        uint32_t ma[U], mb[U];
+        if (ng > 0) {
+            const RowRef row = locate(P, g, C);
+            load_chunks<F, U>(row.w, row.m, cb, ce, lane, va, ma);
+        }
         __syncthreads();
         stage_x<F, NB>(xs, x4, K, t0, tc, bstride);
         __syncthreads();
-        const int cb = t0 / COLS, ce = (t0 + tc) / COLS;
-        for (int r = r0 + wave; r < r1; r += nw) {
-            const RowRef row = locate(P, r, C);
-            float acc[NB];
+
+        float acc[NB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                acc[b] = 0.f;
-            for (int c0 = cb; c0 < ce; c0 += kWave * U) {
-                u32x4 v[U];
-                uint32_t mk[U];
-                load_chunks<F, U>(row.w, row.m, c0, ce, lane, v, mk);
+        for (int b = 0; b < NB; ++b)
+            acc[b] = 0.f;
+        auto consume = [&](int j, const u32x4* v, const uint32_t* mk) {
+            const int t = j / gpr, q = j - t * gpr;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + lane + u * kWave;
-                    if (c < ce)
-                        chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, c - cb, bstride, acc);
+            for (int u = 0; u < U; ++u) {
+                const int c = cb + q * kWave * U + lane + u * kWave;
+                if (c < ce)
+                    chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, c - cb, bstride, acc);
+            }
+            if (q == gpr - 1) {
+                const RowRef row = locate(P, g + t * G, C);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const float sum = wave_sum(acc[b]);
+                    if (lane == 0) {
+                        if (multi)
+                            part[(wave * rpw + t) * NB + b] += sum;
+                        else
+                            row.y[(size_t)b * row.R] = from_f32<DT>(sum);
+                    }
+                    acc[b] = 0.f;
                 }
             }
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const float s = wave_sum(acc[b]);
-                if (lane == 0)
-                    part[(r - r0) * NB + b] += s;
+        };
+        auto fetch = [&](int j, u32x4* v, uint32_t* mk) {
+            const int t = j / gpr, q = j - t * gpr;
+            const RowRef row = locate(P, g + t * G, C);
+            load_chunks<F, U>(row.w, row.m, cb + q * kWave * U, ce, lane, v, mk);
+        };
+        for (int j = 0; j < ng; j += 2) {
+            if (j + 1 < ng)
+                fetch(j + 1, vb, mb);
+            consume(j, va, ma);
+            if (j + 1 < ng) {
+                if (j + 2 < ng)
+                    fetch(j + 2, va, ma);
+                consume(j + 1, vb, mb);
             }
         }
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < (r1 - r0) * NB; i += kTiledBlock) {
-        const int lr = i / NB, b = i - lr * NB;
-        const RowRef row = locate(P, r0 + lr, C);
-        row.y[(size_t)b * row.R] = from_f32<DT>(part[i]);
+    if (multi && lane == 0) {
+        // part[] of this wave was written only by this wave's lane 0: no barrier needed.
+        for (int t = 0; t < nrows; ++t) {
+            const RowRef row = locate(P, g + t * G, C);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                row.y[(size_t)b * row.R] = from_f32<DT>(part[(wave * rpw + t) * NB + b]);
+        }
     }
 }
 
@@ -662,7 +621,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, 
 // ---- host: launch planning -------------------------------------------------------
 
 // Launch-shape overrides, read once, for tuning sweeps (0 = built-in choice):
-// NMSPMV_KERNEL 1 = row-slice, 2 = tiled, 3 = stream; NMSPMV_SLICES,
+// NMSPMV_KERNEL 1 = row-slice, 3 = stream; NMSPMV_SLICES,
 // NMSPMV_ROWS_PER_BLOCK (row-slice); NMSPMV_BLOCKS, NMSPMV_THREADS (stream).
 struct Env {
     int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0;
@@ -700,25 +659,36 @@ int cu_count()
 }
 
 struct Plan {
-    int kind = 0;            // 1 row-slice, 2 tiled, 3 stream
+    int kind = 0;            // 1 row-slice, 3 stream
     int S = 1, rpb = 1, cpl = 1, threads = 256, tile_cols = 0;
     size_t lds = 0;
     unsigned grid = 1;
 };
 
-// Row-slice: S slices per row keep each lane at <= 8 chunks (all loads in
-// flight at once), and rows longer than 256 chunks get at least two slices
-// (measured faster at 512-1024 chunks); more slices while the matrix has
-// fewer than ~16 waves per CU of rows; rows per block fill at most 8 waves
-// and leave at least two blocks per CU.
-bool plan_rowslice(int64_t R, int64_t C, Plan* P)
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+// Row-slice shape (rules from timing sweeps on MI355X at the Llama-3.1-8B,
+// Llama-3.3-70B and Qwen3 projection shapes):
+//  * rows of <= 512 chunks: one wave per row (S = 1), 8 rows per block
+//    (4 when a lane holds more than 5 chunks);
+//  * longer rows: the fewest slices (a power of two) that keep a lane at <= 8
+//    chunks, 8 waves per block (16 for dense rows);
+//  * few rows (under ~16 waves per CU): more slices, down to 64 chunks each;
+//  * at least two blocks per CU.
+bool plan_rowslice(int64_t R, int64_t C, bool dense, Plan* P)
 {
     const int cus = cu_count();
-    int S = C > 4 * kWave ? 2 : 1;
+    const int waves_per_block = dense ? 16 : 8;
+    int S = 1;
     while (S < 16 && (C + S - 1) / S > 8 * kWave)
         S *= 2;
-    while (S < 16 && R * S < 16LL * cus && (C + 2 * S - 1) / (2 * S) >= kWave)
+    int rpb = std::max(1, waves_per_block / S);
+    if (S == 1 && !dense && C > 5 * kWave)
+        rpb = 4;
+    while (S < 16 && R * S < 16LL * cus && (C + 2 * S - 1) / (2 * S) >= kWave) {
         S *= 2;
+        rpb = std::max(1, 8 / S);
+    }
     if (g_env.slices > 0)
         S = g_env.slices;
     const int64_t cps = (C + S - 1) / S;
@@ -727,7 +697,6 @@ bool plan_rowslice(int64_t R, int64_t C, Plan* P)
         cpl *= 2;
     if (cpl > 8)
         return false;
-    int rpb = std::max(1, 8 / S);
     while (rpb > 1 && (R + rpb - 1) / rpb < 2 * cus)
         rpb /= 2;
     if (g_env.rpb > 0)
@@ -743,10 +712,10 @@ bool plan_rowslice(int64_t R, int64_t C, Plan* P)
     return true;
 }
 
-// Chooses the kernel for a matrix shape.  Rows of up to 1024 chunks (2048
-// for dense rows) go to the row-slice kernel; longer rows to the stream
-// kernel, whose few blocks stage x once for many rows; x larger than the LDS
-// budget to the tiled one.  (Thresholds from timing sweeps on MI355X.)
+// Chooses the kernel for a matrix shape.  The row-slice kernel when x fits
+// its LDS budget, rows are at most 2048 chunks and three blocks still fit a
+// CU's LDS (fewer starve it of waves); otherwise the stream kernel, with x in
+// K-tiles when it exceeds the budget.
 template <int F>
 Plan plan_for(int64_t R, int64_t K, int B)
 {
@@ -755,36 +724,29 @@ Plan plan_for(int64_t R, int64_t K, int B)
     const int64_t C = K / COLS;
     const size_t tab = (size_t)table_units<F>() * sizeof(u32x4);
     const size_t xbytes = (size_t)B * (size_t)K * 2;
-    Plan P;
     const bool fits = xbytes <= (size_t)kXTileBudget;
+    Plan P;
     int kind = g_env.kernel;
-    if (kind == 0)
-        kind = !fits ? 2 : (C <= (F == kDense ? 32 : 16) * kWave ? 1 : 3);
-    if (kind == 1 && fits && plan_rowslice(R, C, &P)) {
+    if (kind != 1 && kind != 3)
+        kind = (fits && C <= 32 * kWave && 3 * (tab + xbytes + 1024) <= kLdsPerCu) ? 1 : 3;
+    if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, &P)) {
         P.lds = tab + xbytes + (P.S > 1 ? (size_t)P.rpb * P.S * B * 4 : 0);
         return P;
     }
-    if ((kind == 3 || kind == 1) && fits) {
-        const int cus = cu_count();
-        P.kind = 3;
-        P.threads = (g_env.threads > 0 && g_env.threads <= 512 && g_env.threads % kWave == 0) ? g_env.threads : 512;
-        int64_t blocks = g_env.blocks > 0 ? g_env.blocks : 2LL * cus;
-        const int nw = P.threads / kWave;
-        while (blocks > 1 && (blocks - 1) * nw >= R)
-            --blocks;
-        P.grid = (unsigned)blocks;
-        P.lds = tab + xbytes;
-        return P;
-    }
-    P.kind = 2;
-    P.threads = kTiledBlock;
-    int64_t tile = ((int64_t)kXTileBudget / (2 * B)) / 1024 * 1024;
-    if (tile >= K)
-        tile = K;
+    const int cus = cu_count();
+    P.kind = 3;
+    P.threads = (g_env.threads > 0 && g_env.threads <= 512 && g_env.threads % kWave == 0) ? g_env.threads : 512;
+    const int nw = P.threads / kWave;
+    int64_t blocks = g_env.blocks > 0 ? g_env.blocks : 2LL * cus;
+    while (blocks > 1 && (blocks - 1) * nw >= R)
+        --blocks;
+    int64_t tile = K;
+    if (!fits)
+        tile = ((int64_t)kXTileBudget / (2 * B)) / 1024 * 1024;
+    const int64_t rpw = (R + blocks * nw - 1) / (blocks * nw);
     P.tile_cols = (int)tile;
-    P.rpb = 16;
-    P.lds = tab + (size_t)B * (size_t)tile * 2 + (size_t)P.rpb * B * 4;
-    P.grid = (unsigned)((R + P.rpb - 1) / P.rpb);
+    P.grid = (unsigned)blocks;
+    P.lds = tab + (size_t)B * (size_t)tile * 2 + (tile < K ? (size_t)nw * rpw * B * 4 : 0);
     return P;
 }
 
@@ -804,10 +766,8 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
         case 4: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 4>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
         default: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 8>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
         }
-    } else if (P.kind == 3) {
-        hipLaunchKernelGGL((stream_kernel<F, DT, NB, 4>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K);
     } else {
-        hipLaunchKernelGGL((tiled_kernel<F, DT, NB>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.rpb,
+        hipLaunchKernelGGL((stream_kernel<F, DT, NB, 4>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K,
                            P.tile_cols);
     }
     return hip_status(hipGetLastError());
