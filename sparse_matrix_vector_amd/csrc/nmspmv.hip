@@ -198,6 +198,55 @@ __device__ __forceinline__ void stage_x(u32x4* xs, const u32x4* __restrict__ x4,
     }
 }
 
+// The LDS slot of staged x unit j of batch row b (see stage_x).
+template <int F>
+__device__ __forceinline__ int x_slot(int b, int j, int bstride)
+{
+    if constexpr (F == kDense)
+        return b * bstride + j;
+    else
+        return b * bstride + (j & 1) * (bstride / 2) + (j >> 1);
+}
+
+// x staging in two halves around the weight loads: x_fetch issues this
+// thread's first XU units of x (all of it when x has at most XU * blockDim
+// units) into registers before the weight loads are issued; x_store writes
+// them to LDS, and the rest, if any, straight through.  Loads retire in issue
+// order, so a wave can store its x and reach the block barrier while its
+// weight loads are still in flight.
+constexpr int kXU = 4;
+
+template <int NB>
+__device__ __forceinline__ void x_fetch(const u32x4* __restrict__ x4, int K, u32x4* xr)
+{
+    const int n = NB * (K / 8);
+#pragma unroll
+    for (int u = 0; u < kXU; ++u) {
+        const int i = threadIdx.x + u * blockDim.x;
+        xr[u] = x4[i < n ? i : 0];               // x [NB][K] is contiguous: unit i = batch i/q, unit i%q
+    }
+}
+
+// Units past the end of x go to the spare slot `dummy` (one unit past the
+// kernel's other LDS data), keeping the stores branch-free too.
+template <int F, int NB>
+__device__ __forceinline__ void x_store(u32x4* xs, const u32x4* __restrict__ x4, int K, int bstride, const u32x4* xr,
+                                        u32x4* dummy)
+{
+    const int q = K / 8;
+#pragma unroll
+    for (int u = 0; u < kXU; ++u) {
+        const int i = threadIdx.x + u * blockDim.x;
+        const int b = i / q;
+        u32x4* dst = i < NB * q ? xs + x_slot<F>(b, i - b * q, bstride) : dummy;
+        *dst = xr[u];
+    }
+    for (int i = threadIdx.x + kXU * blockDim.x; i < NB * q; i += blockDim.x) {
+        const int b = i / q;
+        xs[x_slot<F>(b, i - b * q, bstride)] = x4[i];
+    }
+}
+
 // ---- one 16-byte chunk -------------------------------------------------------
 
 // acc[b] += (chunk . x[b][chunk columns]).  xs: staged x, c: the chunk's index
@@ -297,7 +346,10 @@ __device__ __forceinline__ RowRef locate(const Parts& P, int r, int C)
     return o;
 }
 
-// Loads chunks [c0 + lane + 64 u] (u < U, below cend) of a row.
+// Loads chunks [c0 + lane + 64 u] (u < U) of a row.  Every lane issues all U
+// loads -- lanes past cend reload chunk 0, and the consumer zeroes them with
+// chunk_live() -- so the code is branch-free and the compiler can wait for
+// exactly the loads each use needs (loads retire in issue order).
 template <int F, int U>
 __device__ __forceinline__ void load_chunks(const u32x4* __restrict__ wrow, const uint16_t* __restrict__ mrow,
                                             int c0, int cend, int lane, u32x4* v, uint32_t* mk)
@@ -305,14 +357,24 @@ __device__ __forceinline__ void load_chunks(const u32x4* __restrict__ wrow, cons
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = c0 + lane + u * kWave;
-        v[u] = u32x4{0, 0, 0, 0};
-        mk[u] = 0;
-        if (c < cend) {
-            v[u] = __builtin_nontemporal_load(wrow + c);
-            if constexpr (F != kDense)
-                mk[u] = __builtin_nontemporal_load(mrow + c);
-        }
+        const int cc = c < cend ? c : 0;
+        v[u] = __builtin_nontemporal_load(wrow + cc);
+        if constexpr (F != kDense)
+            mk[u] = __builtin_nontemporal_load(mrow + cc);
+        else
+            mk[u] = 0;
     }
+}
+
+// Zeroes a chunk loaded by a lane that had no chunk (values and mask), so it
+// contributes exactly 0 whatever was reloaded.
+__device__ __forceinline__ void chunk_live(bool live, u32x4& v, uint32_t& mk)
+{
+    v.x = live ? v.x : 0u;
+    v.y = live ? v.y : 0u;
+    v.z = live ? v.z : 0u;
+    v.w = live ? v.w : 0u;
+    mk = live ? mk : 0u;
 }
 
 // ---- row-slice kernel ------------------------------------------------------
@@ -328,7 +390,7 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
     extern __shared__ u32x4 smem[];
     constexpr int COLS = chunk_cols<F>();
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lr = wave / S, sl = wave - lr * S;
     const int r = blockIdx.x * rows_per_block + lr;
     const bool active = r < R;
@@ -337,6 +399,8 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
     const int cbeg = sl * cps, cend = active ? min(C, cbeg + cps) : cbeg;
     const RowRef row = locate(P, active ? r : 0, C);
 
+    u32x4 xr[kXU];
+    x_fetch<NB>(x4, K, xr);
     u32x4 v[CPL];
     uint32_t mk[CPL];
     load_chunks<F, CPL>(row.w, row.m, cbeg, cend, lane, v, mk);
@@ -345,8 +409,9 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
     u32x4* xs = smem + table_units<F>();
     const int bstride = K / 8;
     float* part = reinterpret_cast<float*>(xs + NB * bstride);
+    u32x4* dummy = reinterpret_cast<u32x4*>(part + rows_per_block * S * NB);
     build_table<F>(tab);
-    stage_x<F, NB>(xs, x4, K, 0, K, bstride);
+    x_store<F, NB>(xs, x4, K, bstride, xr, dummy);
     __syncthreads();
 
     float acc[NB];
@@ -356,8 +421,9 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
         const int c = cbeg + lane + u * kWave;
-        if (c < cend)
-            chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, c, bstride, acc);
+        const bool live = c < cend;
+        chunk_live(live, v[u], mk[u]);
+        chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, live ? c : 0, bstride, acc);
     }
     float sum[NB];
 #pragma unroll
@@ -403,7 +469,7 @@ __global__ __launch_bounds__(512) void stream_kernel(const Parts P, const u32x4*
     constexpr int COLS = chunk_cols<F>();
     const int lane = threadIdx.x & (kWave - 1);
     const int nw = blockDim.x / kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int g = blockIdx.x * nw + wave;
     const int G = gridDim.x * nw;
     const int C = K / COLS;
@@ -444,8 +510,11 @@ __global__ __launch_bounds__(512) void stream_kernel(const Parts P, const u32x4*
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = cb + q * kWave * U + lane + u * kWave;
-                if (c < ce)
-                    chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, c - cb, bstride, acc);
+                const bool live = c < ce;
+                u32x4 vv = v[u];
+                uint32_t mm = mk[u];
+                chunk_live(live, vv, mm);
+                chunk_dot<F, DT, NB>(vv, mm, tab, xs, live ? c - cb : 0, bstride, acc);
             }
             if (q == gpr - 1) {
                 const RowRef row = locate(P, g + t * G, C);
@@ -665,26 +734,26 @@ struct Plan {
     unsigned grid = 1;
 };
 
-constexpr size_t kLdsPerCu = 160 * 1024;
-
-// Row-slice shape (rules from timing sweeps on MI355X at the Llama-3.1-8B,
-// Llama-3.3-70B and Qwen3 projection shapes):
-//  * rows of <= 512 chunks: one wave per row (S = 1), 8 rows per block
-//    (4 when a lane holds more than 5 chunks);
-//  * longer rows: the fewest slices (a power of two) that keep a lane at <= 8
-//    chunks, 8 waves per block (16 for dense rows);
+// Row-slice shape (rules from timing sweeps on MI355X over the Llama-3.1-8B,
+// Llama-3.3-70B and Qwen3 projection shapes, sparse and dense):
+//  * sparse rows of <= 320 chunks: one wave per row, 8 rows per block;
+//    longer: the fewest slices S >= 2 (a power of two) that keep a lane at
+//    <= 8 chunks, 8 / S rows per block;
+//  * dense rows of <= 512 chunks: one wave per row, 4 rows per block;
+//    longer: the fewest slices that keep a lane at <= 7 chunks, 8 / S rows;
 //  * few rows (under ~16 waves per CU): more slices, down to 64 chunks each;
 //  * at least two blocks per CU.
 bool plan_rowslice(int64_t R, int64_t C, bool dense, Plan* P)
 {
     const int cus = cu_count();
-    const int waves_per_block = dense ? 16 : 8;
-    int S = 1;
-    while (S < 16 && (C + S - 1) / S > 8 * kWave)
-        S *= 2;
-    int rpb = std::max(1, waves_per_block / S);
-    if (S == 1 && !dense && C > 5 * kWave)
-        rpb = 4;
+    int S = 1, rpb = dense ? 4 : 8;
+    if (C > (dense ? 8 : 5) * kWave) {
+        const int64_t max_cps = (dense ? 7 : 8) * kWave;
+        S = 2;
+        while (S < 16 && (C + S - 1) / S > max_cps)
+            S *= 2;
+        rpb = std::max(1, 8 / S);
+    }
     while (S < 16 && R * S < 16LL * cus && (C + 2 * S - 1) / (2 * S) >= kWave) {
         S *= 2;
         rpb = std::max(1, 8 / S);
@@ -692,9 +761,7 @@ bool plan_rowslice(int64_t R, int64_t C, bool dense, Plan* P)
     if (g_env.slices > 0)
         S = g_env.slices;
     const int64_t cps = (C + S - 1) / S;
-    int cpl = 1;
-    while ((int64_t)cpl * kWave < cps)
-        cpl *= 2;
+    const int cpl = (int)((cps + kWave - 1) / kWave);
     if (cpl > 8)
         return false;
     while (rpb > 1 && (R + rpb - 1) / rpb < 2 * cus)
@@ -712,10 +779,10 @@ bool plan_rowslice(int64_t R, int64_t C, bool dense, Plan* P)
     return true;
 }
 
-// Chooses the kernel for a matrix shape.  The row-slice kernel when x fits
-// its LDS budget, rows are at most 2048 chunks and three blocks still fit a
-// CU's LDS (fewer starve it of waves); otherwise the stream kernel, with x in
-// K-tiles when it exceeds the budget.
+// Chooses the kernel for a matrix shape: the row-slice kernel when x fits its
+// LDS budget and rows are at most 1152 chunks (sparse, K <= 18432) or 2048
+// chunks (dense, K <= 16384); otherwise the stream kernel -- whose blocks
+// stage x once for many rows -- with x in K-tiles when it exceeds the budget.
 template <int F>
 Plan plan_for(int64_t R, int64_t K, int B)
 {
@@ -728,9 +795,9 @@ Plan plan_for(int64_t R, int64_t K, int B)
     Plan P;
     int kind = g_env.kernel;
     if (kind != 1 && kind != 3)
-        kind = (fits && C <= 32 * kWave && 3 * (tab + xbytes + 1024) <= kLdsPerCu) ? 1 : 3;
+        kind = (fits && C <= (F == kDense ? 32 : 18) * kWave) ? 1 : 3;
     if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, &P)) {
-        P.lds = tab + xbytes + (P.S > 1 ? (size_t)P.rpb * P.S * B * 4 : 0);
+        P.lds = tab + xbytes + (size_t)P.rpb * P.S * B * 4 + sizeof(u32x4);
         return P;
     }
     const int cus = cu_count();
@@ -760,12 +827,19 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
     const u32x4* x4 = static_cast<const u32x4*>(x);
     (void)hipGetLastError();
     if (P.kind == 1) {
+#define NM_SLICE(CPL) \
+    hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, CPL>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb)
         switch (P.cpl) {
-        case 1: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 1>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
-        case 2: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 2>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
-        case 4: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 4>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
-        default: hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 8>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb); break;
+        case 1: NM_SLICE(1); break;
+        case 2: NM_SLICE(2); break;
+        case 3: NM_SLICE(3); break;
+        case 4: NM_SLICE(4); break;
+        case 5: NM_SLICE(5); break;
+        case 6: NM_SLICE(6); break;
+        case 7: NM_SLICE(7); break;
+        default: NM_SLICE(8); break;
         }
+#undef NM_SLICE
     } else {
         hipLaunchKernelGGL((stream_kernel<F, DT, NB, 4>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K,
                            P.tile_cols);
