@@ -52,6 +52,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kXTileBudget = 56 * 1024;   // LDS bytes for x in the row-slice / stream kernels
+constexpr int kXTileStream = 64 * 1024;   // LDS bytes per x tile in the stream kernel
+constexpr int kLdsMax = 160 * 1024;       // LDS per CU on gfx950
 
 enum Fmt { kDense = 0, kNM24 = 1, kNM48 = 2 };
 
@@ -182,23 +184,8 @@ __device__ __forceinline__ void build_table(u32x4* tab)
 // x in LDS: [NB][bstride] 16-byte units.  Sparse formats split each 32-byte
 // column range of a chunk into two planes (first 16 bytes at unit c, second
 // at unit bstride/2 + c) so that lanes reading consecutive chunks touch
-// consecutive LDS addresses.  `cols` columns starting at global column c0 are
-// staged from x [NB][K].
-template <int F, int NB>
-__device__ __forceinline__ void stage_x(u32x4* xs, const u32x4* __restrict__ x4, int K, int c0, int cols, int bstride)
-{
-    const int q = cols / 8;
-    for (int i = threadIdx.x; i < NB * q; i += blockDim.x) {
-        const int b = i / q, j = i - b * q;
-        const u32x4 val = x4[(size_t)b * (K / 8) + c0 / 8 + j];
-        if constexpr (F == kDense)
-            xs[b * bstride + j] = val;
-        else
-            xs[b * bstride + (j & 1) * (bstride / 2) + (j >> 1)] = val;
-    }
-}
-
-// The LDS slot of staged x unit j of batch row b (see stage_x).
+// consecutive LDS addresses.
+// The LDS slot of staged x unit j of batch row b.
 template <int F>
 __device__ __forceinline__ int x_slot(int b, int j, int bstride)
 {
@@ -244,6 +231,38 @@ __device__ __forceinline__ void x_store(u32x4* xs, const u32x4* __restrict__ x4,
     for (int i = threadIdx.x + kXU * blockDim.x; i < NB * q; i += blockDim.x) {
         const int b = i / q;
         xs[x_slot<F>(b, i - b * q, bstride)] = x4[i];
+    }
+}
+
+// The same for a tile of `cols` columns starting at column c0.
+template <int NB>
+__device__ __forceinline__ void x_fetch_tile(const u32x4* __restrict__ x4, int K, int c0, int cols, u32x4* xr)
+{
+    const int q = cols / 8, n = NB * q;
+#pragma unroll
+    for (int u = 0; u < kXU; ++u) {
+        int i = threadIdx.x + u * blockDim.x;
+        i = i < n ? i : 0;
+        const int b = i / q;
+        xr[u] = x4[(size_t)b * (K / 8) + c0 / 8 + (i - b * q)];
+    }
+}
+
+template <int F, int NB>
+__device__ __forceinline__ void x_store_tile(u32x4* xs, const u32x4* __restrict__ x4, int K, int c0, int cols,
+                                             int bstride, const u32x4* xr, u32x4* dummy)
+{
+    const int q = cols / 8, n = NB * q;
+#pragma unroll
+    for (int u = 0; u < kXU; ++u) {
+        const int i = threadIdx.x + u * blockDim.x;
+        const int b = i / q;
+        u32x4* dst = i < n ? xs + x_slot<F>(b, i - b * q, bstride) : dummy;
+        *dst = xr[u];
+    }
+    for (int i = threadIdx.x + kXU * blockDim.x; i < n; i += blockDim.x) {
+        const int b = i / q;
+        xs[x_slot<F>(b, i - b * q, bstride)] = x4[(size_t)b * (K / 8) + c0 / 8 + (i - b * q)];
     }
 }
 
@@ -420,6 +439,8 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
         acc[b] = 0.f;
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
+        if (u * kWave >= cend - cbeg)          // wave-uniform: nothing left in this slot for any lane
+            break;
         const int c = cbeg + lane + u * kWave;
         const bool live = c < cend;
         chunk_live(live, v[u], mk[u]);
@@ -462,8 +483,8 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
 // one tile a row's sum goes straight to y, with several the wave keeps each
 // of its rows' partial sums in LDS between tiles (slot = wave * rpw + t).
 template <int F, int DT, int NB, int U>
-__global__ __launch_bounds__(512) void stream_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
-                                                     int tile_cols)
+__global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
+                                                      int tile_cols)
 {
     extern __shared__ u32x4 smem[];
     constexpr int COLS = chunk_cols<F>();
@@ -481,6 +502,7 @@ __global__ __launch_bounds__(512) void stream_kernel(const Parts P, const u32x4*
     u32x4* tab = smem;
     u32x4* xs = smem + table_units<F>();
     float* part = reinterpret_cast<float*>(xs + NB * bstride);
+    u32x4* dummy = reinterpret_cast<u32x4*>(part + (multi ? nw * rpw * NB : 0));
     build_table<F>(tab);
     if (multi)
         for (int i = threadIdx.x; i < nw * rpw * NB; i += blockDim.x)
@@ -491,14 +513,19 @@ __global__ __launch_bounds__(512) void stream_kernel(const Parts P, const u32x4*
         const int cb = t0 / COLS, ce = (t0 + tc) / COLS;
         const int gpr = (ce - cb + kWave * U - 1) / (kWave * U);   // groups per row in this tile
         const int ng = nrows * gpr;
+        // This tile's x is fetched before its first weight loads are issued:
+        // loads retire in issue order, so x fetched behind HBM weight loads
+        // would hold every wave at the barrier for a full HBM round trip.
+        u32x4 xr[kXU];
+        x_fetch_tile<NB>(x4, K, t0, tc, xr);
         u32x4 va[U], vb[U];
         uint32_t ma[U], mb[U];
-        if (ng > 0) {
-            const RowRef row = locate(P, g, C);
-            load_chunks<F, U>(row.w, row.m, cb, ce, lane, va, ma);
+        {
+            const RowRef row = locate(P, ng > 0 ? g : 0, C);
+            load_chunks<F, U>(row.w, row.m, cb, ng > 0 ? ce : cb, lane, va, ma);
         }
-        __syncthreads();
-        stage_x<F, NB>(xs, x4, K, t0, tc, bstride);
+        __syncthreads();                          // the previous tile's x is no longer read
+        x_store_tile<F, NB>(xs, x4, K, t0, tc, bstride, xr, dummy);
         __syncthreads();
 
         float acc[NB];
@@ -509,6 +536,10 @@ __global__ __launch_bounds__(512) void stream_kernel(const Parts P, const u32x4*
             const int t = j / gpr, q = j - t * gpr;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
+                // Slots past the row's end for the whole wave are skipped
+                // (a wave-uniform branch); a partly filled slot is zeroed.
+                if (q * kWave * U + u * kWave >= ce - cb)
+                    break;
                 const int c = cb + q * kWave * U + lane + u * kWave;
                 const bool live = c < ce;
                 u32x4 vv = v[u];
@@ -691,9 +722,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, 
 
 // Launch-shape overrides, read once, for tuning sweeps (0 = built-in choice):
 // NMSPMV_KERNEL 1 = row-slice, 3 = stream; NMSPMV_SLICES,
-// NMSPMV_ROWS_PER_BLOCK (row-slice); NMSPMV_BLOCKS, NMSPMV_THREADS (stream).
+// NMSPMV_ROWS_PER_BLOCK (row-slice); NMSPMV_BLOCKS, NMSPMV_THREADS,
+// NMSPMV_TILE_BYTES (stream).
 struct Env {
-    int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0;
+    int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0;
 };
 Env g_env;
 std::once_flag g_env_once;
@@ -709,6 +741,7 @@ void read_env()
     g_env.rpb = get("NMSPMV_ROWS_PER_BLOCK");
     g_env.blocks = get("NMSPMV_BLOCKS");
     g_env.threads = get("NMSPMV_THREADS");
+    g_env.tile_bytes = get("NMSPMV_TILE_BYTES");
 }
 
 int g_cu_count[64] = {};
@@ -802,18 +835,41 @@ Plan plan_for(int64_t R, int64_t K, int B)
     }
     const int cus = cu_count();
     P.kind = 3;
-    P.threads = (g_env.threads > 0 && g_env.threads <= 512 && g_env.threads % kWave == 0) ? g_env.threads : 512;
+    // Two 512-thread blocks per CU; x larger than the tile budget is cut into
+    // equal K-tiles of whole 1024-column units (each tile costs a barrier and
+    // an x restage per block).
+    int threads = 512;
+    if (g_env.threads > 0 && g_env.threads <= 1024 && g_env.threads % kWave == 0)
+        threads = g_env.threads;
+    P.threads = threads;
     const int nw = P.threads / kWave;
     int64_t blocks = g_env.blocks > 0 ? g_env.blocks : 2LL * cus;
     while (blocks > 1 && (blocks - 1) * nw >= R)
         --blocks;
+    const int64_t budget = g_env.tile_bytes > 0 ? g_env.tile_bytes : kXTileStream;
     int64_t tile = K;
-    if (!fits)
-        tile = ((int64_t)kXTileBudget / (2 * B)) / 1024 * 1024;
-    const int64_t rpw = (R + blocks * nw - 1) / (blocks * nw);
+    if ((int64_t)B * K * 2 > budget) {
+        const int64_t ntiles = ((int64_t)B * K * 2 + budget - 1) / budget;
+        tile = ((K + ntiles - 1) / ntiles + 1023) / 1024 * 1024;
+        if (tile >= K)
+            tile = K;
+    }
+    // With several tiles each wave keeps its rows' partial sums in LDS: more
+    // blocks when that would take more than 16 KB, narrower tiles if the
+    // block would still exceed the CU's LDS.
+    int64_t rpw = (R + blocks * nw - 1) / (blocks * nw);
+    if (tile < K) {
+        const int64_t rpw_max = std::max<int64_t>(1, (16 * 1024) / ((int64_t)nw * B * 4));
+        if (rpw > rpw_max) {
+            blocks = (R + nw * rpw_max - 1) / (nw * rpw_max);
+            rpw = (R + blocks * nw - 1) / (blocks * nw);
+        }
+        while (tile > 1024 && tab + (size_t)B * tile * 2 + (size_t)nw * rpw * B * 4 + sizeof(u32x4) > (size_t)kLdsMax)
+            tile -= 1024;
+    }
     P.tile_cols = (int)tile;
     P.grid = (unsigned)blocks;
-    P.lds = tab + (size_t)B * (size_t)tile * 2 + (tile < K ? (size_t)nw * rpw * B * 4 : 0);
+    P.lds = tab + (size_t)B * (size_t)tile * 2 + (tile < K ? (size_t)nw * rpw * B * 4 : 0) + sizeof(u32x4);
     return P;
 }
 
@@ -841,6 +897,15 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
         }
 #undef NM_SLICE
     } else {
+        if (P.lds > 64 * 1024) {
+            static bool raised = false;          // once per instantiation
+            if (!raised) {
+                if (hipFuncSetAttribute((const void*)stream_kernel<F, DT, NB, 4>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
+                    return NM_ERR_HIP;
+                raised = true;
+            }
+        }
         hipLaunchKernelGGL((stream_kernel<F, DT, NB, 4>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K,
                            P.tile_cols);
     }

@@ -330,3 +330,22 @@ def test_gemv_dense_multi(nm, dt, Rs, K, B):
         yref, A = oracle.gemv(bits(W), dt, bits(x))
         ok, worst, idx = oracle.check(bits(y), yref, A, dt)
         assert ok, (worst, idx)
+
+
+@pytest.mark.parametrize("B", [2, 8])
+def test_spmv_multi_tile_many_rows(nm, B):
+    """Several x tiles with more rows than one pass of the grid's waves: the
+    per-wave partial sums in LDS cover many rows."""
+    run_case(nm, 5000, 25600, 2, 4, "bf16", B, seed=14)
+
+
+@pytest.mark.parametrize("B", [3, 8])
+def test_gemv_dense_multi_tile_many_rows(nm, B):
+    tdt = torch.bfloat16
+    R, K = 3000, 25600
+    W = I.weight(R, K, tdt, I.seed_of("dmt", R, K, B))
+    x = I.activation_normal(B, K, tdt, I.seed_of("dmtx", R, K, B))
+    yref, A = oracle.gemv(bits(W), "bf16", bits(x))
+    y = nm.gemv_dense(gpu(W), gpu(x))
+    ok, worst, idx = oracle.check(bits(y), yref, A, "bf16")
+    assert ok, (worst, idx)
