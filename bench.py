@@ -228,10 +228,20 @@ def mlp_single(torch, lib, launches, cur, reps=10):
         us = time_ms(torch, lambda: run(lib.nm_spmv, sargs), reps) / len(sargs) * 1e3
         run(lib.nm_gemv_dense, dargs)
         usd = time_ms(torch, lambda: run(lib.nm_gemv_dense, dargs), reps) / len(dargs) * 1e3
+        # torch's own dense product (hipBLASLt / rocBLAS) on the same weights, as context
+        pairs = [(L.W[L.names.index(name)], L.x, L.yd[L.names.index(name)]) for L in launches if name in L.names]
+
+        def torch_linear():
+            for W, x, yd in pairs:
+                torch.matmul(x, W.t(), out=yd)
+        torch_linear()
+        ust = time_ms(torch, torch_linear, reps) / len(pairs) * 1e3
+        best_dense = min(usd, ust)
         out[name] = {"shape": [R, K], "us": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
                      "pct_of_peak": round(100 * nbytes / us / 1e3 / PEAK_GBS, 2),
                      "dense_us": round(usd, 3), "dense_gbs": round(dbytes / usd / 1e3, 1),
-                     "speedup": round(usd / us, 4)}
+                     "torch_matmul_us": round(ust, 3), "speedup": round(usd / us, 4),
+                     "speedup_vs_best_dense": round(best_dense / us, 4)}
     return out
 
 
