@@ -116,6 +116,17 @@ class Launch:
         return (I32(c), (P * c)(*[W.data_ptr() for W in self.W]), (I64 * c)(*self.R), I64(self.K), I32(self.dtc),
                 P(self.x.data_ptr()), I32(self.B), (P * c)(*[y.data_ptr() for y in self.yd]), P(stream))
 
+    def glu_args(self, stream, dense=False):
+        """Arguments of nm_spmv_swiglu (or nm_gemv_dense_swiglu) for a gate+up launch."""
+        if not hasattr(self, "h"):
+            self.h = self.y[0].new_empty((self.B, self.R[0]))
+        if dense:
+            return (P(self.W[0].data_ptr()), P(self.W[1].data_ptr()), I64(self.R[0]), I64(self.K), I32(self.dtc),
+                    P(self.x.data_ptr()), I32(self.B), P(self.h.data_ptr()), P(stream))
+        return (P(self.values[0].data_ptr()), P(self.masks[0].data_ptr()), P(self.values[1].data_ptr()),
+                P(self.masks[1].data_ptr()), I64(self.R[0]), I64(self.K), I32(self.n), I32(self.m), I32(self.dtc),
+                P(self.x.data_ptr()), I32(self.B), P(self.h.data_ptr()), P(stream))
+
     def part_bytes(self, i):
         R, K = self.R[i], self.K
         return R * K * self.n // self.m * 2 + R * K // 8 + self.B * R * 2
@@ -384,6 +395,22 @@ def main():
         per[kind] = {"rows": sum(group[0].R), "K": group[0].K, "us": round(us, 3), "gbs": round(sb / us / 1e3, 1),
                      "dense_us": round(usd, 3), "dense_gbs": round(db / usd / 1e3, 1), "speedup": round(usd / us, 4),
                      "bytes": sb}
+
+    # ---- gated MLP input as one launch: h = SiLU(gate x) * (up x) ----
+    group = [L for L in launches if L.names == ("gate", "up")]
+    if group:
+        sl = [L.glu_args(cur) for L in group]
+        dl = [L.glu_args(cur, dense=True) for L in group]
+        run(lib.nm_spmv_swiglu, sl)
+        us = time_ms(torch, lambda: run(lib.nm_spmv_swiglu, sl), 5) / len(sl) * 1e3
+        run(lib.nm_gemv_dense_swiglu, dl)
+        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense_swiglu, dl), 5) / len(dl) * 1e3
+        L0 = group[0]
+        sb = L0.sparse_bytes() - L0.B * L0.R[1] * 2          # one output of R rows instead of two
+        db = L0.dense_bytes() - L0.B * L0.R[1] * 2
+        per["gate+up+silu"] = {"rows": L0.R[0], "K": L0.K, "us": round(us, 3), "gbs": round(sb / us / 1e3, 1),
+                               "dense_us": round(usd, 3), "dense_gbs": round(db / usd / 1e3, 1),
+                               "speedup": round(usd / us, 4), "bytes": sb}
 
     if a.workload == "llama31_8b":
         # roofline kernel: the instantiation shared by the K = 4096 launches (3 per layer)

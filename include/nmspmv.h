@@ -130,6 +130,31 @@ int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* ma
 int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t K, int dtype, const void* x, int B,
                         void* const* y, void* stream);
 
+/*
+ * nm_spmv_swiglu -- the gated-MLP input of a decode layer in one launch:
+ *   h[b][r] = SiLU(g) * u,  g = (W_gate x_b)[r],  u = (W_up x_b)[r],
+ *   SiLU(t) = t / (1 + e^-t).
+ * The models the SparseDecoding pages evaluate (Llama-3.1-8B, Llama-3.3-70B,
+ * Qwen3-14B/32B; "SparseDecoding: Decoding-Aware Pruning ...", Abstract) use
+ * this SiLU-gated MLP; the pages themselves do not describe the layer, so
+ * this fusion of the two N:M products that share x is this library's own.
+ *   values_gate, masks_gate, values_up, masks_up  two packed [R][K] matrices
+ *                  (nm_pack layout) with the same K, N:M and dtype.
+ *   x [B][K], h [B][R] (output), dtype as in nm_spmv.
+ * g and u are the fp32 sums nm_spmv would form (never rounded to 16 bits);
+ * SiLU and the product are evaluated in double precision (fp32 would flush
+ * SiLU(g) to 0 below g = -88.7, where bf16 still represents h) and the result
+ * is rounded to fp32, then to dtype, to nearest even.  Rules as for nm_spmv,
+ * plus: h must not overlap any input.
+ */
+int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const void* values_up, const uint8_t* masks_up,
+                   int64_t R, int64_t K, int N, int M, int dtype, const void* x, int B, void* h, void* stream);
+
+/* nm_gemv_dense_swiglu -- the dense baseline of nm_spmv_swiglu: h = SiLU(W_gate x) * (W_up x)
+ * for dense [R][K] W_gate and W_up, in one launch; rules as for nm_gemv_dense. */
+int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_t K, int dtype, const void* x, int B,
+                         void* h, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* nm_status_string(int status);
 

@@ -71,6 +71,11 @@ def _load(path):
         lib.orc_gemv_rows.argtypes = [P, I64, I64, I, P, I, I64, I64, P, P]
         lib.orc_round_array.argtypes = [P, I64, I, P]
         lib.orc_decode_array.argtypes = [P, I64, I, P]
+        lib.orc_silu.argtypes = [ctypes.c_double]
+        lib.orc_silu.restype = ctypes.c_double
+        lib.orc_swiglu.argtypes = [P, P, I64, P]
+        lib.orc_calib_accumulate.argtypes = [P, P, I64, I64, I, P, P]
+        lib.orc_calib_keep.argtypes = [P, P, I64, I64, I, I, I, P]
         for f in ("orc_pack", "orc_expand", "orc_spmv_rows", "orc_gemv_rows"):
             getattr(lib, f).restype = ctypes.c_int
         lib.orc_round_array.restype = None
@@ -172,6 +177,56 @@ def gemv(W, dtype, x, rows=None):
     return y[:, r0:r1].copy(), A[:, r0:r1].copy()
 
 
+def silu(t):
+    """SiLU(t) = t / (1 + e^-t) of one float, in double."""
+    return float(_lib().orc_silu(float(t)))
+
+
+def swiglu(g, u):
+    """h = SiLU(g) * u elementwise, in double (g, u: the exact sums of the
+    gate and up products)."""
+    g = np.ascontiguousarray(g, np.float64)
+    u = np.ascontiguousarray(u, np.float64)
+    assert g.shape == u.shape
+    h = np.zeros(g.shape, np.float64)
+    _lib().orc_swiglu(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+def calib_accumulate(X, dtype, decode=None, H=None, A=None):
+    """Decoding-aware calibration statistics in double: H += sum over decode
+    rows t of x_t x_t^T (X [T][K] 16-bit encodings; decode [T] bytes, nonzero =
+    decode step, None = all rows), and A += the sum of |x_ti x_tj|.  Returns
+    (H, A), each [K][K] float64."""
+    X = _u16(np.atleast_2d(X))
+    T, K = X.shape
+    H = np.zeros((K, K), np.float64) if H is None else np.ascontiguousarray(H, np.float64).copy()
+    A = np.zeros((K, K), np.float64) if A is None else np.ascontiguousarray(A, np.float64).copy()
+    d = None
+    if decode is not None:
+        d = np.ascontiguousarray(decode, np.uint8)
+        assert d.shape == (T,)
+    st = _lib().orc_calib_accumulate(_ptr(X), None if d is None else _ptr(d), T, K, _dt(dtype), _ptr(H), _ptr(A))
+    if st != OK:
+        raise OracleError(st)
+    return H, A
+
+
+def calib_keep(W, hdiag, n, m, dtype):
+    """Keep-mask [R][K] (uint8, 1 = keep) of the n columns per m-group with the
+    largest w^2 * hdiag[c], lower column on ties.  hdiag: float32 values (the
+    diagonal the GPU reads), used exactly."""
+    W = _u16(W)
+    R, K = W.shape
+    h = np.ascontiguousarray(np.asarray(hdiag, np.float32).astype(np.float64))
+    assert h.shape == (K,)
+    keep = np.zeros((R, K), np.uint8)
+    st = _lib().orc_calib_keep(_ptr(W), _ptr(h), R, K, n, m, _dt(dtype), _ptr(keep))
+    if st != OK:
+        raise OracleError(st)
+    return keep
+
+
 # ---- acceptance rule ------------------------------------------------------
 
 _FMT = {FP16: (10, -14), BF16: (7, -126)}   # (fraction bits, min normal exponent)
@@ -211,3 +266,54 @@ def max_terms_bound(n_terms):
     u = math.ldexp(1.0, -24)
     k = n_terms - 1
     return k * u / (1 - k * u)
+
+
+# SiLU is Lipschitz with constant max|SiLU'| = 1.0998 (at t ~ 2.40); 1.1 bounds it.
+SILU_LIP = 1.1
+# Evaluation of SiLU(g) * u from the fp32 sums (a few roundings in double, then
+# one to fp32 before the 16-bit rounding): 2^-24 relative and change; 1e-5
+# covers it with a wide margin.
+GLU_EVAL_REL = 1e-5
+
+
+def swiglu_tolerance(g_ref, u_ref, Ag, Au, dtype, exact_sums=False):
+    """Bound on |h_gpu - h_ref| for h = SiLU(g) * u computed from fp32 sums g,
+    u whose own errors obey the product rule (|e| <= 2e-3 * sum|w*x|; zero when
+    the sums are exact, e.g. integer-valued operands):
+        |SiLU(g)u - SiLU(g_ref)u_ref| <= 1.1 e_g (|u_ref| + e_u) + |SiLU(g_ref)| e_u
+    plus the fp32 evaluation error and one ulp of the output format."""
+    g_ref, u_ref = np.asarray(g_ref, np.float64), np.asarray(u_ref, np.float64)
+    eg = np.zeros_like(g_ref) if exact_sums else REL_TOL * np.asarray(Ag, np.float64)
+    eu = np.zeros_like(u_ref) if exact_sums else REL_TOL * np.asarray(Au, np.float64)
+    h_ref = swiglu(g_ref, u_ref)
+    s_ref = np.abs(swiglu(g_ref, np.ones_like(g_ref)))
+    return (SILU_LIP * eg * (np.abs(u_ref) + eu) + s_ref * eu + GLU_EVAL_REL * np.abs(h_ref) + ulp(h_ref, dtype))
+
+
+def check_swiglu(h_bits, g_ref, u_ref, Ag, Au, dtype, exact_sums=False):
+    """(ok, worst_ratio, index) for a GPU h (16-bit encodings) against
+    SiLU(g_ref) * u_ref."""
+    got = decode(h_bits, dtype)
+    h_ref = swiglu(g_ref, u_ref)
+    err = np.abs(got - h_ref)
+    tol = swiglu_tolerance(g_ref, u_ref, Ag, Au, dtype, exact_sums)
+    ratio = np.where(np.isfinite(err), err / tol, np.inf)
+    idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape) if ratio.size else ()
+    worst = float(ratio[idx]) if ratio.size else 0.0
+    return bool(np.all(err <= tol)), worst, idx
+
+
+def check_calib(H_gpu, H_ref, A, H0=None):
+    """(ok, worst_ratio, index) for a GPU fp32 H against the double H_ref: any
+    fp32 summation order of T exact products (plus the prior contents H0)
+    errs by at most gamma_T * (sum|x_i x_j| + |H0|) (gamma_T < 2e-3 for T up to
+    ~33000); one fp32 ulp at H_ref covers the last rounding."""
+    H_gpu = np.asarray(H_gpu, np.float64)
+    base = np.asarray(A, np.float64) + (0.0 if H0 is None else np.abs(np.asarray(H0, np.float64)))
+    ulp32 = np.spacing(np.abs(H_ref).astype(np.float32)).astype(np.float64)
+    tol = REL_TOL * base + ulp32
+    err = np.abs(H_gpu - H_ref)
+    ratio = np.where(np.isfinite(err), err / tol, np.inf)
+    idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape) if ratio.size else ()
+    worst = float(ratio[idx]) if ratio.size else 0.0
+    return bool(np.all(err <= tol)), worst, idx

@@ -361,3 +361,98 @@ int orc_spmv(const uint16_t* values, const uint8_t* masks, int64_t R, int64_t K,
 {
     return orc_spmv_rows(values, masks, R, K, N, M, dtype, x, B, 0, R, y, A);
 }
+
+/* ---- gated-MLP epilogue --------------------------------------------------------
+ * The decoder MLP of the model families the pages evaluate (Llama-3.1,
+ * Llama-3.3, Qwen3) is SiLU-gated: h = SiLU(W_gate x) * (W_up x) elementwise,
+ * SiLU(t) = t * sigmoid(t) = t / (1 + e^-t).  The pages do not describe the
+ * layer; this is the definition written out, applied to the exact double
+ * sums that orc_spmv / orc_gemv return.
+ */
+double orc_silu(double t)
+{
+    return t / (1.0 + exp(-t));
+}
+
+void orc_swiglu(const double* g, const double* u, int64_t n, double* h)
+{
+    for (int64_t i = 0; i < n; ++i)
+        h[i] = orc_silu(g[i]) * u[i];
+}
+
+/* ---- decoding-aware calibration ---------------------------------------------
+ * "SparseDecoding: Decoding-Aware Pruning ..." (Abstract) and "SparseDecoding
+ * Makes LLM Pruning Aware of Generation" (Key points; section on why fixed-text
+ * calibration misses): the pruning objective is built from the layer inputs
+ * seen while the dense model generates, prefill excluded, and it is
+ * Hessian-guided.  The pages give no formula.  Readings taken here:
+ *   - the Hessian of a linear layer's squared output error is H = sum_t x_t x_t^T
+ *     over its input rows x_t (up to a constant factor, which changes no
+ *     decision); only rows marked as decode steps enter the sum;
+ *   - the N:M keep-mask keeps, per group, the N columns of largest saliency
+ *     w^2 * H_jj (the optimal-brain-surgeon saliency with H taken diagonal),
+ *     ties to the lower column, like the magnitude rule.
+ */
+
+/* H[i][j] += sum over decode rows t of x[t][i] * x[t][j] (row-major K x K),
+ * and A[i][j] += the same sum of |x[t][i] * x[t][j]|.  decode == NULL means
+ * every row is a decode step. */
+int orc_calib_accumulate(const uint16_t* X, const uint8_t* decode, int64_t T, int64_t K, int dtype, double* H,
+                         double* A)
+{
+    if (T < 0 || K < 0 || (dtype != ORC_FP16 && dtype != ORC_BF16))
+        return ORC_BAD_ARG;
+    double* row = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    if (!row)
+        return ORC_BAD_ARG;
+    for (int64_t t = 0; t < T; ++t) {
+        if (decode && !decode[t])
+            continue;                                   /* prefill row: excluded */
+        for (int64_t i = 0; i < K; ++i)
+            row[i] = orc_to_double(X[t * K + i], dtype);
+        for (int64_t i = 0; i < K; ++i)
+            for (int64_t j = 0; j < K; ++j) {
+                double p = row[i] * row[j];             /* exact: two 16-bit significands */
+                H[i * K + j] += p;
+                A[i * K + j] += fabs(p);
+            }
+    }
+    free(row);
+    return ORC_OK;
+}
+
+/* keep[r][c] = 1 for the N columns of each M-group of row r with the largest
+ * saliency w^2 * h[c], 0 elsewhere; equal saliencies go to the lower column.
+ * h holds the Hessian diagonal (fp32 values, passed exactly as doubles).  The
+ * saliency is formed exactly in double (w^2 has at most 22 significant bits,
+ * h 24).  A NaN saliency ranks below every other. */
+int orc_calib_keep(const uint16_t* W, const double* h, int64_t R, int64_t K, int N, int M, int dtype, uint8_t* keep)
+{
+    int st = check_nm(R, K, N, M);
+    if (st != ORC_OK)
+        return st;
+    if (dtype != ORC_FP16 && dtype != ORC_BF16)
+        return ORC_BAD_ARG;
+    double sal[8];
+    int taken[8];
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t g = 0; g < K / M; ++g) {
+            for (int j = 0; j < M; ++j) {
+                int64_t c = g * M + j;
+                double w = orc_to_double(W[r * K + c], dtype);
+                double s = w * w * h[c];
+                sal[j] = isnan(s) ? -1.0 : s;
+                taken[j] = 0;
+                keep[r * K + c] = 0;
+            }
+            for (int k = 0; k < N; ++k) {
+                int best = -1;
+                for (int j = 0; j < M; ++j)
+                    if (!taken[j] && (best < 0 || sal[j] > sal[best]))
+                        best = j;
+                taken[best] = 1;
+                keep[r * K + g * M + best] = 1;
+            }
+        }
+    return ORC_OK;
+}

@@ -7,6 +7,7 @@ step of the computation runs in the HIP kernels of ``libnmspmv.so``.
     values, masks = pack(W, keep=None, n=2, m=4)   # offline: prune + pack
     y = spmv(values, masks, x, n=2, m=4)           # per token: y = W_sparse x
     y = gemv_dense(W, x)                           # dense baseline
+    h = spmv_swiglu((vg, mg), (vu, mu), x)         # SiLU(W_gate x) * (W_up x)
 """
 import ctypes
 
@@ -15,7 +16,8 @@ import torch
 from ._lib import (NM_BF16, NM_ERR_BAD_MASK, NM_ERR_BAD_SHAPE, NM_ERR_HIP, NM_ERR_INVALID_ARG,  # noqa: F401
                    NM_ERR_NONFINITE, NM_ERR_UNSUPPORTED, NM_FP16, NM_OK, NmError, call, lib)
 
-__all__ = ["pack", "spmv", "spmv_multi", "gemv_dense", "gemv_dense_multi", "NmError", "dtype_code", "stream_handle"]
+__all__ = ["pack", "spmv", "spmv_multi", "spmv_swiglu", "gemv_dense", "gemv_dense_multi", "gemv_dense_swiglu",
+           "NmError", "dtype_code", "stream_handle"]
 
 _DT = {torch.float16: NM_FP16, torch.bfloat16: NM_BF16}
 
@@ -144,3 +146,43 @@ def gemv_dense_multi(Ws, x, stream=None):
          (ctypes.c_int64 * len(Ws))(*[W.shape[0] for W in Ws]), K, dtype_code(x.dtype), x2.data_ptr(), B,
          _ptr_array([y.data_ptr() for y in ys]), stream_handle(stream))
     return [y[0] for y in ys] if squeeze else ys
+
+
+def _x2(x):
+    _dev(x, "x")
+    squeeze = x.dim() == 1
+    return (x.unsqueeze(0) if squeeze else x), squeeze
+
+
+def spmv_swiglu(gate, up, x, n=2, m=4, out=None, stream=None):
+    """h = SiLU(W_gate x) * (W_up x) in one launch.  ``gate`` and ``up`` are
+    (values, masks) pairs packed with the same n:m; x is [K] or [B][K];
+    returns [R] or [B][R]."""
+    (vg, mg), (vu, mu) = gate, up
+    for t, name in ((vg, "gate values"), (mg, "gate masks"), (vu, "up values"), (mu, "up masks")):
+        _dev(t, name)
+    x2, squeeze = _x2(x)
+    B, K = x2.shape
+    R = mg.shape[0]
+    if mg.shape != (R, K // 8) or mu.shape != mg.shape or vg.shape != (R, K // m * n) or vu.shape != vg.shape:
+        raise ValueError("gate/up shapes do not match x and n:m")
+    if vg.dtype != x.dtype or vu.dtype != x.dtype:
+        raise ValueError("values must be in x's dtype")
+    h = torch.empty((B, R), dtype=x.dtype, device=x.device) if out is None else _dev(out, "out")
+    call("nm_spmv_swiglu", vg.data_ptr(), mg.data_ptr(), vu.data_ptr(), mu.data_ptr(), R, K, n, m,
+         dtype_code(x.dtype), x2.data_ptr(), B, h.data_ptr(), stream_handle(stream))
+    return h[0] if squeeze else h
+
+
+def gemv_dense_swiglu(W_gate, W_up, x, out=None, stream=None):
+    """Dense baseline of spmv_swiglu: h = SiLU(W_gate x) * (W_up x)."""
+    _dev(W_gate, "W_gate"), _dev(W_up, "W_up")
+    x2, squeeze = _x2(x)
+    B, K = x2.shape
+    R = W_gate.shape[0]
+    if W_gate.shape != (R, K) or W_up.shape != (R, K) or W_gate.dtype != x.dtype or W_up.dtype != x.dtype:
+        raise ValueError("W_gate/W_up must be [R][K] in x's dtype")
+    h = torch.empty((B, R), dtype=x.dtype, device=x.device) if out is None else _dev(out, "out")
+    call("nm_gemv_dense_swiglu", W_gate.data_ptr(), W_up.data_ptr(), R, K, dtype_code(x.dtype), x2.data_ptr(), B,
+         h.data_ptr(), stream_handle(stream))
+    return h[0] if squeeze else h

@@ -200,36 +200,36 @@ __device__ __forceinline__ int x_slot(int b, int j, int bstride)
 // units) into registers before the weight loads are issued; x_store writes
 // them to LDS, and the rest, if any, straight through.  Loads retire in issue
 // order, so a wave can store its x and reach the block barrier while its
-// weight loads are still in flight.
-constexpr int kXU = 4;
+// weight loads are still in flight.  The loads are branch-free (lanes past
+// the end of x reload unit 0, one cache line per wave) so that the compiler
+// can count them exactly; only the LDS stores are predicated.  The launch
+// sizes XU to cover x, so few such reloads happen.
+constexpr int kXU = 4;    // x registers of the stream kernel (per tile)
 
-template <int NB>
+template <int NB, int XU>
 __device__ __forceinline__ void x_fetch(const u32x4* __restrict__ x4, int K, u32x4* xr)
 {
     const int n = NB * (K / 8);
 #pragma unroll
-    for (int u = 0; u < kXU; ++u) {
+    for (int u = 0; u < XU; ++u) {
         const int i = threadIdx.x + u * blockDim.x;
         xr[u] = x4[i < n ? i : 0];               // x [NB][K] is contiguous: unit i = batch i/q, unit i%q
     }
 }
 
-// Units past the end of x go to the spare slot `dummy` (one unit past the
-// kernel's other LDS data), keeping the stores branch-free too.
-template <int F, int NB>
-__device__ __forceinline__ void x_store(u32x4* xs, const u32x4* __restrict__ x4, int K, int bstride, const u32x4* xr,
-                                        u32x4* dummy)
+template <int F, int NB, int XU>
+__device__ __forceinline__ void x_store(u32x4* xs, const u32x4* __restrict__ x4, int K, int bstride, const u32x4* xr)
 {
     const int q = K / 8;
 #pragma unroll
-    for (int u = 0; u < kXU; ++u) {
+    for (int u = 0; u < XU; ++u) {
         const int i = threadIdx.x + u * blockDim.x;
-        const int b = i / q;
-        u32x4* dst = i < NB * q ? xs + x_slot<F>(b, i - b * q, bstride) : dummy;
-        *dst = xr[u];
+        const int b = NB == 1 ? 0 : i / q;      // (NB == 1: i < q whenever it is used)
+        if (i < NB * q)
+            xs[x_slot<F>(b, i - b * q, bstride)] = xr[u];
     }
-    for (int i = threadIdx.x + kXU * blockDim.x; i < NB * q; i += blockDim.x) {
-        const int b = i / q;
+    for (int i = threadIdx.x + XU * blockDim.x; i < NB * q; i += blockDim.x) {
+        const int b = NB == 1 ? 0 : i / q;      // (NB == 1: i < q whenever it is used)
         xs[x_slot<F>(b, i - b * q, bstride)] = x4[i];
     }
 }
@@ -243,25 +243,25 @@ __device__ __forceinline__ void x_fetch_tile(const u32x4* __restrict__ x4, int K
     for (int u = 0; u < kXU; ++u) {
         int i = threadIdx.x + u * blockDim.x;
         i = i < n ? i : 0;
-        const int b = i / q;
+        const int b = NB == 1 ? 0 : i / q;      // (NB == 1: i < q whenever it is used)
         xr[u] = x4[(size_t)b * (K / 8) + c0 / 8 + (i - b * q)];
     }
 }
 
 template <int F, int NB>
 __device__ __forceinline__ void x_store_tile(u32x4* xs, const u32x4* __restrict__ x4, int K, int c0, int cols,
-                                             int bstride, const u32x4* xr, u32x4* dummy)
+                                             int bstride, const u32x4* xr)
 {
     const int q = cols / 8, n = NB * q;
 #pragma unroll
     for (int u = 0; u < kXU; ++u) {
         const int i = threadIdx.x + u * blockDim.x;
-        const int b = i / q;
-        u32x4* dst = i < n ? xs + x_slot<F>(b, i - b * q, bstride) : dummy;
-        *dst = xr[u];
+        const int b = NB == 1 ? 0 : i / q;      // (NB == 1: i < q whenever it is used)
+        if (i < n)
+            xs[x_slot<F>(b, i - b * q, bstride)] = xr[u];
     }
     for (int i = threadIdx.x + kXU * blockDim.x; i < n; i += blockDim.x) {
-        const int b = i / q;
+        const int b = NB == 1 ? 0 : i / q;      // (NB == 1: i < q whenever it is used)
         xs[x_slot<F>(b, i - b * q, bstride)] = x4[(size_t)b * (K / 8) + c0 / 8 + (i - b * q)];
     }
 }
@@ -332,6 +332,11 @@ __device__ __forceinline__ void chunk_dot(const u32x4 v, const uint32_t mk, cons
 // Up to kMaxParts matrices with the same K (and format) multiplied by the
 // same x in one launch, their rows concatenated: part p owns rows
 // [begin[p], begin[p+1]) of the launch.  A single matrix is one part.
+// Gated mode (glu = 1) takes two parts of begin[1] rows each, the gate
+// (part 0) and up (part 1) projections of a gated MLP, and writes one output
+// h = SiLU(gate x) * (up x) to y[0]; its launch rows interleave the parts
+// (row 2i = gate row i, row 2i + 1 = up row i) so that both rows of an output
+// are always reduced by one block.
 constexpr int kMaxParts = 4;
 
 struct Parts {
@@ -340,6 +345,7 @@ struct Parts {
     uint16_t* y[kMaxParts];
     int begin[kMaxParts + 1];
     int count;
+    int glu;
 };
 
 struct RowRef {
@@ -363,6 +369,33 @@ __device__ __forceinline__ RowRef locate(const Parts& P, int r, int C)
     o.y = P.y[p] + rl;
     o.R = P.begin[p + 1] - P.begin[p];
     return o;
+}
+
+// Launch row r (see Parts for the gated interleave).
+__device__ __forceinline__ RowRef row_ref(const Parts& P, int r, int C)
+{
+    if (P.glu) {
+        const int i = r >> 1, p = r & 1;
+        RowRef o;
+        o.w = P.w[p] + (size_t)i * C;
+        o.m = P.m[p] + (size_t)i * C;
+        o.y = P.y[0] + i;
+        o.R = P.begin[1];
+        return o;
+    }
+    return locate(P, r, C);
+}
+
+// The gated-MLP output element: SiLU(g) * u with SiLU(t) = t / (1 + e^-t),
+// from the unrounded fp32 sums.  It is evaluated in double (once per output
+// row, so the cost is nil): in fp32, e^-g overflows for g < -88.7 and SiLU
+// would flush to 0 where bf16 still holds SiLU(g) * u.  The double result is
+// rounded to fp32 and then to the output format, nearest even each time.
+template <int DT>
+__device__ __forceinline__ uint16_t glu_out(float g, float u)
+{
+    const double gd = g;
+    return from_f32<DT>((float)(gd / (1.0 + exp(-gd)) * (double)u));
 }
 
 // Loads chunks [c0 + lane + 64 u] (u < U) of a row.  Every lane issues all U
@@ -402,7 +435,7 @@ __device__ __forceinline__ void chunk_live(bool live, u32x4& v, uint32_t& mk)
 // A lane issues all of its chunk loads (at most CPL) first, then the block
 // stages the selector table and x in LDS, computes, reduces each wave across
 // lanes, and adds a row's S slice sums in slice order.
-template <int F, int DT, int NB, int CPL>
+template <int F, int DT, int NB, int CPL, int XU>
 __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K, int S,
                                                         int rows_per_block)
 {
@@ -416,10 +449,10 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
     const int C = K / COLS;
     const int cps = (C + S - 1) / S;
     const int cbeg = sl * cps, cend = active ? min(C, cbeg + cps) : cbeg;
-    const RowRef row = locate(P, active ? r : 0, C);
+    const RowRef row = row_ref(P, active ? r : 0, C);
 
-    u32x4 xr[kXU];
-    x_fetch<NB>(x4, K, xr);
+    u32x4 xr[XU];
+    x_fetch<NB, XU>(x4, K, xr);
     u32x4 v[CPL];
     uint32_t mk[CPL];
     load_chunks<F, CPL>(row.w, row.m, cbeg, cend, lane, v, mk);
@@ -428,9 +461,8 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
     u32x4* xs = smem + table_units<F>();
     const int bstride = K / 8;
     float* part = reinterpret_cast<float*>(xs + NB * bstride);
-    u32x4* dummy = reinterpret_cast<u32x4*>(part + rows_per_block * S * NB);
     build_table<F>(tab);
-    x_store<F, NB>(xs, x4, K, bstride, xr, dummy);
+    x_store<F, NB, XU>(xs, x4, K, bstride, xr);
     __syncthreads();
 
     float acc[NB];
@@ -450,7 +482,7 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
 #pragma unroll
     for (int b = 0; b < NB; ++b)
         sum[b] = wave_sum(acc[b]);
-    if (S == 1) {
+    if (S == 1 && !P.glu) {
         if (active && lane == 0)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -462,6 +494,22 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
         for (int b = 0; b < NB; ++b)
             part[wave * NB + b] = sum[b];
     __syncthreads();
+    if (P.glu) {
+        // Local rows lr (gate, even) and lr + 1 (up) hold one output row; the
+        // gate row's first slice combines both, each in slice order.
+        if (active && (lr & 1) == 0 && sl == 0 && lane == 0) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float g = part[wave * NB + b], u = part[(wave + S) * NB + b];
+                for (int j = 1; j < S; ++j) {
+                    g += part[(wave + j) * NB + b];
+                    u += part[(wave + S + j) * NB + b];
+                }
+                row.y[(size_t)b * row.R] = glu_out<DT>(g, u);
+            }
+        }
+        return;
+    }
     if (active && sl == 0 && lane == 0) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -494,15 +542,24 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
     const int g = blockIdx.x * nw + wave;
     const int G = gridDim.x * nw;
     const int C = K / COLS;
-    const int rpw = (R + G - 1) / G;                       // rows per wave, at most
-    const int nrows = g < R ? (R - g + G - 1) / G : 0;
+    // The wave's t-th row is launch row g + t G; in gated mode it is the gate
+    // (t even) or up (t odd) row of output row g + (t / 2) G, so both rows of
+    // an output pass through the same wave, one after the other.
+    const int per = P.glu ? 2 : 1;
+    const int Ru = R / per;                                // rows (outputs) dealt to the waves
+    const int rpw = per * ((Ru + G - 1) / G);              // rows per wave, at most
+    const int nrows = per * (g < Ru ? (Ru - g + G - 1) / G : 0);
+    auto lrow = [&](int t) { return P.glu ? 2 * (g + (t >> 1) * G) + (t & 1) : g + t * G; };
     const bool multi = tile_cols < K;
+    float gs[NB];                                          // gated mode, one tile: the gate row's sums
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        gs[b] = 0.f;
     const int bstride = tile_cols / 8;
 
     u32x4* tab = smem;
     u32x4* xs = smem + table_units<F>();
     float* part = reinterpret_cast<float*>(xs + NB * bstride);
-    u32x4* dummy = reinterpret_cast<u32x4*>(part + (multi ? nw * rpw * NB : 0));
     build_table<F>(tab);
     if (multi)
         for (int i = threadIdx.x; i < nw * rpw * NB; i += blockDim.x)
@@ -521,11 +578,11 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
         u32x4 va[U], vb[U];
         uint32_t ma[U], mb[U];
         {
-            const RowRef row = locate(P, ng > 0 ? g : 0, C);
+            const RowRef row = row_ref(P, ng > 0 ? lrow(0) : 0, C);
             load_chunks<F, U>(row.w, row.m, cb, ng > 0 ? ce : cb, lane, va, ma);
         }
         __syncthreads();                          // the previous tile's x is no longer read
-        x_store_tile<F, NB>(xs, x4, K, t0, tc, bstride, xr, dummy);
+        x_store_tile<F, NB>(xs, x4, K, t0, tc, bstride, xr);
         __syncthreads();
 
         float acc[NB];
@@ -548,23 +605,26 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
                 chunk_dot<F, DT, NB>(vv, mm, tab, xs, live ? c - cb : 0, bstride, acc);
             }
             if (q == gpr - 1) {
-                const RowRef row = locate(P, g + t * G, C);
+                const RowRef row = row_ref(P, lrow(t), C);
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const float sum = wave_sum(acc[b]);
                     if (lane == 0) {
                         if (multi)
                             part[(wave * rpw + t) * NB + b] += sum;
-                        else
+                        else if (!P.glu)
                             row.y[(size_t)b * row.R] = from_f32<DT>(sum);
+                        else if (t & 1)
+                            row.y[(size_t)b * row.R] = glu_out<DT>(gs[b], sum);
                     }
+                    gs[b] = sum;
                     acc[b] = 0.f;
                 }
             }
         };
         auto fetch = [&](int j, u32x4* v, uint32_t* mk) {
             const int t = j / gpr, q = j - t * gpr;
-            const RowRef row = locate(P, g + t * G, C);
+            const RowRef row = row_ref(P, lrow(t), C);
             load_chunks<F, U>(row.w, row.m, cb + q * kWave * U, ce, lane, v, mk);
         };
         for (int j = 0; j < ng; j += 2) {
@@ -581,35 +641,34 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
     if (multi && lane == 0) {
         // part[] of this wave was written only by this wave's lane 0: no barrier needed.
         for (int t = 0; t < nrows; ++t) {
-            const RowRef row = locate(P, g + t * G, C);
+            const RowRef row = row_ref(P, lrow(t), C);
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                row.y[(size_t)b * row.R] = from_f32<DT>(part[(wave * rpw + t) * NB + b]);
+            for (int b = 0; b < NB; ++b) {
+                if (!P.glu)
+                    row.y[(size_t)b * row.R] = from_f32<DT>(part[(wave * rpw + t) * NB + b]);
+                else if (t & 1)
+                    row.y[(size_t)b * row.R] =
+                        glu_out<DT>(part[(wave * rpw + t - 1) * NB + b], part[(wave * rpw + t) * NB + b]);
+            }
         }
     }
 }
 
 // ---- generic N:M (any N < M, M in {4, 8}, K % 8 == 0) --------------------------
 
+// One lane step covers one mask byte (8 columns: two 4-groups or one
+// 8-group) and its 8 / M * N values at offset q * that (the fixed step).
 template <int DT, int NB>
-__global__ __launch_bounds__(256) void generic_spmv_kernel(const uint16_t* __restrict__ values,
-                                                           const uint8_t* __restrict__ masks,
-                                                           const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-                                                           int R, int K, int N, int M)
+__device__ __forceinline__ void generic_row(const uint16_t* __restrict__ vrow, const uint8_t* __restrict__ mrow,
+                                            const uint16_t* __restrict__ x, int K, int N, int M, int lane, float* acc)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (row >= R)                                // whole wave leaves together
-        return;
-    const int vpb = 8 / M * N;                   // values per mask byte (fixed step)
-    const size_t vrow = (size_t)(K / M) * N;
-    float acc[NB];
+    const int vpb = 8 / M * N;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
         acc[b] = 0.f;
     for (int q = lane; q < K / 8; q += kWave) {
-        const uint32_t mb = masks[(size_t)row * (K / 8) + q];
-        const uint16_t* vp = values + (size_t)row * vrow + (size_t)q * vpb;
+        const uint32_t mb = mrow[q];
+        const uint16_t* vp = vrow + (size_t)q * vpb;
         int k = 0;
         for (int j = 0; j < 8; ++j) {
             if (((mb >> j) & 1u) && k < vpb) {
@@ -622,11 +681,40 @@ __global__ __launch_bounds__(256) void generic_spmv_kernel(const uint16_t* __res
         }
     }
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const float s = wave_sum(acc[b]);
+    for (int b = 0; b < NB; ++b)
+        acc[b] = wave_sum(acc[b]);
+}
+
+// One wave per output row.  With values2 set (gated mode) the wave also
+// reduces row `row` of the second matrix and writes SiLU(first) * second.
+template <int DT, int NB>
+__global__ __launch_bounds__(256) void generic_spmv_kernel(const uint16_t* __restrict__ values,
+                                                           const uint8_t* __restrict__ masks,
+                                                           const uint16_t* __restrict__ values2,
+                                                           const uint8_t* __restrict__ masks2,
+                                                           const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+                                                           int R, int K, int N, int M)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (row >= R)                                // whole wave leaves together
+        return;
+    const size_t vrow = (size_t)(K / M) * N;
+    float acc[NB];
+    generic_row<DT, NB>(values + (size_t)row * vrow, masks + (size_t)row * (K / 8), x, K, N, M, lane, acc);
+    if (values2) {
+        float acc2[NB];
+        generic_row<DT, NB>(values2 + (size_t)row * vrow, masks2 + (size_t)row * (K / 8), x, K, N, M, lane, acc2);
         if (lane == 0)
-            y[(size_t)b * R + row] = from_f32<DT>(s);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                y[(size_t)b * R + row] = glu_out<DT>(acc[b], acc2[b]);
+        return;
     }
+    if (lane == 0)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            y[(size_t)b * R + row] = from_f32<DT>(acc[b]);
 }
 
 __global__ void fill_zero_kernel(uint16_t* __restrict__ y, int64_t n)
@@ -762,7 +850,7 @@ int cu_count()
 
 struct Plan {
     int kind = 0;            // 1 row-slice, 3 stream
-    int S = 1, rpb = 1, cpl = 1, threads = 256, tile_cols = 0;
+    int S = 1, rpb = 1, cpl = 1, xu = 4, threads = 256, tile_cols = 0;
     size_t lds = 0;
     unsigned grid = 1;
 };
@@ -775,8 +863,11 @@ struct Plan {
 //  * dense rows of <= 512 chunks: one wave per row, 4 rows per block;
 //    longer: the fewest slices that keep a lane at <= 7 chunks, 8 / S rows;
 //  * few rows (under ~16 waves per CU): more slices, down to 64 chunks each;
-//  * at least two blocks per CU.
-bool plan_rowslice(int64_t R, int64_t C, bool dense, Plan* P)
+//  * at least two blocks per CU;
+//  * a single x vector is staged from as few registers as cover it (1, 2 or
+//    4 units per thread); sparse rows cut into slices go in 16-wave blocks
+//    when that lets 2 units cover x (fewer registers, full occupancy).
+bool plan_rowslice(int64_t R, int64_t C, int64_t xunits, bool dense, bool glu, Plan* P)
 {
     const int cus = cu_count();
     int S = 1, rpb = dense ? 4 : 8;
@@ -793,21 +884,30 @@ bool plan_rowslice(int64_t R, int64_t C, bool dense, Plan* P)
     }
     if (g_env.slices > 0)
         S = g_env.slices;
+    if (glu && S > 8)                            // gated rows come in pairs: at least 2 rows per block
+        S = 8;
     const int64_t cps = (C + S - 1) / S;
     const int cpl = (int)((cps + kWave - 1) / kWave);
     if (cpl > 8)
         return false;
     while (rpb > 1 && (R + rpb - 1) / rpb < 2 * cus)
         rpb /= 2;
+    if (xunits <= 2048 && !dense && S >= 2 && rpb * S == 8 && xunits > 2 * 8 * kWave && (R + 2 * rpb - 1) / (2 * rpb) >= 2 * cus)
+        rpb *= 2;
     if (g_env.rpb > 0)
         rpb = g_env.rpb;
+    if (glu)
+        rpb = std::max(2, rpb & ~1);
     if (rpb * S > 16)
         return false;
+    const int64_t threads = (int64_t)rpb * S * kWave;
+    const int64_t per_thread = (xunits + threads - 1) / threads;
     P->kind = 1;
     P->S = S;
     P->rpb = rpb;
     P->cpl = cpl;
-    P->threads = rpb * S * kWave;
+    P->xu = per_thread <= 1 ? 1 : per_thread <= 2 ? 2 : 4;
+    P->threads = (int)threads;
     P->grid = (unsigned)((R + rpb - 1) / rpb);
     return true;
 }
@@ -817,7 +917,7 @@ bool plan_rowslice(int64_t R, int64_t C, bool dense, Plan* P)
 // chunks (dense, K <= 16384); otherwise the stream kernel -- whose blocks
 // stage x once for many rows -- with x in K-tiles when it exceeds the budget.
 template <int F>
-Plan plan_for(int64_t R, int64_t K, int B)
+Plan plan_for(int64_t R, int64_t K, int B, bool glu)
 {
     std::call_once(g_env_once, read_env);
     constexpr int COLS = chunk_cols<F>();
@@ -829,8 +929,10 @@ Plan plan_for(int64_t R, int64_t K, int B)
     int kind = g_env.kernel;
     if (kind != 1 && kind != 3)
         kind = (fits && C <= (F == kDense ? 32 : 18) * kWave) ? 1 : 3;
-    if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, &P)) {
-        P.lds = tab + xbytes + (size_t)P.rpb * P.S * B * 4 + sizeof(u32x4);
+    if (kind == 1 && fits && plan_rowslice(R, C, (int64_t)B * K / 8, F == kDense, glu, &P)) {
+        if (B > 1)
+            P.xu = 4;                            // batched launches: one x register count
+        P.lds = tab + xbytes + (size_t)P.rpb * P.S * B * 4;
         return P;
     }
     const int cus = cu_count();
@@ -843,8 +945,11 @@ Plan plan_for(int64_t R, int64_t K, int B)
         threads = g_env.threads;
     P.threads = threads;
     const int nw = P.threads / kWave;
+    // Rows per wave as the kernel counts them (gated rows go to waves in pairs).
+    const int per = glu ? 2 : 1;
+    const int64_t Ru = R / per;
     int64_t blocks = g_env.blocks > 0 ? g_env.blocks : 2LL * cus;
-    while (blocks > 1 && (blocks - 1) * nw >= R)
+    while (blocks > 1 && (blocks - 1) * nw >= Ru)
         --blocks;
     const int64_t budget = g_env.tile_bytes > 0 ? g_env.tile_bytes : kXTileStream;
     int64_t tile = K;
@@ -857,19 +962,19 @@ Plan plan_for(int64_t R, int64_t K, int B)
     // With several tiles each wave keeps its rows' partial sums in LDS: more
     // blocks when that would take more than 16 KB, narrower tiles if the
     // block would still exceed the CU's LDS.
-    int64_t rpw = (R + blocks * nw - 1) / (blocks * nw);
+    int64_t rpw = per * ((Ru + blocks * nw - 1) / (blocks * nw));
     if (tile < K) {
-        const int64_t rpw_max = std::max<int64_t>(1, (16 * 1024) / ((int64_t)nw * B * 4));
+        const int64_t rpw_max = std::max<int64_t>(per, (16 * 1024) / ((int64_t)nw * B * 4));
         if (rpw > rpw_max) {
-            blocks = (R + nw * rpw_max - 1) / (nw * rpw_max);
-            rpw = (R + blocks * nw - 1) / (blocks * nw);
+            blocks = (Ru + nw * (rpw_max / per) - 1) / (nw * (rpw_max / per));
+            rpw = per * ((Ru + blocks * nw - 1) / (blocks * nw));
         }
-        while (tile > 1024 && tab + (size_t)B * tile * 2 + (size_t)nw * rpw * B * 4 + sizeof(u32x4) > (size_t)kLdsMax)
+        while (tile > 1024 && tab + (size_t)B * tile * 2 + (size_t)nw * rpw * B * 4 > (size_t)kLdsMax)
             tile -= 1024;
     }
     P.tile_cols = (int)tile;
     P.grid = (unsigned)blocks;
-    P.lds = tab + (size_t)B * (size_t)tile * 2 + (tile < K ? (size_t)nw * rpw * B * 4 : 0) + sizeof(u32x4);
+    P.lds = tab + (size_t)B * (size_t)tile * 2 + (tile < K ? (size_t)nw * rpw * B * 4 : 0);
     return P;
 }
 
@@ -879,12 +984,29 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
 template <int F, int DT, int NB>
 int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
 {
-    const Plan P = plan_for<F>(R, K, NB);
+    const Plan P = plan_for<F>(R, K, NB, parts.glu != 0);
     const u32x4* x4 = static_cast<const u32x4*>(x);
     (void)hipGetLastError();
     if (P.kind == 1) {
-#define NM_SLICE(CPL) \
-    hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, CPL>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, P.S, P.rpb)
+        // Single-vector launches pick 1, 2 or 4 x registers per thread;
+        // batched ones always use 4 (fewer instantiations).
+        const int xu = NB == 1 ? P.xu : 4;
+#define NM_SLICE_XU(CPL, XU) \
+    hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, CPL, XU>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, \
+                       P.S, P.rpb)
+#define NM_SLICE(CPL)                                            \
+    do {                                                         \
+        if constexpr (NB == 1) {                                 \
+            if (xu == 1)                                         \
+                NM_SLICE_XU(CPL, 1);                             \
+            else if (xu == 2)                                    \
+                NM_SLICE_XU(CPL, 2);                             \
+            else                                                 \
+                NM_SLICE_XU(CPL, 4);                             \
+        } else {                                                 \
+            NM_SLICE_XU(CPL, 4);                                 \
+        }                                                        \
+    } while (0)
         switch (P.cpl) {
         case 1: NM_SLICE(1); break;
         case 2: NM_SLICE(2); break;
@@ -896,6 +1018,7 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
         default: NM_SLICE(8); break;
         }
 #undef NM_SLICE
+#undef NM_SLICE_XU
     } else {
         if (P.lds > 64 * 1024) {
             static bool raised = false;          // once per instantiation
@@ -1001,12 +1124,13 @@ struct Sparse48 {
 
 template <int DT, int NB>
 struct SparseGeneric {
-    static int run(const void* v, const uint8_t* m, const void* x, void* y, int R, int K, int N, int M, hipStream_t s)
+    static int run(const void* v, const uint8_t* m, const void* v2, const uint8_t* m2, const void* x, void* y, int R,
+                   int K, int N, int M, hipStream_t s)
     {
         (void)hipGetLastError();
         const unsigned grid = (unsigned)((R + 3) / 4);
         hipLaunchKernelGGL((generic_spmv_kernel<DT, NB>), dim3(grid), dim3(256), 0, s, (const uint16_t*)v, m,
-                           (const uint16_t*)x, (uint16_t*)y, R, K, N, M);
+                           (const uint16_t*)v2, m2, (const uint16_t*)x, (uint16_t*)y, R, K, N, M);
         return hip_status(hipGetLastError());
     }
 };
@@ -1044,7 +1168,7 @@ int status_word(uint32_t** out)
 
 extern "C" {
 
-int nm_version(void) { return 100; }
+int nm_version(void) { return 101; }
 
 const char* nm_status_string(int status)
 {
@@ -1128,7 +1252,8 @@ int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* ma
     for (int i = 0; i < count; ++i) {
         if (R[i] == 0)
             continue;
-        if ((st = dispatch<SparseGeneric>(dtype, B, values[i], masks[i], x, y[i], (int)R[i], (int)K, N, M, s)) != NM_OK)
+        if ((st = dispatch<SparseGeneric>(dtype, B, values[i], masks[i], (const void*)nullptr, (const uint8_t*)nullptr, x,
+                                          y[i], (int)R[i], (int)K, N, M, s)) != NM_OK)
             return st;
     }
     return NM_OK;
@@ -1203,6 +1328,80 @@ int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64
 int nm_gemv_dense(const void* W, int64_t R, int64_t K, int dtype, const void* x, int B, void* y, void* stream)
 {
     return nm_gemv_dense_multi(1, &W, &R, K, dtype, x, B, &y, stream);
+}
+
+int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const void* values_up, const uint8_t* masks_up,
+                   int64_t R, int64_t K, int N, int M, int dtype, const void* x, int B, void* h, void* stream)
+{
+    int st = check_dtype(dtype);
+    if (st != NM_OK)
+        return st;
+    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
+        return st;
+    if (B < 1 || B > 8 || 2 * R > INT32_MAX)
+        return NM_ERR_BAD_SHAPE;
+    const size_t xbytes = (size_t)B * (size_t)K * 2, hbytes = (size_t)B * (size_t)R * 2;
+    const size_t vb = (size_t)R * (size_t)(K / M * N) * 2, mb = (size_t)R * (size_t)(K / 8);
+    if (!ptr_ok(x, xbytes, 16) || !ptr_ok(h, hbytes, 2) || !ptr_ok(values_gate, vb, 16) ||
+        !ptr_ok(masks_gate, mb, 16) || !ptr_ok(values_up, vb, 16) || !ptr_ok(masks_up, mb, 16))
+        return NM_ERR_INVALID_ARG;
+    if (overlaps(h, hbytes, x, xbytes) || overlaps(h, hbytes, values_gate, vb) || overlaps(h, hbytes, masks_gate, mb) ||
+        overlaps(h, hbytes, values_up, vb) || overlaps(h, hbytes, masks_up, mb))
+        return NM_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (R == 0)
+        return NM_OK;
+    if (K == 0)                                  // SiLU(0) * 0
+        return launch_zero(h, (int64_t)B * R, s);
+    if (K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8))) {
+        Parts P = {};
+        P.w[0] = static_cast<const u32x4*>(values_gate);
+        P.m[0] = reinterpret_cast<const uint16_t*>(masks_gate);
+        P.w[1] = static_cast<const u32x4*>(values_up);
+        P.m[1] = reinterpret_cast<const uint16_t*>(masks_up);
+        P.y[0] = static_cast<uint16_t*>(h);
+        P.count = 2;
+        P.glu = 1;
+        P.begin[1] = (int)R;
+        for (int i = 2; i <= kMaxParts; ++i)
+            P.begin[i] = (int)(2 * R);
+        return M == 4 ? dispatch<Sparse24>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s)
+                      : dispatch<Sparse48>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s);
+    }
+    return dispatch<SparseGeneric>(dtype, B, values_gate, masks_gate, values_up, masks_up, x, h, (int)R, (int)K, N, M, s);
+}
+
+int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_t K, int dtype, const void* x, int B,
+                         void* h, void* stream)
+{
+    int st = check_dtype(dtype);
+    if (st != NM_OK)
+        return st;
+    if ((st = check_rk(R, K)) != NM_OK)
+        return st;
+    if (B < 1 || B > 8 || 2 * R > INT32_MAX)
+        return NM_ERR_BAD_SHAPE;
+    const size_t xbytes = (size_t)B * (size_t)K * 2, hbytes = (size_t)B * (size_t)R * 2;
+    const size_t wb = (size_t)R * (size_t)K * 2;
+    if (!ptr_ok(x, xbytes, 16) || !ptr_ok(h, hbytes, 2) || !ptr_ok(W_gate, wb, 16) || !ptr_ok(W_up, wb, 16))
+        return NM_ERR_INVALID_ARG;
+    if (overlaps(h, hbytes, x, xbytes) || overlaps(h, hbytes, W_gate, wb) || overlaps(h, hbytes, W_up, wb))
+        return NM_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (R == 0)
+        return NM_OK;
+    if (K == 0)
+        return launch_zero(h, (int64_t)B * R, s);
+    Parts P = {};
+    P.w[0] = static_cast<const u32x4*>(W_gate);
+    P.w[1] = static_cast<const u32x4*>(W_up);
+    P.y[0] = static_cast<uint16_t*>(h);
+    P.count = 2;
+    P.glu = 1;
+    P.begin[1] = (int)R;
+    for (int i = 2; i <= kMaxParts; ++i)
+        P.begin[i] = (int)(2 * R);
+    return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s);
 }
 
 int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int M, int dtype, void* values,

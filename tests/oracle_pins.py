@@ -397,6 +397,140 @@ def pin_errors():
             raise AssertionError(f"shape {(R, K, n, m)} accepted")
 
 
+def pin_silu():
+    """SiLU against closed forms: SiLU(0) = 0; sigmoid(ln 3) = 3/4, so
+    SiLU(+-ln 3) = 3/4 ln 3 and -1/4 ln 3; SiLU(t) - SiLU(-t) = t; SiLU(t) -> t
+    for large t and -> 0 for very negative t; the minimum sits at
+    t* = -1 - W(1/e) (Lambert W) with value t* + 1 (there 1 + t (1 - sigmoid) = 0,
+    so sigmoid = 1 + 1/t and t sigmoid = t + 1)."""
+    from scipy.special import lambertw
+    ln3 = math.log(3.0)
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(ln3) - 0.75 * ln3) <= 4e-16
+    assert abs(oracle.silu(-ln3) + 0.25 * ln3) <= 4e-16
+    for t in np.concatenate([np.linspace(0.01, 30.0, 97), [1e-6, 1e-3, 2.5, 7.0]]):
+        assert abs(oracle.silu(t) - oracle.silu(-t) - t) <= 1e-15 * max(1.0, t)
+    assert oracle.silu(50.0) == 50.0
+    assert oracle.silu(-800.0) == 0.0
+    tstar = -1.0 - float(lambertw(math.exp(-1.0)).real)
+    assert abs(oracle.silu(tstar) - (tstar + 1.0)) <= 1e-15
+    grid = np.linspace(-4.0, 1.0, 5001)
+    vals = np.array([oracle.silu(t) for t in grid])
+    assert abs(grid[int(np.argmin(vals))] - tstar) <= 1e-3
+    assert vals.min() >= tstar + 1.0 - 1e-15
+
+
+def pin_swiglu():
+    """h = SiLU(g) * u elementwise: known values, u = 1 gives SiLU itself, and
+    the roles of g and u are not symmetric (swapping them changes h)."""
+    ln3 = math.log(3.0)
+    h = oracle.swiglu(np.array([ln3, 0.0, -ln3, 2.0]), np.array([2.0, 5.0, 4.0, -1.0]))
+    want = np.array([1.5 * ln3, 0.0, -ln3, -2.0 / (1.0 + math.exp(-2.0))])
+    assert np.all(np.abs(h - want) <= 4e-16 * np.maximum(1.0, np.abs(want)))
+    g = np.linspace(-6.0, 6.0, 49)
+    assert np.array_equal(oracle.swiglu(g, np.ones_like(g)), np.array([oracle.silu(t) for t in g]))
+    assert oracle.swiglu(np.array([3.0]), np.array([-2.0]))[0] != oracle.swiglu(np.array([-2.0]), np.array([3.0]))[0]
+
+
+def _bitmap_to_keep(masks, K):
+    """1-bit-per-column bitmap [R][K/8] -> keep bytes [R][K]."""
+    return np.unpackbits(np.ascontiguousarray(masks, np.uint8), axis=1, bitorder="little")[:, :K]
+
+
+def pin_calib_accumulate(seed=7):
+    """H = sum over decode rows of x x^T against independent routes: numpy's
+    matmul of the selected rows (integer-valued, so exact), one-hot rows
+    (H diagonal), rank-one rows c_t (1..K) (H_ij = sum c_t^2 i j), the decode
+    mask (all-zero mask gives 0; None equals all ones), accumulation across
+    calls, symmetry and the trace."""
+    rng = np.random.default_rng(seed)
+    for dt in ("fp16", "bf16"):
+        T, K = 9, 16
+        Xv = rng.integers(-6, 7, size=(T, K)).astype(np.float64)
+        X = to_bits(Xv, dt)
+        d = (rng.random(T) < 0.6).astype(np.uint8)
+        d[0], d[1] = 0, 1
+        H, A = oracle.calib_accumulate(X, dt, decode=d)
+        Xd = Xv[d != 0]
+        assert np.array_equal(H, Xd.T @ Xd)
+        assert np.array_equal(A, np.abs(Xd).T @ np.abs(Xd))
+        assert np.array_equal(H, H.T) and np.trace(H) == float((Xd ** 2).sum())
+        H0, _ = oracle.calib_accumulate(X, dt, decode=np.zeros(T, np.uint8))
+        assert not H0.any()
+        Hn, _ = oracle.calib_accumulate(X, dt)
+        Ho, _ = oracle.calib_accumulate(X, dt, decode=np.ones(T, np.uint8))
+        assert np.array_equal(Hn, Ho) and np.array_equal(Hn, Xv.T @ Xv)
+        # accumulation: two calls equal one call over both row sets
+        H1, A1 = oracle.calib_accumulate(X[:4], dt)
+        H2, _ = oracle.calib_accumulate(X[4:], dt, H=H1, A=A1)
+        assert np.array_equal(H2, Hn)
+        # one-hot rows: diagonal H
+        idx = rng.integers(0, K, size=T)
+        vals = rng.integers(1, 5, size=T).astype(np.float64)
+        Xo = np.zeros((T, K))
+        Xo[np.arange(T), idx] = vals
+        Ho, _ = oracle.calib_accumulate(to_bits(Xo, dt), dt)
+        want = np.zeros((K, K))
+        for t in range(T):
+            want[idx[t], idx[t]] += vals[t] ** 2
+        assert np.array_equal(Ho, want)
+        # rank-one rows c_t * (1, 2, ..., K)
+        c = np.array([1.0, -2.0, 0.5])
+        Xr = np.outer(c, np.arange(1, K + 1))
+        Hr, _ = oracle.calib_accumulate(to_bits(Xr, dt), dt)
+        assert np.array_equal(Hr, (c ** 2).sum() * np.outer(np.arange(1, K + 1), np.arange(1, K + 1)))
+
+
+def _keep_brute(Wv, h, n, m):
+    """Top-n per m-group by exact rational saliency w^2 h (finite inputs),
+    lower column first on ties, by sorting."""
+    R, K = Wv.shape
+    keep = np.zeros((R, K), np.uint8)
+    for r in range(R):
+        for g0 in range(0, K, m):
+            sal = [Fraction(Wv[r, g0 + j]) ** 2 * Fraction(float(h[g0 + j])) for j in range(m)]
+            order = sorted(range(m), key=lambda j: (-sal[j], j))
+            for j in order[:n]:
+                keep[r, g0 + j] = 1
+    return keep
+
+
+def pin_calib_keep(seed=8):
+    """Saliency keep-mask: equals the magnitude rule when h is constant (a
+    reduction to the pinned top-n by |w|), the top-n of h when |w| is
+    constant, exact-rational brute force on random inputs, and NaN ranks
+    lowest."""
+    rng = np.random.default_rng(seed)
+    for dt in ("fp16", "bf16"):
+        for n, m in ((2, 4), (4, 8), (1, 4), (3, 8)):
+            R, K = 6, 32
+            Wv = np.round(rng.normal(0, 1, (R, K)) * 8) / 8           # many equal magnitudes
+            W = to_bits(Wv, dt)
+            Wv = bits_to_f64(W, dt)
+            # constant h: the magnitude rule
+            _, masks = oracle.pack(W, None, n, m, dt)
+            assert np.array_equal(oracle.calib_keep(W, np.full(K, 3.0), n, m, dt), _bitmap_to_keep(masks, K))
+            # constant |w|: the largest h, lower column on ties
+            ones = to_bits(np.where(rng.random((R, K)) < 0.5, -1.0, 1.0), dt)
+            h = rng.integers(0, 4, size=K).astype(np.float32)
+            got = oracle.calib_keep(ones, h, n, m, dt)
+            want = np.zeros((R, K), np.uint8)
+            for g0 in range(0, K, m):
+                order = sorted(range(m), key=lambda j: (-h[g0 + j], j))
+                want[:, [g0 + j for j in order[:n]]] = 1
+            assert np.array_equal(got, want)
+            # brute force with exact rationals
+            h = (rng.random(K) * 4).astype(np.float32)
+            h[rng.random(K) < 0.2] = 0.0
+            assert np.array_equal(oracle.calib_keep(W, h, n, m, dt), _keep_brute(Wv, h.astype(np.float64), n, m))
+    # NaN saliency ranks below everything (fp16 0x7E00 = NaN)
+    W = np.array([[0x7E00, 0x3C00, 0x7E00, 0x0000, 0x3C00, 0x4000, 0x3C00, 0x4000]], np.uint16)  # NaN 1 NaN 0 | 1 2 1 2
+    keep = oracle.calib_keep(W, np.ones(8, np.float32), 2, 4, "fp16")
+    assert keep.tolist() == [[0, 1, 0, 1, 0, 1, 0, 1]]
+    keep = oracle.calib_keep(W, np.ones(8, np.float32), 3, 4, "fp16")
+    assert keep.tolist() == [[1, 1, 0, 1, 1, 1, 0, 1]]
+
+
 ALL_PINS = [
     pin_golden_rounding,
     pin_decode_exhaustive,
@@ -409,4 +543,8 @@ ALL_PINS = [
     pin_one_hot,
     pin_integer_exact,
     pin_errors,
+    pin_silu,
+    pin_swiglu,
+    pin_calib_accumulate,
+    pin_calib_keep,
 ] + [(lambda f=f: pin_golden_pack(f)) for f in golden_pack_files()]

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = L.lib()
-    assert lib.nm_version() == 100
+    assert lib.nm_version() == 101
     for code, name in [(0, b"NM_OK"), (1, b"NM_ERR_INVALID_ARG"), (2, b"NM_ERR_BAD_SHAPE"), (3, b"NM_ERR_UNSUPPORTED"),
                        (4, b"NM_ERR_BAD_MASK"), (5, b"NM_ERR_NONFINITE"), (6, b"NM_ERR_HIP")]:
         assert lib.nm_status_string(code) == name
@@ -160,3 +160,42 @@ def test_dense_multi_rejects_bad_arguments():
     assert lib.nm_gemv_dense_multi(2, W, R, 64, 0, FAKE2, 9, y, None) == L.NM_ERR_BAD_SHAPE
     Wm = _arr(P, [FAKE, FAKE + 0x10002])
     assert lib.nm_gemv_dense_multi(2, Wm, R, 64, 0, FAKE2, 1, y, None) == L.NM_ERR_INVALID_ARG
+
+
+def swiglu(vg=FAKE, mg=FAKE + 0x1000, vu=FAKE + 0x2000, mu=FAKE + 0x3000, R=16, K=64, N=2, M=4, dt=0, x=FAKE2, B=1,
+           h=FAKE2 + 0x100000):
+    return L.lib().nm_spmv_swiglu(vg, mg, vu, mu, R, K, N, M, dt, x, B, h, None)
+
+
+@pytest.mark.parametrize("kw", [dict(K=12), dict(R=-1), dict(M=3), dict(N=0), dict(N=4), dict(B=0), dict(B=9),
+                                dict(R=2 ** 30 + 1)])
+def test_swiglu_bad_shape(kw):
+    assert swiglu(**kw) == L.NM_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(vg=None), dict(mu=None), dict(x=None), dict(h=None), dict(vu=FAKE + 0x2004),
+                                dict(x=FAKE2 + 2), dict(h=FAKE2 + 0x100001), dict(h=FAKE2),
+                                dict(h=FAKE + 0x2000), dict(h=FAKE + 0x3010)])
+def test_swiglu_invalid_pointer(kw):
+    assert swiglu(**kw) == L.NM_ERR_INVALID_ARG
+
+
+def test_swiglu_dtype_and_empty():
+    assert swiglu(dt=3) == L.NM_ERR_UNSUPPORTED
+    assert swiglu(R=0) == L.NM_OK
+
+
+def test_dense_swiglu_rejects_bad_arguments():
+    lib = L.lib()
+    ok_args = dict(Wg=FAKE, Wu=FAKE + 0x10000, R=16, K=64, dt=0, x=FAKE2, B=1, h=FAKE2 + 0x100000)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return lib.nm_gemv_dense_swiglu(a["Wg"], a["Wu"], a["R"], a["K"], a["dt"], a["x"], a["B"], a["h"], None)
+
+    assert call(K=12) == L.NM_ERR_BAD_SHAPE
+    assert call(B=9) == L.NM_ERR_BAD_SHAPE
+    assert call(dt=2) == L.NM_ERR_UNSUPPORTED
+    assert call(Wu=None) == L.NM_ERR_INVALID_ARG
+    assert call(h=FAKE + 0x10010) == L.NM_ERR_INVALID_ARG     # output over W_up
+    assert call(R=0) == L.NM_OK

@@ -29,6 +29,15 @@ MUTANTS = [
     ("nan_not_rejected", "if (isnan(v))\n            return ORC_NONFINITE;", "if (0)\n            return ORC_NONFINITE;"),
     ("signed_magnitude", "mag[j] = fabs(v);", "mag[j] = v;"),
     ("overflow_not_detected", "if (q + fbits > emax)", "if (q + fbits > emax + 1)"),
+    ("silu_sign_flipped", "return t / (1.0 + exp(-t));", "return t / (1.0 + exp(t));"),
+    ("silu_is_sigmoid", "return t / (1.0 + exp(-t));", "return 1.0 / (1.0 + exp(-t));"),
+    ("swiglu_gate_up_swapped", "h[i] = orc_silu(g[i]) * u[i];", "h[i] = orc_silu(u[i]) * g[i];"),
+    ("calib_prefill_not_excluded", "if (decode && !decode[t])", "if (0 && decode && !decode[t])"),
+    ("calib_diagonal_only", "double p = row[i] * row[j];", "double p = row[i] * row[i];"),
+    ("saliency_abs_w", "double s = w * w * h[c];", "double s = fabs(w) * h[c];"),
+    ("saliency_ignores_h", "double s = w * w * h[c];", "double s = w * w;"),
+    ("saliency_tie_to_highest", "(best < 0 || sal[j] > sal[best])", "(best < 0 || sal[j] >= sal[best])"),
+    ("saliency_nan_ranks_high", "sal[j] = isnan(s) ? -1.0 : s;", "sal[j] = isnan(s) ? 1e300 : s;"),
 ]
 
 
