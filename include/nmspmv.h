@@ -155,6 +155,46 @@ int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const voi
 int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_t K, int dtype, const void* x, int B,
                          void* h, void* stream);
 
+/*
+ * ---- Decoding-aware calibration -----------------------------------------------
+ * SparseDecoding builds its pruning objective from the inputs each layer sees
+ * while the dense model generates, prefill excluded, and guides pruning with
+ * the objective's Hessian ("SparseDecoding: Decoding-Aware Pruning ...",
+ * Abstract; "SparseDecoding Makes LLM Pruning Aware of Generation", Key points
+ * and the section on why fixed-text calibration misses).  The pages give no
+ * formula; these two calls implement the plainest reading, and their output
+ * enters the sparse path through nm_pack's keep-mask.
+ *
+ * nm_calib_accumulate -- H += sum over decode rows t of x_t x_t^T: the Hessian
+ * (up to a constant) of a linear layer's squared output error over its inputs
+ * at decode steps.
+ *   X [T][K] 16-bit (dtype): the layer's input rows, in any order.
+ *   decode [T] bytes: nonzero marks a decode-step row; zero rows (prefill)
+ *          do not enter H.  NULL = every row is a decode step.
+ *   H [K][K] fp32, row-major, accumulated in place (zero it before the first
+ *          call); calls add up, so rows can be streamed in batches.
+ * Products of two 16-bit values are exact in fp32; the sums are fp32 (matrix
+ * cores) in an unspecified order.  K % 8 == 0, K <= 65536; X 16-byte and H
+ * 4-byte aligned; H must not overlap X or decode.  Enqueues and returns.
+ */
+int nm_calib_accumulate(const void* X, const uint8_t* decode, int64_t T, int64_t K, int dtype, float* H, void* stream);
+
+/*
+ * nm_calib_keep_mask -- the N:M keep-mask from a calibration Hessian: per
+ * M-group of each row keep the N columns of largest saliency w^2 * H_jj (the
+ * optimal-brain-surgeon saliency with H taken diagonal), the lower column on
+ * equal saliency; a NaN saliency ranks below every other.  The saliency is
+ * formed exactly (double), so the mask is fully determined by W and H's
+ * diagonal.
+ *   W [R][K] 16-bit (dtype); h: H_jj = h[j * h_stride] (h_stride = K + 1 on a
+ *   full row-major H, 1 on a diagonal vector); keep [R][K] bytes, written 1
+ *   (keep) or 0, exactly N ones per group: pass it to nm_pack.
+ * Shape rules as for nm_pack, h_stride >= 1; W 16-byte, keep 8-byte and h
+ * 4-byte aligned; keep must not overlap W or h.  Enqueues and returns.
+ */
+int nm_calib_keep_mask(const void* W, const float* h, int64_t h_stride, int64_t R, int64_t K, int N, int M, int dtype,
+                       uint8_t* keep, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* nm_status_string(int status);
 

@@ -8,6 +8,8 @@ step of the computation runs in the HIP kernels of ``libnmspmv.so``.
     y = spmv(values, masks, x, n=2, m=4)           # per token: y = W_sparse x
     y = gemv_dense(W, x)                           # dense baseline
     h = spmv_swiglu((vg, mg), (vu, mu), x)         # SiLU(W_gate x) * (W_up x)
+    H = calib_accumulate(X, decode)                # decoding-aware calibration
+    keep = calib_keep_mask(W, H, n=2, m=4)         # -> pack(W, keep, 2, 4)
 """
 import ctypes
 
@@ -17,7 +19,7 @@ from ._lib import (NM_BF16, NM_ERR_BAD_MASK, NM_ERR_BAD_SHAPE, NM_ERR_HIP, NM_ER
                    NM_ERR_NONFINITE, NM_ERR_UNSUPPORTED, NM_FP16, NM_OK, NmError, call, lib)
 
 __all__ = ["pack", "spmv", "spmv_multi", "spmv_swiglu", "gemv_dense", "gemv_dense_multi", "gemv_dense_swiglu",
-           "NmError", "dtype_code", "stream_handle"]
+           "calib_accumulate", "calib_keep_mask", "NmError", "dtype_code", "stream_handle"]
 
 _DT = {torch.float16: NM_FP16, torch.bfloat16: NM_BF16}
 
@@ -186,3 +188,45 @@ def gemv_dense_swiglu(W_gate, W_up, x, out=None, stream=None):
     call("nm_gemv_dense_swiglu", W_gate.data_ptr(), W_up.data_ptr(), R, K, dtype_code(x.dtype), x2.data_ptr(), B,
          h.data_ptr(), stream_handle(stream))
     return h[0] if squeeze else h
+
+
+def calib_accumulate(X, decode=None, H=None, stream=None):
+    """H += sum over decode rows t of X[t]^T X[t] (fp32 [K][K]).  X is [T][K]
+    16-bit; decode is a bool/uint8 [T] tensor (nonzero = decode step) or None
+    (all rows).  A new zeroed H is made when none is given."""
+    _dev(X, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be [T][K]")
+    T, K = X.shape
+    if H is None:
+        H = torch.zeros((K, K), dtype=torch.float32, device=X.device)
+    _dev(H, "H")
+    if H.shape != (K, K) or H.dtype != torch.float32:
+        raise ValueError("H must be float32 [K][K]")
+    dp = None
+    if decode is not None:
+        _dev(decode, "decode")
+        if decode.shape != (T,) or decode.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("decode must be a bool/uint8 [T] tensor")
+        dp = decode.data_ptr()
+    call("nm_calib_accumulate", X.data_ptr(), dp, T, K, dtype_code(X.dtype), H.data_ptr(), stream_handle(stream))
+    return H
+
+
+def calib_keep_mask(W, H, n=2, m=4, stream=None):
+    """Keep-mask (uint8 [R][K], n ones per m-group) of the columns with the
+    largest w^2 * H_jj; H is the [K][K] calibration Hessian or its diagonal [K]."""
+    _dev(W, "W"), _dev(H, "H")
+    R, K = W.shape
+    if H.dtype != torch.float32:
+        raise ValueError("H must be float32")
+    if H.shape == (K, K):
+        stride = K + 1
+    elif H.shape == (K,):
+        stride = 1
+    else:
+        raise ValueError("H must be [K][K] or [K]")
+    keep = torch.empty((R, K), dtype=torch.uint8, device=W.device)
+    call("nm_calib_keep_mask", W.data_ptr(), H.data_ptr(), stride, R, K, n, m, dtype_code(W.dtype), keep.data_ptr(),
+         stream_handle(stream))
+    return keep

@@ -9,10 +9,10 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "nmspmv.hip")
+SRC = [os.path.join(HERE, "csrc", "nmspmv.hip"), os.path.join(HERE, "csrc", "nmcalib.hip")]
 LIB = os.path.join(HERE, "libnmspmv.so")
-# (source, library): the product library and the measurement probes beside it
-TARGETS = [(SRC, LIB), (os.path.join(HERE, "csrc", "nmprobe.hip"), os.path.join(HERE, "libnmprobe.so"))]
+# (sources, library): the product library and the measurement probes beside it
+TARGETS = [(SRC, LIB), ([os.path.join(HERE, "csrc", "nmprobe.hip")], os.path.join(HERE, "libnmprobe.so"))]
 ARCH = "gfx950"
 
 
@@ -34,7 +34,7 @@ def build_one(src, lib, verbose=False):
            # packed-fp32 instructions stay off (the compiler would otherwise form them from float code)
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-fno-gpu-rdc", "-Wall", "-Wno-unused-result",
-           "-I", os.path.join(ROOT, "include"), src, "-o", lib + ".tmp"]
+           "-I", os.path.join(ROOT, "include"), *src, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)

@@ -199,3 +199,36 @@ def test_dense_swiglu_rejects_bad_arguments():
     assert call(Wu=None) == L.NM_ERR_INVALID_ARG
     assert call(h=FAKE + 0x10010) == L.NM_ERR_INVALID_ARG     # output over W_up
     assert call(R=0) == L.NM_OK
+
+
+def test_calib_accumulate_rejects_bad_arguments():
+    lib = L.lib()
+    acc = lambda X=FAKE, d=None, T=4, K=64, dt=0, H=FAKE2: lib.nm_calib_accumulate(X, d, T, K, dt, H, None)  # noqa: E731
+    assert acc(K=12) == L.NM_ERR_BAD_SHAPE
+    assert acc(T=-1) == L.NM_ERR_BAD_SHAPE
+    assert acc(K=65544) == L.NM_ERR_BAD_SHAPE
+    assert acc(dt=7) == L.NM_ERR_UNSUPPORTED
+    assert acc(X=None) == L.NM_ERR_INVALID_ARG
+    assert acc(X=FAKE + 8) == L.NM_ERR_INVALID_ARG
+    assert acc(H=FAKE2 + 2) == L.NM_ERR_INVALID_ARG
+    assert acc(H=FAKE + 0x100) == L.NM_ERR_INVALID_ARG          # H over X
+    assert acc(d=FAKE2 + 0x40) == L.NM_ERR_INVALID_ARG          # decode flags inside H
+    assert acc(T=0) == L.NM_OK and acc(K=0) == L.NM_OK
+
+
+def test_calib_keep_mask_rejects_bad_arguments():
+    lib = L.lib()
+
+    def keep(W=FAKE, h=FAKE2, hs=1, R=4, K=64, N=2, M=4, dt=0, out=FAKE2 + 0x100000):
+        return lib.nm_calib_keep_mask(W, h, hs, R, K, N, M, dt, out, None)
+
+    assert keep(K=12) == L.NM_ERR_BAD_SHAPE
+    assert keep(N=4) == L.NM_ERR_BAD_SHAPE
+    assert keep(M=5) == L.NM_ERR_BAD_SHAPE
+    assert keep(hs=0) == L.NM_ERR_BAD_SHAPE
+    assert keep(dt=9) == L.NM_ERR_UNSUPPORTED
+    assert keep(W=FAKE + 4) == L.NM_ERR_INVALID_ARG
+    assert keep(out=FAKE2 + 0x100004) == L.NM_ERR_INVALID_ARG
+    assert keep(h=None) == L.NM_ERR_INVALID_ARG
+    assert keep(out=FAKE) == L.NM_ERR_INVALID_ARG               # keep over W
+    assert keep(R=0) == L.NM_OK
