@@ -70,6 +70,9 @@ def parse():
     p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a graph")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-glu", action="store_true",
+                   help="skip the gated gate+up launch (its grid equals the plain gate+up launch's, which would mix "
+                        "the two in a kernel trace keyed by kernel and grid)")
     return p.parse_args()
 
 
@@ -398,7 +401,7 @@ def main():
 
     # ---- gated MLP input as one launch: h = SiLU(gate x) * (up x) ----
     group = [L for L in launches if L.names == ("gate", "up")]
-    if group:
+    if group and not a.no_glu:
         sl = [L.glu_args(cur) for L in group]
         dl = [L.glu_args(cur, dense=True) for L in group]
         run(lib.nm_spmv_swiglu, sl)
