@@ -52,7 +52,7 @@ def workloads(I):
                                  f"bf16, batch 1, Laplace x", I.QWEN3_14B_MLP, 40, "bf16", n, m, 1, MLP_ONLY, "laplace")
         w[f"qwen3_32b_{nmk}"] = (f"Qwen3-32B MLP projections: 64 layers x (gate+up fused, down), {n}:{m} sparse, "
                                  f"bf16, batch 1, Laplace x", I.QWEN3_32B_MLP, 64, "bf16", n, m, 1, MLP_ONLY, "laplace")
-    for B in (1, 2, 4, 8):
+    for B in (1, 2, 4, 8, 16, 32):
         w[f"qwen3_32b_b{B}"] = (f"Qwen3-32B MLP projections: 64 layers x (gate+up fused, down), 2:4 sparse, bf16, "
                                 f"batch {B}", I.QWEN3_32B_MLP, 64, "bf16", 2, 4, B, MLP_ONLY, "normal")
     return w
@@ -70,6 +70,9 @@ def parse():
     p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a graph")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--crossover", action="store_true",
+                   help="batch crossover study instead of the step: Qwen3-32B MLP shapes (2:4 bf16) at B = 1..32, "
+                        "sparse vs the dense kernel vs torch's matmul; prints one JSON line")
     p.add_argument("--no-glu", action="store_true",
                    help="skip the gated gate+up launch (its grid equals the plain gate+up launch's, which would mix "
                         "the two in a kernel trace keyed by kernel and grid)")
@@ -338,6 +341,49 @@ def measured_traffic():
     return rec["traffic_bytes_per_launch"] if rec.get("source_sha256") == sha else None
 
 
+def crossover(torch, nm, I, batches=(1, 2, 4, 8, 16, 32)):
+    """Sparse 2:4 (nm_spmv), dense (nm_gemv_dense) and torch.matmul (hipBLASLt)
+    on the Qwen3-32B MLP shapes over a range of batch sizes, each timed over
+    enough weight instances to exceed the 256 MB MALL."""
+    lib = nm.lib()
+    cur = torch.cuda.current_stream().cuda_stream
+    dt = torch.bfloat16
+    out = {}
+    for name in ("gate", "down"):
+        R, K = I.QWEN3_32B_MLP[name]
+        n_inst = 6
+        Ws = [I.weight(R, K, dt, I.seed_of("xover", name, i), device="cuda") for i in range(n_inst)]
+        packed = [nm.pack(W, None, 2, 4) for W in Ws]
+        torch.cuda.synchronize()
+        rows = []
+        for B in batches:
+            x = I.activation_normal(B, K, dt, I.seed_of("xover_x", name, B), device="cuda")
+            y = torch.empty((B, R), dtype=dt, device="cuda")
+            sargs = [(P(v.data_ptr()), P(mk.data_ptr()), I64(R), I64(K), I32(2), I32(4), I32(1), P(x.data_ptr()),
+                      I32(B), P(y.data_ptr()), P(cur)) for v, mk in packed]
+            dargs = [(P(W.data_ptr()), I64(R), I64(K), I32(1), P(x.data_ptr()), I32(B), P(y.data_ptr()), P(cur))
+                     for W in Ws]
+            run(lib.nm_spmv, sargs)
+            us = time_ms(torch, lambda: run(lib.nm_spmv, sargs), 5) / n_inst * 1e3
+            run(lib.nm_gemv_dense, dargs)
+            usd = time_ms(torch, lambda: run(lib.nm_gemv_dense, dargs), 5) / n_inst * 1e3
+
+            def torch_mm():
+                for W in Ws:
+                    torch.matmul(x, W.t(), out=y)
+            torch_mm()
+            ust = time_ms(torch, torch_mm, 5) / n_inst * 1e3
+            sb = R * K // 2 * 2 + R * K // 8 + B * (R + K) * 2
+            db = R * K * 2 + B * (R + K) * 2
+            rows.append({"B": B, "sparse_us": round(us, 2), "sparse_gbs": round(sb / us / 1e3, 1),
+                         "dense_us": round(usd, 2), "dense_gbs": round(db / usd / 1e3, 1), "torch_us": round(ust, 2),
+                         "speedup_vs_dense": round(usd / us, 3), "speedup_vs_torch": round(ust / us, 3)})
+        out[name] = {"shape": [R, K], "rows": rows}
+        del Ws, packed
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -352,6 +398,11 @@ def main():
     if a.workload not in specs:
         print(f"unknown workload {a.workload}; one of {sorted(specs)}", file=sys.stderr)
         sys.exit(2)
+    if a.crossover:
+        torch.cuda.set_device(0)
+        print(json.dumps({"crossover": crossover(torch, nm, I), "workload": "Qwen3-32B MLP, 2:4 sparse, bf16"}),
+              flush=True)
+        return
     spec = specs[a.workload]
     desc, _, layers, dts, n, m, B = spec[:7]
     layers = a.layers or layers

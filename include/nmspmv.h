@@ -32,7 +32,7 @@
  * - dtype is NM_FP16 (IEEE binary16) or NM_BF16 (bfloat16); W, values, x and y
  *   all use it.
  * - Shapes: R >= 0, K >= 0, K % 8 == 0, M in {4, 8}, 1 <= N < M, K % M == 0,
- *   1 <= B <= 8, and R, K below 2^31.  Anything else returns NM_ERR_BAD_SHAPE
+ *   1 <= B <= 32, and R, K below 2^31.  Anything else returns NM_ERR_BAD_SHAPE
  *   (or NM_ERR_UNSUPPORTED for a dtype that is not one of the two) before
  *   any work is queued; outputs are then untouched.
  * - Alignment: W, values, masks and x must be 16-byte aligned; y 2-byte
@@ -85,7 +85,7 @@ int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int
             void* values, uint8_t* masks, void* stream);
 
 /*
- * nm_spmv -- y = W_sparse * x for 1..8 activation vectors: the decode-time
+ * nm_spmv -- y = W_sparse * x for 1..32 activation vectors: the decode-time
  * N:M sparse matrix-vector product of the SparseDecoding abstract and of the
  * "Key points" of "SparseDecoding Makes LLM Pruning Aware of Generation".
  *   values, masks  packed as nm_pack writes them (R rows, K dense columns).
@@ -95,7 +95,9 @@ int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int
  *   x [B][K] 16-bit, y [B][R] 16-bit (output).
  *   y[b][r] = sum over kept columns c of W[r][c] * x[b][c]; every product and
  *   sum is formed in fp32 (in an unspecified order) and the sum is rounded
- *   once to the output dtype, to nearest even.
+ *   once to the output dtype, to nearest even.  (Beyond 8 vectors the
+ *   products run on the matrix cores, fp32 accumulation; the arithmetic
+ *   contract is the same.)
  * Enqueues on stream and returns; y is complete when the stream reaches it.
  */
 int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int N, int M, int dtype,

@@ -69,7 +69,7 @@ def pack(W, keep=None, n=2, m=4, stream=None):
 
 
 def spmv(values, masks, x, n=2, m=4, out=None, stream=None):
-    """y = W_sparse x.  x is [K] or [B][K] (B <= 8); returns [R] or [B][R]."""
+    """y = W_sparse x.  x is [K] or [B][K] (B <= 32); returns [R] or [B][R]."""
     _dev(values, "values"), _dev(masks, "masks"), _dev(x, "x")
     R = masks.shape[0]
     K = masks.shape[1] * 8

@@ -654,6 +654,210 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
     }
 }
 
+// ---- matrix-core kernel for batched products ----------------------------------
+
+// With several activation vectors the VALU kernels above pay one byte-permute
+// and one dot2 per group per vector; at B >= 4 that, not HBM, sets their pace.
+// Here the matrix cores take the batch: a wave multiplies a 16-row tile of W
+// by x^T (16 batch columns per tile of the batch) with v_mfma_f32_16x16x16,
+// over one K-slice.  Lane l (i = l % 16, quarter q = l / 16) streams chunks
+// c = cbeg + 4 t + q of row r0 + i; each chunk's 16 (dense: 8) columns are
+// COLS / 4 k-blocks of 4 columns, and the A operand of a k-block -- 4 dense
+// weights of one row -- is rebuilt from the packed values with two byte
+// permutes (2:4: one group; 4:8: half a group; dense: a copy).  The B operand
+// is the same 4 columns of x row i, read from L2 (x is small); lanes of batch
+// rows past B repeat row B - 1 and their outputs are dropped.  The matrix
+// core reduces over k, so no cross-lane reduction is needed: the slices of a
+// tile add up in LDS in slice order.  Loads run two rounds of U chunk steps
+// ahead (two register buffers).
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c)
+{
+    if constexpr (DT == NM_FP16)
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
+                                                     0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                         0, 0);
+}
+
+// 2:4.  Nibble n marks the kept columns j0 < j1 of a 4-column group; the two
+// selectors (dense dword 0 = columns 0, 1; dword 1 = columns 2, 3) move the
+// group's first stored value (bytes 0, 1 of its dword) to column j0, the
+// second (bytes 2, 3) to j1, and zero bytes (0x0C) elsewhere.  Nibbles
+// without exactly two bits give zeros.
+__device__ u32x2 expand24(uint32_t n)
+{
+    uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu};
+    if (__builtin_popcount(n) == 2) {
+        const uint32_t js[2] = {(uint32_t)__builtin_ctz(n), 31u - (uint32_t)__builtin_clz(n)};
+        for (uint32_t k = 0; k < 2; ++k) {
+            const uint32_t p = js[k], shift = 16 * (p & 1);
+            sel[p >> 1] = (sel[p >> 1] & ~(0xFFFFu << shift)) | (((2 * k) | ((2 * k + 1) << 8)) << shift);
+        }
+    }
+    return u32x2{sel[0], sel[1]};
+}
+
+// 16-byte LDS units of the matrix-core kernel's expansion table: 2:4 keeps
+// 16 entries of 8 bytes, 4:8 the 256-entry select48 table.
+template <int F>
+constexpr int mfma_table_units()
+{
+    return F == kNM24 ? 16 * 8 / 16 : (F == kNM48 ? 256 : 0);
+}
+
+// The A operand of k-block s (dense columns 4 s .. 4 s + 3 of the chunk).
+template <int F>
+__device__ __forceinline__ u32x2 a_frag(const uint32_t* w, uint32_t m, int s, const u32x4* tab)
+{
+    if constexpr (F == kDense) {
+        return u32x2{w[2 * s], w[2 * s + 1]};
+    } else if constexpr (F == kNM24) {
+        const u32x2 sel = reinterpret_cast<const u32x2*>(tab)[(m >> (4 * s)) & 0xFu];
+        return u32x2{__builtin_amdgcn_perm(w[s], w[s], sel.x), __builtin_amdgcn_perm(w[s], w[s], sel.y)};
+    } else {
+        const int g = s >> 1;
+        const u32x4 sel = tab[(m >> (8 * g)) & 0xFFu];
+        const uint32_t s0 = (s & 1) ? sel.z : sel.x, s1 = (s & 1) ? sel.w : sel.y;
+        return u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], s0), __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], s1)};
+    }
+}
+
+template <int F, int DT, int NT, int U>
+__global__ __launch_bounds__(1024) void mfma_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K, int B,
+                                                    int S, int tiles_per_block)
+{
+    extern __shared__ u32x4 smem[];
+    constexpr int COLS = chunk_cols<F>();
+    constexpr int XC = COLS / 8;                 // 16-byte x units per chunk
+    constexpr int KB = COLS / 4;                 // k-blocks per chunk
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lt = wave / S, sl = wave - lt * S;
+    const int r0 = (blockIdx.x * tiles_per_block + lt) * 16;
+    const int C = K / COLS;
+    const int cps = ((C + S - 1) / S + 3) & ~3;  // chunks per slice, whole steps of 4
+    const int cbeg = min(C, sl * cps), cend = min(C, cbeg + cps);
+    const int nsteps = r0 < R ? (cend - cbeg + 3) / 4 : 0;
+    const int nrounds = (nsteps + U - 1) / U;
+    const int i = lane & 15, q = lane >> 4;
+    const RowRef row = row_ref(P, min(r0 + i, R - 1), C);
+    const int q8 = K / 8;
+    int xrow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        xrow[nt] = min(16 * nt + i, B - 1) * q8;
+
+    u32x4 va[U], vb[U];
+    uint32_t ma[U], mb[U];
+    u32x4 xa[NT][U][XC], xb[NT][U][XC];
+    auto fetch = [&](int t0, u32x4* v, uint32_t* mk, u32x4 (&xv)[NT][U][XC]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = cbeg + 4 * (t0 + u) + q;
+            const int cc = c < cend ? c : 0;
+            v[u] = __builtin_nontemporal_load(row.w + cc);
+            if constexpr (F != kDense)
+                mk[u] = __builtin_nontemporal_load(row.m + cc);
+            else
+                mk[u] = 0;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int h = 0; h < XC; ++h)
+                    xv[nt][u][h] = x4[xrow[nt] + cc * XC + h];
+        }
+    };
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const u32x4* tab = smem;
+    auto consume = [&](int t0, const u32x4* v, const uint32_t* mk, const u32x4 (&xv)[NT][U][XC]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (4 * (t0 + u) >= cend - cbeg)     // wave-uniform: this step is past the slice for every lane
+                break;
+            const bool live = cbeg + 4 * (t0 + u) + q < cend;
+            const uint32_t w[4] = {live ? v[u].x : 0u, live ? v[u].y : 0u, live ? v[u].z : 0u, live ? v[u].w : 0u};
+            const uint32_t m = live ? mk[u] : 0u;
+#pragma unroll
+            for (int s = 0; s < KB; ++s) {
+                const u32x2 a = a_frag<F>(w, m, s, tab);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const u32x4 xx = xv[nt][u][s >> 1];
+                    const u32x2 b = (s & 1) ? u32x2{xx.z, xx.w} : u32x2{xx.x, xx.y};
+                    acc[nt] = mfma16<DT>(a, b, acc[nt]);
+                }
+            }
+        }
+    };
+
+    if (nrounds > 0)
+        fetch(0, va, ma, xa);
+    if constexpr (F == kNM24) {
+        if (threadIdx.x < 16)
+            reinterpret_cast<u32x2*>(smem)[threadIdx.x] = expand24(threadIdx.x);
+    } else if constexpr (F == kNM48) {
+        for (unsigned t = threadIdx.x; t < 256; t += blockDim.x)
+            smem[t] = select48(t);
+    }
+    __syncthreads();
+    for (int j = 0; j < nrounds; j += 2) {
+        if (j + 1 < nrounds)
+            fetch((j + 1) * U, vb, mb, xb);
+        consume(j * U, va, ma, xa);
+        if (j + 1 < nrounds) {
+            if (j + 2 < nrounds)
+                fetch((j + 2) * U, va, ma, xa);
+            consume((j + 1) * U, vb, mb, xb);
+        }
+    }
+
+    // Slice sums: D[4 q + v][i] of this wave's tile (row 4 q + v, batch column i).
+    float* part = reinterpret_cast<float*>(smem + mfma_table_units<F>());
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            part[((wave * NT + nt) * kWave + lane) * 4 + v] = acc[nt][v];
+    __syncthreads();
+    if (sl != 0 || r0 >= R)
+        return;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int b = 16 * nt + i;
+        float sum[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float t = part[((wave * NT + nt) * kWave + lane) * 4 + v];
+            for (int j = 1; j < S; ++j)
+                t += part[(((wave + j) * NT + nt) * kWave + lane) * 4 + v];
+            sum[v] = t;
+        }
+        if (b >= B)
+            continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = r0 + 4 * q + v;
+            if (r >= R)
+                continue;
+            const RowRef o = row_ref(P, r, C);
+            if (!P.glu)
+                o.y[(size_t)b * o.R] = from_f32<DT>(sum[v]);
+            else if ((v & 1) == 0)                // rows r (gate) and r + 1 (up) of one output
+                o.y[(size_t)b * o.R] = glu_out<DT>(sum[v], sum[v + 1]);
+        }
+    }
+}
+
 // ---- generic N:M (any N < M, M in {4, 8}, K % 8 == 0) --------------------------
 
 // One lane step covers one mask byte (8 columns: two 4-groups or one
@@ -811,9 +1015,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, 
 // Launch-shape overrides, read once, for tuning sweeps (0 = built-in choice):
 // NMSPMV_KERNEL 1 = row-slice, 3 = stream; NMSPMV_SLICES,
 // NMSPMV_ROWS_PER_BLOCK (row-slice); NMSPMV_BLOCKS, NMSPMV_THREADS,
-// NMSPMV_TILE_BYTES (stream).
+// NMSPMV_TILE_BYTES (stream); NMSPMV_MFMA_MIN_B (smallest batch sent to the
+// matrix-core kernel), NMSPMV_MFMA_SLICES.
 struct Env {
-    int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0;
+    int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0;
 };
 Env g_env;
 std::once_flag g_env_once;
@@ -830,6 +1035,8 @@ void read_env()
     g_env.blocks = get("NMSPMV_BLOCKS");
     g_env.threads = get("NMSPMV_THREADS");
     g_env.tile_bytes = get("NMSPMV_TILE_BYTES");
+    g_env.mfma_min_b = get("NMSPMV_MFMA_MIN_B");
+    g_env.mfma_slices = get("NMSPMV_MFMA_SLICES");
 }
 
 int g_cu_count[64] = {};
@@ -979,6 +1186,69 @@ Plan plan_for(int64_t R, int64_t K, int B, bool glu)
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
+
+constexpr int kMaxBatch = 32;       // activation vectors per call
+constexpr int kVectorMaxBatch = 8;  // the VALU kernels' limit; larger batches use the matrix cores
+
+// Batches of at least this many vectors go to the matrix-core kernel (by
+// default only those beyond the VALU kernels' limit: at B <= 8 the VALU
+// kernels measured faster on every workload shape).
+int mfma_min_batch()
+{
+    std::call_once(g_env_once, read_env);
+    return g_env.mfma_min_b > 0 ? g_env.mfma_min_b : kVectorMaxBatch + 1;
+}
+
+// Matrix-core launch shape: 16-row tiles; K-slices (a power of two, each at
+// least 4 chunk steps) until the launch has ~24 waves per CU; slices of a
+// tile share a block, with 8 waves per block where tiles are small enough.
+template <int F>
+Plan plan_mfma(int64_t R, int64_t K, int NT)
+{
+    std::call_once(g_env_once, read_env);
+    constexpr int COLS = chunk_cols<F>();
+    const int cus = cu_count();
+    const int64_t C = K / COLS, tiles = (R + 15) / 16;
+    int S = 1;
+    while (S < 16 && tiles * S < 24LL * cus && (C + 2 * S - 1) / (2 * S) >= 16)
+        S *= 2;
+    if (g_env.mfma_slices > 0 && g_env.mfma_slices <= 16)
+        S = g_env.mfma_slices;
+    int tpb = std::max(1, 8 / S);
+    while (tpb > 1 && (tiles + tpb - 1) / tpb < 2 * cus)
+        tpb /= 2;
+    Plan P;
+    P.kind = 4;
+    P.S = S;
+    P.rpb = tpb;
+    P.threads = S * tpb * kWave;
+    P.grid = (unsigned)((tiles + tpb - 1) / tpb);
+    P.lds = (size_t)mfma_table_units<F>() * sizeof(u32x4) + (size_t)S * tpb * NT * kWave * 4 * sizeof(float);
+    return P;
+}
+
+template <int F, int DT>
+int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
+{
+    const int NT = B > 16 ? 2 : 1;
+    const Plan P = plan_mfma<F>(R, K, NT);
+    const u32x4* x4 = static_cast<const u32x4*>(x);
+    (void)hipGetLastError();
+    if (NT == 1)
+        hipLaunchKernelGGL((mfma_kernel<F, DT, 1, 2>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, B, P.S,
+                           P.rpb);
+    else
+        hipLaunchKernelGGL((mfma_kernel<F, DT, 2, 2>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, B, P.S,
+                           P.rpb);
+    return hip_status(hipGetLastError());
+}
+
+template <int F>
+int launch_mfma_dt(int dtype, const Parts* parts, const void* x, int R, int K, int B, hipStream_t s)
+{
+    return dtype == NM_FP16 ? launch_mfma<F, NM_FP16>(*parts, x, R, K, B, s)
+                            : launch_mfma<F, NM_BF16>(*parts, x, R, K, B, s);
+}
 
 // Launches the chosen kernel over the concatenated rows of `parts` (R in total).
 template <int F, int DT, int NB>
@@ -1164,6 +1434,22 @@ int status_word(uint32_t** out)
     return NM_OK;
 }
 
+// The generic kernel takes at most 8 vectors per launch: larger batches go
+// through it 8 rows of x (and y) at a time.
+int generic_batches(int dtype, int B, const void* v, const uint8_t* m, const void* v2, const uint8_t* m2, const void* x,
+                    void* y, int64_t R, int64_t K, int N, int M, hipStream_t s)
+{
+    for (int b0 = 0; b0 < B; b0 += kVectorMaxBatch) {
+        const int nb = std::min(kVectorMaxBatch, B - b0);
+        const void* xb = static_cast<const uint16_t*>(x) + (size_t)b0 * (size_t)K;
+        void* yb = static_cast<uint16_t*>(y) + (size_t)b0 * (size_t)R;
+        const int st = dispatch<SparseGeneric>(dtype, nb, v, m, v2, m2, xb, yb, (int)R, (int)K, N, M, s);
+        if (st != NM_OK)
+            return st;
+    }
+    return NM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1194,7 +1480,7 @@ int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* ma
         return count < 1 || count > kMaxParts ? NM_ERR_BAD_SHAPE : NM_ERR_INVALID_ARG;
     if ((st = check_rk(0, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
         return st;
-    if (B < 1 || B > 8)
+    if (B < 1 || B > kMaxBatch)
         return NM_ERR_BAD_SHAPE;
     int64_t total = 0;
     for (int i = 0; i < count; ++i) {
@@ -1246,14 +1532,16 @@ int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* ma
         }
         for (int i = P.count + 1; i <= kMaxParts; ++i)
             P.begin[i] = P.begin[P.count];
+        if (B >= mfma_min_batch() || B > kVectorMaxBatch)
+            return M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)total, (int)K, B, s)
+                          : launch_mfma_dt<kNM48>(dtype, &P, x, (int)total, (int)K, B, s);
         return M == 4 ? dispatch<Sparse24>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s)
                       : dispatch<Sparse48>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s);
     }
     for (int i = 0; i < count; ++i) {
         if (R[i] == 0)
             continue;
-        if ((st = dispatch<SparseGeneric>(dtype, B, values[i], masks[i], (const void*)nullptr, (const uint8_t*)nullptr, x,
-                                          y[i], (int)R[i], (int)K, N, M, s)) != NM_OK)
+        if ((st = generic_batches(dtype, B, values[i], masks[i], nullptr, nullptr, x, y[i], R[i], K, N, M, s)) != NM_OK)
             return st;
     }
     return NM_OK;
@@ -1275,7 +1563,7 @@ int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64
         return count < 1 || count > kMaxParts ? NM_ERR_BAD_SHAPE : NM_ERR_INVALID_ARG;
     if ((st = check_rk(0, K)) != NM_OK)
         return st;
-    if (B < 1 || B > 8)
+    if (B < 1 || B > kMaxBatch)
         return NM_ERR_BAD_SHAPE;
     int64_t total = 0;
     for (int i = 0; i < count; ++i) {
@@ -1322,6 +1610,8 @@ int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64
     }
     for (int i = P.count + 1; i <= kMaxParts; ++i)
         P.begin[i] = P.begin[P.count];
+    if (B >= mfma_min_batch() || B > kVectorMaxBatch)
+        return launch_mfma_dt<kDense>(dtype, &P, x, (int)total, (int)K, B, s);
     return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s);
 }
 
@@ -1338,7 +1628,7 @@ int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const voi
         return st;
     if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
         return st;
-    if (B < 1 || B > 8 || 2 * R > INT32_MAX)
+    if (B < 1 || B > kMaxBatch || 2 * R > INT32_MAX)
         return NM_ERR_BAD_SHAPE;
     const size_t xbytes = (size_t)B * (size_t)K * 2, hbytes = (size_t)B * (size_t)R * 2;
     const size_t vb = (size_t)R * (size_t)(K / M * N) * 2, mb = (size_t)R * (size_t)(K / 8);
@@ -1365,10 +1655,13 @@ int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const voi
         P.begin[1] = (int)R;
         for (int i = 2; i <= kMaxParts; ++i)
             P.begin[i] = (int)(2 * R);
+        if (B >= mfma_min_batch() || B > kVectorMaxBatch)
+            return M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)(2 * R), (int)K, B, s)
+                          : launch_mfma_dt<kNM48>(dtype, &P, x, (int)(2 * R), (int)K, B, s);
         return M == 4 ? dispatch<Sparse24>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s)
                       : dispatch<Sparse48>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s);
     }
-    return dispatch<SparseGeneric>(dtype, B, values_gate, masks_gate, values_up, masks_up, x, h, (int)R, (int)K, N, M, s);
+    return generic_batches(dtype, B, values_gate, masks_gate, values_up, masks_up, x, h, R, K, N, M, s);
 }
 
 int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_t K, int dtype, const void* x, int B,
@@ -1379,7 +1672,7 @@ int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_
         return st;
     if ((st = check_rk(R, K)) != NM_OK)
         return st;
-    if (B < 1 || B > 8 || 2 * R > INT32_MAX)
+    if (B < 1 || B > kMaxBatch || 2 * R > INT32_MAX)
         return NM_ERR_BAD_SHAPE;
     const size_t xbytes = (size_t)B * (size_t)K * 2, hbytes = (size_t)B * (size_t)R * 2;
     const size_t wb = (size_t)R * (size_t)K * 2;
@@ -1401,6 +1694,8 @@ int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_
     P.begin[1] = (int)R;
     for (int i = 2; i <= kMaxParts; ++i)
         P.begin[i] = (int)(2 * R);
+    if (B >= mfma_min_batch() || B > kVectorMaxBatch)
+        return launch_mfma_dt<kDense>(dtype, &P, x, (int)(2 * R), (int)K, B, s);
     return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s);
 }
 
