@@ -386,6 +386,37 @@ __device__ __forceinline__ RowRef row_ref(const Parts& P, int r, int C)
     return locate(P, r, C);
 }
 
+// Launch row r for a row index that differs across lanes: the part is chosen
+// by selects over the (wave-uniform) part table, never by a dynamic index.
+__device__ __forceinline__ RowRef row_ref_lane(const Parts& P, int r, int C)
+{
+    const int rr = P.glu ? (r >> 1) : r;
+    int p = P.glu ? (r & 1) : 0;
+    if (!P.glu) {
+#pragma unroll
+        for (int k = 1; k < kMaxParts; ++k)
+            p = (k < P.count && r >= P.begin[k]) ? k : p;
+    }
+    const u32x4* w = P.w[0];
+    const uint16_t* m = P.m[0];
+    int b0 = 0, R0 = P.begin[1];
+#pragma unroll
+    for (int k = 1; k < kMaxParts; ++k) {
+        const bool on = p == k;
+        w = on ? P.w[k] : w;
+        m = on ? P.m[k] : m;
+        b0 = on ? P.begin[k] : b0;
+        R0 = on ? P.begin[k + 1] - P.begin[k] : R0;
+    }
+    const int rl = P.glu ? rr : r - b0;
+    RowRef o;
+    o.w = w + (size_t)rl * C;
+    o.m = m + (size_t)rl * C;
+    o.y = (P.glu ? P.y[0] : P.y[0]) + rl;
+    o.R = P.glu ? P.begin[1] : R0;
+    return o;
+}
+
 // The gated-MLP output element: SiLU(g) * u with SiLU(t) = t / (1 + e^-t),
 // from the unrounded fp32 sums.  It is evaluated in double (once per output
 // row, so the cost is nil): in fp32, e^-g overflows for g < -88.7 and SiLU
@@ -657,19 +688,19 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
 // ---- matrix-core kernel for batched products ----------------------------------
 
 // With several activation vectors the VALU kernels above pay one byte-permute
-// and one dot2 per group per vector; at B >= 4 that, not HBM, sets their pace.
-// Here the matrix cores take the batch: a wave multiplies a 16-row tile of W
-// by x^T (16 batch columns per tile of the batch) with v_mfma_f32_16x16x16,
-// over one K-slice.  Lane l (i = l % 16, quarter q = l / 16) streams chunks
-// c = cbeg + 4 t + q of row r0 + i; each chunk's 16 (dense: 8) columns are
+// and one dot2 per group per vector, plus the LDS reads of every vector's x;
+// from B ~ 6 that, not HBM, sets their pace.  Here the matrix cores take the
+// batch: a wave multiplies a 16-row tile of W by x^T (16 batch columns per
+// tile of the batch) with v_mfma_f32_16x16x16 over one K-slice.  In the
+// operand layout lane l (i = l % 16, quarter q = l / 16) holds chunk
+// c0 + 4 t + q of tile row i at step t; each chunk's 16 (dense: 8) columns are
 // COLS / 4 k-blocks of 4 columns, and the A operand of a k-block -- 4 dense
 // weights of one row -- is rebuilt from the packed values with two byte
 // permutes (2:4: one group; 4:8: half a group; dense: a copy).  The B operand
 // is the same 4 columns of x row i, read from L2 (x is small); lanes of batch
 // rows past B repeat row B - 1 and their outputs are dropped.  The matrix
 // core reduces over k, so no cross-lane reduction is needed: the slices of a
-// tile add up in LDS in slice order.  Loads run two rounds of U chunk steps
-// ahead (two register buffers).
+// tile add up in LDS in slice order.
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -704,12 +735,33 @@ __device__ u32x2 expand24(uint32_t n)
     return u32x2{sel[0], sel[1]};
 }
 
-// 16-byte LDS units of the matrix-core kernel's expansion table: 2:4 keeps
-// 16 entries of 8 bytes, 4:8 the 256-entry select48 table.
+// 16-byte LDS units of the matrix-core kernels' expansion tables: 256
+// entries for both sparse formats, one per mask byte (2:4: the two groups'
+// expand24 selector pairs; 4:8: select48).
 template <int F>
 constexpr int mfma_table_units()
 {
-    return F == kNM24 ? 16 * 8 / 16 : (F == kNM48 ? 256 : 0);
+    return F == kDense ? 0 : 256;
+}
+
+// Table entry of mask byte b for 2:4: the selector pairs of its low and high
+// nibble.
+__device__ u32x4 expand24_byte(uint32_t b)
+{
+    const u32x2 lo = expand24(b & 0xFu), hi = expand24(b >> 4);
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+template <int F>
+__device__ __forceinline__ void build_mfma_table(u32x4* tab)
+{
+    if constexpr (F == kNM24) {
+        for (unsigned t = threadIdx.x; t < 256; t += blockDim.x)
+            tab[t] = expand24_byte(t);
+    } else if constexpr (F == kNM48) {
+        for (unsigned t = threadIdx.x; t < 256; t += blockDim.x)
+            tab[t] = select48(t);
+    }
 }
 
 // The A operand of k-block s (dense columns 4 s .. 4 s + 3 of the chunk).
@@ -719,8 +771,9 @@ __device__ __forceinline__ u32x2 a_frag(const uint32_t* w, uint32_t m, int s, co
     if constexpr (F == kDense) {
         return u32x2{w[2 * s], w[2 * s + 1]};
     } else if constexpr (F == kNM24) {
-        const u32x2 sel = reinterpret_cast<const u32x2*>(tab)[(m >> (4 * s)) & 0xFu];
-        return u32x2{__builtin_amdgcn_perm(w[s], w[s], sel.x), __builtin_amdgcn_perm(w[s], w[s], sel.y)};
+        const u32x4 sel = tab[(m >> (8 * (s >> 1))) & 0xFFu];          // one read serves k-blocks 2g, 2g + 1
+        const uint32_t s0 = (s & 1) ? sel.z : sel.x, s1 = (s & 1) ? sel.w : sel.y;
+        return u32x2{__builtin_amdgcn_perm(w[s], w[s], s0), __builtin_amdgcn_perm(w[s], w[s], s1)};
     } else {
         const int g = s >> 1;
         const u32x4 sel = tab[(m >> (8 * g)) & 0xFFu];
@@ -729,131 +782,194 @@ __device__ __forceinline__ u32x2 a_frag(const uint32_t* w, uint32_t m, int s, co
     }
 }
 
-template <int F, int DT, int NT, int U>
-__global__ __launch_bounds__(1024) void mfma_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K, int B,
-                                                    int S, int tiles_per_block)
+
+// Loading in the operand layout would stream each row in 64-byte pieces (one
+// per lane quarter): a load instruction would touch 16 rows, and the per-CU
+// limit on outstanding cache-line requests, not HBM, would set the pace
+// (measured: ~2 TB/s).  So a wave loads its 16-row tile in stages of 16 chunks per row:
+// each load instruction reads 256 contiguous bytes of four rows (full lines),
+// the stage goes to a wave-private LDS buffer, and the matrix-core operands
+// are read back from there.  The next stage's loads are in flight while the
+// current one is multiplied; x for a stage is fetched from L2 just before the
+// next stage's weight loads, so it never waits behind them.  Each lane's row
+// pointers are formed once, by selects over the parts (an index into the
+// kernel arguments that varies by lane would become a memory load).
+constexpr int kStageChunks = 16;                                  // chunks per row per stage
+constexpr int kStagePitch = kStageChunks * 16 + 16;               // bytes per values row (rows 4 banks apart)
+constexpr int kStageMPitch = kStageChunks * 2 + 4;                // bytes per mask row (an odd dword count)
+constexpr int kStageBytes = 16 * kStagePitch + 16 * kStageMPitch; // per wave
+
+template <int F, int DT, int NT>
+__global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
+                                                         int B, int S, int tiles_per_block)
 {
     extern __shared__ u32x4 smem[];
     constexpr int COLS = chunk_cols<F>();
     constexpr int XC = COLS / 8;                 // 16-byte x units per chunk
     constexpr int KB = COLS / 4;                 // k-blocks per chunk
+    constexpr int T = kStageChunks / 4;          // matrix-core steps per stage
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lt = wave / S, sl = wave - lt * S;
     const int r0 = (blockIdx.x * tiles_per_block + lt) * 16;
     const int C = K / COLS;
-    const int cps = ((C + S - 1) / S + 3) & ~3;  // chunks per slice, whole steps of 4
+    const int cps = ((C + S - 1) / S + kStageChunks - 1) / kStageChunks * kStageChunks;
     const int cbeg = min(C, sl * cps), cend = min(C, cbeg + cps);
-    const int nsteps = r0 < R ? (cend - cbeg + 3) / 4 : 0;
-    const int nrounds = (nsteps + U - 1) / U;
-    const int i = lane & 15, q = lane >> 4;
-    const RowRef row = row_ref(P, min(r0 + i, R - 1), C);
-    const int q8 = K / 8;
+    const int nst = r0 < R ? (cend - cbeg + kStageChunks - 1) / kStageChunks : 0;
+    const int i = lane & 15, q = lane >> 4;      // matrix-core layout
+    constexpr int RPL = kWave / kStageChunks;    // rows per load instruction
+    constexpr int NL = 16 / RPL;                 // load instructions per stage
+    const int lrow = lane / kStageChunks, lc = lane % kStageChunks;  // load layout: row RPL rr + lrow, chunk c0 + lc
     int xrow[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-        xrow[nt] = min(16 * nt + i, B - 1) * q8;
-
-    u32x4 va[U], vb[U];
-    uint32_t ma[U], mb[U];
-    u32x4 xa[NT][U][XC], xb[NT][U][XC];
-    auto fetch = [&](int t0, u32x4* v, uint32_t* mk, u32x4 (&xv)[NT][U][XC]) {
+        xrow[nt] = min(16 * nt + i, B - 1) * (K / 8);
+    const u32x4* wp[NL];
+    const uint16_t* mp[NL];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = cbeg + 4 * (t0 + u) + q;
-            const int cc = c < cend ? c : 0;
-            v[u] = __builtin_nontemporal_load(row.w + cc);
+    for (int rr = 0; rr < NL; ++rr) {
+        const RowRef row = row_ref_lane(P, min(r0 + RPL * rr + lrow, R - 1), C);
+        wp[rr] = row.w;
+        mp[rr] = row.m;
+    }
+    const u32x4* tab = smem;
+    uint8_t* stage = reinterpret_cast<uint8_t*>(smem + mfma_table_units<F>()) + (size_t)wave * kStageBytes;
+    uint8_t* stage_m = stage + 16 * kStagePitch;
+
+    // Two weight register buffers (the stage being staged and the one after
+    // it in flight) and one for a stage's x.
+    u32x4 va[NL], vb[NL];
+    uint32_t ma[NL], mb[NL];
+    u32x4 xv[NT][T][XC];
+    auto fetch_w = [&](int c0, u32x4* v, uint32_t* m) {
+        const int c = c0 + lc;
+        const int cc = c < cend ? c : 0;
+#pragma unroll
+        for (int rr = 0; rr < NL; ++rr) {
+            v[rr] = __builtin_nontemporal_load(wp[rr] + cc);
             if constexpr (F != kDense)
-                mk[u] = __builtin_nontemporal_load(row.m + cc);
+                m[rr] = __builtin_nontemporal_load(mp[rr] + cc);
             else
-                mk[u] = 0;
+                m[rr] = 0;
+        }
+    };
+    auto fetch_x = [&](int c0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int c = c0 + 4 * t + q;
+            const int cc = c < cend ? c : 0;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int h = 0; h < XC; ++h)
-                    xv[nt][u][h] = x4[xrow[nt] + cc * XC + h];
+                    xv[nt][t][h] = x4[xrow[nt] + cc * XC + h];
+        }
+    };
+    auto stash = [&](const u32x4* v, const uint32_t* m) {
+#pragma unroll
+        for (int rr = 0; rr < NL; ++rr) {
+            const int row = RPL * rr + lrow;
+            *reinterpret_cast<u32x4*>(stage + row * kStagePitch + lc * 16) = v[rr];
+            if constexpr (F != kDense)
+                *reinterpret_cast<uint16_t*>(stage_m + row * kStageMPitch + lc * 2) = (uint16_t)m[rr];
         }
     };
     f32x4 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
         acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const u32x4* tab = smem;
-    auto consume = [&](int t0, const u32x4* v, const uint32_t* mk, const u32x4 (&xv)[NT][U][XC]) {
+    auto consume = [&](int c0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (4 * (t0 + u) >= cend - cbeg)     // wave-uniform: this step is past the slice for every lane
-                break;
-            const bool live = cbeg + 4 * (t0 + u) + q < cend;
-            const uint32_t w[4] = {live ? v[u].x : 0u, live ? v[u].y : 0u, live ? v[u].z : 0u, live ? v[u].w : 0u};
-            const uint32_t m = live ? mk[u] : 0u;
+        for (int t = 0; t < T; ++t) {
+            const int j = 4 * t + q;
+            const bool live = c0 + j < cend;
+            const u32x4 vv = *reinterpret_cast<const u32x4*>(stage + i * kStagePitch + j * 16);
+            uint32_t mm = 0;
+            if constexpr (F != kDense)
+                mm = *reinterpret_cast<const uint16_t*>(stage_m + i * kStageMPitch + j * 2);
+            const uint32_t w[4] = {live ? vv.x : 0u, live ? vv.y : 0u, live ? vv.z : 0u, live ? vv.w : 0u};
+            mm = live ? mm : 0u;
 #pragma unroll
             for (int s = 0; s < KB; ++s) {
-                const u32x2 a = a_frag<F>(w, m, s, tab);
+                const u32x2 a = a_frag<F>(w, mm, s, tab);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const u32x4 xx = xv[nt][u][s >> 1];
+                    const u32x4 xx = xv[nt][t][s >> 1];
                     const u32x2 b = (s & 1) ? u32x2{xx.z, xx.w} : u32x2{xx.x, xx.y};
                     acc[nt] = mfma16<DT>(a, b, acc[nt]);
                 }
             }
         }
     };
+    // One pipeline step: multiply stage st (in LDS, its x in registers),
+    // stage st + 1 (its weights arrived in `cur`), fetch x of st + 1, then
+    // the weights of st + 3 into `cur` (st + 2 is in flight in the other
+    // buffer).  Loads past the slice's end read chunk 0 and are never used.
+    auto step = [&](int c0, u32x4* cv, uint32_t* cm) {
+        __builtin_amdgcn_sched_barrier(0);
+        consume(c0);
+        __builtin_amdgcn_sched_barrier(0);
+        stash(cv, cm);                           // after this stage's LDS reads (in order within the wave)
+        fetch_x(c0 + kStageChunks);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_w(c0 + 3 * kStageChunks, cv, cm);
+    };
 
-    if (nrounds > 0)
-        fetch(0, va, ma, xa);
-    if constexpr (F == kNM24) {
-        if (threadIdx.x < 16)
-            reinterpret_cast<u32x2*>(smem)[threadIdx.x] = expand24(threadIdx.x);
-    } else if constexpr (F == kNM48) {
-        for (unsigned t = threadIdx.x; t < 256; t += blockDim.x)
-            smem[t] = select48(t);
-    }
+    build_mfma_table<F>(smem);
     __syncthreads();
-    for (int j = 0; j < nrounds; j += 2) {
-        if (j + 1 < nrounds)
-            fetch((j + 1) * U, vb, mb, xb);
-        consume(j * U, va, ma, xa);
-        if (j + 1 < nrounds) {
-            if (j + 2 < nrounds)
-                fetch((j + 2) * U, va, ma, xa);
-            consume((j + 1) * U, vb, mb, xb);
+    // Every load inside the loop is unconditional, so the compiler counts
+    // outstanding loads exactly (a conditional load makes it wait for all).
+    if (nst > 0) {
+        fetch_w(cbeg, va, ma);
+        stash(va, ma);
+        fetch_x(cbeg);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_w(cbeg + kStageChunks, va, ma);
+        fetch_w(cbeg + 2 * kStageChunks, vb, mb);
+        int c0 = cbeg;
+        int st = 0;
+        for (; st + 2 <= nst; st += 2, c0 += 2 * kStageChunks) {
+            step(c0, va, ma);
+            step(c0 + kStageChunks, vb, mb);
         }
+        if (st < nst)
+            consume(c0);
     }
 
-    // Slice sums: D[4 q + v][i] of this wave's tile (row 4 q + v, batch column i).
-    float* part = reinterpret_cast<float*>(smem + mfma_table_units<F>());
+    // Slice sums: D[4 q + v][i] of this wave's tile (row 4 q + v, batch column 16 nt + i).
+    float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem + mfma_table_units<F>()) +
+                                           (size_t)blockDim.x / kWave * kStageBytes);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            part[((wave * NT + nt) * kWave + lane) * 4 + v] = acc[nt][v];
+        for (int vv = 0; vv < 4; ++vv)
+            part[((wave * NT + nt) * kWave + lane) * 4 + vv] = acc[nt][vv];
     __syncthreads();
     if (sl != 0 || r0 >= R)
         return;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int b = 16 * nt + i;
-        float sum[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float t = part[((wave * NT + nt) * kWave + lane) * 4 + v];
-            for (int j = 1; j < S; ++j)
-                t += part[(((wave + j) * NT + nt) * kWave + lane) * 4 + v];
-            sum[v] = t;
-        }
         if (b >= B)
             continue;
+        float sum[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = r0 + 4 * q + v;
+        for (int vv = 0; vv < 4; ++vv) {
+            float t = part[((wave * NT + nt) * kWave + lane) * 4 + vv];
+            for (int j = 1; j < S; ++j)
+                t += part[(((wave + j) * NT + nt) * kWave + lane) * 4 + vv];
+            sum[vv] = t;
+        }
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+            const int r = r0 + 4 * q + vv;
             if (r >= R)
                 continue;
             const RowRef o = row_ref(P, r, C);
             if (!P.glu)
-                o.y[(size_t)b * o.R] = from_f32<DT>(sum[v]);
-            else if ((v & 1) == 0)                // rows r (gate) and r + 1 (up) of one output
-                o.y[(size_t)b * o.R] = glu_out<DT>(sum[v], sum[v + 1]);
+                o.y[(size_t)b * o.R] = from_f32<DT>(sum[vv]);
+            else if ((vv & 1) == 0)              // rows r (gate) and r + 1 (up) of one output
+                o.y[(size_t)b * o.R] = glu_out<DT>(sum[vv], sum[vv + 1]);
         }
     }
 }
@@ -1190,57 +1306,73 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
 constexpr int kMaxBatch = 32;       // activation vectors per call
 constexpr int kVectorMaxBatch = 8;  // the VALU kernels' limit; larger batches use the matrix cores
 
-// Batches of at least this many vectors go to the matrix-core kernel (by
-// default only those beyond the VALU kernels' limit: at B <= 8 the VALU
-// kernels measured faster on every workload shape).
-int mfma_min_batch()
+// Batches of at least this many vectors go to the matrix-core kernels (from
+// timing on MI355X over the Llama-3.1-8B and Qwen3-32B MLP shapes: the VALU
+// kernels win below, the staged matrix-core kernel at and above).
+int mfma_min_batch(bool dense)
 {
     std::call_once(g_env_once, read_env);
-    return g_env.mfma_min_b > 0 ? g_env.mfma_min_b : kVectorMaxBatch + 1;
+    if (g_env.mfma_min_b > 0)
+        return g_env.mfma_min_b;
+    return dense ? 4 : 6;
 }
 
-// Matrix-core launch shape: 16-row tiles; K-slices (a power of two, each at
-// least 4 chunk steps) until the launch has ~24 waves per CU; slices of a
-// tile share a block, with 8 waves per block where tiles are small enough.
+
+// Staged matrix-core launch shape: 16-row tiles; 1, 2, 4 or 8 K-slices (each
+// at least one 32-chunk stage) until the launch has ~12 waves per CU (the
+// kernel's register use allows 3 per SIMD); the slices of a tile, or 4 tiles,
+// share a block of at most 8 waves.
 template <int F>
-Plan plan_mfma(int64_t R, int64_t K, int NT)
+Plan plan_mfma_stage(int64_t R, int64_t K, int NT)
 {
     std::call_once(g_env_once, read_env);
     constexpr int COLS = chunk_cols<F>();
     const int cus = cu_count();
     const int64_t C = K / COLS, tiles = (R + 15) / 16;
     int S = 1;
-    while (S < 16 && tiles * S < 24LL * cus && (C + 2 * S - 1) / (2 * S) >= 16)
+    while (S < 8 && tiles * S < 12LL * cus && C / (2 * S) >= kStageChunks)
         S *= 2;
-    if (g_env.mfma_slices > 0 && g_env.mfma_slices <= 16)
+    if (g_env.mfma_slices > 0 && g_env.mfma_slices <= 8)
         S = g_env.mfma_slices;
-    int tpb = std::max(1, 8 / S);
+    int tpb = std::max(1, 4 / S);
     while (tpb > 1 && (tiles + tpb - 1) / tpb < 2 * cus)
         tpb /= 2;
     Plan P;
-    P.kind = 4;
+    P.kind = 5;
     P.S = S;
     P.rpb = tpb;
     P.threads = S * tpb * kWave;
     P.grid = (unsigned)((tiles + tpb - 1) / tpb);
-    P.lds = (size_t)mfma_table_units<F>() * sizeof(u32x4) + (size_t)S * tpb * NT * kWave * 4 * sizeof(float);
+    const size_t waves = (size_t)S * tpb;
+    P.lds = (size_t)mfma_table_units<F>() * sizeof(u32x4) + waves * kStageBytes + waves * NT * kWave * 4 * sizeof(float);
     return P;
 }
 
+template <int F, int DT, int NT>
+int launch_mfma_nt(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
+{
+    const Plan P = plan_mfma_stage<F>(R, K, NT);
+    if (P.lds > 64 * 1024) {
+        static bool raised = false;              // once per instantiation
+        if (!raised) {
+            if (hipFuncSetAttribute((const void*)mfma_stage_kernel<F, DT, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kLdsMax) != hipSuccess)
+                return NM_ERR_HIP;
+            raised = true;
+        }
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((mfma_stage_kernel<F, DT, NT>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
+                       static_cast<const u32x4*>(x), R, K, B, P.S, P.rpb);
+    return hip_status(hipGetLastError());
+}
+
+// Up to 16 vectors are one tile of the matrix cores' batch dimension; 17 to
+// 32 take two, both fed by the same weight loads.
 template <int F, int DT>
 int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
-    const int NT = B > 16 ? 2 : 1;
-    const Plan P = plan_mfma<F>(R, K, NT);
-    const u32x4* x4 = static_cast<const u32x4*>(x);
-    (void)hipGetLastError();
-    if (NT == 1)
-        hipLaunchKernelGGL((mfma_kernel<F, DT, 1, 2>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, B, P.S,
-                           P.rpb);
-    else
-        hipLaunchKernelGGL((mfma_kernel<F, DT, 2, 2>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, B, P.S,
-                           P.rpb);
-    return hip_status(hipGetLastError());
+    return B > 16 ? launch_mfma_nt<F, DT, 2>(parts, x, R, K, B, s) : launch_mfma_nt<F, DT, 1>(parts, x, R, K, B, s);
 }
 
 template <int F>
@@ -1532,7 +1664,7 @@ int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* ma
         }
         for (int i = P.count + 1; i <= kMaxParts; ++i)
             P.begin[i] = P.begin[P.count];
-        if (B >= mfma_min_batch() || B > kVectorMaxBatch)
+        if (B >= mfma_min_batch(false) || B > kVectorMaxBatch)
             return M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)total, (int)K, B, s)
                           : launch_mfma_dt<kNM48>(dtype, &P, x, (int)total, (int)K, B, s);
         return M == 4 ? dispatch<Sparse24>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s)
@@ -1610,7 +1742,7 @@ int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64
     }
     for (int i = P.count + 1; i <= kMaxParts; ++i)
         P.begin[i] = P.begin[P.count];
-    if (B >= mfma_min_batch() || B > kVectorMaxBatch)
+    if (B >= mfma_min_batch(true) || B > kVectorMaxBatch)
         return launch_mfma_dt<kDense>(dtype, &P, x, (int)total, (int)K, B, s);
     return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s);
 }
@@ -1655,7 +1787,7 @@ int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const voi
         P.begin[1] = (int)R;
         for (int i = 2; i <= kMaxParts; ++i)
             P.begin[i] = (int)(2 * R);
-        if (B >= mfma_min_batch() || B > kVectorMaxBatch)
+        if (B >= mfma_min_batch(false) || B > kVectorMaxBatch)
             return M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)(2 * R), (int)K, B, s)
                           : launch_mfma_dt<kNM48>(dtype, &P, x, (int)(2 * R), (int)K, B, s);
         return M == 4 ? dispatch<Sparse24>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s)
@@ -1694,7 +1826,7 @@ int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_
     P.begin[1] = (int)R;
     for (int i = 2; i <= kMaxParts; ++i)
         P.begin[i] = (int)(2 * R);
-    if (B >= mfma_min_batch() || B > kVectorMaxBatch)
+    if (B >= mfma_min_batch(true) || B > kVectorMaxBatch)
         return launch_mfma_dt<kDense>(dtype, &P, x, (int)(2 * R), (int)K, B, s);
     return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s);
 }

@@ -157,7 +157,7 @@ def test_dense_multi_rejects_bad_arguments():
     y = _arr(P, [FAKE2 + 0x100000, FAKE2 + 0x200000])
     assert lib.nm_gemv_dense_multi(0, W, R, 64, 0, FAKE2, 1, y, None) == L.NM_ERR_BAD_SHAPE
     assert lib.nm_gemv_dense_multi(2, None, R, 64, 0, FAKE2, 1, y, None) == L.NM_ERR_INVALID_ARG
-    assert lib.nm_gemv_dense_multi(2, W, R, 64, 0, FAKE2, 9, y, None) == L.NM_ERR_BAD_SHAPE
+    assert lib.nm_gemv_dense_multi(2, W, R, 64, 0, FAKE2, 33, y, None) == L.NM_ERR_BAD_SHAPE
     Wm = _arr(P, [FAKE, FAKE + 0x10002])
     assert lib.nm_gemv_dense_multi(2, Wm, R, 64, 0, FAKE2, 1, y, None) == L.NM_ERR_INVALID_ARG
 
