@@ -76,6 +76,8 @@ def _load(path):
         lib.orc_swiglu.argtypes = [P, P, I64, P]
         lib.orc_calib_accumulate.argtypes = [P, P, I64, I64, I, P, P]
         lib.orc_calib_keep.argtypes = [P, P, I64, I64, I, I, I, P]
+        lib.orc_hybrid_row_loss.argtypes = [P, P, P, I64, I64, I, I, I, P]
+        lib.orc_hybrid_select.argtypes = [P, I64, I64, P]
         for f in ("orc_pack", "orc_expand", "orc_spmv_rows", "orc_gemv_rows"):
             getattr(lib, f).restype = ctypes.c_int
         lib.orc_round_array.restype = None
@@ -225,6 +227,49 @@ def calib_keep(W, hdiag, n, m, dtype):
     if st != OK:
         raise OracleError(st)
     return keep
+
+
+def hybrid_row_loss(W, n, m, dtype, keep=None, h=None):
+    """Per-row pruning loss L_r = sum over pruned columns of w^2 h[c] (h: float32
+    values used exactly, or None for 1), pruned by the keep-mask or by top-n
+    magnitude.  Returns float64 [R]."""
+    W = _u16(W)
+    R, K = W.shape
+    kp = None if keep is None else np.ascontiguousarray(keep, np.uint8)
+    hv = None if h is None else np.ascontiguousarray(np.asarray(h, np.float32).astype(np.float64))
+    loss = np.zeros(R, np.float64)
+    st = _lib().orc_hybrid_row_loss(_ptr(W), None if kp is None else _ptr(kp), None if hv is None else _ptr(hv),
+                                    R, K, n, m, _dt(dtype), _ptr(loss))
+    if st != OK:
+        raise OracleError(st)
+    return loss
+
+
+def hybrid_select(loss, n_dense):
+    """uint8 [R] flags of the n_dense rows of largest loss (NaN lowest, lower row first)."""
+    loss = np.ascontiguousarray(loss, np.float64)
+    flags = np.zeros(loss.shape[0], np.uint8)
+    st = _lib().orc_hybrid_select(_ptr(loss), loss.shape[0], n_dense, _ptr(flags))
+    if st != OK:
+        raise OracleError(st)
+    return flags
+
+
+def hybrid_spmv(W, flags, n, m, dtype, x, keep=None):
+    """The hybrid matrix's product: rows flagged dense use W as is, the others
+    its n:m pruned form (keep-mask or top-n).  Returns (y, A) [B][R] in double."""
+    W = _u16(W)
+    R, K = W.shape
+    x = _u16(np.atleast_2d(x))
+    d = np.asarray(flags, bool)
+    y = np.zeros((x.shape[0], R))
+    A = np.zeros((x.shape[0], R))
+    if (~d).any():
+        v, mk = pack(W[~d], None if keep is None else np.asarray(keep)[~d], n, m, dtype)
+        y[:, ~d], A[:, ~d] = spmv(v, mk, K, n, m, dtype, x)
+    if d.any():
+        y[:, d], A[:, d] = gemv(W[d], dtype, x)
+    return y, A
 
 
 # ---- acceptance rule ------------------------------------------------------

@@ -456,3 +456,68 @@ int orc_calib_keep(const uint16_t* W, const double* h, int64_t R, int64_t K, int
         }
     return ORC_OK;
 }
+
+/* ---- hybrid sparse + dense rows ----------------------------------------------
+ * The Spense abstract on the fifth page (thelatestinai.com page for arXiv
+ * 2610.02598) splits a weight matrix into a 2:4-sparse region and a dense
+ * region and stresses choosing the dense region well; it gives neither the
+ * region's shape nor the rule.  Readings taken here: the dense region is a
+ * set of whole rows (output channels), and the rows kept dense are those
+ * whose pruning loses most, the loss of a row being
+ *     L_r = sum over its pruned columns c of w[r][c]^2 * h[c]
+ * (the diagonal saliency of the calibration reading, h = 1 without one).
+ * The pruned columns are those the keep-mask drops, or, without one, those
+ * top-N by magnitude drops (the nm_pack rule).
+ */
+
+/* L_r for every row: groups in column order, and within a group the pruned
+ * columns in ascending order; each term (w*w)*h is exact in double and the
+ * running sum is rounded once per term.  h == NULL means h = 1. */
+int orc_hybrid_row_loss(const uint16_t* W, const uint8_t* keep, const double* h, int64_t R, int64_t K, int N, int M,
+                        int dtype, double* loss)
+{
+    int st = check_nm(R, K, N, M);
+    if (st != ORC_OK)
+        return st;
+    if (dtype != ORC_FP16 && dtype != ORC_BF16)
+        return ORC_BAD_ARG;
+    int chosen[8];
+    for (int64_t r = 0; r < R; ++r) {
+        double l = 0.0;
+        for (int64_t g = 0; g < K / M; ++g) {
+            const uint16_t* w = W + r * K + g * M;
+            st = select_group(w, keep ? keep + r * K + g * M : NULL, N, M, dtype, chosen);
+            if (st != ORC_OK)
+                return st;
+            for (int j = 0; j < M; ++j) {
+                if (chosen[j])
+                    continue;
+                double v = orc_to_double(w[j], dtype);
+                double hv = h ? h[g * M + j] : 1.0;
+                double term = v * v * hv;
+                l = l + term;
+            }
+        }
+        loss[r] = l;
+    }
+    return ORC_OK;
+}
+
+/* flags[r] = 1 for the n_dense rows of largest loss (a NaN loss lowest),
+ * the lower row first among equals; 0 for the others. */
+int orc_hybrid_select(const double* loss, int64_t R, int64_t n_dense, uint8_t* flags)
+{
+    if (R < 0 || n_dense < 0 || n_dense > R)
+        return ORC_BAD_SHAPE;
+    for (int64_t r = 0; r < R; ++r) {
+        double lr = isnan(loss[r]) ? -1.0 : loss[r];
+        int64_t above = 0;
+        for (int64_t s = 0; s < R; ++s) {
+            double ls = isnan(loss[s]) ? -1.0 : loss[s];
+            if (ls > lr || (ls == lr && s < r))
+                ++above;
+        }
+        flags[r] = above < n_dense ? 1 : 0;
+    }
+    return ORC_OK;
+}

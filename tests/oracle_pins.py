@@ -531,6 +531,58 @@ def pin_calib_keep(seed=8):
     assert keep.tolist() == [[1, 1, 0, 1, 1, 1, 0, 1]]
 
 
+def pin_hybrid(seed=9):
+    """Hybrid rows: the row loss against exact rationals over the pruned
+    columns (taken from the pinned packer's bitmap), in top-n and keep-mask
+    modes; scaling h by 4 scales the loss by 4 exactly; the row choice against
+    a sort (loss descending, row ascending), with n_dense = 0 and = R, ties
+    and a NaN loss; and the hybrid product reduces to the sparse product with
+    no dense rows and to the dense product with all rows dense."""
+    rng = np.random.default_rng(seed)
+    for dt in ("fp16", "bf16"):
+        for n, m in ((2, 4), (4, 8), (1, 4)):
+            R, K = 9, 32
+            Wv = np.round(rng.normal(0, 1, (R, K)) * 8) / 8
+            W = to_bits(Wv, dt)
+            Wv = bits_to_f64(W, dt)
+            h = (rng.random(K) * 4).astype(np.float32)
+            rand_keep = np.zeros((R, K), np.uint8)
+            for r in range(R):
+                for g0 in range(0, K, m):
+                    rand_keep[r, g0 + rng.choice(m, size=n, replace=False)] = 1
+            for keep in (None, rand_keep):
+                loss = oracle.hybrid_row_loss(W, n, m, dt, keep=keep, h=h)
+                kept = _bitmap_to_keep(oracle.pack(W, keep, n, m, dt)[1], K).astype(bool)
+                for r in range(R):
+                    exact = sum(Fraction(Wv[r, c]) ** 2 * Fraction(float(h[c])) for c in range(K) if not kept[r, c])
+                    assert abs(Fraction(loss[r]) - exact) <= Fraction(1, 10 ** 12) * (1 + abs(exact))
+                assert np.array_equal(oracle.hybrid_row_loss(W, n, m, dt, keep=keep, h=4 * h), 4 * loss)
+            loss1 = oracle.hybrid_row_loss(W, n, m, dt)
+            for r in range(R):
+                _, mk = oracle.pack(W[r:r + 1], None, n, m, dt)
+                kept = _bitmap_to_keep(mk, K)[0].astype(bool)
+                assert loss1[r] == math.fsum(Wv[r, c] ** 2 for c in range(K) if not kept[c]) or \
+                    abs(loss1[r] - math.fsum(Wv[r, c] ** 2 for c in range(K) if not kept[c])) <= 1e-12 * loss1[r]
+    loss = np.array([3.0, 1.0, 3.0, float("nan"), 0.0, 7.0, 1.0])
+    for nd in range(len(loss) + 1):
+        order = sorted(range(len(loss)), key=lambda r: (-(loss[r] if loss[r] == loss[r] else -1.0), r))
+        want = np.zeros(len(loss), np.uint8)
+        want[order[:nd]] = 1
+        assert np.array_equal(oracle.hybrid_select(loss, nd), want)
+    # the product reduces to the plain ones
+    R, K = 6, 64
+    W = to_bits(np.round(rng.normal(0, 1, (R, K)) * 16) / 16, "fp16")
+    x = to_bits(np.round(rng.normal(0, 1, (2, K)) * 16) / 16, "fp16")
+    v, mk = oracle.pack(W, None, 2, 4, "fp16")
+    ys, _ = oracle.spmv(v, mk, K, 2, 4, "fp16", x)
+    yd, _ = oracle.gemv(W, "fp16", x)
+    assert np.array_equal(oracle.hybrid_spmv(W, np.zeros(R, np.uint8), 2, 4, "fp16", x)[0], ys)
+    assert np.array_equal(oracle.hybrid_spmv(W, np.ones(R, np.uint8), 2, 4, "fp16", x)[0], yd)
+    f = np.array([1, 0, 0, 1, 0, 1], np.uint8)
+    yh = oracle.hybrid_spmv(W, f, 2, 4, "fp16", x)[0]
+    assert np.array_equal(yh[:, f == 1], yd[:, f == 1]) and np.array_equal(yh[:, f == 0], ys[:, f == 0])
+
+
 ALL_PINS = [
     pin_golden_rounding,
     pin_decode_exhaustive,
@@ -547,4 +599,5 @@ ALL_PINS = [
     pin_swiglu,
     pin_calib_accumulate,
     pin_calib_keep,
+    pin_hybrid,
 ] + [(lambda f=f: pin_golden_pack(f)) for f in golden_pack_files()]

@@ -38,6 +38,11 @@ MUTANTS = [
     ("saliency_ignores_h", "double s = w * w * h[c];", "double s = w * w;"),
     ("saliency_tie_to_highest", "(best < 0 || sal[j] > sal[best])", "(best < 0 || sal[j] >= sal[best])"),
     ("saliency_nan_ranks_high", "sal[j] = isnan(s) ? -1.0 : s;", "sal[j] = isnan(s) ? 1e300 : s;"),
+    ("hybrid_loss_counts_kept", "                if (chosen[j])\n                    continue;\n                double v",
+     "                if (!chosen[j])\n                    continue;\n                double v"),
+    ("hybrid_loss_ignores_h", "double hv = h ? h[g * M + j] : 1.0;", "double hv = 1.0;"),
+    ("hybrid_select_ascending", "if (ls > lr || (ls == lr && s < r))", "if (ls < lr || (ls == lr && s < r))"),
+    ("hybrid_select_ties_to_higher", "if (ls > lr || (ls == lr && s < r))", "if (ls > lr || (ls == lr && s > r))"),
 ]
 
 
