@@ -197,6 +197,60 @@ int nm_calib_accumulate(const void* X, const uint8_t* decode, int64_t T, int64_t
 int nm_calib_keep_mask(const void* W, const float* h, int64_t h_stride, int64_t R, int64_t K, int N, int M, int dtype,
                        uint8_t* keep, void* stream);
 
+/*
+ * ---- Hybrid sparse + dense rows -------------------------------------------------
+ * The Spense abstract ("Semi-structured 2:4 sparsity ...", on the
+ * thelatestinai.com page for arXiv 2610.02598) splits a weight matrix into a
+ * 2:4-sparse region and a dense region and stresses choosing the dense region
+ * well; it fixes neither the region's shape nor the rule.  This library's
+ * reading: the dense region is a set of whole rows (output channels), the rows
+ * whose pruning loses most,  L_r = sum over the row's pruned columns c of
+ * w[r][c]^2 * h[c]  (h the calibration Hessian's diagonal, or 1).  The sparse
+ * rows are packed as nm_pack packs them, the dense rows kept as they are, and
+ * two row lists say where each part's rows go in y.
+ *
+ * nm_hybrid_row_loss -- L_r for every row, in double: W [R][K] 16-bit (2-byte
+ * aligned); keep as in nm_pack (NULL: the top-N magnitude rule decides what is
+ * pruned); h[c * h_stride] fp32 (4-byte aligned) or NULL for 1; loss [R] double
+ * (8-byte aligned, output).  Terms are summed per row in column order, one
+ * rounding per term.  Waits for completion.  A keep-mask group without N kept
+ * -> NM_ERR_BAD_MASK; a NaN weight under the magnitude rule ->
+ * NM_ERR_NONFINITE (loss then unspecified).
+ */
+int nm_hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int64_t h_stride, int64_t R, int64_t K, int N,
+                       int M, int dtype, double* loss, void* stream);
+
+/* nm_hybrid_select_rows -- flags[r] = 1 for the n_dense (0..R) rows of largest
+ * loss, 0 elsewhere; a NaN loss ranks lowest, the lower row first among
+ * equals.  loss [R] double (8-byte aligned), flags [R] bytes.  Enqueues. */
+int nm_hybrid_select_rows(const double* loss, int64_t R, int64_t n_dense, uint8_t* flags, void* stream);
+
+/*
+ * nm_hybrid_pack -- build the hybrid matrix from W and the row flags (exactly
+ * n_dense nonzero, else NM_ERR_BAD_MASK): rows_dense [n_dense] and
+ * rows_sparse [R - n_dense] (int32, 4-byte aligned) list the flagged and the
+ * other rows in increasing order; W_dense [n_dense][K] holds the flagged rows
+ * of W; values / masks hold the other rows packed as nm_pack packs them (keep
+ * as in nm_pack, indexed by the rows of W).  Alignment and error rules as for
+ * nm_pack; no output may overlap an input or another output.  Waits for
+ * completion.
+ */
+int nm_hybrid_pack(const void* W, const uint8_t* keep, const uint8_t* flags, int64_t n_dense, int64_t R, int64_t K,
+                   int N, int M, int dtype, void* values, uint8_t* masks, void* W_dense, int32_t* rows_sparse,
+                   int32_t* rows_dense, void* stream);
+
+/*
+ * nm_spmv_hybrid -- y = W_hybrid x: y[b][rows_sparse[i]] from sparse row i as
+ * nm_spmv computes it, y[b][rows_dense[j]] from dense row j as nm_gemv_dense
+ * does.  The lists must partition 0..R-1 (as nm_hybrid_pack writes them);
+ * otherwise y is unspecified, but entries are clamped into 0..R-1, never
+ * written out of bounds.  Rules as for nm_spmv (x [B][K], y [B][R], B <= 32).
+ * Enqueues.
+ */
+int nm_spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows_sparse, const void* W_dense,
+                   const int32_t* rows_dense, int64_t n_dense, int64_t R, int64_t K, int N, int M, int dtype,
+                   const void* x, int B, void* y, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* nm_status_string(int status);
 

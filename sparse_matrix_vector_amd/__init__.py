@@ -10,6 +10,8 @@ step of the computation runs in the HIP kernels of ``libnmspmv.so``.
     h = spmv_swiglu((vg, mg), (vu, mu), x)         # SiLU(W_gate x) * (W_up x)
     H = calib_accumulate(X, decode)                # decoding-aware calibration
     keep = calib_keep_mask(W, H, n=2, m=4)         # -> pack(W, keep, 2, 4)
+    hyb = hybrid_pack(W, hybrid_select_rows(hybrid_row_loss(W), n_dense))
+    y = spmv_hybrid(hyb, x)                        # sparse rows + dense rows
 """
 import ctypes
 
@@ -19,7 +21,8 @@ from ._lib import (NM_BF16, NM_ERR_BAD_MASK, NM_ERR_BAD_SHAPE, NM_ERR_HIP, NM_ER
                    NM_ERR_NONFINITE, NM_ERR_UNSUPPORTED, NM_FP16, NM_OK, NmError, call, lib)
 
 __all__ = ["pack", "spmv", "spmv_multi", "spmv_swiglu", "gemv_dense", "gemv_dense_multi", "gemv_dense_swiglu",
-           "calib_accumulate", "calib_keep_mask", "NmError", "dtype_code", "stream_handle"]
+           "calib_accumulate", "calib_keep_mask", "hybrid_row_loss", "hybrid_select_rows", "hybrid_pack", "spmv_hybrid",
+           "Hybrid", "NmError", "dtype_code", "stream_handle"]
 
 _DT = {torch.float16: NM_FP16, torch.bfloat16: NM_BF16}
 
@@ -230,3 +233,86 @@ def calib_keep_mask(W, H, n=2, m=4, stream=None):
     call("nm_calib_keep_mask", W.data_ptr(), H.data_ptr(), stride, R, K, n, m, dtype_code(W.dtype), keep.data_ptr(),
          stream_handle(stream))
     return keep
+
+
+class Hybrid:
+    """A hybrid matrix: sparse rows packed (values, masks), dense rows as they
+    are (W_dense), and the y rows of each (rows_sparse, rows_dense)."""
+
+    def __init__(self, values, masks, W_dense, rows_sparse, rows_dense, R, K, n, m):
+        self.values, self.masks, self.W_dense = values, masks, W_dense
+        self.rows_sparse, self.rows_dense = rows_sparse, rows_dense
+        self.R, self.K, self.n, self.m = R, K, n, m
+
+    @property
+    def n_dense(self):
+        return self.rows_dense.shape[0]
+
+
+def hybrid_row_loss(W, n=2, m=4, keep=None, H=None, stream=None):
+    """Per-row pruning loss (float64 [R]): sum over pruned columns of w^2 * H_jj
+    (H: [K][K] or its diagonal [K], float32; None for 1)."""
+    _dev(W, "W")
+    R, K = W.shape
+    kp = None
+    if keep is not None:
+        _dev(keep, "keep")
+        kp = keep.data_ptr()
+    hp, hs = None, 0
+    if H is not None:
+        _dev(H, "H")
+        if H.dtype != torch.float32:
+            raise ValueError("H must be float32")
+        hp, hs = H.data_ptr(), (K + 1 if H.shape == (K, K) else 1)
+        if H.shape not in ((K, K), (K,)):
+            raise ValueError("H must be [K][K] or [K]")
+    loss = torch.empty(R, dtype=torch.float64, device=W.device)
+    call("nm_hybrid_row_loss", W.data_ptr(), kp, hp, hs, R, K, n, m, dtype_code(W.dtype), loss.data_ptr(),
+         stream_handle(stream))
+    return loss
+
+
+def hybrid_select_rows(loss, n_dense, stream=None):
+    """uint8 [R] flags of the n_dense rows of largest loss."""
+    _dev(loss, "loss")
+    if loss.dtype != torch.float64 or loss.dim() != 1:
+        raise ValueError("loss must be float64 [R]")
+    flags = torch.empty(loss.shape[0], dtype=torch.uint8, device=loss.device)
+    call("nm_hybrid_select_rows", loss.data_ptr(), loss.shape[0], n_dense, flags.data_ptr(), stream_handle(stream))
+    return flags
+
+
+def hybrid_pack(W, flags, n_dense=None, n=2, m=4, keep=None, stream=None):
+    """Build a Hybrid from W and row flags (n_dense nonzero; counted on the
+    host when not given)."""
+    _dev(W, "W"), _dev(flags, "flags")
+    R, K = W.shape
+    if n_dense is None:
+        n_dense = int(flags.count_nonzero().item())
+    Rs = R - n_dense
+    values = torch.empty((Rs, K // m * n), dtype=W.dtype, device=W.device)
+    masks = torch.empty((Rs, K // 8), dtype=torch.uint8, device=W.device)
+    W_dense = torch.empty((n_dense, K), dtype=W.dtype, device=W.device)
+    rows_sparse = torch.empty(Rs, dtype=torch.int32, device=W.device)
+    rows_dense = torch.empty(n_dense, dtype=torch.int32, device=W.device)
+    kp = None
+    if keep is not None:
+        _dev(keep, "keep")
+        kp = keep.data_ptr()
+    call("nm_hybrid_pack", W.data_ptr(), kp, flags.data_ptr(), n_dense, R, K, n, m, dtype_code(W.dtype),
+         values.data_ptr(), masks.data_ptr(), W_dense.data_ptr(), rows_sparse.data_ptr(), rows_dense.data_ptr(),
+         stream_handle(stream))
+    return Hybrid(values, masks, W_dense, rows_sparse, rows_dense, R, K, n, m)
+
+
+def spmv_hybrid(hyb, x, out=None, stream=None):
+    """y = W_hybrid x; x [K] or [B][K] -> [R] or [B][R]."""
+    x2, squeeze = _x2(x)
+    B, K = x2.shape
+    if K != hyb.K:
+        raise ValueError("x does not match the matrix")
+    y = torch.empty((B, hyb.R), dtype=x.dtype, device=x.device) if out is None else _dev(out, "out")
+    call("nm_spmv_hybrid", hyb.values.data_ptr(), hyb.masks.data_ptr(), hyb.rows_sparse.data_ptr(),
+         hyb.W_dense.data_ptr(), hyb.rows_dense.data_ptr(), hyb.n_dense, hyb.R, K, hyb.n, hyb.m, dtype_code(x.dtype),
+         x2.data_ptr(), B, y.data_ptr(), stream_handle(stream))
+    return y[0] if squeeze else y

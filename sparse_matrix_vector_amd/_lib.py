@@ -25,6 +25,10 @@ SIGNATURES = {
     "nm_gemv_dense_swiglu": (_I, [_P, _P, _I64, _I64, _I, _P, _I, _P, _P]),
     "nm_calib_accumulate": (_I, [_P, _P, _I64, _I64, _I, _P, _P]),
     "nm_calib_keep_mask": (_I, [_P, _P, _I64, _I64, _I64, _I, _I, _I, _P, _P]),
+    "nm_hybrid_row_loss": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P, _P]),
+    "nm_hybrid_select_rows": (_I, [_P, _I64, _I64, _P, _P]),
+    "nm_hybrid_pack": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "nm_spmv_hybrid": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P, _I, _P, _P]),
     "nm_status_string": (ctypes.c_char_p, [_I]),
     "nm_version": (_I, []),
 }

@@ -20,6 +20,7 @@
 
 #include <cstdint>
 
+#include "nm_decode.h"
 #include "nmspmv.h"
 
 namespace {
@@ -136,29 +137,6 @@ __global__ __launch_bounds__(256) void calib_accumulate_kernel(const uint16_t* _
 
 // ---- saliency keep-mask -----------------------------------------------------------
 
-// Exact decode of a 16-bit weight (DT) or of an fp32 word into double, from
-// the formats' fields, independent of the denormal mode.
-__device__ __forceinline__ double fields_to_f64(uint32_t bits, int fbits, int ebits)
-{
-    const int bias = (1 << (ebits - 1)) - 1;
-    const uint32_t emax = (1u << ebits) - 1;
-    const uint32_t sign = bits >> (fbits + ebits), e = (bits >> fbits) & emax, f = bits & ((1u << fbits) - 1);
-    double v;
-    if (e == emax)
-        v = f ? __builtin_nan("") : __builtin_inf();
-    else if (e == 0)
-        v = ldexp((double)f, 1 - bias - fbits);
-    else
-        v = ldexp((double)(f | (1u << fbits)), (int)e - bias - fbits);
-    return sign ? -v : v;
-}
-
-template <int DT>
-__device__ __forceinline__ double w_to_f64(uint32_t bits)
-{
-    return DT == NM_FP16 ? fields_to_f64(bits, 10, 5) : fields_to_f64(bits, 7, 8);
-}
-
 // One thread per (row, 8 columns): two 4-groups or one 8-group.  Saliency
 // w^2 h is exact in double (w^2 has at most 22 significant bits, h 24); a NaN
 // saliency ranks below every other.  Column j is kept when fewer than N group
@@ -177,8 +155,8 @@ __global__ __launch_bounds__(256) void calib_keep_kernel(const u32x4* __restrict
     double s[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const double w = w_to_f64<DT>((words[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        const double hv = fields_to_f64(__builtin_bit_cast(uint32_t, h[(c0 + e) * h_stride]), 23, 8);
+        const double w = nm_decode::w_to_f64<DT>((words[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        const double hv = nm_decode::f32_to_f64(h[(c0 + e) * h_stride]);
         const double v = w * w * hv;
         s[e] = v != v ? -1.0 : v;
     }

@@ -42,6 +42,7 @@
 #include <cstdlib>
 #include <mutex>
 
+#include "nm_decode.h"
 #include "nmspmv.h"
 
 namespace {
@@ -339,14 +340,25 @@ __device__ __forceinline__ void chunk_dot(const u32x4 v, const uint32_t mk, cons
 // are always reduced by one block.
 constexpr int kMaxParts = 4;
 
+// A part may also scatter its rows into a larger y: with ymap[p] set, its row
+// i goes to y row ymap[p][i] of a y whose batch stride is ystride[p] (the
+// hybrid format's sparse and dense rows); map entries are clamped into
+// [0, ystride), so a bad map can never write outside y.
 struct Parts {
     const u32x4* w[kMaxParts];
     const uint16_t* m[kMaxParts];
     uint16_t* y[kMaxParts];
+    const int32_t* ymap[kMaxParts];
+    int ystride[kMaxParts];
     int begin[kMaxParts + 1];
     int count;
     int glu;
 };
+
+__device__ __forceinline__ int mapped_row(const int32_t* ymap, int stride, int rl)
+{
+    return ymap ? min(max(ymap[rl], 0), stride - 1) : rl;
+}
 
 struct RowRef {
     const u32x4* w;      // the row's chunks
@@ -366,8 +378,8 @@ __device__ __forceinline__ RowRef locate(const Parts& P, int r, int C)
     RowRef o;
     o.w = P.w[p] + (size_t)rl * C;
     o.m = P.m[p] + (size_t)rl * C;
-    o.y = P.y[p] + rl;
-    o.R = P.begin[p + 1] - P.begin[p];
+    o.R = P.ymap[p] ? P.ystride[p] : P.begin[p + 1] - P.begin[p];
+    o.y = P.y[p] + mapped_row(P.ymap[p], o.R, rl);
     return o;
 }
 
@@ -386,8 +398,9 @@ __device__ __forceinline__ RowRef row_ref(const Parts& P, int r, int C)
     return locate(P, r, C);
 }
 
-// Launch row r for a row index that differs across lanes: the part is chosen
-// by selects over the (wave-uniform) part table, never by a dynamic index.
+// Weight pointers of launch row r for a row index that differs across lanes:
+// the part is chosen by selects over the (wave-uniform) part table, never by
+// a dynamic index (which would become a memory load).  y is left unset.
 __device__ __forceinline__ RowRef row_ref_lane(const Parts& P, int r, int C)
 {
     const int rr = P.glu ? (r >> 1) : r;
@@ -399,21 +412,19 @@ __device__ __forceinline__ RowRef row_ref_lane(const Parts& P, int r, int C)
     }
     const u32x4* w = P.w[0];
     const uint16_t* m = P.m[0];
-    int b0 = 0, R0 = P.begin[1];
 #pragma unroll
     for (int k = 1; k < kMaxParts; ++k) {
         const bool on = p == k;
         w = on ? P.w[k] : w;
         m = on ? P.m[k] : m;
-        b0 = on ? P.begin[k] : b0;
-        R0 = on ? P.begin[k + 1] - P.begin[k] : R0;
     }
+    const int b0 = P.glu ? 0 : (p == 0 ? 0 : p == 1 ? P.begin[1] : p == 2 ? P.begin[2] : P.begin[3]);
     const int rl = P.glu ? rr : r - b0;
-    RowRef o;
+    RowRef o;                                    // only the weight pointers are used in the lane layout
     o.w = w + (size_t)rl * C;
     o.m = m + (size_t)rl * C;
-    o.y = (P.glu ? P.y[0] : P.y[0]) + rl;
-    o.R = P.glu ? P.begin[1] : R0;
+    o.y = nullptr;
+    o.R = 0;
     return o;
 }
 
@@ -1013,7 +1024,8 @@ __global__ __launch_bounds__(256) void generic_spmv_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ values2,
                                                            const uint8_t* __restrict__ masks2,
                                                            const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-                                                           int R, int K, int N, int M)
+                                                           int R, int K, int N, int M, const int32_t* __restrict__ ymap,
+                                                           int ystride)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -1022,19 +1034,21 @@ __global__ __launch_bounds__(256) void generic_spmv_kernel(const uint16_t* __res
     const size_t vrow = (size_t)(K / M) * N;
     float acc[NB];
     generic_row<DT, NB>(values + (size_t)row * vrow, masks + (size_t)row * (K / 8), x, K, N, M, lane, acc);
+    const int ys = ymap ? ystride : R;
+    const int yr = mapped_row(ymap, ys, row);
     if (values2) {
         float acc2[NB];
         generic_row<DT, NB>(values2 + (size_t)row * vrow, masks2 + (size_t)row * (K / 8), x, K, N, M, lane, acc2);
         if (lane == 0)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                y[(size_t)b * R + row] = glu_out<DT>(acc[b], acc2[b]);
+                y[(size_t)b * ys + yr] = glu_out<DT>(acc[b], acc2[b]);
         return;
     }
     if (lane == 0)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-            y[(size_t)b * R + row] = from_f32<DT>(acc[b]);
+            y[(size_t)b * ys + yr] = from_f32<DT>(acc[b]);
 }
 
 __global__ void fill_zero_kernel(uint16_t* __restrict__ y, int64_t n)
@@ -1056,16 +1070,25 @@ __device__ __forceinline__ uint32_t inf_code()
 }
 
 // One thread per (row, mask byte) = 8 columns: two 4-groups or one 8-group.
+// With rowmap set, output row o packs source row rowmap[o] of W (and keep);
+// bpr = K / 8 mask bytes per row.
+__device__ __forceinline__ int64_t source_unit(const int32_t* rowmap, int64_t i, int64_t bpr)
+{
+    return rowmap ? (int64_t)rowmap[i / bpr] * bpr + i % bpr : i;
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void pack_check_kernel(const u32x4* __restrict__ W, const uint8_t* __restrict__ keep,
-                                                         int64_t nbytes, int N, int M, uint32_t* __restrict__ status)
+                                                         int64_t nbytes, int N, int M, uint32_t* __restrict__ status,
+                                                         const int32_t* __restrict__ rowmap, int64_t bpr)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nbytes)
         return;
+    const int64_t u = source_unit(rowmap, i, bpr);
     uint32_t bad = 0;
     if (keep) {
-        const uint8_t* kp = keep + 8 * i;
+        const uint8_t* kp = keep + 8 * u;
         for (int g = 0; g < 8; g += M) {
             int cnt = 0;
             for (int j = 0; j < M; ++j)
@@ -1074,7 +1097,7 @@ __global__ __launch_bounds__(256) void pack_check_kernel(const u32x4* __restrict
                 bad |= kStatusBadMask;
         }
     } else {
-        const u32x4 w = W[i];
+        const u32x4 w = W[u];
         const uint32_t words[4] = {w.x, w.y, w.z, w.w};
         for (int d = 0; d < 4; ++d)
             if ((words[d] & 0x7FFFu) > inf_code<DT>() || ((words[d] >> 16) & 0x7FFFu) > inf_code<DT>())
@@ -1087,18 +1110,20 @@ __global__ __launch_bounds__(256) void pack_check_kernel(const u32x4* __restrict
 template <int DT>
 __global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, const uint8_t* __restrict__ keep,
                                                    int64_t nbytes, int N, int M, uint16_t* __restrict__ values,
-                                                   uint8_t* __restrict__ masks)
+                                                   uint8_t* __restrict__ masks, const int32_t* __restrict__ rowmap,
+                                                   int64_t bpr)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nbytes)
         return;
-    const u32x4 wv = W[i];
+    const int64_t u = source_unit(rowmap, i, bpr);
+    const u32x4 wv = W[u];
     uint16_t w[8];
     w[0] = wv.x & 0xFFFF; w[1] = wv.x >> 16; w[2] = wv.y & 0xFFFF; w[3] = wv.y >> 16;
     w[4] = wv.z & 0xFFFF; w[5] = wv.z >> 16; w[6] = wv.w & 0xFFFF; w[7] = wv.w >> 16;
     uint32_t kb = 0;
     if (keep) {
-        const uint8_t* kp = keep + 8 * i;
+        const uint8_t* kp = keep + 8 * u;
         for (int j = 0; j < 8; ++j)
             kb |= (uint32_t)(kp[j] != 0) << j;
     } else {
@@ -1124,6 +1149,148 @@ __global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, 
         if (((kb >> j) & 1u) && k < vpb)         // the check pass guarantees k < vpb; the guard keeps writes in bounds
             out[k++] = w[j];
     masks[i] = (uint8_t)kb;
+}
+
+// ---- hybrid sparse + dense rows --------------------------------------------------
+
+// The Spense abstract (fifth page) splits a matrix into a 2:4-sparse and a
+// dense region; here the dense region is a set of whole rows, those whose
+// pruning loses most.  L_r = sum over the row's pruned columns of w^2 h[c],
+// one thread per row: groups in column order, pruned columns ascending, each
+// term (w*w)*h exact in double and one rounding per added term (explicit
+// round-to-nearest operations, no contraction), so the sum is the same
+// number the oracle forms.  The pruned columns are those the keep-mask drops,
+// or those the top-N magnitude rule (nm_pack's) drops.  Keep-mask groups
+// without N kept, or NaN weights under the magnitude rule, set the status
+// word (as nm_pack's check does).
+template <int DT>
+__global__ __launch_bounds__(256) void hybrid_loss_kernel(const uint16_t* __restrict__ W, const uint8_t* __restrict__ keep,
+                                                          const float* __restrict__ h, int64_t h_stride, int R, int K,
+                                                          int N, int M, double* __restrict__ loss,
+                                                          uint32_t* __restrict__ status)
+{
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= R)
+        return;
+    const uint16_t* w = W + (size_t)r * K;
+    const uint8_t* kp = keep ? keep + (size_t)r * K : nullptr;
+    double l = 0.0;
+    uint32_t bad = 0;
+    for (int g = 0; g < K / M; ++g) {
+        uint32_t wv[8];
+        for (int j = 0; j < M; ++j)
+            wv[j] = w[g * M + j];
+        uint32_t kept = 0;
+        if (kp) {
+            int cnt = 0;
+            for (int j = 0; j < M; ++j) {
+                const uint32_t k = kp[g * M + j] != 0;
+                kept |= k << j;
+                cnt += (int)k;
+            }
+            if (cnt != N)
+                bad |= kStatusBadMask;
+        } else {
+            for (int j = 0; j < M; ++j) {
+                const uint32_t mj = wv[j] & 0x7FFFu;
+                if (mj > (DT == NM_FP16 ? 0x7C00u : 0x7F80u))
+                    bad |= kStatusNaN;
+                int beats = 0;
+                for (int k = 0; k < M; ++k) {
+                    const uint32_t mk = wv[k] & 0x7FFFu;
+                    beats += (mk > mj) || (mk == mj && k < j);
+                }
+                kept |= (uint32_t)(beats < N) << j;
+            }
+        }
+        for (int j = 0; j < M; ++j) {
+            if ((kept >> j) & 1u)
+                continue;
+            const double v = nm_decode::w_to_f64<DT>(wv[j]);
+            const double hv = h ? nm_decode::f32_to_f64(h[(int64_t)(g * M + j) * h_stride]) : 1.0;
+            l = __dadd_rn(l, __dmul_rn(__dmul_rn(v, v), hv));
+        }
+    }
+    loss[r] = l;
+    if (bad)
+        atomicOr(status, bad);
+}
+
+// flags[r] = 1 for the n_dense rows of largest loss (a NaN loss ranks lowest,
+// the lower row first among equals): row r's rank counts the rows ahead of
+// it, against 256-row tiles of the losses staged in LDS.
+__global__ __launch_bounds__(256) void hybrid_select_kernel(const double* __restrict__ loss, int R, int n_dense,
+                                                            uint8_t* __restrict__ flags)
+{
+    __shared__ double tile[256];
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    const double lr0 = r < R ? loss[r] : 0.0;
+    const double lr = lr0 != lr0 ? -1.0 : lr0;
+    int above = 0;
+    for (int s0 = 0; s0 < R; s0 += 256) {
+        __syncthreads();
+        if (s0 + (int)threadIdx.x < R) {
+            const double v = loss[s0 + threadIdx.x];
+            tile[threadIdx.x] = v != v ? -1.0 : v;
+        }
+        __syncthreads();
+        const int ns = min(256, R - s0);
+        for (int k = 0; k < ns; ++k) {
+            const double ls = tile[k];
+            above += (ls > lr) || (ls == lr && s0 + k < r);
+        }
+    }
+    if (r < R)
+        flags[r] = above < n_dense ? 1 : 0;
+}
+
+// One block: the rows flagged dense, in order, to rows_dense (at most n_dense
+// of them are written), the others to rows_sparse (at most R - n_dense); a
+// flag count other than n_dense sets the status word.
+__global__ __launch_bounds__(1024) void hybrid_partition_kernel(const uint8_t* __restrict__ flags, int R, int n_dense,
+                                                                int32_t* __restrict__ rows_sparse,
+                                                                int32_t* __restrict__ rows_dense,
+                                                                uint32_t* __restrict__ status)
+{
+    __shared__ int wave_count[1024 / kWave];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, nw = blockDim.x / kWave;
+    int dense_before = 0;                        // flagged rows before this pass (block-uniform)
+    for (int r0 = 0; r0 < R; r0 += blockDim.x) {
+        const int r = r0 + tid;
+        const bool f = r < R && flags[r] != 0;
+        const uint64_t ball = __ballot(f);
+        const int lane_before = __popcll(ball & ((1ull << lane) - 1));
+        if (lane == 0)
+            wave_count[wave] = __popcll(ball);
+        __syncthreads();
+        int wave_before = 0, total = 0;
+        for (int k = 0; k < nw; ++k) {
+            wave_before += k < wave ? wave_count[k] : 0;
+            total += wave_count[k];
+        }
+        if (r < R) {
+            const int d = dense_before + wave_before + lane_before;   // flagged rows before r
+            if (f) {
+                if (d < n_dense)
+                    rows_dense[d] = r;
+            } else if (r - d < R - n_dense) {
+                rows_sparse[r - d] = r;
+            }
+        }
+        dense_before += total;
+        __syncthreads();                         // wave_count is rewritten next pass
+    }
+    if (tid == 0 && dense_before != n_dense)
+        atomicOr(status, kStatusBadMask);
+}
+
+// W_dense[j] = W[rows_dense[j]], 16-byte units.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ W, const int32_t* __restrict__ rows,
+                                                          int64_t nunits, int64_t upr, u32x4* __restrict__ out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nunits)
+        out[i] = W[(int64_t)rows[i / upr] * upr + i % upr];
 }
 
 // ---- host: launch planning -------------------------------------------------------
@@ -1527,12 +1694,12 @@ struct Sparse48 {
 template <int DT, int NB>
 struct SparseGeneric {
     static int run(const void* v, const uint8_t* m, const void* v2, const uint8_t* m2, const void* x, void* y, int R,
-                   int K, int N, int M, hipStream_t s)
+                   int K, int N, int M, const int32_t* ymap, int ystride, hipStream_t s)
     {
         (void)hipGetLastError();
         const unsigned grid = (unsigned)((R + 3) / 4);
         hipLaunchKernelGGL((generic_spmv_kernel<DT, NB>), dim3(grid), dim3(256), 0, s, (const uint16_t*)v, m,
-                           (const uint16_t*)v2, m2, (const uint16_t*)x, (uint16_t*)y, R, K, N, M);
+                           (const uint16_t*)v2, m2, (const uint16_t*)x, (uint16_t*)y, R, K, N, M, ymap, ystride);
         return hip_status(hipGetLastError());
     }
 };
@@ -1567,19 +1734,109 @@ int status_word(uint32_t** out)
 }
 
 // The generic kernel takes at most 8 vectors per launch: larger batches go
-// through it 8 rows of x (and y) at a time.
+// through it 8 rows of x (and y) at a time.  ymap / ystride as in Parts.
 int generic_batches(int dtype, int B, const void* v, const uint8_t* m, const void* v2, const uint8_t* m2, const void* x,
-                    void* y, int64_t R, int64_t K, int N, int M, hipStream_t s)
+                    void* y, int64_t R, int64_t K, int N, int M, hipStream_t s, const int32_t* ymap = nullptr,
+                    int ystride = 0)
 {
+    const int64_t ys = ymap ? ystride : R;
     for (int b0 = 0; b0 < B; b0 += kVectorMaxBatch) {
         const int nb = std::min(kVectorMaxBatch, B - b0);
         const void* xb = static_cast<const uint16_t*>(x) + (size_t)b0 * (size_t)K;
-        void* yb = static_cast<uint16_t*>(y) + (size_t)b0 * (size_t)R;
-        const int st = dispatch<SparseGeneric>(dtype, nb, v, m, v2, m2, xb, yb, (int)R, (int)K, N, M, s);
+        void* yb = static_cast<uint16_t*>(y) + (size_t)b0 * (size_t)ys;
+        const int st = dispatch<SparseGeneric>(dtype, nb, v, m, v2, m2, xb, yb, (int)R, (int)K, N, M, ymap, ystride, s);
         if (st != NM_OK)
             return st;
     }
     return NM_OK;
+}
+
+// Pack R_out rows (output row o from source row rowmap[o], or o itself):
+// check every group first (status word, synchronous), then pack; returns
+// when the outputs are complete.  Arguments are already validated.
+int pack_rows(const void* W, const uint8_t* keep, const int32_t* rowmap, int64_t R, int64_t K, int N, int M, int dtype,
+              void* values, uint8_t* masks, hipStream_t s)
+{
+    int st = NM_OK;
+    const int64_t nbytes = R * (K / 8);
+    if (nbytes == 0)
+        return NM_OK;
+    std::lock_guard<std::mutex> lock(g_pack_mutex);
+    uint32_t* status = nullptr;
+    if ((st = status_word(&status)) != NM_OK)
+        return st;
+    const unsigned grid = (unsigned)((nbytes + 255) / 256);
+    (void)hipGetLastError();
+    if (hipMemsetAsync(status, 0, sizeof(uint32_t), s) != hipSuccess)
+        return NM_ERR_HIP;
+    if (dtype == NM_FP16)
+        hipLaunchKernelGGL(pack_check_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
+                           status, rowmap, K / 8);
+    else
+        hipLaunchKernelGGL(pack_check_kernel<NM_BF16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
+                           status, rowmap, K / 8);
+    if (hipGetLastError() != hipSuccess)
+        return NM_ERR_HIP;
+    uint32_t host_status = 0;
+    if (hipMemcpyAsync(&host_status, status, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return NM_ERR_HIP;
+    if (host_status & kStatusBadMask)
+        return NM_ERR_BAD_MASK;
+    if (host_status & kStatusNaN)
+        return NM_ERR_NONFINITE;
+    if (dtype == NM_FP16)
+        hipLaunchKernelGGL(pack_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
+                           (uint16_t*)values, masks, rowmap, K / 8);
+    else
+        hipLaunchKernelGGL(pack_kernel<NM_BF16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
+                           (uint16_t*)values, masks, rowmap, K / 8);
+    if (hipGetLastError() != hipSuccess)
+        return NM_ERR_HIP;
+    return hip_status(hipStreamSynchronize(s));
+}
+
+// Enqueues `launch(status)` (kernels that may set status bits), waits, and
+// translates the bits: a bad keep-mask or row count -> NM_ERR_BAD_MASK, a NaN
+// under the magnitude rule -> NM_ERR_NONFINITE.
+template <typename Fn>
+int with_status(hipStream_t s, Fn launch)
+{
+    std::lock_guard<std::mutex> lock(g_pack_mutex);
+    uint32_t* status = nullptr;
+    int st = status_word(&status);
+    if (st != NM_OK)
+        return st;
+    (void)hipGetLastError();
+    if (hipMemsetAsync(status, 0, sizeof(uint32_t), s) != hipSuccess)
+        return NM_ERR_HIP;
+    launch(status);
+    if (hipGetLastError() != hipSuccess)
+        return NM_ERR_HIP;
+    uint32_t host_status = 0;
+    if (hipMemcpyAsync(&host_status, status, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return NM_ERR_HIP;
+    if (host_status & kStatusBadMask)
+        return NM_ERR_BAD_MASK;
+    if (host_status & kStatusNaN)
+        return NM_ERR_NONFINITE;
+    return NM_OK;
+}
+
+// One part of a hybrid matrix (sparse rows or dense rows), scattered into y.
+Parts mapped_part(const void* w, const uint8_t* m, const int32_t* rows, int64_t Rp, int64_t R, void* y)
+{
+    Parts P = {};
+    P.w[0] = static_cast<const u32x4*>(w);
+    P.m[0] = reinterpret_cast<const uint16_t*>(m);
+    P.y[0] = static_cast<uint16_t*>(y);
+    P.ymap[0] = rows;
+    P.ystride[0] = (int)R;
+    P.count = 1;
+    for (int i = 1; i <= kMaxParts; ++i)
+        P.begin[i] = (int)Rp;
+    return P;
 }
 
 }  // namespace
@@ -1847,43 +2104,159 @@ int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int
         overlaps(masks, mbytes, W, wbytes) || overlaps(masks, mbytes, keep, kbytes) ||
         overlaps(values, vbytes, masks, mbytes))
         return NM_ERR_INVALID_ARG;
-    const int64_t nbytes = R * (K / 8);
-    if (nbytes == 0)
+    return pack_rows(W, keep, nullptr, R, K, N, M, dtype, values, masks, static_cast<hipStream_t>(stream));
+}
+
+int nm_hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int64_t h_stride, int64_t R, int64_t K, int N,
+                       int M, int dtype, double* loss, void* stream)
+{
+    int st = check_dtype(dtype);
+    if (st != NM_OK)
+        return st;
+    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
+        return st;
+    if (h && h_stride < 1)
+        return NM_ERR_BAD_SHAPE;
+    const size_t wbytes = (size_t)R * (size_t)K * 2, kbytes = keep ? (size_t)R * (size_t)K : 0;
+    const size_t hbytes = h && K > 0 ? ((size_t)(K - 1) * (size_t)h_stride + 1) * 4 : 0;
+    const size_t lbytes = (size_t)R * 8;
+    if (!ptr_ok(W, wbytes, 2) || !ptr_ok(loss, lbytes, 8) || (h && !ptr_ok(h, hbytes, 4)))
+        return NM_ERR_INVALID_ARG;
+    if (overlaps(loss, lbytes, W, wbytes) || overlaps(loss, lbytes, keep, kbytes) || overlaps(loss, lbytes, h, hbytes))
+        return NM_ERR_INVALID_ARG;
+    if (R == 0)
         return NM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    std::lock_guard<std::mutex> lock(g_pack_mutex);
-    uint32_t* status = nullptr;
-    if ((st = status_word(&status)) != NM_OK)
-        return st;
-    const unsigned grid = (unsigned)((nbytes + 255) / 256);
+    const unsigned grid = (unsigned)((R + 255) / 256);
+    return with_status(s, [&](uint32_t* status) {
+        if (dtype == NM_FP16)
+            hipLaunchKernelGGL(hybrid_loss_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const uint16_t*)W, keep, h,
+                               h_stride, (int)R, (int)K, N, M, loss, status);
+        else
+            hipLaunchKernelGGL(hybrid_loss_kernel<NM_BF16>, dim3(grid), dim3(256), 0, s, (const uint16_t*)W, keep, h,
+                               h_stride, (int)R, (int)K, N, M, loss, status);
+    });
+}
+
+int nm_hybrid_select_rows(const double* loss, int64_t R, int64_t n_dense, uint8_t* flags, void* stream)
+{
+    if (R < 0 || R > INT32_MAX || n_dense < 0 || n_dense > R)
+        return NM_ERR_BAD_SHAPE;
+    if (!ptr_ok(loss, (size_t)R * 8, 8) || !ptr_ok(flags, (size_t)R, 1) || overlaps(flags, (size_t)R, loss, (size_t)R * 8))
+        return NM_ERR_INVALID_ARG;
+    if (R == 0)
+        return NM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (hipMemsetAsync(status, 0, sizeof(uint32_t), s) != hipSuccess)
-        return NM_ERR_HIP;
-    if (dtype == NM_FP16)
-        hipLaunchKernelGGL(pack_check_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
-                           status);
-    else
-        hipLaunchKernelGGL(pack_check_kernel<NM_BF16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
-                           status);
-    if (hipGetLastError() != hipSuccess)
-        return NM_ERR_HIP;
-    uint32_t host_status = 0;
-    if (hipMemcpyAsync(&host_status, status, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess)
-        return NM_ERR_HIP;
-    if (host_status & kStatusBadMask)
-        return NM_ERR_BAD_MASK;
-    if (host_status & kStatusNaN)
-        return NM_ERR_NONFINITE;
-    if (dtype == NM_FP16)
-        hipLaunchKernelGGL(pack_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
-                           (uint16_t*)values, masks);
-    else
-        hipLaunchKernelGGL(pack_kernel<NM_BF16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
-                           (uint16_t*)values, masks);
-    if (hipGetLastError() != hipSuccess)
-        return NM_ERR_HIP;
+    hipLaunchKernelGGL(hybrid_select_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, loss, (int)R,
+                       (int)n_dense, flags);
+    return hip_status(hipGetLastError());
+}
+
+int nm_hybrid_pack(const void* W, const uint8_t* keep, const uint8_t* flags, int64_t n_dense, int64_t R, int64_t K,
+                   int N, int M, int dtype, void* values, uint8_t* masks, void* W_dense, int32_t* rows_sparse,
+                   int32_t* rows_dense, void* stream)
+{
+    int st = check_dtype(dtype);
+    if (st != NM_OK)
+        return st;
+    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
+        return st;
+    if (n_dense < 0 || n_dense > R)
+        return NM_ERR_BAD_SHAPE;
+    const int64_t Rs = R - n_dense;
+    const size_t wbytes = (size_t)R * (size_t)K * 2, kbytes = keep ? (size_t)R * (size_t)K : 0;
+    const size_t vbytes = (size_t)Rs * (size_t)(K / M * N) * 2, mbytes = (size_t)Rs * (size_t)(K / 8);
+    const size_t dbytes = (size_t)n_dense * (size_t)K * 2;
+    const size_t sbytes = (size_t)Rs * 4, ibytes = (size_t)n_dense * 4;
+    if (!ptr_ok(W, wbytes, 16) || !ptr_ok(flags, (size_t)R, 1) || !ptr_ok(values, vbytes, 16) ||
+        !ptr_ok(masks, mbytes, 16) || !ptr_ok(W_dense, dbytes, 16) || !ptr_ok(rows_sparse, sbytes, 4) ||
+        !ptr_ok(rows_dense, ibytes, 4))
+        return NM_ERR_INVALID_ARG;
+    const void* outs[5] = {values, masks, W_dense, rows_sparse, rows_dense};
+    const size_t osz[5] = {vbytes, mbytes, dbytes, sbytes, ibytes};
+    for (int i = 0; i < 5; ++i) {
+        if (overlaps(outs[i], osz[i], W, wbytes) || overlaps(outs[i], osz[i], keep, kbytes) ||
+            overlaps(outs[i], osz[i], flags, (size_t)R))
+            return NM_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(outs[i], osz[i], outs[j], osz[j]))
+                return NM_ERR_INVALID_ARG;
+    }
+    if (R == 0)
+        return NM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = with_status(s, [&](uint32_t* status) {
+        hipLaunchKernelGGL(hybrid_partition_kernel, dim3(1), dim3(1024), 0, s, flags, (int)R, (int)n_dense, rows_sparse,
+                           rows_dense, status);
+    });
+    if (st != NM_OK)
+        return st;
+    if (K == 0)
+        return NM_OK;
+    if ((st = pack_rows(W, keep, rows_sparse, Rs, K, N, M, dtype, values, masks, s)) != NM_OK)
+        return st;
+    const int64_t upr = K / 8, nunits = n_dense * upr;
+    if (nunits > 0) {
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((nunits + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const u32x4*>(W), rows_dense, nunits, upr, static_cast<u32x4*>(W_dense));
+        if (hipGetLastError() != hipSuccess)
+            return NM_ERR_HIP;
+    }
     return hip_status(hipStreamSynchronize(s));
+}
+
+int nm_spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows_sparse, const void* W_dense,
+                   const int32_t* rows_dense, int64_t n_dense, int64_t R, int64_t K, int N, int M, int dtype,
+                   const void* x, int B, void* y, void* stream)
+{
+    int st = check_dtype(dtype);
+    if (st != NM_OK)
+        return st;
+    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
+        return st;
+    if (n_dense < 0 || n_dense > R || B < 1 || B > kMaxBatch)
+        return NM_ERR_BAD_SHAPE;
+    const int64_t Rs = R - n_dense;
+    const size_t vbytes = (size_t)Rs * (size_t)(K / M * N) * 2, mbytes = (size_t)Rs * (size_t)(K / 8);
+    const size_t dbytes = (size_t)n_dense * (size_t)K * 2, sbytes = (size_t)Rs * 4, ibytes = (size_t)n_dense * 4;
+    const size_t xbytes = (size_t)B * (size_t)K * 2, ybytes = (size_t)B * (size_t)R * 2;
+    if (!ptr_ok(values, vbytes, 16) || !ptr_ok(masks, mbytes, 16) || !ptr_ok(rows_sparse, sbytes, 4) ||
+        !ptr_ok(W_dense, dbytes, 16) || !ptr_ok(rows_dense, ibytes, 4) || !ptr_ok(x, xbytes, 16) ||
+        !ptr_ok(y, ybytes, 2))
+        return NM_ERR_INVALID_ARG;
+    if (overlaps(y, ybytes, values, vbytes) || overlaps(y, ybytes, masks, mbytes) || overlaps(y, ybytes, W_dense, dbytes) ||
+        overlaps(y, ybytes, rows_sparse, sbytes) || overlaps(y, ybytes, rows_dense, ibytes) ||
+        overlaps(y, ybytes, x, xbytes))
+        return NM_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (R == 0)
+        return NM_OK;
+    if (K == 0)
+        return launch_zero(y, (int64_t)B * R, s);
+    if (Rs > 0) {
+        const Parts P = mapped_part(values, masks, rows_sparse, Rs, R, y);
+        if (K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8))) {
+            if (B >= mfma_min_batch(false) || B > kVectorMaxBatch)
+                st = M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)Rs, (int)K, B, s)
+                            : launch_mfma_dt<kNM48>(dtype, &P, x, (int)Rs, (int)K, B, s);
+            else
+                st = M == 4 ? dispatch<Sparse24>(dtype, B, &P, x, (int)Rs, (int)K, s)
+                            : dispatch<Sparse48>(dtype, B, &P, x, (int)Rs, (int)K, s);
+        } else {
+            st = generic_batches(dtype, B, values, masks, nullptr, nullptr, x, y, Rs, K, N, M, s, rows_sparse, (int)R);
+        }
+        if (st != NM_OK)
+            return st;
+    }
+    if (n_dense > 0) {
+        const Parts P = mapped_part(W_dense, nullptr, rows_dense, n_dense, R, y);
+        if (B >= mfma_min_batch(true) || B > kVectorMaxBatch)
+            return launch_mfma_dt<kDense>(dtype, &P, x, (int)n_dense, (int)K, B, s);
+        return dispatch<Dense>(dtype, B, &P, x, (int)n_dense, (int)K, s);
+    }
+    return NM_OK;
 }
 
 }  // extern "C"

@@ -232,3 +232,51 @@ def test_calib_keep_mask_rejects_bad_arguments():
     assert keep(h=None) == L.NM_ERR_INVALID_ARG
     assert keep(out=FAKE) == L.NM_ERR_INVALID_ARG               # keep over W
     assert keep(R=0) == L.NM_OK
+
+
+def test_hybrid_calls_reject_bad_arguments():
+    lib = L.lib()
+    # row loss
+    assert lib.nm_hybrid_row_loss(FAKE, None, None, 0, 4, 12, 2, 4, 0, FAKE2, None) == L.NM_ERR_BAD_SHAPE
+    assert lib.nm_hybrid_row_loss(FAKE, None, FAKE2 + 0x1000, 0, 4, 64, 2, 4, 0, FAKE2, None) == L.NM_ERR_BAD_SHAPE
+    assert lib.nm_hybrid_row_loss(FAKE, None, None, 0, 4, 64, 2, 4, 0, FAKE2 + 4, None) == L.NM_ERR_INVALID_ARG
+    assert lib.nm_hybrid_row_loss(FAKE, None, None, 0, 4, 64, 2, 4, 0, FAKE + 8, None) == L.NM_ERR_INVALID_ARG
+    assert lib.nm_hybrid_row_loss(FAKE, None, None, 0, 4, 64, 2, 4, 5, FAKE2, None) == L.NM_ERR_UNSUPPORTED
+    assert lib.nm_hybrid_row_loss(FAKE, None, None, 0, 0, 64, 2, 4, 0, FAKE2, None) == L.NM_OK
+    # row choice
+    assert lib.nm_hybrid_select_rows(FAKE, 10, 11, FAKE2, None) == L.NM_ERR_BAD_SHAPE
+    assert lib.nm_hybrid_select_rows(FAKE, 10, -1, FAKE2, None) == L.NM_ERR_BAD_SHAPE
+    assert lib.nm_hybrid_select_rows(FAKE + 4, 10, 2, FAKE2, None) == L.NM_ERR_INVALID_ARG
+    assert lib.nm_hybrid_select_rows(FAKE, 10, 2, FAKE + 16, None) == L.NM_ERR_INVALID_ARG     # flags over loss
+    assert lib.nm_hybrid_select_rows(FAKE, 0, 0, FAKE2, None) == L.NM_OK
+    # pack: outputs must not overlap each other or the inputs
+    P = 0x4000000
+    args = dict(W=P, keep=None, flags=P + 0x100000, nd=2, R=8, K=64, N=2, M=4, dt=0, values=P + 0x200000,
+                masks=P + 0x300000, Wd=P + 0x400000, rs=P + 0x500000, rd=P + 0x600000)
+
+    def pack(**kw):
+        a = dict(args, **kw)
+        return lib.nm_hybrid_pack(a["W"], a["keep"], a["flags"], a["nd"], a["R"], a["K"], a["N"], a["M"], a["dt"],
+                                  a["values"], a["masks"], a["Wd"], a["rs"], a["rd"], None)
+
+    assert pack(nd=9) == L.NM_ERR_BAD_SHAPE
+    assert pack(K=12) == L.NM_ERR_BAD_SHAPE
+    assert pack(values=P + 0x200008) == L.NM_ERR_INVALID_ARG
+    assert pack(rd=P + 0x600002) == L.NM_ERR_INVALID_ARG
+    assert pack(Wd=P + 0x200000) == L.NM_ERR_INVALID_ARG            # W_dense over values
+    assert pack(rs=P + 0x10) == L.NM_ERR_INVALID_ARG                # rows over W
+    assert pack(R=0, nd=0) == L.NM_OK
+    # product
+    def spmv(**kw):
+        a = dict(v=P, m=P + 0x100000, rs=P + 0x200000, Wd=P + 0x300000, rd=P + 0x400000, nd=2, R=8, K=64, N=2, M=4,
+                 dt=0, x=P + 0x500000, B=1, y=P + 0x600000)
+        a.update(kw)
+        return lib.nm_spmv_hybrid(a["v"], a["m"], a["rs"], a["Wd"], a["rd"], a["nd"], a["R"], a["K"], a["N"], a["M"],
+                                  a["dt"], a["x"], a["B"], a["y"], None)
+
+    assert spmv(B=33) == L.NM_ERR_BAD_SHAPE
+    assert spmv(nd=9) == L.NM_ERR_BAD_SHAPE
+    assert spmv(y=P + 0x500000) == L.NM_ERR_INVALID_ARG              # y over x
+    assert spmv(y=P + 0x400004) == L.NM_ERR_INVALID_ARG              # y over rows_dense
+    assert spmv(rs=P + 0x200002) == L.NM_ERR_INVALID_ARG
+    assert spmv(R=0, nd=0) == L.NM_OK
