@@ -262,6 +262,53 @@ def mlp_single(torch, lib, launches, cur, reps=10):
     return out
 
 
+def hybrid_gate(torch, nm, lib, launches, cur, fracs=(0.05, 0.10), reps=5):
+    """The hybrid sparse + dense row format on the gate projections: the rows
+    of largest pruning loss kept dense (5% and 10% of them), the rest 2:4,
+    timed back to back over the layers' weights against nm_gemv_dense."""
+    out = {}
+    Ls = [L for L in launches if "gate" in L.names]
+    if not Ls:
+        return out
+    i = Ls[0].names.index("gate")
+    R, K, B = Ls[0].R[i], Ls[0].K, Ls[0].B
+    for frac in fracs:
+        nd = int(round(frac * R))
+        hybs = []
+        for L in Ls:
+            W = L.W[L.names.index("gate")]
+            flags = nm.hybrid_select_rows(nm.hybrid_row_loss(W, L.n, L.m), nd)
+            hybs.append((nm.hybrid_pack(W, flags, nd, L.n, L.m), L))
+        ys = [torch.empty_like(L.y[i]) for _, L in hybs]     # own outputs: L.y is checked against the oracle later
+        args = [(P(h.values.data_ptr()), P(h.masks.data_ptr()), P(h.rows_sparse.data_ptr()), P(h.W_dense.data_ptr()),
+                 P(h.rows_dense.data_ptr()), I64(nd), I64(R), I64(K), I32(h.n), I32(h.m), I32(L.dtc),
+                 P(L.x.data_ptr()), I32(B), P(y.data_ptr()), P(cur)) for (h, L), y in zip(hybs, ys)]
+        run(lib.nm_spmv_hybrid, args)
+        us = time_ms(torch, lambda: run(lib.nm_spmv_hybrid, args), reps) / len(args) * 1e3
+        h0, L0 = hybs[0]
+        Rs = R - nd
+        nbytes = Rs * K * h0.n // h0.m * 2 + Rs * K // 8 + nd * K * 2 + R * 4 + B * (K + R) * 2
+        out[f"{int(frac * 100)}pct_dense_rows"] = {"shape": [R, K], "dense_rows": nd, "us": round(us, 3),
+                                                   "gbs": round(nbytes / us / 1e3, 1), "bytes": nbytes}
+        del hybs, args, ys
+        torch.cuda.empty_cache()
+    return out
+
+
+def calib_throughput(torch, nm, I, K=4096, T=512, reps=5):
+    """nm_calib_accumulate at the Llama-3.1-8B hidden size: H += X^T X over T
+    decode rows, timed; matrix-core TFLOP/s and the H read-modify-write rate."""
+    X = I.activation_normal(T, K, torch.bfloat16, I.seed_of("bench_calib"), device="cuda")
+    H = torch.zeros((K, K), dtype=torch.float32, device="cuda")
+    nm.calib_accumulate(X, None, H=H)
+    ms = time_ms(torch, lambda: nm.calib_accumulate(X, None, H=H), reps)
+    flops = 2.0 * K * K * T
+    nbytes = 2 * 4 * K * K + T * K * 2
+    return {"K": K, "T": T, "us": round(ms * 1e3, 2), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "pct_of_bf16_peak": round(100 * flops / (ms * 1e-3) / 2.5e15, 2),
+            "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(launches, budget_s, torch, label):
     """CPU oracle (plain C, fp64, one thread) on layer 0's projections, packed
     by the oracle itself from the same weights; repeated until about budget_s
@@ -480,6 +527,10 @@ def main():
     achieved = rbytes / rus / 1e3
 
     mlp = mlp_single(torch, lib, launches, cur, reps=10 if layers <= 64 else 3)
+    extras = {}
+    if a.workload == "llama31_8b" and not a.no_glu:
+        extras["hybrid_gate"] = hybrid_gate(torch, nm, lib, launches, cur)
+        extras["calib_accumulate"] = calib_throughput(torch, nm, I)
     ceiling = read_ceiling(torch, cur)
     copy_bytes = copy_calibration(torch, cur)
     worst = sampled_parity(launches, torch)
@@ -511,6 +562,7 @@ def main():
         "us_per_layer": round(ms_step * 1e3 / layers, 2),
         "per_launch": per,
         "mlp_shapes": mlp,
+        "extras": extras,
         "read_ceiling_gbs": round(ceiling, 1),
         "copy_calibration_bytes": copy_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
