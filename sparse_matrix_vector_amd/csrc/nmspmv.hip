@@ -55,6 +55,8 @@ constexpr int kWave = 64;
 constexpr int kXTileBudget = 56 * 1024;   // LDS bytes for x in the row-slice / stream kernels
 constexpr int kXTileStream = 64 * 1024;   // LDS bytes per x tile in the stream kernel
 constexpr int kLdsMax = 160 * 1024;       // LDS per CU on gfx950
+constexpr int kMaxBatch = 32;       // activation vectors per call
+constexpr int kVectorMaxBatch = 8;  // the VALU kernels' limit; larger batches use the matrix cores
 
 enum Fmt { kDense = 0, kNM24 = 1, kNM48 = 2 };
 
@@ -746,50 +748,26 @@ __device__ u32x2 expand24(uint32_t n)
     return u32x2{sel[0], sel[1]};
 }
 
-// 16-byte LDS units of the matrix-core kernels' expansion tables: 256
-// entries for both sparse formats, one per mask byte (2:4: the two groups'
-// expand24 selector pairs; 4:8: select48).
+// 16-byte LDS units of the matrix-core kernels' expansion tables.  2:4: one
+// expand24 selector pair per nibble (16 entries of 8 bytes: 64 lanes reading
+// arbitrary entries touch distinct banks or share a word); 4:8: one select48
+// entry per mask byte.
 template <int F>
 constexpr int mfma_table_units()
 {
-    return F == kDense ? 0 : 256;
-}
-
-// Table entry of mask byte b for 2:4: the selector pairs of its low and high
-// nibble.
-__device__ u32x4 expand24_byte(uint32_t b)
-{
-    const u32x2 lo = expand24(b & 0xFu), hi = expand24(b >> 4);
-    return u32x4{lo.x, lo.y, hi.x, hi.y};
+    return F == kDense ? 0 : F == kNM24 ? 8 : 256;
 }
 
 template <int F>
 __device__ __forceinline__ void build_mfma_table(u32x4* tab)
 {
     if constexpr (F == kNM24) {
-        for (unsigned t = threadIdx.x; t < 256; t += blockDim.x)
-            tab[t] = expand24_byte(t);
+        u32x2* t2 = reinterpret_cast<u32x2*>(tab);
+        for (unsigned t = threadIdx.x; t < 16; t += blockDim.x)
+            t2[t] = expand24(t);
     } else if constexpr (F == kNM48) {
         for (unsigned t = threadIdx.x; t < 256; t += blockDim.x)
             tab[t] = select48(t);
-    }
-}
-
-// The A operand of k-block s (dense columns 4 s .. 4 s + 3 of the chunk).
-template <int F>
-__device__ __forceinline__ u32x2 a_frag(const uint32_t* w, uint32_t m, int s, const u32x4* tab)
-{
-    if constexpr (F == kDense) {
-        return u32x2{w[2 * s], w[2 * s + 1]};
-    } else if constexpr (F == kNM24) {
-        const u32x4 sel = tab[(m >> (8 * (s >> 1))) & 0xFFu];          // one read serves k-blocks 2g, 2g + 1
-        const uint32_t s0 = (s & 1) ? sel.z : sel.x, s1 = (s & 1) ? sel.w : sel.y;
-        return u32x2{__builtin_amdgcn_perm(w[s], w[s], s0), __builtin_amdgcn_perm(w[s], w[s], s1)};
-    } else {
-        const int g = s >> 1;
-        const u32x4 sel = tab[(m >> (8 * g)) & 0xFFu];
-        const uint32_t s0 = (s & 1) ? sel.z : sel.x, s1 = (s & 1) ? sel.w : sel.y;
-        return u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], s0), __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], s1)};
     }
 }
 
@@ -807,7 +785,7 @@ __device__ __forceinline__ u32x2 a_frag(const uint32_t* w, uint32_t m, int s, co
 // kernel arguments that varies by lane would become a memory load).
 constexpr int kStageChunks = 16;                                  // chunks per row per stage
 constexpr int kStagePitch = kStageChunks * 16 + 16;               // bytes per values row (rows 4 banks apart)
-constexpr int kStageMPitch = kStageChunks * 2 + 4;                // bytes per mask row (an odd dword count)
+constexpr int kStageMPitch = kStageChunks * 2 + 8;                // bytes per mask row (8-byte reads, rows 10 banks apart)
 constexpr int kStageBytes = 16 * kStagePitch + 16 * kStageMPitch; // per wave
 
 template <int F, int DT, int NT>
@@ -881,35 +859,72 @@ __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u3
         for (int rr = 0; rr < NL; ++rr) {
             const int row = RPL * rr + lrow;
             *reinterpret_cast<u32x4*>(stage + row * kStagePitch + lc * 16) = v[rr];
-            if constexpr (F != kDense)
-                *reinterpret_cast<uint16_t*>(stage_m + row * kStageMPitch + lc * 2) = (uint16_t)m[rr];
+            if constexpr (F != kDense)                 // chunk 4 t + q at 4 q + t: a lane's four masks adjoin
+                *reinterpret_cast<uint16_t*>(stage_m + row * kStageMPitch + ((lc & 3) * 4 + (lc >> 2)) * 2) =
+                    (uint16_t)m[rr];
         }
     };
     f32x4 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
         acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A stage's LDS reads go out together (the lane's four chunks and, in one
+    // 8-byte read, their masks), then the selector reads, then the permutes
+    // and matrix-core steps: two LDS round trips per stage, not two per chunk.
+    // A chunk past the slice's end multiplies as zeros: its mask is cleared
+    // (no selector then picks a value; x is finite) or, dense, its values.
     auto consume = [&](int c0) {
+        u32x4 vv[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            vv[t] = *reinterpret_cast<const u32x4*>(stage + i * kStagePitch + (4 * t + q) * 16);
+        uint32_t mk[T] = {};
+        if constexpr (F != kDense) {
+            const u32x2 mq = *reinterpret_cast<const u32x2*>(stage_m + i * kStageMPitch + q * 8);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const uint32_t m16 = ((t < 2 ? mq.x : mq.y) >> (16 * (t & 1))) & 0xFFFFu;
+                mk[t] = c0 + 4 * t + q < cend ? m16 : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                if (c0 + 4 * t + q >= cend)
+                    vv[t] = u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int j = 4 * t + q;
-            const bool live = c0 + j < cend;
-            const u32x4 vv = *reinterpret_cast<const u32x4*>(stage + i * kStagePitch + j * 16);
-            uint32_t mm = 0;
-            if constexpr (F != kDense)
-                mm = *reinterpret_cast<const uint16_t*>(stage_m + i * kStageMPitch + j * 2);
-            const uint32_t w[4] = {live ? vv.x : 0u, live ? vv.y : 0u, live ? vv.z : 0u, live ? vv.w : 0u};
-            mm = live ? mm : 0u;
+            const uint32_t w[4] = {vv[t].x, vv[t].y, vv[t].z, vv[t].w};
+            u32x2 a[KB];
+            if constexpr (F == kDense) {
 #pragma unroll
-            for (int s = 0; s < KB; ++s) {
-                const u32x2 a = a_frag<F>(w, mm, s, tab);
+                for (int s = 0; s < KB; ++s)
+                    a[s] = u32x2{w[2 * s], w[2 * s + 1]};
+            } else if constexpr (F == kNM24) {
+                const u32x2* t2 = reinterpret_cast<const u32x2*>(tab);
+#pragma unroll
+                for (int s = 0; s < KB; ++s) {               // k-block s = group s: one nibble, one dword
+                    const u32x2 sel = t2[(mk[t] >> (4 * s)) & 0xFu];
+                    a[s] = u32x2{__builtin_amdgcn_perm(w[s], w[s], sel.x), __builtin_amdgcn_perm(w[s], w[s], sel.y)};
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {                // group g: k-blocks 2 g, 2 g + 1
+                    const u32x4 sel = tab[(mk[t] >> (8 * g)) & 0xFFu];
+                    a[2 * g] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.x),
+                                     __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.y)};
+                    a[2 * g + 1] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.z),
+                                         __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.w)};
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < KB; ++s)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     const u32x4 xx = xv[nt][t][s >> 1];
                     const u32x2 b = (s & 1) ? u32x2{xx.z, xx.w} : u32x2{xx.x, xx.y};
-                    acc[nt] = mfma16<DT>(a, b, acc[nt]);
+                    acc[nt] = mfma16<DT>(a[s], b, acc[nt]);
                 }
-            }
         }
     };
     // One pipeline step: multiply stage st (in LDS, its x in registers),
@@ -982,6 +997,279 @@ __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u3
             else if ((vv & 1) == 0)              // rows r (gate) and r + 1 (up) of one output
                 o.y[(size_t)b * o.R] = glu_out<DT>(sum[vv], sum[vv + 1]);
         }
+    }
+}
+
+// ---- matrix-core kernel, LDS ring (batches of up to 16 vectors) ---------------
+
+// The staged kernel above passes every weight byte through registers on its
+// way to LDS, which caps a CU at 3 waves and ~2 stages in flight, and its x
+// loads queue behind weight loads issued after them.  Here the weights go
+// straight from HBM to a two-slot LDS ring per wave (16-byte global-to-LDS
+// loads), x goes to registers in the same stage order, and a wave's slice of
+// K is short enough that a launch has several waves per SIMD.  Layout of one
+// slot (16 rows x 16 chunks of a 16-row tile):
+//  * values: four 1 KB blocks of 4 rows x 256 bytes; the lane at position p
+//    of row r loads chunk p ^ r, so the 16 rows' copies of a chunk fall in
+//    different banks when the operand layout reads them back;
+//  * masks: 16 rows x 32 bytes; position p of a row holds mask dword
+//    2 (p % 4) + p / 4, so that dwords 0, 2, 4, 6 (chunks 4 t + q, q < 2) and
+//    1, 3, 5, 7 (q >= 2) each form one 16-byte read.
+// A load instruction's LDS destination is its base (M0) + 16 bytes x lane;
+// these kernels declare no static LDS, so dynamic LDS starts at offset 0.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+template <int BYTES>
+__device__ __forceinline__ void load_to_lds(const void* g, uint32_t lds_offset)
+{
+    static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte lanes");
+#if defined(__HIP_DEVICE_COMPILE__)
+    lds_void_t* dst = (lds_void_t*)((lds_u8_t*)nullptr + lds_offset);
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_global_load_lds(g, dst, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(g, dst, 4, 0, 0);
+#else
+    (void)g;
+    (void)lds_offset;
+#endif
+}
+
+// s_waitcnt with vmcnt <= N (N < 64) and the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+constexpr int kRingValues = 16 * kStageChunks * 16;               // 4 KB
+constexpr int kRingMasks = 16 * kStageChunks * 2;                 // 512 B
+
+// x units (16 bytes) per batch row per stage, and batch rows per x load
+// instruction (64 lanes of 16 bytes).
+template <int F>
+constexpr int ring_x_units()
+{
+    return kStageChunks * chunk_cols<F>() / 8;
+}
+
+// Batch rows of x staged per slot: B rounded up to whole load instructions.
+template <int F>
+__host__ __device__ constexpr int ring_x_rows(int B)
+{
+    return (B + kWave / ring_x_units<F>() - 1) / (kWave / ring_x_units<F>()) * (kWave / ring_x_units<F>());
+}
+
+template <int F>
+__host__ __device__ constexpr int ring_slot_bytes(int B)
+{
+    return kRingValues + (F == kDense ? 0 : kRingMasks) + ring_x_rows<F>(B) * ring_x_units<F>() * 16;
+}
+
+template <int F, int DT>
+__global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
+                                                        int B, int S, int tiles_per_block)
+{
+    extern __shared__ u32x4 smem[];
+    constexpr int COLS = chunk_cols<F>();
+    constexpr int XC = COLS / 8;                 // 16-byte x units per chunk
+    constexpr int KB = COLS / 4;                 // k-blocks per chunk
+    constexpr int T = kStageChunks / 4;          // matrix-core steps per stage
+    constexpr int NM = F == kDense ? 0 : 2;      // mask load instructions per stage
+    constexpr int UPR = ring_x_units<F>();       // x units per batch row per stage
+    constexpr int RPX = kWave / UPR;             // batch rows per x load instruction
+    constexpr int TAB = mfma_table_units<F>() * 16;
+    constexpr int XOFF = kRingValues + (F == kDense ? 0 : kRingMasks);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lt = wave / S, sl = wave - lt * S;
+    const int r0 = (blockIdx.x * tiles_per_block + lt) * 16;
+    // Slice sl takes stages sl, sl + S, sl + 2 S, ... of the row: the waves
+    // of a launch move through K together.
+    const int C = K / COLS;
+    const int NS = (C + kStageChunks - 1) / kStageChunks;
+    const int nst = (r0 < R && sl < NS) ? (NS - sl + S - 1) / S : 0;
+    const int i = lane & 15, q = lane >> 4;      // operand layout: row / batch column i, k-quarter q
+    const int nxi = ring_x_rows<F>(B) / RPX;     // x load instructions per stage (1 .. 8)
+    const int slot_bytes = ring_slot_bytes<F>(B);
+
+    // Per-lane sources.  Values: instruction rr, row 4 rr + lane / 16, chunk
+    // (lane % 16) ^ row.  Masks: instruction h, row 8 h + lane / 8, dword
+    // 2 (lane % 4) + (lane % 8) / 4.  x: instruction n, batch row
+    // n RPX + lane / UPR (past B: row B - 1 again, never read), unit
+    // (lane % UPR) ^ (row % 16) of the stage.
+    const u32x4* vsrc[4];
+    int vchunk[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int row = 4 * rr + (lane >> 4);
+        vsrc[rr] = row_ref_lane(P, min(r0 + row, R - 1), C).w;
+        vchunk[rr] = (lane & 15) ^ row;
+    }
+    const uint16_t* msrc[2] = {nullptr, nullptr};
+    const int mchunk = 2 * (2 * (lane & 3) + ((lane & 7) >> 2));
+    if constexpr (NM > 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            msrc[h] = row_ref_lane(P, min(r0 + 8 * h + (lane >> 3), R - 1), C).m;
+    }
+    const uint32_t ring = (uint32_t)TAB + (uint32_t)wave * 2u * (uint32_t)slot_bytes;
+    const uint8_t* ring_p = reinterpret_cast<const uint8_t*>(smem) + ring;
+
+    // Stage st into slot `slot`; chunks past the row's end load the stage's
+    // first chunk instead (in bounds; never multiplied).
+    auto issue = [&](int st, int slot) {
+        const int c0 = (sl + st * S) * kStageChunks;
+        const uint32_t base = ring + (uint32_t)(slot * slot_bytes);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int c = c0 + vchunk[rr];
+            load_to_lds<16>(vsrc[rr] + (c < C ? c : c0), base + rr * 1024);
+        }
+        if constexpr (NM > 0) {
+            const int c = c0 + mchunk;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                load_to_lds<4>(msrc[h] + (c < C ? c : c0), base + kRingValues + h * 256);
+        }
+        for (int n = 0; n < nxi; ++n) {
+            const int b = n * RPX + lane / UPR;
+            const int u = (lane % UPR) ^ (b & 15);
+            const u32x4* xs = x4 + (size_t)min(b, B - 1) * (K / 8) + c0 * XC;
+            load_to_lds<16>(xs + (c0 + u / XC < C ? u : u % XC), base + XOFF + n * 1024);
+        }
+    };
+    auto wait_stage = [&]() {                    // all but the loads of the stage issued last
+        switch (nxi) {
+        case 1: wait_vmcnt<4 + NM + 1>(); break;
+        case 2: wait_vmcnt<4 + NM + 2>(); break;
+        case 3: wait_vmcnt<4 + NM + 3>(); break;
+        case 4: wait_vmcnt<4 + NM + 4>(); break;
+        case 5: wait_vmcnt<4 + NM + 5>(); break;
+        case 6: wait_vmcnt<4 + NM + 6>(); break;
+        case 7: wait_vmcnt<4 + NM + 7>(); break;
+        default: wait_vmcnt<4 + NM + 8>(); break;
+        }
+    };
+
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const u32x4* tab = smem;
+    const int xi = min(i, B - 1);                // batch columns past B read row B - 1; results dropped
+    // Multiply stage st from `slot`: one round of value, mask and x reads, one
+    // of selector reads, then the permutes and matrix-core steps.  A chunk
+    // past the row's end multiplies as zeros (mask cleared: no selector picks
+    // a value, and x is finite; dense: values cleared).
+    auto consume = [&](int st, int slot) {
+        const int c0 = (sl + st * S) * kStageChunks;
+        const uint8_t* sv = ring_p + slot * slot_bytes;
+        const uint8_t* sx = sv + XOFF + xi * (UPR * 16);
+        u32x4 vv[T], xx[T][XC];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            vv[t] = *reinterpret_cast<const u32x4*>(sv + (i >> 2) * 1024 + (i & 3) * 256 + (((4 * t + q) ^ i) * 16));
+#pragma unroll
+            for (int h = 0; h < XC; ++h)
+                xx[t][h] = *reinterpret_cast<const u32x4*>(sx + ((((4 * t + q) * XC + h) ^ (xi & 15)) * 16));
+        }
+        uint32_t mk[T] = {};
+        if constexpr (F != kDense) {
+            const u32x4 md = *reinterpret_cast<const u32x4*>(sv + kRingValues + i * 32 + (q >> 1) * 16);
+            const uint32_t mw[4] = {md.x, md.y, md.z, md.w};
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const uint32_t m16 = (mw[t] >> (16 * (q & 1))) & 0xFFFFu;
+                mk[t] = c0 + 4 * t + q < C ? m16 : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                if (c0 + 4 * t + q >= C)
+                    vv[t] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const uint32_t w[4] = {vv[t].x, vv[t].y, vv[t].z, vv[t].w};
+            u32x2 a[KB];
+            if constexpr (F == kDense) {
+#pragma unroll
+                for (int s = 0; s < KB; ++s)
+                    a[s] = u32x2{w[2 * s], w[2 * s + 1]};
+            } else if constexpr (F == kNM24) {
+                const u32x2* t2 = reinterpret_cast<const u32x2*>(tab);
+#pragma unroll
+                for (int s = 0; s < KB; ++s) {
+                    const u32x2 sel = t2[(mk[t] >> (4 * s)) & 0xFu];
+                    a[s] = u32x2{__builtin_amdgcn_perm(w[s], w[s], sel.x), __builtin_amdgcn_perm(w[s], w[s], sel.y)};
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const u32x4 sel = tab[(mk[t] >> (8 * g)) & 0xFFu];
+                    a[2 * g] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.x),
+                                     __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.y)};
+                    a[2 * g + 1] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.z),
+                                         __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.w)};
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < KB; ++s) {
+                const u32x4 xv = xx[t][s >> 1];
+                acc = mfma16<DT>(a[s], (s & 1) ? u32x2{xv.z, xv.w} : u32x2{xv.x, xv.y}, acc);
+            }
+        }
+    };
+
+    build_mfma_table<F>(smem);
+    __syncthreads();
+    // Two stages in flight: issue st + 1, wait until only its loads are
+    // outstanding (loads complete in order), multiply st.  The last stage is
+    // peeled so that every wait in the loop has the same count.
+    if (nst > 0) {
+        issue(0, 0);
+        int st = 0;
+        for (; st + 1 < nst; ++st) {
+            issue(st + 1, (st + 1) & 1);
+            wait_stage();
+            __builtin_amdgcn_sched_barrier(0);
+            consume(st, st & 1);
+            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the slot's reads are done before it is refilled
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vmcnt<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        consume(st, st & 1);
+    }
+
+    // Slice sums through the wave's own ring (no loads into it are pending):
+    // D[4 q + v][i] of this wave's tile (row 4 q + v, batch column i).
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    float* part = reinterpret_cast<float*>(smem) + ring / 4;
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv)
+        part[lane * 4 + vv] = acc[vv];
+    __syncthreads();
+    if (sl != 0 || r0 >= R || i >= B)
+        return;
+    float sum[4];
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) {
+        float t = part[lane * 4 + vv];
+        for (int j = 1; j < S; ++j)
+            t += part[j * (2 * slot_bytes / 4) + lane * 4 + vv];
+        sum[vv] = t;
+    }
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) {
+        const int r = r0 + 4 * q + vv;
+        if (r >= R)
+            continue;
+        const RowRef o = row_ref(P, r, C);
+        if (!P.glu)
+            o.y[(size_t)i * o.R] = from_f32<DT>(sum[vv]);
+        else if ((vv & 1) == 0)                  // rows r (gate) and r + 1 (up) of one output
+            o.y[(size_t)i * o.R] = glu_out<DT>(sum[vv], sum[vv + 1]);
     }
 }
 
@@ -1296,10 +1584,11 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 // ---- host: launch planning -------------------------------------------------------
 
 // Launch-shape overrides, read once, for tuning sweeps (0 = built-in choice):
-// NMSPMV_KERNEL 1 = row-slice, 3 = stream; NMSPMV_SLICES,
-// NMSPMV_ROWS_PER_BLOCK (row-slice); NMSPMV_BLOCKS, NMSPMV_THREADS,
-// NMSPMV_TILE_BYTES (stream); NMSPMV_MFMA_MIN_B (smallest batch sent to the
-// matrix-core kernel), NMSPMV_MFMA_SLICES.
+// NMSPMV_KERNEL 1 = row-slice, 3 = stream, 5 = staged matrix-core (instead of
+// the LDS ring); NMSPMV_SLICES, NMSPMV_ROWS_PER_BLOCK (row-slice);
+// NMSPMV_BLOCKS, NMSPMV_THREADS, NMSPMV_TILE_BYTES (stream);
+// NMSPMV_MFMA_MIN_B (smallest batch sent to the matrix-core kernels),
+// NMSPMV_MFMA_SLICES.
 struct Env {
     int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0;
 };
@@ -1468,21 +1757,33 @@ Plan plan_for(int64_t R, int64_t K, int B, bool glu)
     return P;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
-
-constexpr int kMaxBatch = 32;       // activation vectors per call
-constexpr int kVectorMaxBatch = 8;  // the VALU kernels' limit; larger batches use the matrix cores
-
-// Batches of at least this many vectors go to the matrix-core kernels (from
-// timing on MI355X over the Llama-3.1-8B and Qwen3-32B MLP shapes: the VALU
-// kernels win below, the staged matrix-core kernel at and above).
-int mfma_min_batch(bool dense)
+// Whether a batch goes to the matrix-core kernels rather than the VALU ones
+// (timing on MI355X at the Qwen3-32B MLP shapes with weights streamed from
+// HBM).  The LDS-ring kernel wins from 5 vectors (sparse) over the row-slice
+// kernel and from 3 where x is too long for it and the VALU path would be
+// the K-tiled stream kernel; dense from 4 either way; the staged kernel
+// (sparse rows with K % 32 != 0) from 6.  Above 8 vectors only the matrix
+// cores take the batch.  NMSPMV_MFMA_MIN_B overrides the threshold.
+template <int F>
+bool use_mfma(int64_t R, int64_t K, int B, bool glu)
 {
     std::call_once(g_env_once, read_env);
+    if (B > kVectorMaxBatch)
+        return true;
     if (g_env.mfma_min_b > 0)
-        return g_env.mfma_min_b;
-    return dense ? 4 : 6;
+        return B >= g_env.mfma_min_b;
+    const bool dense = F == kDense;
+    if (!dense && K % 32 != 0)
+        return B >= 6;
+    if (dense)
+        return B >= 4;
+    return B >= (plan_for<F>(R, K, B, glu).kind == 3 ? 3 : 5);
 }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
+
+
+// (The matrix-core choice, use_mfma, follows the launch planning below.)
 
 
 // Staged matrix-core launch shape: 16-row tiles; 1, 2, 4 or 8 K-slices (each
@@ -1534,11 +1835,67 @@ int launch_mfma_nt(const Parts& parts, const void* x, int R, int K, int B, hipSt
     return hip_status(hipGetLastError());
 }
 
-// Up to 16 vectors are one tile of the matrix cores' batch dimension; 17 to
-// 32 take two, both fed by the same weight loads.
+// LDS-ring launch shape: one 16-row tile per block, its K split into S
+// stage-interleaved slices (one wave each).  S (a power of two) doubles while
+// the launch has fewer than ~4 waves per CU (8 above 8 vectors), each slice
+// keeps at least two stages and the block's rings fit the CU's LDS (at most 8
+// waves, the kernel's launch bound).  Measured on MI355X: ~4-8 resident waves
+// per CU stream best; more waves only add x and LDS traffic.
+template <int F>
+Plan plan_mfma_ring(int64_t R, int64_t K, int B)
+{
+    std::call_once(g_env_once, read_env);
+    constexpr int COLS = chunk_cols<F>();
+    const int cus = cu_count();
+    const int64_t C = K / COLS, tiles = (R + 15) / 16, NS = (C + kStageChunks - 1) / kStageChunks;
+    const size_t tab = (size_t)mfma_table_units<F>() * sizeof(u32x4);
+    const int wmax = (int)std::min<size_t>(8, (kLdsMax - tab) / (2 * (size_t)ring_slot_bytes<F>(B)));
+    int S = 1;
+    const int64_t target = (B > 8 ? 8LL : 4LL) * cus;   // waves wanted in the launch
+    while (2 * S <= wmax && tiles * S < target && NS >= 4LL * S)
+        S *= 2;
+    if (g_env.mfma_slices > 0 && g_env.mfma_slices <= wmax)
+        S = g_env.mfma_slices;
+    const int tpb = 1;
+    Plan P;
+    P.kind = 6;
+    P.S = S;
+    P.rpb = tpb;
+    P.threads = S * tpb * kWave;
+    P.grid = (unsigned)((tiles + tpb - 1) / tpb);
+    P.lds = (size_t)mfma_table_units<F>() * sizeof(u32x4) + (size_t)S * tpb * 2 * ring_slot_bytes<F>(B);
+    return P;
+}
+
+template <int F, int DT>
+int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
+{
+    const Plan P = plan_mfma_ring<F>(R, K, B);
+    if (P.lds > 64 * 1024) {
+        static bool raised = false;              // once per instantiation
+        if (!raised) {
+            if (hipFuncSetAttribute((const void*)mfma_ring_kernel<F, DT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kLdsMax) != hipSuccess)
+                return NM_ERR_HIP;
+            raised = true;
+        }
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((mfma_ring_kernel<F, DT>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
+                       static_cast<const u32x4*>(x), R, K, B, P.S, P.rpb);
+    return hip_status(hipGetLastError());
+}
+
+// Up to 16 vectors are one tile of the matrix cores' batch dimension and run
+// on the LDS-ring kernel (sparse formats when a mask row is a whole number of
+// dwords, K % 32 == 0); 17 to 32 take two tiles, both fed by the same weight
+// loads, on the staged kernel.
 template <int F, int DT>
 int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
+    std::call_once(g_env_once, read_env);
+    if (B <= 16 && (F == kDense || K % 32 == 0) && g_env.kernel != 5)
+        return launch_mfma_ring<F, DT>(parts, x, R, K, B, s);
     return B > 16 ? launch_mfma_nt<F, DT, 2>(parts, x, R, K, B, s) : launch_mfma_nt<F, DT, 1>(parts, x, R, K, B, s);
 }
 
@@ -1921,7 +2278,7 @@ int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* ma
         }
         for (int i = P.count + 1; i <= kMaxParts; ++i)
             P.begin[i] = P.begin[P.count];
-        if (B >= mfma_min_batch(false) || B > kVectorMaxBatch)
+        if (M == 4 ? use_mfma<kNM24>(total, K, B, false) : use_mfma<kNM48>(total, K, B, false))
             return M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)total, (int)K, B, s)
                           : launch_mfma_dt<kNM48>(dtype, &P, x, (int)total, (int)K, B, s);
         return M == 4 ? dispatch<Sparse24>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s)
@@ -1999,7 +2356,7 @@ int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64
     }
     for (int i = P.count + 1; i <= kMaxParts; ++i)
         P.begin[i] = P.begin[P.count];
-    if (B >= mfma_min_batch(true) || B > kVectorMaxBatch)
+    if (use_mfma<kDense>(total, K, B, false))
         return launch_mfma_dt<kDense>(dtype, &P, x, (int)total, (int)K, B, s);
     return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s);
 }
@@ -2044,7 +2401,7 @@ int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const voi
         P.begin[1] = (int)R;
         for (int i = 2; i <= kMaxParts; ++i)
             P.begin[i] = (int)(2 * R);
-        if (B >= mfma_min_batch(false) || B > kVectorMaxBatch)
+        if (M == 4 ? use_mfma<kNM24>(2 * R, K, B, true) : use_mfma<kNM48>(2 * R, K, B, true))
             return M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)(2 * R), (int)K, B, s)
                           : launch_mfma_dt<kNM48>(dtype, &P, x, (int)(2 * R), (int)K, B, s);
         return M == 4 ? dispatch<Sparse24>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s)
@@ -2083,7 +2440,7 @@ int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_
     P.begin[1] = (int)R;
     for (int i = 2; i <= kMaxParts; ++i)
         P.begin[i] = (int)(2 * R);
-    if (B >= mfma_min_batch(true) || B > kVectorMaxBatch)
+    if (use_mfma<kDense>(2 * R, K, B, true))
         return launch_mfma_dt<kDense>(dtype, &P, x, (int)(2 * R), (int)K, B, s);
     return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s);
 }
@@ -2238,7 +2595,7 @@ int nm_spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows
     if (Rs > 0) {
         const Parts P = mapped_part(values, masks, rows_sparse, Rs, R, y);
         if (K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8))) {
-            if (B >= mfma_min_batch(false) || B > kVectorMaxBatch)
+            if (M == 4 ? use_mfma<kNM24>(Rs, K, B, false) : use_mfma<kNM48>(Rs, K, B, false))
                 st = M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)Rs, (int)K, B, s)
                             : launch_mfma_dt<kNM48>(dtype, &P, x, (int)Rs, (int)K, B, s);
             else
@@ -2252,7 +2609,7 @@ int nm_spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows
     }
     if (n_dense > 0) {
         const Parts P = mapped_part(W_dense, nullptr, rows_dense, n_dense, R, y);
-        if (B >= mfma_min_batch(true) || B > kVectorMaxBatch)
+        if (use_mfma<kDense>(n_dense, K, B, false))
             return launch_mfma_dt<kDense>(dtype, &P, x, (int)n_dense, (int)K, B, s);
         return dispatch<Dense>(dtype, B, &P, x, (int)n_dense, (int)K, s);
     }
