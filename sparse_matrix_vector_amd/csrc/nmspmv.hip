@@ -1044,31 +1044,52 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt vmcnt <= n for a wave-uniform n in 0 .. 63 (the count is an
+// immediate, so one branch per value).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n)
+{
+    switch (n) {
+#define NM_WAIT_CASE(k) \
+    case k: wait_vmcnt<k>(); break;
+#define NM_WAIT_CASES8(k) NM_WAIT_CASE(k) NM_WAIT_CASE(k + 1) NM_WAIT_CASE(k + 2) NM_WAIT_CASE(k + 3) \
+    NM_WAIT_CASE(k + 4) NM_WAIT_CASE(k + 5) NM_WAIT_CASE(k + 6) NM_WAIT_CASE(k + 7)
+        NM_WAIT_CASES8(0) NM_WAIT_CASES8(8) NM_WAIT_CASES8(16) NM_WAIT_CASES8(24)
+        NM_WAIT_CASES8(32) NM_WAIT_CASES8(40) NM_WAIT_CASES8(48) NM_WAIT_CASES8(56)
+#undef NM_WAIT_CASES8
+#undef NM_WAIT_CASE
+    default: wait_vmcnt<0>(); break;
+    }
+}
+
 constexpr int kRingValues = 16 * kStageChunks * 16;               // 4 KB
 constexpr int kRingMasks = 16 * kStageChunks * 2;                 // 512 B
 
-// x units (16 bytes) per batch row per stage, and batch rows per x load
-// instruction (64 lanes of 16 bytes).
+// x units (16 bytes) per batch row per stage.
 template <int F>
 constexpr int ring_x_units()
 {
     return kStageChunks * chunk_cols<F>() / 8;
 }
 
-// Batch rows of x staged per slot: B rounded up to whole load instructions.
+// Batch rows of x staged per slot: B rounded up to whole load instructions
+// (64 lanes of 16 bytes).
 template <int F>
 __host__ __device__ constexpr int ring_x_rows(int B)
 {
     return (B + kWave / ring_x_units<F>() - 1) / (kWave / ring_x_units<F>()) * (kWave / ring_x_units<F>());
 }
 
-template <int F>
+// One ring slot: TW tiles' values and masks, then the stage's x.
+template <int F, int TW>
 __host__ __device__ constexpr int ring_slot_bytes(int B)
 {
-    return kRingValues + (F == kDense ? 0 : kRingMasks) + ring_x_rows<F>(B) * ring_x_units<F>() * 16;
+    return TW * (kRingValues + (F == kDense ? 0 : kRingMasks)) + ring_x_rows<F>(B) * ring_x_units<F>() * 16;
 }
 
-template <int F, int DT>
+// A wave multiplies TW 16-row tiles (rows 16 TW w .. 16 TW w + 16 TW - 1) by
+// the same staged x, so each byte of x brought to LDS serves TW tiles; NT
+// batch tiles of 16 vectors share each weight operand.
+template <int F, int DT, int TW, int NT>
 __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
                                                         int B, int S, int tiles_per_block)
 {
@@ -1077,43 +1098,48 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     constexpr int XC = COLS / 8;                 // 16-byte x units per chunk
     constexpr int KB = COLS / 4;                 // k-blocks per chunk
     constexpr int T = kStageChunks / 4;          // matrix-core steps per stage
-    constexpr int NM = F == kDense ? 0 : 2;      // mask load instructions per stage
+    constexpr int NM = F == kDense ? 0 : 2;      // mask load instructions per stage and tile
     constexpr int UPR = ring_x_units<F>();       // x units per batch row per stage
     constexpr int RPX = kWave / UPR;             // batch rows per x load instruction
     constexpr int TAB = mfma_table_units<F>() * 16;
-    constexpr int XOFF = kRingValues + (F == kDense ? 0 : kRingMasks);
+    constexpr int TBYTES = kRingValues + (F == kDense ? 0 : kRingMasks);   // one tile's part of a slot
+    constexpr int XOFF = TW * TBYTES;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lt = wave / S, sl = wave - lt * S;
-    const int r0 = (blockIdx.x * tiles_per_block + lt) * 16;
+    const int r0 = (blockIdx.x * tiles_per_block + lt) * 16 * TW;
     // Slice sl takes stages sl, sl + S, sl + 2 S, ... of the row: the waves
     // of a launch move through K together.
     const int C = K / COLS;
     const int NS = (C + kStageChunks - 1) / kStageChunks;
     const int nst = (r0 < R && sl < NS) ? (NS - sl + S - 1) / S : 0;
     const int i = lane & 15, q = lane >> 4;      // operand layout: row / batch column i, k-quarter q
-    const int nxi = ring_x_rows<F>(B) / RPX;     // x load instructions per stage (1 .. 8)
-    const int slot_bytes = ring_slot_bytes<F>(B);
+    const int nxi = ring_x_rows<F>(B) / RPX;     // x load instructions per stage (1 .. 16)
+    const int slot_bytes = ring_slot_bytes<F, TW>(B);
+    const int nload = TW * (4 + NM) + nxi;       // loads per stage
 
-    // Per-lane sources.  Values: instruction rr, row 4 rr + lane / 16, chunk
-    // (lane % 16) ^ row.  Masks: instruction h, row 8 h + lane / 8, dword
+    // Per-lane sources.  Values: tile tw, instruction rr, row 4 rr + lane / 16,
+    // chunk (lane % 16) ^ row.  Masks: instruction h, row 8 h + lane / 8, dword
     // 2 (lane % 4) + (lane % 8) / 4.  x: instruction n, batch row
     // n RPX + lane / UPR (past B: row B - 1 again, never read), unit
     // (lane % UPR) ^ (row % 16) of the stage.
-    const u32x4* vsrc[4];
+    const u32x4* vsrc[TW][4];
     int vchunk[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int row = 4 * rr + (lane >> 4);
-        vsrc[rr] = row_ref_lane(P, min(r0 + row, R - 1), C).w;
-        vchunk[rr] = (lane & 15) ^ row;
-    }
-    const uint16_t* msrc[2] = {nullptr, nullptr};
+    for (int rr = 0; rr < 4; ++rr)
+        vchunk[rr] = (lane & 15) ^ (4 * rr + (lane >> 4));
+    const uint16_t* msrc[TW][2] = {};
     const int mchunk = 2 * (2 * (lane & 3) + ((lane & 7) >> 2));
-    if constexpr (NM > 0) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            msrc[h] = row_ref_lane(P, min(r0 + 8 * h + (lane >> 3), R - 1), C).m;
+    for (int tw = 0; tw < TW; ++tw) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            vsrc[tw][rr] = row_ref_lane(P, min(r0 + 16 * tw + 4 * rr + (lane >> 4), R - 1), C).w;
+        if constexpr (NM > 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                msrc[tw][h] = row_ref_lane(P, min(r0 + 16 * tw + 8 * h + (lane >> 3), R - 1), C).m;
+        }
     }
     const uint32_t ring = (uint32_t)TAB + (uint32_t)wave * 2u * (uint32_t)slot_bytes;
     const uint8_t* ring_p = reinterpret_cast<const uint8_t*>(smem) + ring;
@@ -1124,15 +1150,18 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
         const int c0 = (sl + st * S) * kStageChunks;
         const uint32_t base = ring + (uint32_t)(slot * slot_bytes);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int c = c0 + vchunk[rr];
-            load_to_lds<16>(vsrc[rr] + (c < C ? c : c0), base + rr * 1024);
-        }
-        if constexpr (NM > 0) {
-            const int c = c0 + mchunk;
+        for (int tw = 0; tw < TW; ++tw) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                load_to_lds<4>(msrc[h] + (c < C ? c : c0), base + kRingValues + h * 256);
+            for (int rr = 0; rr < 4; ++rr) {
+                const int c = c0 + vchunk[rr];
+                load_to_lds<16>(vsrc[tw][rr] + (c < C ? c : c0), base + tw * TBYTES + rr * 1024);
+            }
+            if constexpr (NM > 0) {
+                const int c = c0 + mchunk;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    load_to_lds<4>(msrc[tw][h] + (c < C ? c : c0), base + tw * TBYTES + kRingValues + h * 256);
+            }
         }
         for (int n = 0; n < nxi; ++n) {
             const int b = n * RPX + lane / UPR;
@@ -1141,136 +1170,162 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
             load_to_lds<16>(xs + (c0 + u / XC < C ? u : u % XC), base + XOFF + n * 1024);
         }
     };
-    auto wait_stage = [&]() {                    // all but the loads of the stage issued last
-        switch (nxi) {
-        case 1: wait_vmcnt<4 + NM + 1>(); break;
-        case 2: wait_vmcnt<4 + NM + 2>(); break;
-        case 3: wait_vmcnt<4 + NM + 3>(); break;
-        case 4: wait_vmcnt<4 + NM + 4>(); break;
-        case 5: wait_vmcnt<4 + NM + 5>(); break;
-        case 6: wait_vmcnt<4 + NM + 6>(); break;
-        case 7: wait_vmcnt<4 + NM + 7>(); break;
-        default: wait_vmcnt<4 + NM + 8>(); break;
-        }
-    };
 
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[TW][NT];
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            acc[tw][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const u32x4* tab = smem;
-    const int xi = min(i, B - 1);                // batch columns past B read row B - 1; results dropped
-    // Multiply stage st from `slot`: one round of value, mask and x reads, one
-    // of selector reads, then the permutes and matrix-core steps.  A chunk
-    // past the row's end multiplies as zeros (mask cleared: no selector picks
-    // a value, and x is finite; dense: values cleared).
+    int xi[NT];                                  // batch columns past B read row B - 1; results dropped
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        xi[nt] = min(16 * nt + i, B - 1);
+    // Multiply stage st from `slot`: the x operands once, then per tile one
+    // round of value and mask reads, one of selector reads, the permutes and
+    // the matrix-core steps.  A chunk past the row's end multiplies as zeros
+    // (mask cleared: no selector picks a value, and x is finite; dense:
+    // values cleared).
     auto consume = [&](int st, int slot) {
         const int c0 = (sl + st * S) * kStageChunks;
-        const uint8_t* sv = ring_p + slot * slot_bytes;
-        const uint8_t* sx = sv + XOFF + xi * (UPR * 16);
-        u32x4 vv[T], xx[T][XC];
+        const uint8_t* sv0 = ring_p + slot * slot_bytes;
+        u32x4 xx[NT][T][XC];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            vv[t] = *reinterpret_cast<const u32x4*>(sv + (i >> 2) * 1024 + (i & 3) * 256 + (((4 * t + q) ^ i) * 16));
-#pragma unroll
-            for (int h = 0; h < XC; ++h)
-                xx[t][h] = *reinterpret_cast<const u32x4*>(sx + ((((4 * t + q) * XC + h) ^ (xi & 15)) * 16));
-        }
-        uint32_t mk[T] = {};
-        if constexpr (F != kDense) {
-            const u32x4 md = *reinterpret_cast<const u32x4*>(sv + kRingValues + i * 32 + (q >> 1) * 16);
-            const uint32_t mw[4] = {md.x, md.y, md.z, md.w};
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const uint32_t m16 = (mw[t] >> (16 * (q & 1))) & 0xFFFFu;
-                mk[t] = c0 + 4 * t + q < C ? m16 : 0u;
-            }
-        } else {
+        for (int nt = 0; nt < NT; ++nt) {
+            const uint8_t* sx = sv0 + XOFF + xi[nt] * (UPR * 16);
 #pragma unroll
             for (int t = 0; t < T; ++t)
-                if (c0 + 4 * t + q >= C)
-                    vv[t] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int h = 0; h < XC; ++h)
+                    xx[nt][t][h] =
+                        *reinterpret_cast<const u32x4*>(sx + ((((4 * t + q) * XC + h) ^ (xi[nt] & 15)) * 16));
         }
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const uint32_t w[4] = {vv[t].x, vv[t].y, vv[t].z, vv[t].w};
-            u32x2 a[KB];
-            if constexpr (F == kDense) {
+        for (int tw = 0; tw < TW; ++tw) {
+            const uint8_t* sv = sv0 + tw * TBYTES;
+            u32x4 vv[T];
 #pragma unroll
-                for (int s = 0; s < KB; ++s)
-                    a[s] = u32x2{w[2 * s], w[2 * s + 1]};
-            } else if constexpr (F == kNM24) {
-                const u32x2* t2 = reinterpret_cast<const u32x2*>(tab);
+            for (int t = 0; t < T; ++t)
+                vv[t] = *reinterpret_cast<const u32x4*>(sv + (i >> 2) * 1024 + (i & 3) * 256 + (((4 * t + q) ^ i) * 16));
+            uint32_t mk[T] = {};
+            if constexpr (F != kDense) {
+                const u32x4 md = *reinterpret_cast<const u32x4*>(sv + kRingValues + i * 32 + (q >> 1) * 16);
+                const uint32_t mw[4] = {md.x, md.y, md.z, md.w};
 #pragma unroll
-                for (int s = 0; s < KB; ++s) {
-                    const u32x2 sel = t2[(mk[t] >> (4 * s)) & 0xFu];
-                    a[s] = u32x2{__builtin_amdgcn_perm(w[s], w[s], sel.x), __builtin_amdgcn_perm(w[s], w[s], sel.y)};
+                for (int t = 0; t < T; ++t) {
+                    const uint32_t m16 = (mw[t] >> (16 * (q & 1))) & 0xFFFFu;
+                    mk[t] = c0 + 4 * t + q < C ? m16 : 0u;
                 }
             } else {
 #pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const u32x4 sel = tab[(mk[t] >> (8 * g)) & 0xFFu];
-                    a[2 * g] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.x),
-                                     __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.y)};
-                    a[2 * g + 1] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.z),
-                                         __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.w)};
-                }
+                for (int t = 0; t < T; ++t)
+                    if (c0 + 4 * t + q >= C)
+                        vv[t] = u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
-            for (int s = 0; s < KB; ++s) {
-                const u32x4 xv = xx[t][s >> 1];
-                acc = mfma16<DT>(a[s], (s & 1) ? u32x2{xv.z, xv.w} : u32x2{xv.x, xv.y}, acc);
+            for (int t = 0; t < T; ++t) {
+                const uint32_t w[4] = {vv[t].x, vv[t].y, vv[t].z, vv[t].w};
+                u32x2 a[KB];
+                if constexpr (F == kDense) {
+#pragma unroll
+                    for (int s = 0; s < KB; ++s)
+                        a[s] = u32x2{w[2 * s], w[2 * s + 1]};
+                } else if constexpr (F == kNM24) {
+                    const u32x2* t2 = reinterpret_cast<const u32x2*>(tab);
+#pragma unroll
+                    for (int s = 0; s < KB; ++s) {
+                        const u32x2 sel = t2[(mk[t] >> (4 * s)) & 0xFu];
+                        a[s] = u32x2{__builtin_amdgcn_perm(w[s], w[s], sel.x), __builtin_amdgcn_perm(w[s], w[s], sel.y)};
+                    }
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        const u32x4 sel = tab[(mk[t] >> (8 * g)) & 0xFFu];
+                        a[2 * g] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.x),
+                                         __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.y)};
+                        a[2 * g + 1] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.z),
+                                             __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.w)};
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < KB; ++s)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const u32x4 xv = xx[nt][t][s >> 1];
+                        acc[tw][nt] =
+                            mfma16<DT>(a[s], (s & 1) ? u32x2{xv.z, xv.w} : u32x2{xv.x, xv.y}, acc[tw][nt]);
+                    }
             }
         }
     };
 
     build_mfma_table<F>(smem);
     __syncthreads();
-    // Two stages in flight: issue st + 1, wait until only its loads are
-    // outstanding (loads complete in order), multiply st.  The last stage is
-    // peeled so that every wait in the loop has the same count.
+    // One stage in flight while the previous one is multiplied: issue st + 1,
+    // wait until only its loads are outstanding (loads complete in order),
+    // multiply st.  No load in the loop writes registers, so issuing the last
+    // stage's successor conditionally costs the compiler's own wait counting
+    // nothing.
     if (nst > 0) {
         issue(0, 0);
-        int st = 0;
-        for (; st + 1 < nst; ++st) {
-            issue(st + 1, (st + 1) & 1);
-            wait_stage();
+        for (int st = 0; st < nst; ++st) {
+            if (st + 1 < nst) {
+                issue(st + 1, (st + 1) & 1);
+                wait_vmcnt_dyn(nload);
+            } else {
+                wait_vmcnt<0>();
+            }
             __builtin_amdgcn_sched_barrier(0);
             consume(st, st & 1);
             __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the slot's reads are done before it is refilled
             __builtin_amdgcn_sched_barrier(0);
         }
-        wait_vmcnt<0>();
-        __builtin_amdgcn_sched_barrier(0);
-        consume(st, st & 1);
     }
 
     // Slice sums through the wave's own ring (no loads into it are pending):
-    // D[4 q + v][i] of this wave's tile (row 4 q + v, batch column i).
+    // D[4 q + v][i] of tile tw and batch tile nt (row 16 tw + 4 q + v, batch
+    // column 16 nt + i).
     __builtin_amdgcn_s_waitcnt(0xC07F);
     float* part = reinterpret_cast<float*>(smem) + ring / 4;
 #pragma unroll
-    for (int vv = 0; vv < 4; ++vv)
-        part[lane * 4 + vv] = acc[vv];
+    for (int tw = 0; tw < TW; ++tw)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+                part[((tw * NT + nt) * kWave + lane) * 4 + vv] = acc[tw][nt][vv];
     __syncthreads();
-    if (sl != 0 || r0 >= R || i >= B)
+    if (sl != 0 || r0 >= R)
         return;
-    float sum[4];
 #pragma unroll
-    for (int vv = 0; vv < 4; ++vv) {
-        float t = part[lane * 4 + vv];
-        for (int j = 1; j < S; ++j)
-            t += part[j * (2 * slot_bytes / 4) + lane * 4 + vv];
-        sum[vv] = t;
-    }
+    for (int tw = 0; tw < TW; ++tw)
 #pragma unroll
-    for (int vv = 0; vv < 4; ++vv) {
-        const int r = r0 + 4 * q + vv;
-        if (r >= R)
-            continue;
-        const RowRef o = row_ref(P, r, C);
-        if (!P.glu)
-            o.y[(size_t)i * o.R] = from_f32<DT>(sum[vv]);
-        else if ((vv & 1) == 0)                  // rows r (gate) and r + 1 (up) of one output
-            o.y[(size_t)i * o.R] = glu_out<DT>(sum[vv], sum[vv + 1]);
-    }
+        for (int nt = 0; nt < NT; ++nt) {
+            const int b = 16 * nt + i;
+            if (b >= B)
+                continue;
+            float sum[4];
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+                const int e = ((tw * NT + nt) * kWave + lane) * 4 + vv;
+                float t = part[e];
+                for (int j = 1; j < S; ++j)
+                    t += part[j * (2 * slot_bytes / 4) + e];
+                sum[vv] = t;
+            }
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+                const int r = r0 + 16 * tw + 4 * q + vv;
+                if (r >= R)
+                    continue;
+                const RowRef o = row_ref(P, r, C);
+                if (!P.glu)
+                    o.y[(size_t)b * o.R] = from_f32<DT>(sum[vv]);
+                else if ((vv & 1) == 0)          // rows r (gate) and r + 1 (up) of one output
+                    o.y[(size_t)b * o.R] = glu_out<DT>(sum[vv], sum[vv + 1]);
+            }
+        }
 }
 
 // ---- generic N:M (any N < M, M in {4, 8}, K % 8 == 0) --------------------------
@@ -1590,7 +1645,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 // NMSPMV_MFMA_MIN_B (smallest batch sent to the matrix-core kernels),
 // NMSPMV_MFMA_SLICES.
 struct Env {
-    int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0;
+    int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0,
+        ring_tiles = 0;
 };
 Env g_env;
 std::once_flag g_env_once;
@@ -1609,6 +1665,7 @@ void read_env()
     g_env.tile_bytes = get("NMSPMV_TILE_BYTES");
     g_env.mfma_min_b = get("NMSPMV_MFMA_MIN_B");
     g_env.mfma_slices = get("NMSPMV_MFMA_SLICES");
+    g_env.ring_tiles = get("NMSPMV_RING_TILES");
 }
 
 int g_cu_count[64] = {};
@@ -1835,66 +1892,85 @@ int launch_mfma_nt(const Parts& parts, const void* x, int R, int K, int B, hipSt
     return hip_status(hipGetLastError());
 }
 
-// LDS-ring launch shape: one 16-row tile per block, its K split into S
-// stage-interleaved slices (one wave each).  S (a power of two) doubles while
-// the launch has fewer than ~4 waves per CU (8 above 8 vectors), each slice
-// keeps at least two stages and the block's rings fit the CU's LDS (at most 8
-// waves, the kernel's launch bound).  Measured on MI355X: ~4-8 resident waves
-// per CU stream best; more waves only add x and LDS traffic.
+// LDS-ring launch shape (rules from sweeps on MI355X at the Qwen3-32B MLP
+// shapes, weights streamed from HBM): up to 8 vectors one 16-row tile per
+// wave, above 8 two (x, then 16 rows per stage, is shared by both); one block
+// per wave group, K split into S stage-interleaved slices (one wave each).  S
+// (a power of two) doubles while the launch has fewer than ~4 waves per CU
+// (~3 with two tiles), each slice keeps at least two stages and the block's
+// rings fit the CU's LDS (at most 8 waves, the kernel's launch bound).  A few
+// resident waves per CU stream best; more only add x and LDS traffic.
 template <int F>
 Plan plan_mfma_ring(int64_t R, int64_t K, int B)
 {
     std::call_once(g_env_once, read_env);
     constexpr int COLS = chunk_cols<F>();
     const int cus = cu_count();
-    const int64_t C = K / COLS, tiles = (R + 15) / 16, NS = (C + kStageChunks - 1) / kStageChunks;
+    const int64_t C = K / COLS, NS = (C + kStageChunks - 1) / kStageChunks;
+    int TW = B > 8 ? 2 : 1;
+    if (B <= 16 && (g_env.ring_tiles == 1 || g_env.ring_tiles == 2))
+        TW = g_env.ring_tiles;                   // above 16 vectors the kernel always takes two
+    const int64_t tiles = (R + 16 * TW - 1) / (16 * TW);
     const size_t tab = (size_t)mfma_table_units<F>() * sizeof(u32x4);
-    const int wmax = (int)std::min<size_t>(8, (kLdsMax - tab) / (2 * (size_t)ring_slot_bytes<F>(B)));
+    const size_t ring = 2 * (size_t)(TW == 2 ? ring_slot_bytes<F, 2>(B) : ring_slot_bytes<F, 1>(B));
+    const int wmax = (int)std::min<size_t>(8, (kLdsMax - tab) / ring);
+    const int64_t target = (TW == 2 ? 3LL : 4LL) * cus;   // waves wanted in the launch
     int S = 1;
-    const int64_t target = (B > 8 ? 8LL : 4LL) * cus;   // waves wanted in the launch
     while (2 * S <= wmax && tiles * S < target && NS >= 4LL * S)
         S *= 2;
     if (g_env.mfma_slices > 0 && g_env.mfma_slices <= wmax)
         S = g_env.mfma_slices;
-    const int tpb = 1;
     Plan P;
     P.kind = 6;
     P.S = S;
-    P.rpb = tpb;
-    P.threads = S * tpb * kWave;
-    P.grid = (unsigned)((tiles + tpb - 1) / tpb);
-    P.lds = (size_t)mfma_table_units<F>() * sizeof(u32x4) + (size_t)S * tpb * 2 * ring_slot_bytes<F>(B);
+    P.rpb = 1;
+    P.cpl = TW;
+    P.threads = S * kWave;
+    P.grid = (unsigned)tiles;
+    P.lds = tab + (size_t)S * ring;
     return P;
 }
 
-template <int F, int DT>
-int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
+template <int F, int DT, int TW, int NT>
+int launch_mfma_ring_tw(const Plan& P, const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
-    const Plan P = plan_mfma_ring<F>(R, K, B);
     if (P.lds > 64 * 1024) {
         static bool raised = false;              // once per instantiation
         if (!raised) {
-            if (hipFuncSetAttribute((const void*)mfma_ring_kernel<F, DT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    kLdsMax) != hipSuccess)
+            if (hipFuncSetAttribute((const void*)mfma_ring_kernel<F, DT, TW, NT>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
                 return NM_ERR_HIP;
             raised = true;
         }
     }
     (void)hipGetLastError();
-    hipLaunchKernelGGL((mfma_ring_kernel<F, DT>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
+    hipLaunchKernelGGL((mfma_ring_kernel<F, DT, TW, NT>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
                        static_cast<const u32x4*>(x), R, K, B, P.S, P.rpb);
     return hip_status(hipGetLastError());
 }
 
-// Up to 16 vectors are one tile of the matrix cores' batch dimension and run
-// on the LDS-ring kernel (sparse formats when a mask row is a whole number of
-// dwords, K % 32 == 0); 17 to 32 take two tiles, both fed by the same weight
-// loads, on the staged kernel.
+// Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles).
+template <int F, int DT>
+int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
+{
+    const Plan P = plan_mfma_ring<F>(R, K, B);
+    if (B > 16)
+        return launch_mfma_ring_tw<F, DT, 2, 2>(P, parts, x, R, K, B, s);
+    return P.cpl == 2 ? launch_mfma_ring_tw<F, DT, 2, 1>(P, parts, x, R, K, B, s)
+                      : launch_mfma_ring_tw<F, DT, 1, 1>(P, parts, x, R, K, B, s);
+}
+
+// The LDS-ring kernel takes dense rows at any batch, and sparse rows whose
+// mask row is a whole number of dwords (K % 32 == 0) up to 16 vectors; other
+// sparse batches run on the staged kernel (measured: above 16 vectors its
+// registers-only x beats the ring, whose LDS then holds ~3 waves per CU),
+// where up to 16 vectors are one tile of the matrix cores' batch dimension
+// and 17 to 32 take two, both fed by the same weight loads.
 template <int F, int DT>
 int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
     std::call_once(g_env_once, read_env);
-    if (B <= 16 && (F == kDense || K % 32 == 0) && g_env.kernel != 5)
+    if ((F == kDense || (K % 32 == 0 && B <= 16)) && g_env.kernel != 5)
         return launch_mfma_ring<F, DT>(parts, x, R, K, B, s);
     return B > 16 ? launch_mfma_nt<F, DT, 2>(parts, x, R, K, B, s) : launch_mfma_nt<F, DT, 1>(parts, x, R, K, B, s);
 }
