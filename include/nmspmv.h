@@ -95,9 +95,10 @@ int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int
  *   x [B][K] 16-bit, y [B][R] 16-bit (output).
  *   y[b][r] = sum over kept columns c of W[r][c] * x[b][c]; every product and
  *   sum is formed in fp32 (in an unspecified order) and the sum is rounded
- *   once to the output dtype, to nearest even.  (From 6 vectors up -- 4 for
- *   nm_gemv_dense -- the products run on the matrix cores with fp32
- *   accumulation; the arithmetic contract is the same.)
+ *   once to the output dtype, to nearest even.  (Batches of a few vectors
+ *   and up -- about 5 for nm_spmv, 3 where K is long, 4 for nm_gemv_dense --
+ *   run on the matrix cores with fp32 accumulation; the arithmetic contract
+ *   is the same.)
  * Enqueues on stream and returns; y is complete when the stream reaches it.
  */
 int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int N, int M, int dtype,

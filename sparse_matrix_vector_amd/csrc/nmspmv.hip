@@ -1893,13 +1893,14 @@ int launch_mfma_nt(const Parts& parts, const void* x, int R, int K, int B, hipSt
 }
 
 // LDS-ring launch shape (rules from sweeps on MI355X at the Qwen3-32B MLP
-// shapes, weights streamed from HBM): up to 8 vectors one 16-row tile per
-// wave, above 8 two (x, then 16 rows per stage, is shared by both); one block
-// per wave group, K split into S stage-interleaved slices (one wave each).  S
-// (a power of two) doubles while the launch has fewer than ~4 waves per CU
-// (~3 with two tiles), each slice keeps at least two stages and the block's
-// rings fit the CU's LDS (at most 8 waves, the kernel's launch bound).  A few
-// resident waves per CU stream best; more only add x and LDS traffic.
+// shapes, weights streamed from HBM): 16-row tiles, one per wave up to 8
+// vectors, two above (x, then 16 rows per stage, serves both), four for
+// sparse rows above 16 (a sparse stage spans twice the columns, so twice the
+// x per weight byte); a block holds one wave group, its K split into S
+// stage-interleaved slices (one wave each).  S is the largest power of two
+// (each slice keeping at least four stages, at most 8 waves a block, the
+// kernel's launch bound) whose launch still fits the CUs' LDS in one round:
+// a second, partly filled round costs more than the extra waves gain.
 template <int F>
 Plan plan_mfma_ring(int64_t R, int64_t K, int B)
 {
@@ -1907,17 +1908,23 @@ Plan plan_mfma_ring(int64_t R, int64_t K, int B)
     constexpr int COLS = chunk_cols<F>();
     const int cus = cu_count();
     const int64_t C = K / COLS, NS = (C + kStageChunks - 1) / kStageChunks;
-    int TW = B > 8 ? 2 : 1;
+    int TW = B > 16 && F != kDense ? 4 : B > 8 ? 2 : 1;
     if (B <= 16 && (g_env.ring_tiles == 1 || g_env.ring_tiles == 2))
-        TW = g_env.ring_tiles;                   // above 16 vectors the kernel always takes two
+        TW = g_env.ring_tiles;                   // above 16 vectors the tile count is fixed
+    if (B > 16 && F != kDense && (g_env.ring_tiles == 2 || g_env.ring_tiles == 4))
+        TW = g_env.ring_tiles;
     const int64_t tiles = (R + 16 * TW - 1) / (16 * TW);
     const size_t tab = (size_t)mfma_table_units<F>() * sizeof(u32x4);
-    const size_t ring = 2 * (size_t)(TW == 2 ? ring_slot_bytes<F, 2>(B) : ring_slot_bytes<F, 1>(B));
+    const size_t ring = 2 * (size_t)(TW == 4   ? ring_slot_bytes<F, 4>(B)
+                                     : TW == 2 ? ring_slot_bytes<F, 2>(B)
+                                               : ring_slot_bytes<F, 1>(B));
     const int wmax = (int)std::min<size_t>(8, (kLdsMax - tab) / ring);
-    const int64_t target = (TW == 2 ? 3LL : 4LL) * cus;   // waves wanted in the launch
+    // Waves resident at once with S-wave blocks (LDS-bound).
+    auto resident = [&](int S) { return (int64_t)(kLdsMax / (tab + S * ring)) * S * cus; };
     int S = 1;
-    while (2 * S <= wmax && tiles * S < target && NS >= 4LL * S)
-        S *= 2;
+    for (int s2 = 2; s2 <= wmax && NS >= 4LL * s2; s2 *= 2)
+        if (tiles * s2 <= resident(s2))
+            S = s2;
     if (g_env.mfma_slices > 0 && g_env.mfma_slices <= wmax)
         S = g_env.mfma_slices;
     Plan P;
@@ -1949,28 +1956,31 @@ int launch_mfma_ring_tw(const Plan& P, const Parts& parts, const void* x, int R,
     return hip_status(hipGetLastError());
 }
 
-// Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles).
+// Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles, four
+// for sparse rows, whose x per weight byte is twice the dense rows').
 template <int F, int DT>
 int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
     const Plan P = plan_mfma_ring<F>(R, K, B);
     if (B > 16)
-        return launch_mfma_ring_tw<F, DT, 2, 2>(P, parts, x, R, K, B, s);
+        return P.cpl == 4 ? launch_mfma_ring_tw<F, DT, 4, 2>(P, parts, x, R, K, B, s)
+                          : launch_mfma_ring_tw<F, DT, 2, 2>(P, parts, x, R, K, B, s);
     return P.cpl == 2 ? launch_mfma_ring_tw<F, DT, 2, 1>(P, parts, x, R, K, B, s)
                       : launch_mfma_ring_tw<F, DT, 1, 1>(P, parts, x, R, K, B, s);
 }
 
 // The LDS-ring kernel takes dense rows at any batch, and sparse rows whose
-// mask row is a whole number of dwords (K % 32 == 0) up to 16 vectors; other
-// sparse batches run on the staged kernel (measured: above 16 vectors its
-// registers-only x beats the ring, whose LDS then holds ~3 waves per CU),
-// where up to 16 vectors are one tile of the matrix cores' batch dimension
-// and 17 to 32 take two, both fed by the same weight loads.
+// mask row is a whole number of dwords (K % 32 == 0): up to 16 vectors
+// always, above 16 when there is at least one 64-row wave per CU (measured:
+// with fewer the staged kernel wins).  Other sparse batches run on the staged
+// kernel, where up to 16 vectors are one tile of the matrix cores' batch
+// dimension and 17 to 32 take two, both fed by the same weight loads.
 template <int F, int DT>
 int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
     std::call_once(g_env_once, read_env);
-    if ((F == kDense || (K % 32 == 0 && B <= 16)) && g_env.kernel != 5)
+    const bool ring_fits = F == kDense || (K % 32 == 0 && (B <= 16 || (int64_t)R >= 64LL * cu_count()));
+    if (ring_fits && g_env.kernel != 5)
         return launch_mfma_ring<F, DT>(parts, x, R, K, B, s);
     return B > 16 ? launch_mfma_nt<F, DT, 2>(parts, x, R, K, B, s) : launch_mfma_nt<F, DT, 1>(parts, x, R, K, B, s);
 }
