@@ -1,0 +1,145 @@
+"""GPU parity of the LDS-ring matrix-core kernel's configurations through the
+C ABI, against the oracle: one 16-row tile per wave (5 to 8 vectors), two (9
+to 16), four for sparse rows above 16 vectors on matrices with at least one
+64-row wave per CU, two batch tiles for dense rows above 16; odd batch sizes
+(x rows are staged in pairs, the last one repeated), K with a partial last
+stage, row counts that end inside a wave's tiles, fused launches whose part
+boundaries fall inside a wave's rows, and the gated epilogue."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_matrix_vector_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+TD = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def nm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_matrix_vector_amd as nm
+    nm.lib()
+    return nm
+
+
+def bits(t):
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def sparse_case(nm, W, x, n, m, dt, rows=None):
+    v, mk = nm.pack(W if W.is_cuda else W.cuda(), None, n, m)
+    y = nm.spmv(v, mk, x.cuda(), n, m)
+    rows = list(range(W.shape[0])) if rows is None else rows
+    ov, om = oracle.pack(bits(W[rows]), None, n, m, dt)
+    yref, A = oracle.spmv(ov, om, W.shape[1], n, m, dt, bits(x))
+    ok, worst, idx = oracle.check(bits(y[:, rows]), yref, A, dt)
+    assert ok, f"outside tolerance: worst {worst:.3f} at {idx}"
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("B", [5, 7, 8, 9, 13, 16])
+@pytest.mark.parametrize("R,K", [(37, 1056), (200, 4128), (1000, 8192)])
+def test_ring_sparse(nm, dt, n, m, B, R, K):
+    """K = 1056 and 4128 end in a partial stage (66 and 258 chunks of 16)."""
+    tdt = TD[dt]
+    W = I.weight(R, K, tdt, I.seed_of("rgW", R, K, n, m, dt))
+    x = I.activation_normal(B, K, tdt, I.seed_of("rgx", R, K, dt, B), outlier_frac=0.01)
+    sparse_case(nm, W, x, n, m, dt)
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("B", [7, 13])
+def test_ring_sparse_integer_exact(nm, dt, n, m, B):
+    """Exact sums: one and two tiles per wave bit for bit."""
+    R, K = 77, 2080
+    tdt = TD[dt]
+    W = I.integer_valued(R, K, tdt, I.seed_of("rgiW", dt, n, m), scale=1 / 16)
+    x = I.integer_valued(B, K, tdt, I.seed_of("rgix", dt, n, m, B))
+    ov, om = oracle.pack(bits(W), None, n, m, dt)
+    yref, _ = oracle.spmv(ov, om, K, n, m, dt, bits(x))
+    v, mk = nm.pack(W.cuda(), None, n, m)
+    y = nm.spmv(v, mk, x.cuda(), n, m)
+    assert np.array_equal(bits(y), oracle.round_to(yref, dt))
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("B", [17, 25, 32])
+def test_ring_sparse_four_tiles(nm, dt, n, m, B):
+    """Above 16 vectors on a matrix with one 64-row wave per CU and 40 rows
+    more (the last wave's tiles end inside the matrix); sampled rows,
+    including the last 40."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    R, K = 64 * cus + 40, 1056
+    tdt = TD[dt]
+    W = I.weight(R, K, tdt, I.seed_of("rg4W", n, m, dt), device="cuda")
+    x = I.activation_normal(B, K, tdt, I.seed_of("rg4x", dt, B), device="cuda", outlier_frac=0.01)
+    g = np.random.default_rng(I.seed_of("rg4r", B))
+    rows = sorted(set(g.choice(R, size=40, replace=False).tolist()) | set(range(R - 40, R)) | {0, 63, 64})
+    sparse_case(nm, W, x, n, m, dt, rows=rows)
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("B", [5, 12, 17, 24, 32])
+@pytest.mark.parametrize("R,K", [(70, 1000), (300, 4104)])
+def test_ring_dense(nm, dt, B, R, K):
+    """Dense rows: chunks of 8 columns, so K = 1000 and 4104 end in a partial
+    stage; above 16 vectors two batch tiles share each weight operand."""
+    tdt = TD[dt]
+    W = I.weight(R, K, tdt, I.seed_of("rgdW", R, K, dt))
+    x = I.activation_normal(B, K, tdt, I.seed_of("rgdx", R, K, dt, B), outlier_frac=0.01)
+    y = nm.gemv_dense(W.cuda(), x.cuda())
+    yref, A = oracle.gemv(bits(W), dt, bits(x))
+    ok, worst, idx = oracle.check(bits(y), yref, A, dt)
+    assert ok, (worst, idx)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("B", [6, 12])
+def test_ring_multi_part(nm, n, m, B):
+    """Fused parts of 40, 0, 77 and 13 rows: boundaries inside 16- and
+    32-row wave tiles."""
+    dt, tdt = "fp16", torch.float16
+    Rs, K = (40, 0, 77, 13), 2048
+    x = I.activation_normal(B, K, tdt, I.seed_of("rgmx", B, n, m))
+    parts, ref = [], []
+    for i, R in enumerate(Rs):
+        W = I.weight(R, K, tdt, I.seed_of("rgmW", i, R, n, m))
+        ov, om = oracle.pack(bits(W), None, n, m, dt)
+        ref.append(oracle.spmv(ov, om, K, n, m, dt, bits(x)))
+        parts.append(nm.pack(W.cuda(), None, n, m))
+    ys = nm.spmv_multi(parts, x.cuda(), n, m)
+    for y, (yref, A), R in zip(ys, ref, Rs):
+        assert y.shape == (B, R)
+        ok, worst, idx = oracle.check(bits(y), yref, A, dt)
+        assert ok, (R, worst, idx)
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("B", [6, 12])
+def test_ring_swiglu(nm, dt, B):
+    """Gated epilogue with one and two tiles per wave, sparse and dense."""
+    R, K, n, m = 300, 2080, 2, 4
+    tdt = TD[dt]
+    Wg = I.weight(R, K, tdt, I.seed_of("rggW", dt, B))
+    Wu = I.weight(R, K, tdt, I.seed_of("rguW", dt, B))
+    x = I.activation_normal(B, K, tdt, I.seed_of("rggx", dt, B), outlier_frac=0.01)
+    g, u = nm.pack(Wg.cuda(), None, n, m), nm.pack(Wu.cuda(), None, n, m)
+    h = nm.spmv_swiglu(g, u, x.cuda(), n, m)
+    hd = nm.gemv_dense_swiglu(Wg.cuda(), Wu.cuda(), x.cuda())
+    gv, gm = oracle.pack(bits(Wg), None, n, m, dt)
+    uv, um = oracle.pack(bits(Wu), None, n, m, dt)
+    gref, Ag = oracle.spmv(gv, gm, K, n, m, dt, bits(x))
+    uref, Au = oracle.spmv(uv, um, K, n, m, dt, bits(x))
+    ok, worst, idx = oracle.check_swiglu(bits(h), gref, uref, Ag, Au, dt)
+    assert ok, ("sparse", worst, idx)
+    gdr, Agd = oracle.gemv(bits(Wg), dt, bits(x))
+    udr, Aud = oracle.gemv(bits(Wu), dt, bits(x))
+    ok, worst, idx = oracle.check_swiglu(bits(hd), gdr, udr, Agd, Aud, dt)
+    assert ok, ("dense", worst, idx)
