@@ -14,8 +14,9 @@
 //     lower column on ties, as a keep-mask for nm_pack.
 //
 // The accumulation is a dense contraction over the token axis, so it runs on
-// the matrix cores: v_mfma_f32_32x32x8 (fp16 / bf16 in, fp32 out), 128 x 128
-// tiles of H per 256-thread block, 32 token rows per step staged in LDS.
+// the matrix cores: v_mfma_f32_32x32x16 (fp16 / bf16 in, fp32 out), 128 x 128
+// tiles of H per 256-thread block, 64 token rows per step staged in LDS
+// column by column.  Its traffic is H's read and write (8 K^2 bytes).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -32,86 +33,132 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 128;        // H tile per block (rows i and columns j)
-constexpr int kTT = 32;           // token rows per staging step
-constexpr int kPitch = kTile + 8; // LDS row pitch in halves: rows t and t + 4 land 16 banks apart
+constexpr int kTT = 64;           // token rows per staging step
+constexpr int kTPitch = kTT + 8;  // LDS halves per staged column: 16-byte reads of 16 columns hit distinct banks
+constexpr int kTW = kTT / 4;      // token rows per wave per step
 
 // ---- H += X_d^T X_d --------------------------------------------------------------
 
-// v_mfma_f32_32x32x8 operand layout (one block): lane l holds A[l % 32][4 (l / 32) + e]
-// and B[4 (l / 32) + e][l % 32], e = 0..3, and the result D[i][j] for j = l % 32,
-// i = 8 (v / 4) + 4 (l / 32) + v % 4 in accumulator v.  Here A = X^T (i, t) and
-// B = X (t, j), so both fragments are 4 tokens of one column.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// v_mfma_f32_32x32x16 (gfx950): lane l supplies 8 k-values of row l % 32 of A
+// and of column l % 32 of B (A and B assign k to lanes and registers the same
+// way), and holds D[i][j] for j = l % 32, i = 8 (v / 4) + 4 (l / 32) + v % 4 in
+// accumulator v.  Here A = X^T (i, t) and B = X (t, j): both fragments are 8
+// tokens of one column, and lane half h = l / 32 takes tokens 8 h .. 8 h + 7
+// of the 16-token step, so the sum runs over exactly those tokens whatever
+// order the hardware gives k inside the instruction.
 template <int DT>
-__device__ __forceinline__ f32x16 mfma(u32x2 a, u32x2 b, f32x16 acc)
+__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 acc)
 {
     if constexpr (DT == NM_FP16)
-        return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), acc, 0, 0,
-                                                    0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0, 0,
+                                                      0);
     else
-        return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), acc,
-                                                        0, 0, 0);
-}
-
-// Tokens t .. t + 3 of column c of a staged tile [token][column], packed in
-// token order (lanes 0-31 read 32 consecutive columns: no bank conflicts).
-__device__ __forceinline__ u32x2 frag(const uint16_t* tile, int t, int c)
-{
-    const uint32_t v0 = tile[t * kPitch + c], v1 = tile[(t + 1) * kPitch + c];
-    const uint32_t v2 = tile[(t + 2) * kPitch + c], v3 = tile[(t + 3) * kPitch + c];
-    return u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                       0, 0, 0);
 }
 
 // Block (bj, bi) owns H[128 bi .. +128][128 bj .. +128]; wave w owns the 64 x 64
-// quarter (w / 2, w % 2) as 2 x 2 MFMA blocks.  Each step stages 32 token rows
-// of X's two column ranges, zeroing rows past T and prefill rows.
+// quarter (w / 2, w % 2) as 2 x 2 matrix-core blocks.  The block's H tile is
+// read at the start (its HBM traffic overlaps the whole token loop: H is the
+// kernel's dominant traffic) and written back once.  Each step stages 64
+// token rows of X's two column ranges in LDS transposed, [column][token], so
+// that an operand (8 tokens of a column) is one 16-byte read: wave w loads
+// tokens 16 w .. 16 w + 15, lanes 0-31 four columns of the i range and lanes
+// 32-63 four of the j range (8-byte loads, 256 contiguous bytes per token
+// row per half-wave), transposes them in registers with byte permutes and
+// writes two 16-byte runs per column.  The next step's loads are in flight
+// while the current one is multiplied (a step is long enough that the L2
+// latency of those loads mostly hides behind its 16 matrix-core steps per
+// wave).  Tokens past T, prefill tokens and columns past K are zero.
 template <int DT>
 __global__ __launch_bounds__(256) void calib_accumulate_kernel(const uint16_t* __restrict__ X,
                                                                const uint8_t* __restrict__ decode, int T, int K,
                                                                float* __restrict__ H)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t xi[kTT * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t xj[kTT * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kTile * kTPitch];   // [range][column][token]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i0 = blockIdx.y * kTile, j0 = blockIdx.x * kTile;
     const int wi = (wave >> 1) * 64, wj = (wave & 1) * 64;
+
+    // H tile, read now, in the accumulator layout.
+    f32x16 hv[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int j = j0 + wj + 32 * n + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = i0 + wi + 32 * m + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                hv[m][n][v] = (i < K && j < K) ? H[(size_t)i * K + j] : 0.f;
+            }
+        }
     f32x16 acc[2][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                acc[a][b][v] = 0.f;
+                acc[m][n][v] = 0.f;
 
-    // Staging: thread -> token row tt = tid / 8 and 16 columns 16 q .. 16 q + 15
-    // (q = tid % 8) of each range: two 16-byte loads and stores per range.
-    const int tt = tid >> 3, q = tid & 7;
+    // Staging role: range r (0: columns i0.., 1: j0..), columns c4 .. c4 + 3
+    // of it, tokens 8 wave .. 8 wave + 7 of the step.
+    const int r = lane >> 5, c4 = 4 * (lane & 31);
+    const int col = (r == 0 ? i0 : j0) + c4;
+    const bool col_ok = col < K;                   // K % 4 == 0: four columns in or out together
+    const uint16_t* src = X + (col_ok ? col : 0);
+    u32x2 ld[kTW];
+    auto load_step = [&](int t0) {
+#pragma unroll
+        for (int e = 0; e < kTW; ++e) {
+            const int t = t0 + kTW * wave + e;
+            ld[e] = *reinterpret_cast<const u32x2*>(src + (size_t)(t < T ? t : 0) * K);
+        }
+    };
+    auto store_step = [&](int t0) {
+        uint32_t w[kTW][2];
+#pragma unroll
+        for (int e = 0; e < kTW; ++e) {
+            const int t = t0 + kTW * wave + e;
+            const bool live = col_ok && t < T && (!decode || decode[t]);
+            w[e][0] = live ? ld[e].x : 0u;
+            w[e][1] = live ? ld[e].y : 0u;
+        }
+        // Column c4 + u (u = 0..3) takes half u % 2 of word u / 2 of each token.
+#pragma unroll
+        for (int g = 0; g < kTW / 8; ++g)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;   // high or low halves of two words
+                const uint32_t(*wg)[2] = w + 8 * g;
+                u32x4 o;
+                o.x = __builtin_amdgcn_perm(wg[1][u >> 1], wg[0][u >> 1], sel);
+                o.y = __builtin_amdgcn_perm(wg[3][u >> 1], wg[2][u >> 1], sel);
+                o.z = __builtin_amdgcn_perm(wg[5][u >> 1], wg[4][u >> 1], sel);
+                o.w = __builtin_amdgcn_perm(wg[7][u >> 1], wg[6][u >> 1], sel);
+                *reinterpret_cast<u32x4*>(&xs[(r * kTile + c4 + u) * kTPitch + kTW * wave + 8 * g]) = o;
+            }
+    };
+
+    load_step(0);
     for (int t0 = 0; t0 < T; t0 += kTT) {
-        const int t = t0 + tt;
-        const bool live = t < T && (!decode || decode[t]);
-        u32x4 vi[2], vj[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int ci = i0 + 16 * q + 8 * h, cj = j0 + 16 * q + 8 * h;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            vi[h] = live && ci < K ? *reinterpret_cast<const u32x4*>(X + (size_t)t * K + ci) : z;
-            vj[h] = live && cj < K ? *reinterpret_cast<const u32x4*>(X + (size_t)t * K + cj) : z;
-        }
         __syncthreads();                          // the previous step's tiles are no longer read
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            *reinterpret_cast<u32x4*>(&xi[tt * kPitch + 16 * q + 8 * h]) = vi[h];
-            *reinterpret_cast<u32x4*>(&xj[tt * kPitch + 16 * q + 8 * h]) = vj[h];
-        }
+        store_step(t0);
         __syncthreads();
+        if (t0 + kTT < T)
+            load_step(t0 + kTT);                  // in flight during this step's products
 #pragma unroll
-        for (int k = 0; k < kTT / 8; ++k) {
-            const int tk = 8 * k + 4 * (lane >> 5);
-            u32x2 a[2], b[2];
+        for (int k = 0; k < kTT / 16; ++k) {
+            const int tk = 16 * k + 8 * (lane >> 5);
+            u32x4 a[2], b[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                a[m] = frag(xi, tk, wi + 32 * m + (lane & 31));
-                b[m] = frag(xj, tk, wj + 32 * m + (lane & 31));
+                a[m] = *reinterpret_cast<const u32x4*>(&xs[(wi + 32 * m + (lane & 31)) * kTPitch + tk]);
+                b[m] = *reinterpret_cast<const u32x4*>(&xs[(kTile + wj + 32 * m + (lane & 31)) * kTPitch + tk]);
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
@@ -120,7 +167,7 @@ __global__ __launch_bounds__(256) void calib_accumulate_kernel(const uint16_t* _
                     acc[m][n] = mfma<DT>(a[m], b[n], acc[m][n]);
         }
     }
-    // H += the block's sums (32 consecutive columns per half-wave: coalesced).
+    // H = H + the block's sums (32 consecutive columns per half-wave: coalesced).
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -130,7 +177,7 @@ __global__ __launch_bounds__(256) void calib_accumulate_kernel(const uint16_t* _
             for (int v = 0; v < 16; ++v) {
                 const int i = i0 + wi + 32 * m + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 if (i < K && j < K)
-                    H[(size_t)i * K + j] += acc[m][n][v];
+                    H[(size_t)i * K + j] = hv[m][n][v] + acc[m][n][v];
             }
         }
 }
