@@ -222,9 +222,18 @@ def copy_calibration(torch, cur, nbytes=256 << 20):
     return nbytes
 
 
-def mlp_single(torch, lib, launches, cur, reps=10):
+def trials_us(torch, body, trials, launches):
+    """(min, median, max) per-launch microseconds over `trials` timed bursts
+    of body() (each burst: `launches` launches)."""
+    import statistics
+    ts = sorted(time_ms(torch, body, 1) / launches * 1e3 for _ in range(trials))
+    return ts[0], statistics.median(ts), ts[-1]
+
+
+def mlp_single(torch, lib, launches, cur, reps=10, trials=20):
     """MLP projections (gate, up, down) as single nm_spmv / nm_gemv_dense
-    launches, back to back over every layer's weights."""
+    launches, back to back over every layer's weights; per-launch time is the
+    median over `trials` bursts (min and max beside it)."""
     out = {}
     for name in ("gate", "up", "down"):
         sargs, dargs, nbytes, dbytes = [], [], 0, 0
@@ -242,9 +251,10 @@ def mlp_single(torch, lib, launches, cur, reps=10):
         if not sargs:
             continue
         run(lib.nm_spmv, sargs)
-        us = time_ms(torch, lambda: run(lib.nm_spmv, sargs), reps) / len(sargs) * 1e3
+        ts = trials_us(torch, lambda: run(lib.nm_spmv, sargs), trials, len(sargs))
         run(lib.nm_gemv_dense, dargs)
-        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense, dargs), reps) / len(dargs) * 1e3
+        td = trials_us(torch, lambda: run(lib.nm_gemv_dense, dargs), trials, len(dargs))
+        us, usd = ts[1], td[1]
         # torch's own dense product (hipBLASLt / rocBLAS) on the same weights, as context
         pairs = [(L.W[L.names.index(name)], L.x, L.yd[L.names.index(name)]) for L in launches if name in L.names]
 
@@ -254,9 +264,11 @@ def mlp_single(torch, lib, launches, cur, reps=10):
         torch_linear()
         ust = time_ms(torch, torch_linear, reps) / len(pairs) * 1e3
         best_dense = min(usd, ust)
-        out[name] = {"shape": [R, K], "us": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
+        out[name] = {"shape": [R, K], "us": round(us, 3), "us_min": round(ts[0], 3), "us_max": round(ts[2], 3),
+                     "trials": trials, "gbs": round(nbytes / us / 1e3, 1),
                      "pct_of_peak": round(100 * nbytes / us / 1e3 / PEAK_GBS, 2),
-                     "dense_us": round(usd, 3), "dense_gbs": round(dbytes / usd / 1e3, 1),
+                     "dense_us": round(usd, 3), "dense_us_min": round(td[0], 3), "dense_us_max": round(td[2], 3),
+                     "dense_gbs": round(dbytes / usd / 1e3, 1),
                      "torch_matmul_us": round(ust, 3), "speedup": round(usd / us, 4),
                      "speedup_vs_best_dense": round(best_dense / us, 4)}
     return out
@@ -312,7 +324,8 @@ def calib_throughput(torch, nm, I, K=4096, T=512, reps=5):
 def cpu_baseline(launches, budget_s, torch, label):
     """CPU oracle (plain C, fp64, one thread) on layer 0's projections, packed
     by the oracle itself from the same weights; repeated until about budget_s
-    seconds of oracle time."""
+    seconds of oracle time.  Beside it, the same calls split by rows over the
+    host's worker threads (up to OMP_NUM_THREADS)."""
     import numpy as np
 
     import oracle
@@ -334,6 +347,31 @@ def cpu_baseline(launches, budget_s, torch, label):
             elapsed += time.perf_counter() - t0
             done += nbytes
         reps += 1
+    # The same oracle calls over row ranges on the host's worker threads (the
+    # C oracle runs outside Python's lock), as an all-cores reference figure.
+    nthreads = max(1, min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))))
+    all_threads = None
+    if nthreads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        def rows_job(job):
+            v, m, L, xb, dts, r0, r1 = job
+            oracle.spmv(v, m, L.K, L.n, L.m, dts, xb, rows=(r0, r1))
+        done_mt, t_mt, reps_mt = 0, 0.0, 0
+        with ThreadPoolExecutor(nthreads) as ex:
+            while t_mt < min(budget_s, 5.0) or reps_mt == 0:
+                for v, m, L, xb, nbytes, dts in work:
+                    R = m.shape[0]
+                    step = (R + nthreads - 1) // nthreads
+                    jobs = [(v, m, L, xb, dts, r0, min(R, r0 + step)) for r0 in range(0, R, step)]
+                    t0 = time.perf_counter()
+                    list(ex.map(rows_job, jobs))
+                    t_mt += time.perf_counter() - t0
+                    done_mt += nbytes
+                reps_mt += 1
+        all_threads = {"value": round(done_mt / t_mt / 1e9, 4), "unit": "GB/s", "cores": nthreads,
+                       "sample": f"the same projections x {reps_mt}, rows split over {nthreads} threads, "
+                                 f"{t_mt:.1f} s, {t_mt / reps_mt * 1e3:.0f} ms per layer"}
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -345,7 +383,8 @@ def cpu_baseline(launches, budget_s, torch, label):
         pass
     return {"value": round(done / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{label}: layer 0's projections x {reps}, fp64 scalar C oracle, 1 thread, {elapsed:.1f} s, "
-                      f"{elapsed / reps * 1e3:.0f} ms per layer; host {cpu}, {os.cpu_count()} logical CPUs"}
+                      f"{elapsed / reps * 1e3:.0f} ms per layer; host {cpu}, {os.cpu_count()} logical CPUs",
+            "all_threads": all_threads}
 
 
 def sampled_parity(launches, torch):

@@ -6,7 +6,7 @@
 // fixed-step traversal, used because decoding is memory-bound and the weight
 // bytes read per token set the time.  The pages' kernel was written for A100;
 // this one is designed for CDNA4 (wave64, 160 KB LDS per CU, HBM3E) and shares
-// nothing with the CPU checker.
+// no code with the CPU oracle that the tests compare it against.
 //
 // Format (include/nmspmv.h): values [R][K*N/M] 16-bit, group g of a row at
 // value g*N; masks [R][K/8], one bit per dense column, LSB first.
@@ -34,6 +34,14 @@
 //                    in flight while computing (long rows, few blocks); x in
 //                    K-tiles when B*K*2 bytes exceed the LDS tile.
 //   generic_spmv_kernel  any N:M with M in {4, 8} and K % 8 == 0 (untuned).
+//   mfma_ring_kernel  batches of a few vectors and up: 16-row tiles of W times
+//                    x^T on the matrix cores (v_mfma_f32_16x16x16), the packed
+//                    values expanded to the operand in registers; weights,
+//                    masks and x streamed into a per-wave LDS ring by
+//                    global-to-LDS loads.
+//   mfma_stage_kernel  the same product with the weights staged through
+//                    registers (sparse rows with K % 32 != 0, and sparse
+//                    batches above 16 on matrices too short for the ring).
 
 #include <hip/hip_runtime.h>
 
