@@ -1,0 +1,80 @@
+"""bench.py's host-side contract, on the CPU: more than one GPU is refused with
+a message, and the CPU baseline (the oracle, one thread and split over the
+host's threads) runs on a small stand-in projection and reports its figures."""
+import os
+import subprocess
+import sys
+
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from sparse_matrix_vector_amd import inputs as I  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+class _Launch:
+    """The fields cpu_baseline reads from a bench launch."""
+
+    def __init__(self, R, K, seed):
+        self.layer, self.dtc, self.n, self.m, self.K, self.B = 0, 0, 2, 4, K, 1
+        self.x = I.activation_normal(1, K, torch.float16, seed)
+        self.W = [I.weight(R, K, torch.float16, seed + 1)]
+        self.R = [R]
+
+    def part_bytes(self, i):
+        return self.R[i] * self.K * 9 // 8
+
+
+def test_cpu_baseline_reports_one_and_all_threads():
+    out = bench.cpu_baseline([_Launch(96, 512, 3)], 0.05, torch, "stand-in")
+    assert out["kind"] == "oracle" and out["cores"] == 1 and out["unit"] == "GB/s" and out["value"] > 0
+    assert "1 thread" in out["sample"]
+    at = out["all_threads"]
+    if (os.cpu_count() or 1) > 1 and int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)) > 1:
+        assert at["cores"] > 1 and at["value"] > 0
+    else:
+        assert at is None
+
+
+def test_trials_statistics_order():
+    calls = []
+
+    class _Ev:
+        def __init__(self, enable_timing=True):
+            pass
+
+        def record(self, s=None):
+            pass
+
+        def synchronize(self):
+            pass
+
+        def elapsed_time(self, other):
+            calls.append(1)
+            return [3.0, 1.0, 2.0][len(calls) - 1]
+
+    class _Cuda:
+        Event = _Ev
+
+        @staticmethod
+        def synchronize():
+            pass
+
+        @staticmethod
+        def current_stream():
+            return None
+
+    class _Torch:
+        cuda = _Cuda
+
+    lo, med, hi = bench.trials_us(_Torch, lambda: None, 3, 1)
+    assert (lo, med, hi) == (1000.0, 2000.0, 3000.0)
