@@ -1052,23 +1052,6 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// s_waitcnt vmcnt <= n for a wave-uniform n in 0 .. 63 (the count is an
-// immediate, so one branch per value).
-__device__ __forceinline__ void wait_vmcnt_dyn(int n)
-{
-    switch (n) {
-#define NM_WAIT_CASE(k) \
-    case k: wait_vmcnt<k>(); break;
-#define NM_WAIT_CASES8(k) NM_WAIT_CASE(k) NM_WAIT_CASE(k + 1) NM_WAIT_CASE(k + 2) NM_WAIT_CASE(k + 3) \
-    NM_WAIT_CASE(k + 4) NM_WAIT_CASE(k + 5) NM_WAIT_CASE(k + 6) NM_WAIT_CASE(k + 7)
-        NM_WAIT_CASES8(0) NM_WAIT_CASES8(8) NM_WAIT_CASES8(16) NM_WAIT_CASES8(24)
-        NM_WAIT_CASES8(32) NM_WAIT_CASES8(40) NM_WAIT_CASES8(48) NM_WAIT_CASES8(56)
-#undef NM_WAIT_CASES8
-#undef NM_WAIT_CASE
-    default: wait_vmcnt<0>(); break;
-    }
-}
-
 constexpr int kRingValues = 16 * kStageChunks * 16;               // 4 KB
 constexpr int kRingMasks = 16 * kStageChunks * 2;                 // 512 B
 
@@ -1097,7 +1080,17 @@ __host__ __device__ constexpr int ring_slot_bytes(int B)
 // A wave multiplies TW 16-row tiles (rows 16 TW w .. 16 TW w + 16 TW - 1) by
 // the same staged x, so each byte of x brought to LDS serves TW tiles; NT
 // batch tiles of 16 vectors share each weight operand.
-template <int F, int DT, int TW, int NT>
+//
+// SHX (one K-slice per tile): the block's waves share one staged x.  Each
+// wave keeps its two-slot weight ring; x goes to a two-slot ring of the
+// block, its load instructions dealt round-robin over the waves.  Per stage
+// a wave waits for its own loads, then all meet at a barrier (no memory
+// fence: each wave's wait already covers its loads into LDS), so after it
+// every piece of the stage's x is in place; only then is the next stage's
+// x issued, into the slot whose last reads every wave finished before that
+// barrier.  Every wave runs all stages (tiles past R read clamped rows and
+// store nothing), so the barrier counts match.
+template <int F, int DT, int TW, int NT, bool SHX>
 __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
                                                         int B, int S, int tiles_per_block)
 {
@@ -1111,7 +1104,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     constexpr int RPX = kWave / UPR;             // batch rows per x load instruction
     constexpr int TAB = mfma_table_units<F>() * 16;
     constexpr int TBYTES = kRingValues + (F == kDense ? 0 : kRingMasks);   // one tile's part of a slot
-    constexpr int XOFF = TW * TBYTES;
+    constexpr int XOFF = TW * TBYTES;            // x within a wave's slot (without SHX)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lt = wave / S, sl = wave - lt * S;
@@ -1120,11 +1113,15 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     // of a launch move through K together.
     const int C = K / COLS;
     const int NS = (C + kStageChunks - 1) / kStageChunks;
-    const int nst = (r0 < R && sl < NS) ? (NS - sl + S - 1) / S : 0;
+    const int nst = SHX ? NS : (r0 < R && sl < NS) ? (NS - sl + S - 1) / S : 0;
     const int i = lane & 15, q = lane >> 4;      // operand layout: row / batch column i, k-quarter q
     const int nxi = ring_x_rows<F>(B) / RPX;     // x load instructions per stage (1 .. 16)
-    const int slot_bytes = ring_slot_bytes<F, TW>(B);
-    const int nload = TW * (4 + NM) + nxi;       // loads per stage
+    const int nwaves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
+    // Without SHX a slot holds the wave's tiles and x; with it, only the tiles.
+    const int slot_bytes = SHX ? TW * TBYTES : ring_slot_bytes<F, TW>(B);
+    const int xslot_bytes = ring_x_rows<F>(B) * UPR * 16;
+    const uint32_t xring = (uint32_t)TAB + (uint32_t)nwaves * 2u * (uint32_t)slot_bytes;   // SHX: the block's x
+    constexpr int NW = TW * (4 + NM);            // weight loads per stage
 
     // Per-lane sources.  Values: tile tw, instruction rr, row 4 rr + lane / 16,
     // chunk (lane % 16) ^ row.  Masks: instruction h, row 8 h + lane / 8, dword
@@ -1152,9 +1149,10 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     const uint32_t ring = (uint32_t)TAB + (uint32_t)wave * 2u * (uint32_t)slot_bytes;
     const uint8_t* ring_p = reinterpret_cast<const uint8_t*>(smem) + ring;
 
-    // Stage st into slot `slot`; chunks past the row's end load the stage's
-    // first chunk instead (in bounds; never multiplied).
-    auto issue = [&](int st, int slot) {
+    // Stage st's weights into slot `slot`, and (issue_x) its x; chunks past the
+    // row's end load the stage's first chunk instead (in bounds; never
+    // multiplied).
+    auto issue_w = [&](int st, int slot) {
         const int c0 = (sl + st * S) * kStageChunks;
         const uint32_t base = ring + (uint32_t)(slot * slot_bytes);
 #pragma unroll
@@ -1171,11 +1169,16 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
                     load_to_lds<4>(msrc[tw][h] + (c < C ? c : c0), base + tw * TBYTES + kRingValues + h * 256);
             }
         }
-        for (int n = 0; n < nxi; ++n) {
+    };
+    auto issue_x = [&](int st, int slot) {
+        const int c0 = (sl + st * S) * kStageChunks;
+        const uint32_t xbase =
+            SHX ? xring + (uint32_t)(slot * xslot_bytes) : ring + (uint32_t)(slot * slot_bytes) + (uint32_t)XOFF;
+        for (int n = SHX ? wave : 0; n < nxi; n += SHX ? nwaves : 1) {
             const int b = n * RPX + lane / UPR;
             const int u = (lane % UPR) ^ (b & 15);
             const u32x4* xs = x4 + (size_t)min(b, B - 1) * (K / 8) + c0 * XC;
-            load_to_lds<16>(xs + (c0 + u / XC < C ? u : u % XC), base + XOFF + n * 1024);
+            load_to_lds<16>(xs + (c0 + u / XC < C ? u : u % XC), xbase + n * 1024);
         }
     };
 
@@ -1198,10 +1201,11 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     auto consume = [&](int st, int slot) {
         const int c0 = (sl + st * S) * kStageChunks;
         const uint8_t* sv0 = ring_p + slot * slot_bytes;
+        const uint8_t* sxs = SHX ? reinterpret_cast<const uint8_t*>(smem) + xring + slot * xslot_bytes : sv0 + XOFF;
         u32x4 xx[NT][T][XC];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const uint8_t* sx = sv0 + XOFF + xi[nt] * (UPR * 16);
+            const uint8_t* sx = sxs + xi[nt] * (UPR * 16);
 #pragma unroll
             for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -1270,20 +1274,30 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
 
     build_mfma_table<F>(smem);
     __syncthreads();
-    // One stage in flight while the previous one is multiplied: issue st + 1,
-    // wait until only its loads are outstanding (loads complete in order),
-    // multiply st.  No load in the loop writes registers, so issuing the last
-    // stage's successor conditionally costs the compiler's own wait counting
-    // nothing.
+    // One stage in flight while the previous one is multiplied: issue the
+    // weights of st + 1, wait until only those are outstanding (loads complete
+    // in order, so st's weights and its x, issued after them, have landed),
+    // meet the block (SHX), issue the x of st + 1 (a short L2 read, done during
+    // the products of st), multiply st.  The wait counts are fixed; no load in
+    // the loop writes registers.
     if (nst > 0) {
-        issue(0, 0);
+        issue_w(0, 0);
+        issue_x(0, 0);
         for (int st = 0; st < nst; ++st) {
-            if (st + 1 < nst) {
-                issue(st + 1, (st + 1) & 1);
-                wait_vmcnt_dyn(nload);
+            const bool more = st + 1 < nst;
+            if (more) {
+                issue_w(st + 1, (st + 1) & 1);
+                wait_vmcnt<NW>();
             } else {
                 wait_vmcnt<0>();
             }
+            if constexpr (SHX) {                 // every wave's share of the stage's x has landed
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
+            if (more)
+                issue_x(st + 1, (st + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
             consume(st, st & 1);
             __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the slot's reads are done before it is refilled
@@ -1654,7 +1668,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 // NMSPMV_MFMA_SLICES.
 struct Env {
     int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0,
-        ring_tiles = 0;
+        ring_tiles = 0, ring_share = 0;
 };
 Env g_env;
 std::once_flag g_env_once;
@@ -1674,6 +1688,7 @@ void read_env()
     g_env.mfma_min_b = get("NMSPMV_MFMA_MIN_B");
     g_env.mfma_slices = get("NMSPMV_MFMA_SLICES");
     g_env.ring_tiles = get("NMSPMV_RING_TILES");
+    g_env.ring_share = get("NMSPMV_RING_SHARE");
 }
 
 int g_cu_count[64] = {};
@@ -1943,25 +1958,49 @@ Plan plan_mfma_ring(int64_t R, int64_t K, int B)
     P.threads = S * kWave;
     P.grid = (unsigned)tiles;
     P.lds = tab + (size_t)S * ring;
+    // One slice per tile: up to 4 waves (one tile group each) share a block's
+    // staged x (2 with two tiles per wave, none with four), while the launch
+    // keeps at least one block per CU.
+    int W = TW == 1 ? 4 : TW == 2 ? 2 : 1;
+    if (g_env.ring_share > 0)
+        W = std::min(g_env.ring_share, 8);
+    while (W > 1 && (tiles + W - 1) / W < cus)
+        W /= 2;
+    if (S == 1 && W > 1) {
+        const size_t wring = 2 * (size_t)TW * (kRingValues + (F == kDense ? 0 : kRingMasks));
+        const size_t xslot = (size_t)ring_x_rows<F>(B) * ring_x_units<F>() * 16;
+        P.kind = 7;
+        P.rpb = W;
+        P.threads = W * kWave;
+        P.grid = (unsigned)((tiles + W - 1) / W);
+        P.lds = tab + W * wring + 2 * xslot;
+    }
     return P;
 }
 
-template <int F, int DT, int TW, int NT>
-int launch_mfma_ring_tw(const Plan& P, const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
+template <int F, int DT, int TW, int NT, bool SHX>
+int launch_mfma_ring_k(const Plan& P, const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
     if (P.lds > 64 * 1024) {
         static bool raised = false;              // once per instantiation
         if (!raised) {
-            if (hipFuncSetAttribute((const void*)mfma_ring_kernel<F, DT, TW, NT>,
+            if (hipFuncSetAttribute((const void*)mfma_ring_kernel<F, DT, TW, NT, SHX>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
                 return NM_ERR_HIP;
             raised = true;
         }
     }
     (void)hipGetLastError();
-    hipLaunchKernelGGL((mfma_ring_kernel<F, DT, TW, NT>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
+    hipLaunchKernelGGL((mfma_ring_kernel<F, DT, TW, NT, SHX>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
                        static_cast<const u32x4*>(x), R, K, B, P.S, P.rpb);
     return hip_status(hipGetLastError());
+}
+
+template <int F, int DT, int TW, int NT>
+int launch_mfma_ring_tw(const Plan& P, const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
+{
+    return P.kind == 7 ? launch_mfma_ring_k<F, DT, TW, NT, true>(P, parts, x, R, K, B, s)
+                       : launch_mfma_ring_k<F, DT, TW, NT, false>(P, parts, x, R, K, B, s);
 }
 
 // Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles, four
