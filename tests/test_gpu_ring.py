@@ -143,3 +143,75 @@ def test_ring_swiglu(nm, dt, B):
     udr, Aud = oracle.gemv(bits(Wu), dt, bits(x))
     ok, worst, idx = oracle.check_swiglu(bits(hd), gdr, udr, Agd, Aud, dt)
     assert ok, ("dense", worst, idx)
+
+
+def _large_R(extra):
+    """Enough 16-row tiles that a launch with one K-slice fills every CU with
+    blocks of four waves sharing x, plus `extra` rows (a partial last block)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return 64 * cus + extra
+
+
+def _sample(R, seed, k=48):
+    g = np.random.default_rng(seed)
+    return sorted(set(g.choice(R, size=k, replace=False).tolist()) | set(range(R - 40, R)) | {0, 15, 16, 63, 64})
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("B", [5, 8, 9, 16])
+def test_ring_shared_x(nm, dt, n, m, B):
+    """Blocks whose waves share one staged x: four waves of one tile (up to 8
+    vectors) or two of two tiles (9 to 16); K = 1056 ends in a partial stage,
+    R in the middle of a block."""
+    R, K = _large_R(40), 1056
+    tdt = TD[dt]
+    W = I.weight(R, K, tdt, I.seed_of("rgsW", n, m, dt), device="cuda")
+    x = I.activation_normal(B, K, tdt, I.seed_of("rgsx", dt, B), device="cuda", outlier_frac=0.01)
+    sparse_case(nm, W, x, n, m, dt, rows=_sample(R, I.seed_of("rgsr", B)))
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("B", [4, 8, 12])
+def test_ring_shared_x_dense(nm, dt, B):
+    """K = 504: 63 chunks of 8 columns, under 8 stages, so one K-slice and
+    blocks that share x."""
+    R, K = _large_R(24), 504
+    tdt = TD[dt]
+    W = I.weight(R, K, tdt, I.seed_of("rgsdW", dt), device="cuda")
+    x = I.activation_normal(B, K, tdt, I.seed_of("rgsdx", dt, B), device="cuda", outlier_frac=0.01)
+    y = nm.gemv_dense(W, x)
+    rows = _sample(R, I.seed_of("rgsdr", B))
+    yref, A = oracle.gemv(bits(W[rows]), dt, bits(x))
+    ok, worst, idx = oracle.check(bits(y[:, rows]), yref, A, dt)
+    assert ok, (worst, idx)
+
+
+@pytest.mark.parametrize("B", [6, 12])
+def test_ring_shared_x_swiglu_and_parts(nm, B):
+    """The gated epilogue (launch rows interleave gate and up) and a fused
+    launch of three parts, both on blocks that share x."""
+    dt, tdt, n, m = "bf16", torch.bfloat16, 2, 4
+    Rh, K = _large_R(8) // 2, 1056                 # 5 stages: one K-slice
+    Wg = I.weight(Rh, K, tdt, I.seed_of("rgsgW", B), device="cuda")
+    Wu = I.weight(Rh, K, tdt, I.seed_of("rgsuW", B), device="cuda")
+    x = I.activation_normal(B, K, tdt, I.seed_of("rgsgx", B), device="cuda", outlier_frac=0.01)
+    g, u = nm.pack(Wg, None, n, m), nm.pack(Wu, None, n, m)
+    h = nm.spmv_swiglu(g, u, x, n, m)
+    rows = _sample(Rh, I.seed_of("rgsgr", B), k=32)
+    gv, gm = oracle.pack(bits(Wg[rows]), None, n, m, dt)
+    uv, um = oracle.pack(bits(Wu[rows]), None, n, m, dt)
+    gref, Ag = oracle.spmv(gv, gm, K, n, m, dt, bits(x))
+    uref, Au = oracle.spmv(uv, um, K, n, m, dt, bits(x))
+    ok, worst, idx = oracle.check_swiglu(bits(h[:, rows]), gref, uref, Ag, Au, dt)
+    assert ok, ("swiglu", worst, idx)
+    # three parts: the first two end inside blocks of 64 rows
+    Rs = (Rh + 7, 33, Rh - 1)
+    Ws = [I.weight(R, K, tdt, I.seed_of("rgspW", i, B), device="cuda") for i, R in enumerate(Rs)]
+    ys = nm.spmv_multi([nm.pack(Wp, None, n, m) for Wp in Ws], x, n, m)
+    for i, (Wp, y, R) in enumerate(zip(Ws, ys, Rs)):
+        rr = sorted(set(_sample(R, I.seed_of("rgspr", i, B), k=16)) | {R - 1}) if R > 64 else list(range(R))
+        ov, om = oracle.pack(bits(Wp[rr]), None, n, m, dt)
+        yref, A = oracle.spmv(ov, om, K, n, m, dt, bits(x))
+        ok, worst, idx = oracle.check(bits(y[:, rr]), yref, A, dt)
+        assert ok, ("part", i, worst, idx)
