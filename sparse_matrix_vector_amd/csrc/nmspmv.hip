@@ -30,6 +30,8 @@
 // Kernel shapes (chosen per matrix shape on the host):
 //   rowslice_kernel  a wave owns one (row, K-slice) item and issues all of its
 //                    loads before anything else; many short-lived waves.
+//   hybrid_rowslice_kernel  a hybrid matrix's sparse and dense rows in one
+//                    launch: two row-slice plans side by side.
 //   stream_kernel    waves walk rows g, g+G, ... with the next group of loads
 //                    in flight while computing (long rows, few blocks); x in
 //                    K-tiles when B*K*2 bytes exceed the LDS tile.
@@ -487,16 +489,18 @@ __device__ __forceinline__ void chunk_live(bool live, u32x4& v, uint32_t& mk)
 // A lane issues all of its chunk loads (at most CPL) first, then the block
 // stages the selector table and x in LDS, computes, reduces each wave across
 // lanes, and adds a row's S slice sums in slice order.
+// The body takes its block index as an argument so that one launch can run
+// two plans side by side (hybrid_rowslice_kernel).
 template <int F, int DT, int NB, int CPL, int XU>
-__global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K, int S,
-                                                        int rows_per_block)
+__device__ __forceinline__ void rowslice_body(const Parts& P, const u32x4* __restrict__ x4, int R, int K, int S,
+                                              int rows_per_block, unsigned blk)
 {
     extern __shared__ u32x4 smem[];
     constexpr int COLS = chunk_cols<F>();
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lr = wave / S, sl = wave - lr * S;
-    const int r = blockIdx.x * rows_per_block + lr;
+    const int r = blk * rows_per_block + lr;
     const bool active = r < R;
     const int C = K / COLS;
     const int cps = (C + S - 1) / S;
@@ -571,6 +575,32 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
             row.y[(size_t)b * row.R] = from_f32<DT>(t);
         }
     }
+}
+
+template <int F, int DT, int NB, int CPL, int XU>
+__global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K, int S,
+                                                        int rows_per_block)
+{
+    rowslice_body<F, DT, NB, CPL, XU>(P, x4, R, K, S, rows_per_block, blockIdx.x);
+}
+
+// A hybrid matrix (sparse rows PS plus dense rows PD, both scattered into one
+// y) in a single launch, so the dense rows do not pay a launch's start-up and
+// drain of their own: blocks [0, sparse_blocks) run the sparse rows' row-slice
+// plan, the rest the dense rows' plan with twice the slices and half the rows
+// per block -- a dense row has twice the chunks of a sparse one at the same
+// K, so both plans give a lane the same CPL chunks and a block the same
+// waves and x registers.
+template <int F, int DT, int NB, int CPL, int XU>
+__global__ __launch_bounds__(1024) void hybrid_rowslice_kernel(const Parts PS, const Parts PD,
+                                                               const u32x4* __restrict__ x4, int RS, int RD, int K,
+                                                               int S, int rows_per_block, int sparse_blocks)
+{
+    const unsigned blk = blockIdx.x;
+    if (blk < (unsigned)sparse_blocks)
+        rowslice_body<F, DT, NB, CPL, XU>(PS, x4, RS, K, S, rows_per_block, blk);
+    else
+        rowslice_body<kDense, DT, NB, CPL, XU>(PD, x4, RD, K, 2 * S, rows_per_block / 2, blk - sparse_blocks);
 }
 
 // ---- streaming kernel --------------------------------------------------------
@@ -1665,10 +1695,11 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 // the LDS ring); NMSPMV_SLICES, NMSPMV_ROWS_PER_BLOCK (row-slice);
 // NMSPMV_BLOCKS, NMSPMV_THREADS, NMSPMV_TILE_BYTES (stream);
 // NMSPMV_MFMA_MIN_B (smallest batch sent to the matrix-core kernels),
-// NMSPMV_MFMA_SLICES.
+// NMSPMV_MFMA_SLICES; NMSPMV_HYBRID_SPLIT=1 runs a hybrid matrix's sparse and
+// dense rows as two launches.
 struct Env {
     int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0,
-        ring_tiles = 0, ring_share = 0;
+        ring_tiles = 0, ring_share = 0, hybrid_split = 0;
 };
 Env g_env;
 std::once_flag g_env_once;
@@ -1689,6 +1720,7 @@ void read_env()
     g_env.mfma_slices = get("NMSPMV_MFMA_SLICES");
     g_env.ring_tiles = get("NMSPMV_RING_TILES");
     g_env.ring_share = get("NMSPMV_RING_SHARE");
+    g_env.hybrid_split = get("NMSPMV_HYBRID_SPLIT");
 }
 
 int g_cu_count[64] = {};
@@ -2092,6 +2124,59 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
                            P.tile_cols);
     }
     return hip_status(hipGetLastError());
+}
+
+// A hybrid matrix's sparse rows (PS, RS of them) and dense rows (PD, RD) at a
+// single x vector in one hybrid_rowslice_kernel launch.  It applies when the
+// sparse rows get a row-slice plan with an even number of rows per block (the
+// dense rows take half as many, over twice the slices); *launched is false,
+// and nothing is launched, otherwise.
+template <int F, int DT>
+int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS, int RD, int K, hipStream_t s,
+                        bool* launched)
+{
+    *launched = false;
+    const Plan P = plan_for<F>(RS, K, 1, false);
+    if (P.kind != 1 || P.rpb < 2 || P.rpb % 2 != 0)
+        return NM_OK;
+    const int64_t dense_rpb = P.rpb / 2;
+    const int64_t sblocks = P.grid, blocks = sblocks + (RD + dense_rpb - 1) / dense_rpb;
+    const u32x4* x4 = static_cast<const u32x4*>(x);
+    (void)hipGetLastError();
+#define NM_HYB_XU(CPL, XU)                                                                                      \
+    hipLaunchKernelGGL((hybrid_rowslice_kernel<F, DT, 1, CPL, XU>), dim3((unsigned)blocks), dim3(P.threads), P.lds, \
+                       s, PS, PD, x4, RS, RD, K, P.S, P.rpb, (int)sblocks)
+#define NM_HYB(CPL)                 \
+    do {                            \
+        if (P.xu == 1)              \
+            NM_HYB_XU(CPL, 1);      \
+        else if (P.xu == 2)         \
+            NM_HYB_XU(CPL, 2);      \
+        else                        \
+            NM_HYB_XU(CPL, 4);      \
+    } while (0)
+    switch (P.cpl) {
+    case 1: NM_HYB(1); break;
+    case 2: NM_HYB(2); break;
+    case 3: NM_HYB(3); break;
+    case 4: NM_HYB(4); break;
+    case 5: NM_HYB(5); break;
+    case 6: NM_HYB(6); break;
+    case 7: NM_HYB(7); break;
+    default: NM_HYB(8); break;
+    }
+#undef NM_HYB
+#undef NM_HYB_XU
+    *launched = true;
+    return hip_status(hipGetLastError());
+}
+
+template <int F>
+int launch_hybrid_fused_dt(int dtype, const Parts& PS, const Parts& PD, const void* x, int RS, int RD, int K,
+                           hipStream_t s, bool* launched)
+{
+    return dtype == NM_FP16 ? launch_hybrid_fused<F, NM_FP16>(PS, PD, x, RS, RD, K, s, launched)
+                            : launch_hybrid_fused<F, NM_BF16>(PS, PD, x, RS, RD, K, s, launched);
 }
 
 // ---- host: argument rules ------------------------------------------------------
@@ -2725,9 +2810,22 @@ int nm_spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows
         return NM_OK;
     if (K == 0)
         return launch_zero(y, (int64_t)B * R, s);
+    const bool tuned = K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8));
+    if (B == 1 && Rs > 0 && n_dense > 0 && tuned) {
+        std::call_once(g_env_once, read_env);
+        if (g_env.hybrid_split != 1) {
+            const Parts PS = mapped_part(values, masks, rows_sparse, Rs, R, y);
+            const Parts PD = mapped_part(W_dense, nullptr, rows_dense, n_dense, R, y);
+            bool launched = false;
+            st = M == 4 ? launch_hybrid_fused_dt<kNM24>(dtype, PS, PD, x, (int)Rs, (int)n_dense, (int)K, s, &launched)
+                        : launch_hybrid_fused_dt<kNM48>(dtype, PS, PD, x, (int)Rs, (int)n_dense, (int)K, s, &launched);
+            if (launched || st != NM_OK)
+                return st;
+        }
+    }
     if (Rs > 0) {
         const Parts P = mapped_part(values, masks, rows_sparse, Rs, R, y);
-        if (K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8))) {
+        if (tuned) {
             if (M == 4 ? use_mfma<kNM24>(Rs, K, B, false) : use_mfma<kNM48>(Rs, K, B, false))
                 st = M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)Rs, (int)K, B, s)
                             : launch_mfma_dt<kNM48>(dtype, &P, x, (int)Rs, (int)K, B, s);

@@ -98,6 +98,32 @@ def test_hybrid_pack_and_spmv(nm, dt, n, m, K, B, frac):
     assert ok, (worst, idx)
 
 
+# Single-vector shapes whose sparse rows get a row-slice plan with an even
+# number of rows per block (at least ~1024 sparse rows on a 256-CU part), so
+# sparse and dense rows run in one launch: one slice (K = 1040, 4096), two
+# (K = 8192; dense rows at four), four (K = 18432; dense rows at eight, one per
+# block); ragged row counts on both sides.
+@pytest.mark.parametrize("dt,n,m,K,R,frac", [
+    ("fp16", 2, 4, 1040, 4097, 0.1),
+    ("bf16", 4, 8, 4096, 4096, 0.05),
+    ("bf16", 2, 4, 8192, 4100, 0.5),
+    ("fp16", 4, 8, 8192, 3001, 0.3),
+    ("fp16", 2, 4, 18432, 2100, 0.25),
+])
+def test_hybrid_one_launch_shapes(nm, dt, n, m, K, R, frac):
+    tdt = TD[dt]
+    W = I.weight(R, K, tdt, I.seed_of("h1W", dt, n, m, K, R), device="cuda")
+    x = I.activation_normal(1, K, tdt, I.seed_of("h1x", dt, K), device="cuda", outlier_frac=0.01)
+    nd = int(round(frac * R))
+    flags = nm.hybrid_select_rows(nm.hybrid_row_loss(W, n, m), nd)
+    hyb = nm.hybrid_pack(W, flags, nd, n, m)
+    y = nm.spmv_hybrid(hyb, x)
+    f = flags.cpu().numpy().astype(bool)
+    yref, A = oracle.hybrid_spmv(bits(W), f, n, m, dt, bits(x))
+    ok, worst, idx = oracle.check(bits(y), yref, A, dt)
+    assert ok, (worst, idx)
+
+
 def test_hybrid_with_calibrated_keep(nm):
     """The two offline pieces together: a calibration keep-mask drives both
     the sparse rows' pattern and the loss that picks the dense rows."""
