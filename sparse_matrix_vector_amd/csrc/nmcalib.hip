@@ -14,9 +14,10 @@
 //     lower column on ties, as a keep-mask for nm_pack.
 //
 // The accumulation is a dense contraction over the token axis, so it runs on
-// the matrix cores: v_mfma_f32_32x32x16 (fp16 / bf16 in, fp32 out), 128 x 128
-// tiles of H per 256-thread block, 64 token rows per step staged in LDS
-// column by column.  Its traffic is H's read and write (8 K^2 bytes).
+// the matrix cores: v_mfma_f32_32x32x16 (fp16 / bf16 in, fp32 out), one
+// 128 x 128 tile of the upper triangle of H per 256-thread block (added to
+// its mirror tile too), 64 token rows per step staged in LDS column by column.
+// Its traffic is H's read and write (8 K^2 bytes).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -36,6 +37,8 @@ constexpr int kTile = 128;        // H tile per block (rows i and columns j)
 constexpr int kTT = 64;           // token rows per staging step
 constexpr int kTPitch = kTT + 8;  // LDS halves per staged column: 16-byte reads of 16 columns hit distinct banks
 constexpr int kTW = kTT / 4;      // token rows per wave per step
+constexpr int kMPitch = 64 + 1;   // floats per row of a wave's transposed half-quarter (mirror tile)
+static_assert(4 * 32 * kMPitch * 4 <= 2 * kTile * kTPitch * 2, "mirror staging fits in the X staging area");
 
 // ---- H += X_d^T X_d --------------------------------------------------------------
 
@@ -60,42 +63,53 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 acc)
                                                        0, 0, 0);
 }
 
-// Block (bj, bi) owns H[128 bi .. +128][128 bj .. +128]; wave w owns the 64 x 64
-// quarter (w / 2, w % 2) as 2 x 2 matrix-core blocks.  The block's H tile is
-// read at the start (its HBM traffic overlaps the whole token loop: H is the
-// kernel's dominant traffic) and written back once.  Each step stages 64
-// token rows of X's two column ranges in LDS transposed, [column][token], so
-// that an operand (8 tokens of a column) is one 16-byte read: wave w loads
-// tokens 16 w .. 16 w + 15, lanes 0-31 four columns of the i range and lanes
-// 32-63 four of the j range (8-byte loads, 256 contiguous bytes per token
-// row per half-wave), transposes them in registers with byte permutes and
-// writes two 16-byte runs per column.  The next step's loads are in flight
-// while the current one is multiplied (a step is long enough that the L2
-// latency of those loads mostly hides behind its 16 matrix-core steps per
-// wave).  Tokens past T, prefill tokens and columns past K are zero.
+// H is symmetric, so a block computes one tile S = X_I^T X_J of the upper
+// triangle (bi <= bj, tiles numbered column by column) and adds it to both
+// H[I][J] and, off the diagonal, H[J][I] (as S^T): half the matrix-core work
+// and half the re-reads of X of covering every tile.
+__device__ __forceinline__ void tile_of(int id, int& bi, int& bj)
+{
+    int c = (int)((sqrtf(8.f * (float)id + 1.f) - 1.f) * 0.5f);
+    while ((c + 1) * (c + 2) / 2 <= id)
+        ++c;
+    while (c * (c + 1) / 2 > id)
+        --c;
+    bj = c;
+    bi = id - c * (c + 1) / 2;
+}
+
+// Block id -> tile (bi, bj) owns S = X[:, 128 bi .. +128]^T X[:, 128 bj ..
+// +128]; wave w owns the 64 x 64 quarter (w / 2, w % 2) as 2 x 2 matrix-core
+// blocks.  The registers stay few enough for three blocks per CU (at
+// K = 4096, all 528 tiles resident at once), so H is read only after the
+// token loop, when the other blocks' loops overlap it.
+// Each step stages 64 token rows of X's two column ranges in LDS transposed,
+// [column][token], so that an operand (8 tokens of a column) is one 16-byte
+// read: wave w loads tokens 16 w .. 16 w + 15, lanes 0-31 four columns of the
+// I range and lanes 32-63 four of the J range (8-byte loads, 256 contiguous
+// bytes per token row per half-wave), transposes them in registers with byte
+// permutes and writes two 16-byte runs per column.  The next step's loads are
+// in flight while a step is multiplied; every load is issued whatever the
+// token count (tokens past T reload row 0 and are zeroed when staged), so
+// that the compiler waits for exactly the step it stages.  The decode flags
+// ride with the loads (lane l of a wave fetches its token l % 16) and are
+// read across the wave when staged.  Tokens past T, prefill tokens and
+// columns past K are zero.
+// Off the diagonal, S^T is added into H[J][I] through LDS, 32 rows of a
+// wave's quarter at a time, so that each H row is read and written as 64
+// consecutive floats.
 template <int DT>
-__global__ __launch_bounds__(256) void calib_accumulate_kernel(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(256, 3) void calib_accumulate_kernel(const uint16_t* __restrict__ X,
                                                                const uint8_t* __restrict__ decode, int T, int K,
                                                                float* __restrict__ H)
 {
     __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kTile * kTPitch];   // [range][column][token]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int i0 = blockIdx.y * kTile, j0 = blockIdx.x * kTile;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bi, bj;
+    tile_of(blockIdx.x, bi, bj);
+    const int i0 = bi * kTile, j0 = bj * kTile;
     const int wi = (wave >> 1) * 64, wj = (wave & 1) * 64;
 
-    // H tile, read now, in the accumulator layout.
-    f32x16 hv[2][2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int j = j0 + wj + 32 * n + (lane & 31);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int i = i0 + wi + 32 * m + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                hv[m][n][v] = (i < K && j < K) ? H[(size_t)i * K + j] : 0.f;
-            }
-        }
     f32x16 acc[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -105,28 +119,35 @@ __global__ __launch_bounds__(256) void calib_accumulate_kernel(const uint16_t* _
             for (int v = 0; v < 16; ++v)
                 acc[m][n][v] = 0.f;
 
-    // Staging role: range r (0: columns i0.., 1: j0..), columns c4 .. c4 + 3
-    // of it, tokens 8 wave .. 8 wave + 7 of the step.
+    // Staging role: range r (0: columns I, 1: J), columns c4 .. c4 + 3 of it,
+    // tokens kTW wave .. kTW wave + kTW - 1 of the step.
     const int r = lane >> 5, c4 = 4 * (lane & 31);
     const int col = (r == 0 ? i0 : j0) + c4;
     const bool col_ok = col < K;                   // K % 4 == 0: four columns in or out together
-    const uint16_t* src = X + (col_ok ? col : 0);
-    u32x2 ld[kTW];
-    auto load_step = [&](int t0) {
+    const uint32_t loff = 2u * (uint32_t)(col_ok ? col : 0);   // the lane's byte offset in a token row
+    const uint8_t* flags = decode ? decode : reinterpret_cast<const uint8_t*>(X);   // (read, then ignored)
+    struct Step {
+        u32x2 w[kTW];
+        uint32_t f;                                // decode flag of token (lane % kTW) of the wave's rows
+    };
+    auto load_step = [&](Step& st, int t0) {
 #pragma unroll
         for (int e = 0; e < kTW; ++e) {
-            const int t = t0 + kTW * wave + e;
-            ld[e] = *reinterpret_cast<const u32x2*>(src + (size_t)(t < T ? t : 0) * K);
+            const int t = t0 + kTW * wave + e;  // wave-uniform: a scalar row base plus the lane's offset
+            const char* row = reinterpret_cast<const char*>(X) + (size_t)(t < T ? t : 0) * K * 2;
+            st.w[e] = *reinterpret_cast<const u32x2*>(row + loff);
         }
+        const int tf = t0 + kTW * wave + (lane & (kTW - 1));
+        st.f = flags[tf < T ? tf : 0];
     };
-    auto store_step = [&](int t0) {
+    auto store_step = [&](const Step& st, int t0) {
         uint32_t w[kTW][2];
 #pragma unroll
         for (int e = 0; e < kTW; ++e) {
             const int t = t0 + kTW * wave + e;
-            const bool live = col_ok && t < T && (!decode || decode[t]);
-            w[e][0] = live ? ld[e].x : 0u;
-            w[e][1] = live ? ld[e].y : 0u;
+            const bool live = col_ok && t < T && (!decode || __builtin_amdgcn_readlane((int)st.f, e) != 0);
+            w[e][0] = live ? st.w[e].x : 0u;
+            w[e][1] = live ? st.w[e].y : 0u;
         }
         // Column c4 + u (u = 0..3) takes half u % 2 of word u / 2 of each token.
 #pragma unroll
@@ -143,14 +164,7 @@ __global__ __launch_bounds__(256) void calib_accumulate_kernel(const uint16_t* _
                 *reinterpret_cast<u32x4*>(&xs[(r * kTile + c4 + u) * kTPitch + kTW * wave + 8 * g]) = o;
             }
     };
-
-    load_step(0);
-    for (int t0 = 0; t0 < T; t0 += kTT) {
-        __syncthreads();                          // the previous step's tiles are no longer read
-        store_step(t0);
-        __syncthreads();
-        if (t0 + kTT < T)
-            load_step(t0 + kTT);                  // in flight during this step's products
+    auto multiply = [&]() {
 #pragma unroll
         for (int k = 0; k < kTT / 16; ++k) {
             const int tk = 16 * k + 8 * (lane >> 5);
@@ -166,20 +180,73 @@ __global__ __launch_bounds__(256) void calib_accumulate_kernel(const uint16_t* _
                 for (int n = 0; n < 2; ++n)
                     acc[m][n] = mfma<DT>(a[m], b[n], acc[m][n]);
         }
+    };
+
+    Step st;
+    load_step(st, 0);
+    for (int t0 = 0; t0 < T; t0 += kTT) {
+        __syncthreads();                          // the previous step's tiles are no longer read
+        store_step(st, t0);
+        __syncthreads();
+        load_step(st, t0 + kTT);                  // in flight during this step's products
+        multiply();
     }
-    // H = H + the block's sums (32 consecutive columns per half-wave: coalesced).
+    // H[I][J] += the block's sums, one 32-row half of the wave's quarter at a
+    // time (its 32 values read, then written: 32 consecutive columns per
+    // half-wave), addressed from the tile's corner.
+    float* const Ht = H + (size_t)i0 * K + j0;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2; ++m) {
+        float h[2][16];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            const int j = j0 + wj + 32 * n + (lane & 31);
+            const int jl = wj + 32 * n + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int i = i0 + wi + 32 * m + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (i < K && j < K)
-                    H[(size_t)i * K + j] = hv[m][n][v] + acc[m][n][v];
+                const int il = wi + 32 * m + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                h[n][v] = (i0 + il < K && j0 + jl < K) ? Ht[(uint32_t)(il * K + jl)] : 0.f;
             }
         }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int jl = wj + 32 * n + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int il = wi + 32 * m + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (i0 + il < K && j0 + jl < K)
+                    Ht[(uint32_t)(il * K + jl)] = h[n][v] + acc[m][n][v];
+            }
+        }
+    }
+    if (bi == bj)
+        return;
+    // H[J][I] += S^T: rows j = 32 n + (lane % 32) of the wave's quarter go to
+    // LDS as tq[j][i], then each of those 32 H rows is updated by all 64 lanes.
+    float* tq = reinterpret_cast<float*>(xs) + wave * 32 * kMPitch;
+    float* const Hm = H + (size_t)j0 * K + i0;   // the mirror tile's corner
+    const int ci = i0 + wi + lane;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        __syncthreads();                          // xs (or the previous half) is no longer read
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                tq[(lane & 31) * kMPitch + 32 * m + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = acc[m][n][v];
+        __syncthreads();
+        float h[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const int jl = wj + 32 * n + e;
+            h[e] = (j0 + jl < K && ci < K) ? Hm[(uint32_t)(jl * K + wi + lane)] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const int jl = wj + 32 * n + e;
+            if (j0 + jl < K && ci < K)
+                Hm[(uint32_t)(jl * K + wi + lane)] = h[e] + tq[e * kMPitch + lane];
+        }
+    }
 }
 
 // ---- saliency keep-mask -----------------------------------------------------------
@@ -260,13 +327,14 @@ int nm_calib_accumulate(const void* X, const uint8_t* decode, int64_t T, int64_t
     if (T == 0 || K == 0)
         return NM_OK;
     const unsigned nb = (unsigned)((K + kTile - 1) / kTile);
+    const unsigned tiles = nb * (nb + 1) / 2;     // upper triangle, diagonal included
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (dtype == NM_FP16)
-        hipLaunchKernelGGL(calib_accumulate_kernel<NM_FP16>, dim3(nb, nb), dim3(256), 0, s,
+        hipLaunchKernelGGL(calib_accumulate_kernel<NM_FP16>, dim3(tiles), dim3(256), 0, s,
                            static_cast<const uint16_t*>(X), decode, (int)T, (int)K, H);
     else
-        hipLaunchKernelGGL(calib_accumulate_kernel<NM_BF16>, dim3(nb, nb), dim3(256), 0, s,
+        hipLaunchKernelGGL(calib_accumulate_kernel<NM_BF16>, dim3(tiles), dim3(256), 0, s,
                            static_cast<const uint16_t*>(X), decode, (int)T, (int)K, H);
     return launched();
 }

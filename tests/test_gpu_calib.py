@@ -55,6 +55,23 @@ def test_calib_accumulate(nm, dt, T, K, masked):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("T,K", [(150, 392), (300, 520), (64, 256), (129, 136)])
+def test_calib_accumulate_onto_unsymmetric_h(nm, dt, T, K):
+    """H starts as an arbitrary (unsymmetric) matrix: every entry, on both
+    sides of the diagonal, must receive its own H0 plus the sums.  Token
+    counts give an odd number of 64-row steps, a partial last step and an
+    exact one; K gives ragged edge tiles and several off-diagonal tiles."""
+    X = I.activation_normal(T, K, TD[dt], I.seed_of("calU", T, K, dt))
+    d = decode_flags(T, I.seed_of("caldU", T))
+    H0 = torch.from_numpy(np.random.default_rng(T + K).standard_normal((K, K)).astype(np.float32))
+    H = H0.cuda()
+    nm.calib_accumulate(X.cuda(), torch.from_numpy(d).cuda(), H=H)
+    Href, A = oracle.calib_accumulate(bits(X), dt, decode=d, H=H0.numpy().astype(np.float64))
+    ok, worst, idx = oracle.check_calib(H.cpu().numpy(), Href, A, H0=H0.numpy())
+    assert ok, (worst, idx)
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
 def test_calib_accumulate_integer_exact(nm, dt):
     """Integer-valued rows: every partial sum is an integer below 2^24, so H
     must equal the exact sums in any order."""
