@@ -37,7 +37,7 @@
 //                    K-tiles when B*K*2 bytes exceed the LDS tile.
 //   generic_spmv_kernel  any N:M with M in {4, 8} and K % 8 == 0 (untuned).
 //   mfma_ring_kernel  batches of a few vectors and up: 16-row tiles of W times
-//                    x^T on the matrix cores (v_mfma_f32_16x16x16), the packed
+//                    x^T on the matrix cores (v_mfma_f32_16x16x32), the packed
 //                    values expanded to the operand in registers; weights,
 //                    masks and x streamed into a per-wave LDS ring by
 //                    global-to-LDS loads.
@@ -742,30 +742,34 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
 // and one dot2 per group per vector, plus the LDS reads of every vector's x;
 // from B ~ 6 that, not HBM, sets their pace.  Here the matrix cores take the
 // batch: a wave multiplies a 16-row tile of W by x^T (16 batch columns per
-// tile of the batch) with v_mfma_f32_16x16x16 over one K-slice.  In the
+// tile of the batch) with v_mfma_f32_16x16x32 over one K-slice.  In the
 // operand layout lane l (i = l % 16, quarter q = l / 16) holds chunk
 // c0 + 4 t + q of tile row i at step t; each chunk's 16 (dense: 8) columns are
-// COLS / 4 k-blocks of 4 columns, and the A operand of a k-block -- 4 dense
-// weights of one row -- is rebuilt from the packed values with two byte
-// permutes (2:4: one group; 4:8: half a group; dense: a copy).  The B operand
-// is the same 4 columns of x row i, read from L2 (x is small); lanes of batch
-// rows past B repeat row B - 1 and their outputs are dropped.  The matrix
-// core reduces over k, so no cross-lane reduction is needed: the slices of a
-// tile add up in LDS in slice order.
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+// COLS / 4 k-blocks of 4 columns, and the weights of a k-block -- 4 dense
+// weights of one row -- are rebuilt from the packed values with two byte
+// permutes (2:4: one group; 4:8: half a group; dense: a copy).  A matrix-core
+// step takes two k-blocks (8 columns of the chunk) per lane as its A operand
+// and the same 8 columns of x row i, one staged 16-byte unit, as its B
+// operand; lanes of batch rows past B repeat row B - 1 and their outputs are
+// dropped.  gfx950's K = 32 form runs at twice the rate of the 16x16x16 one;
+// only the pairing of A's and B's k-values matters, and both take the lane's
+// 8 halves in column order.  The matrix core reduces over k, so no
+// cross-lane reduction is needed: the slices of a tile add up in LDS in slice
+// order.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
 template <int DT>
-__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c)
+__device__ __forceinline__ f32x4 mfma16k32(u32x4 a, u32x4 b, f32x4 c)
 {
     if constexpr (DT == NM_FP16)
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
-                                                     0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a), __builtin_bit_cast(f16x8v, b), c, 0,
+                                                      0, 0);
     else
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
-                                                         0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a), __builtin_bit_cast(bf16x8v, b), c,
+                                                       0, 0, 0);
 }
 
 // 2:4.  Nibble n marks the kept columns j0 < j1 of a 4-column group; the two
@@ -955,14 +959,13 @@ __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u3
                                          __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.w)};
                 }
             }
+            // Two 4-column k-blocks (8 columns, one x unit) per matrix-core step.
 #pragma unroll
-            for (int s = 0; s < KB; ++s)
+            for (int h = 0; h < KB / 2; ++h)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const u32x4 xx = xv[nt][t][s >> 1];
-                    const u32x2 b = (s & 1) ? u32x2{xx.z, xx.w} : u32x2{xx.x, xx.y};
-                    acc[nt] = mfma16<DT>(a[s], b, acc[nt]);
-                }
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[nt] = mfma16k32<DT>(u32x4{a[2 * h].x, a[2 * h].y, a[2 * h + 1].x, a[2 * h + 1].y},
+                                            xv[nt][t][h], acc[nt]);
         }
     };
     // One pipeline step: multiply stage st (in LDS, its x in registers),
@@ -1290,14 +1293,14 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
                                              __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.w)};
                     }
                 }
+                // Two 4-column k-blocks (8 columns of the chunk, one staged x
+                // unit) per matrix-core step.
 #pragma unroll
-                for (int s = 0; s < KB; ++s)
+                for (int h = 0; h < KB / 2; ++h)
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const u32x4 xv = xx[nt][t][s >> 1];
-                        acc[tw][nt] =
-                            mfma16<DT>(a[s], (s & 1) ? u32x2{xv.z, xv.w} : u32x2{xv.x, xv.y}, acc[tw][nt]);
-                    }
+                    for (int nt = 0; nt < NT; ++nt)
+                        acc[tw][nt] = mfma16k32<DT>(u32x4{a[2 * h].x, a[2 * h].y, a[2 * h + 1].x, a[2 * h + 1].y},
+                                                    xx[nt][t][h], acc[tw][nt]);
             }
         }
     };
