@@ -1695,7 +1695,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 
 // Launch-shape overrides, read once, for tuning sweeps (0 = built-in choice):
 // NMSPMV_KERNEL 1 = row-slice, 3 = stream, 5 = staged matrix-core (instead of
-// the LDS ring); NMSPMV_SLICES, NMSPMV_ROWS_PER_BLOCK (row-slice);
+// the LDS ring), 6 = the LDS ring wherever K allows it; NMSPMV_SLICES, NMSPMV_ROWS_PER_BLOCK (row-slice);
 // NMSPMV_BLOCKS, NMSPMV_THREADS, NMSPMV_TILE_BYTES (stream);
 // NMSPMV_MFMA_MIN_B (smallest batch sent to the matrix-core kernels),
 // NMSPMV_MFMA_SLICES; NMSPMV_HYBRID_SPLIT=1 runs a hybrid matrix's sparse and
@@ -1952,9 +1952,10 @@ int launch_mfma_nt(const Parts& parts, const void* x, int R, int K, int B, hipSt
 
 // LDS-ring launch shape (rules from sweeps on MI355X at the Qwen3-32B MLP
 // shapes, weights streamed from HBM): 16-row tiles, one per wave up to 8
-// vectors, two above (x, then 16 rows per stage, serves both), four for
-// sparse rows above 16 (a sparse stage spans twice the columns, so twice the
-// x per weight byte); a block holds one wave group, its K split into S
+// vectors, two above (x, then 16 rows per stage, serves both; four tiles a
+// wave, tried for sparse rows above 16, double the LDS a wave holds and halve
+// the waves a CU keeps -- slower than two tiles with x shared by two waves);
+// a block holds one wave group, its K split into S
 // stage-interleaved slices (one wave each).  S is the largest power of two
 // (each slice keeping at least four stages, at most 8 waves a block, the
 // kernel's launch bound) whose launch still fits the CUs' LDS in one round:
@@ -1966,16 +1967,12 @@ Plan plan_mfma_ring(int64_t R, int64_t K, int B)
     constexpr int COLS = chunk_cols<F>();
     const int cus = cu_count();
     const int64_t C = K / COLS, NS = (C + kStageChunks - 1) / kStageChunks;
-    int TW = B > 16 && F != kDense ? 4 : B > 8 ? 2 : 1;
+    int TW = B > 8 ? 2 : 1;
     if (B <= 16 && (g_env.ring_tiles == 1 || g_env.ring_tiles == 2))
         TW = g_env.ring_tiles;                   // above 16 vectors the tile count is fixed
-    if (B > 16 && F != kDense && (g_env.ring_tiles == 2 || g_env.ring_tiles == 4))
-        TW = g_env.ring_tiles;
     const int64_t tiles = (R + 16 * TW - 1) / (16 * TW);
     const size_t tab = (size_t)mfma_table_units<F>() * sizeof(u32x4);
-    const size_t ring = 2 * (size_t)(TW == 4   ? ring_slot_bytes<F, 4>(B)
-                                     : TW == 2 ? ring_slot_bytes<F, 2>(B)
-                                               : ring_slot_bytes<F, 1>(B));
+    const size_t ring = 2 * (size_t)(TW == 2 ? ring_slot_bytes<F, 2>(B) : ring_slot_bytes<F, 1>(B));
     const int wmax = (int)std::min<size_t>(8, (kLdsMax - tab) / ring);
     // Waves resident at once with S-wave blocks (LDS-bound).
     auto resident = [&](int S) { return (int64_t)(kLdsMax / (tab + S * ring)) * S * cus; };
@@ -1994,9 +1991,9 @@ Plan plan_mfma_ring(int64_t R, int64_t K, int B)
     P.grid = (unsigned)tiles;
     P.lds = tab + (size_t)S * ring;
     // One slice per tile: up to 4 waves (one tile group each) share a block's
-    // staged x (2 with two tiles per wave, none with four), while the launch
-    // keeps at least one block per CU.
-    int W = TW == 1 ? 4 : TW == 2 ? 2 : 1;
+    // staged x (2 with two tiles per wave), while the launch keeps at least
+    // one block per CU.
+    int W = TW == 1 ? 4 : 2;
     if (g_env.ring_share > 0)
         W = std::min(g_env.ring_share, 8);
     while (W > 1 && (tiles + W - 1) / W < cus)
@@ -2038,30 +2035,30 @@ int launch_mfma_ring_tw(const Plan& P, const Parts& parts, const void* x, int R,
                        : launch_mfma_ring_k<F, DT, TW, NT, false>(P, parts, x, R, K, B, s);
 }
 
-// Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles, four
-// for sparse rows, whose x per weight byte is twice the dense rows').
+// Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles).
 template <int F, int DT>
 int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
     const Plan P = plan_mfma_ring<F>(R, K, B);
     if (B > 16)
-        return P.cpl == 4 ? launch_mfma_ring_tw<F, DT, 4, 2>(P, parts, x, R, K, B, s)
-                          : launch_mfma_ring_tw<F, DT, 2, 2>(P, parts, x, R, K, B, s);
+        return launch_mfma_ring_tw<F, DT, 2, 2>(P, parts, x, R, K, B, s);
     return P.cpl == 2 ? launch_mfma_ring_tw<F, DT, 2, 1>(P, parts, x, R, K, B, s)
                       : launch_mfma_ring_tw<F, DT, 1, 1>(P, parts, x, R, K, B, s);
 }
 
 // The LDS-ring kernel takes dense rows at any batch, and sparse rows whose
 // mask row is a whole number of dwords (K % 32 == 0): up to 16 vectors
-// always, above 16 when there is at least one 64-row wave per CU (measured:
-// with fewer the staged kernel wins).  Other sparse batches run on the staged
+// always, above 16 when there is at least one 64-row block (two waves of two
+// tiles sharing x) per CU (measured: with fewer the ring needs K-slices,
+// whose waves cannot share x, and does no better than the staged kernel).  Other sparse batches run on the staged
 // kernel, where up to 16 vectors are one tile of the matrix cores' batch
 // dimension and 17 to 32 take two, both fed by the same weight loads.
 template <int F, int DT>
 int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
     std::call_once(g_env_once, read_env);
-    const bool ring_fits = F == kDense || (K % 32 == 0 && (B <= 16 || (int64_t)R >= 64LL * cu_count()));
+    const bool ring_fits = F == kDense || (K % 32 == 0 && (B <= 16 || (int64_t)R >= 64LL * cu_count() ||
+                                                       g_env.kernel == 6));
     if (ring_fits && g_env.kernel != 5)
         return launch_mfma_ring<F, DT>(parts, x, R, K, B, s);
     return B > 16 ? launch_mfma_nt<F, DT, 2>(parts, x, R, K, B, s) : launch_mfma_nt<F, DT, 1>(parts, x, R, K, B, s);

@@ -1,7 +1,7 @@
 """GPU parity of the LDS-ring matrix-core kernel's configurations through the
 C ABI, against the oracle: one 16-row tile per wave (5 to 8 vectors), two (9
-to 16), four for sparse rows above 16 vectors on matrices with at least one
-64-row wave per CU, two batch tiles for dense rows above 16; odd batch sizes
+to 16, and above 16 with two batch tiles), x shared by the waves of a block
+when a tile keeps one K-slice; odd batch sizes
 (x rows are staged in pairs, the last one repeated), K with a partial last
 stage, row counts that end inside a wave's tiles, fused launches whose part
 boundaries fall inside a wave's rows, and the gated epilogue."""
@@ -71,10 +71,11 @@ def test_ring_sparse_integer_exact(nm, dt, n, m, B):
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
 @pytest.mark.parametrize("B", [17, 25, 32])
-def test_ring_sparse_four_tiles(nm, dt, n, m, B):
-    """Above 16 vectors on a matrix with one 64-row wave per CU and 40 rows
-    more (the last wave's tiles end inside the matrix); sampled rows,
-    including the last 40."""
+def test_ring_sparse_above_16(nm, dt, n, m, B):
+    """Above 16 vectors (two batch tiles) on a matrix with one 64-row block
+    per CU and 40 rows more: two waves of two tiles share x, and the last
+    block's tiles end inside the matrix; sampled rows, including the last
+    40."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     R, K = 64 * cus + 40, 1056
     tdt = TD[dt]
