@@ -173,10 +173,10 @@ def test_ring_shared_x(nm, dt, n, m, B):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
-@pytest.mark.parametrize("B", [4, 8, 12])
+@pytest.mark.parametrize("B", [4, 8, 12, 20, 32])
 def test_ring_shared_x_dense(nm, dt, B):
     """K = 504: 63 chunks of 8 columns, under 8 stages, so one K-slice and
-    blocks that share x."""
+    blocks that share x (above 16 vectors with two batch tiles)."""
     R, K = _large_R(24), 504
     tdt = TD[dt]
     W = I.weight(R, K, tdt, I.seed_of("rgsdW", dt), device="cuda")
