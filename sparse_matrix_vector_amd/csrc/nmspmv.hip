@@ -2128,15 +2128,25 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
 
 // A hybrid matrix's sparse rows (PS, RS of them) and dense rows (PD, RD) at a
 // single x vector in one hybrid_rowslice_kernel launch.  It applies when the
-// sparse rows get a row-slice plan with an even number of rows per block (the
-// dense rows take half as many, over twice the slices); *launched is false,
-// and nothing is launched, otherwise.
+// sparse rows get a row-slice plan (taken with at least two rows per block)
+// with an even number of rows per block (the dense rows take half as many,
+// over twice the slices); *launched is false, and nothing is launched,
+// otherwise.
 template <int F, int DT>
 int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS, int RD, int K, hipStream_t s,
                         bool* launched)
 {
     *launched = false;
-    const Plan P = plan_for<F>(RS, K, 1, false);
+    Plan P = plan_for<F>(RS, K, 1, false);
+    if (P.kind == 1 && P.rpb == 1 && g_env.rpb == 0 && P.S <= 8) {
+        // Few sparse rows: the plan went to one row per block to keep two
+        // blocks per CU; here the dense rows add blocks of their own, so take
+        // two rows per block (and the LDS for their partial sums).
+        P.rpb = 2;
+        P.threads = 2 * P.S * kWave;
+        P.grid = (unsigned)((RS + 1) / 2);
+        P.lds = (size_t)table_units<F>() * sizeof(u32x4) + (size_t)K * 2 + (size_t)P.rpb * P.S * 4;
+    }
     if (P.kind != 1 || P.rpb < 2 || P.rpb % 2 != 0)
         return NM_OK;
     const int64_t dense_rpb = P.rpb / 2;

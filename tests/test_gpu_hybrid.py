@@ -98,17 +98,18 @@ def test_hybrid_pack_and_spmv(nm, dt, n, m, K, B, frac):
     assert ok, (worst, idx)
 
 
-# Single-vector shapes whose sparse rows get a row-slice plan with an even
-# number of rows per block (at least ~1024 sparse rows on a 256-CU part), so
-# sparse and dense rows run in one launch: one slice (K = 1040, 4096), two
-# (K = 8192; dense rows at four), four (K = 18432; dense rows at eight, one per
-# block); ragged row counts on both sides.
+# Single-vector shapes whose sparse and dense rows run in one launch: one
+# slice (K = 1040, 4096), two (K = 8192; dense rows at four), four (K = 18432,
+# or few rows; dense rows at eight, one per block); few sparse rows (taken two
+# per block); ragged row counts on both sides.
 @pytest.mark.parametrize("dt,n,m,K,R,frac", [
     ("fp16", 2, 4, 1040, 4097, 0.1),
     ("bf16", 4, 8, 4096, 4096, 0.05),
     ("bf16", 2, 4, 8192, 4100, 0.5),
     ("fp16", 4, 8, 8192, 3001, 0.3),
     ("fp16", 2, 4, 18432, 2100, 0.25),
+    ("fp16", 2, 4, 4096, 1024, 0.05),           # few sparse rows: two per block in the one launch
+    ("bf16", 4, 8, 1040, 600, 0.2),
 ])
 def test_hybrid_one_launch_shapes(nm, dt, n, m, K, R, frac):
     tdt = TD[dt]
