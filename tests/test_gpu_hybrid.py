@@ -125,6 +125,35 @@ def test_hybrid_one_launch_shapes(nm, dt, n, m, K, R, frac):
     assert ok, (worst, idx)
 
 
+@pytest.mark.parametrize("R,K,B", [(4097, 1040, 1), (130, 1040, 2)])   # one launch; two launches
+def test_hybrid_bad_row_lists_stay_inside_y(nm, R, K, B):
+    """Row lists that do not partition 0..R-1 leave y unspecified, but every
+    entry is clamped into 0..R-1: rows out of range on both lists (past R,
+    negative) write inside y, never past it.  y is the front of a larger
+    buffer whose tail must keep its sentinel; rows the lists still map
+    correctly, and that no clamped entry lands on, hold their products."""
+    dt, tdt, n, m = "fp16", torch.float16, 2, 4
+    W = I.weight(R, K, tdt, I.seed_of("hbW", R), device="cuda")
+    x = I.activation_normal(B, K, tdt, I.seed_of("hbx", R, B), device="cuda")
+    nd = R // 10
+    flags = nm.hybrid_select_rows(nm.hybrid_row_loss(W, n, m), nd)
+    hyb = nm.hybrid_pack(W, flags, nd, n, m)
+    rs, rd = hyb.rows_sparse.cpu().numpy().copy(), hyb.rows_dense.cpu().numpy().copy()
+    hyb.rows_sparse[1] = R + 100                   # clamps to R - 1
+    hyb.rows_sparse[2] = -7                        # clamps to 0
+    hyb.rows_dense[0] = 1 << 30                    # clamps to R - 1
+    big = torch.full((B * R + 256,), 12345.0, dtype=tdt, device="cuda")
+    nm.spmv_hybrid(hyb, x, out=big[:B * R].view(B, R))
+    assert torch.all(big[B * R:].cpu() == 12345.0)
+    f = flags.cpu().numpy().astype(bool)
+    yref, A = oracle.hybrid_spmv(bits(W), f, n, m, dt, bits(x))
+    touched = {0, R - 1, int(rs[1]), int(rs[2]), int(rd[0])}
+    keep = np.array([r for r in range(R) if r not in touched])
+    y = bits(big[:B * R].view(B, R))
+    ok, worst, idx = oracle.check(y[:, keep], yref[:, keep], A[:, keep], dt)
+    assert ok, (worst, idx)
+
+
 def test_hybrid_with_calibrated_keep(nm):
     """The two offline pieces together: a calibration keep-mask drives both
     the sparse rows' pattern and the loss that picks the dense rows."""
