@@ -16,7 +16,8 @@
 // The accumulation is a dense contraction over the token axis, so it runs on
 // the matrix cores: v_mfma_f32_32x32x16 (fp16 / bf16 in, fp32 out), one
 // 128 x 128 tile of the upper triangle of H per 256-thread block (added to
-// its mirror tile too), 64 token rows per step staged in LDS column by column.
+// its mirror tile too), X streamed into an LDS ring by global-to-LDS loads
+// and read back transposed (ds_read_b64_tr_b16).
 // Its traffic is H's read and write (8 K^2 bytes).
 #include <hip/hip_runtime.h>
 
@@ -34,11 +35,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 128;        // H tile per block (rows i and columns j)
-constexpr int kTT = 64;           // token rows per staging step
-constexpr int kTPitch = kTT + 8;  // LDS halves per staged column: 16-byte reads of 16 columns hit distinct banks
-constexpr int kTW = kTT / 4;      // token rows per wave per step
+constexpr int kTS = 32;           // token rows per stage
+constexpr int kSlots = 3;         // stages in the block's LDS ring
+constexpr int kRowBytes = kTile * 2;                    // one token row of one column range
+constexpr int kRangeBytes = kTS * kRowBytes;            // 8 KB
+constexpr int kFlagBytes = 4 * 256;                     // each wave's 64 decode-flag dwords
+constexpr int kSlotBytes = 2 * kRangeBytes + kFlagBytes;
 constexpr int kMPitch = 64 + 1;   // floats per row of a wave's transposed half-quarter (mirror tile)
-static_assert(4 * 32 * kMPitch * 4 <= 2 * kTile * kTPitch * 2, "mirror staging fits in the X staging area");
+constexpr int kMirrorBytes = 4 * 32 * kMPitch * 4;
+static_assert(kMirrorBytes <= kSlots * kSlotBytes, "the mirror staging fits in the ring");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
 
 // ---- H += X_d^T X_d --------------------------------------------------------------
 
@@ -78,37 +87,150 @@ __device__ __forceinline__ void tile_of(int id, int& bi, int& bj)
     bi = id - c * (c + 1) / 2;
 }
 
+// Global-to-LDS loads into the kernel's dynamic LDS (which starts at offset
+// 0): 16 bytes per lane to lds_offset + 16 lane, or one byte per lane,
+// zero-extended, to lds_offset + 4 lane (lds_offset wave-uniform).  The LDS
+// side is addressed by offset, not through the array the kernel reads, so
+// the compiler does not wait for these loads before every LDS read; the
+// kernel's own waits and barriers order them.
+template <int BYTES>
+__device__ __forceinline__ void dma(const void* g, uint32_t lds_offset)
+{
+    static_assert(BYTES == 16 || BYTES == 1, "16- or 1-byte lanes");
+#if defined(__HIP_DEVICE_COMPILE__)
+    lds_void_t* dst = (lds_void_t*)((lds_u8_t*)nullptr + lds_offset);
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_global_load_lds(g, dst, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(g, dst, 1, 0, 0);
+#else
+    (void)g;
+    (void)lds_offset;
+#endif
+}
+
+// s_waitcnt with vmcnt <= N and the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Position of 16-byte column unit u in token row t (0..31) of a staged range:
+// u ^ swz(t), so that the operand reads below, four rows by four units per
+// half-wave, fall in distinct banks.
+__device__ __forceinline__ int swz(int t) { return 4 * ((t + (t >> 3)) & 3); }
+
+// LDS byte address of the 8 bytes lane `lane` hands to transposing read s of
+// the operand "8 tokens (tb .. tb + 7 of the stage) of column c0 + l % 32 of
+// the range at rng" for lane l.  In a group of 16 lanes, ds_read_b64_tr_b16
+// gives lane i half (i % 4) of the 8 bytes that lane 4 e + i / 4 addresses,
+// as its element e; so lane j addresses token tb + 4 s + j / 4, columns
+// c0 + 4 (j % 4) .. + 3, and lane i receives 4 tokens of column c0 + i.
+__device__ __forceinline__ uint32_t operand_addr(uint32_t rng, int c0, int tb, int lane, int s)
+{
+    const int g = lane >> 4, j = lane & 15;
+    const int cb = c0 + 16 * (g & 1), t = tb + 8 * (g >> 1) + (j >> 2) + 4 * s;
+    const int u = cb / 8 + ((j & 3) >> 1);
+    return rng + (uint32_t)(t * kRowBytes + ((u ^ swz(t)) * 16) + 8 * (j & 1));
+}
+
+// The four operands of one 16-token matrix-core step (a[m]: range I, columns
+// wi + 32 m; b[m]: range J, columns wj + 32 m), eight transposing reads.
+// They are issued in one asm block that waits for them itself: the compiler
+// knows nothing of what the builtin form reads and would otherwise wait for
+// every global-to-LDS load in flight before each read.
+__device__ __forceinline__ void step_operands(uint32_t slot, int wi, int wj, int tb, int lane, u32x4* a, u32x4* b)
+{
+    uint32_t ad[8];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            ad[2 * m + s] = operand_addr(slot, wi + 32 * m, tb, lane, s);
+            ad[4 + 2 * m + s] = operand_addr(slot + kRangeBytes, wj + 32 * m, tb, lane, s);
+        }
+    u32x2 r[8];
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+        : "memory");
+#else
+    for (int i = 0; i < 8; ++i)
+        r[i] = u32x2{ad[i], 0u};
+#endif
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        a[m] = u32x4{r[2 * m].x, r[2 * m].y, r[2 * m + 1].x, r[2 * m + 1].y};
+        b[m] = u32x4{r[4 + 2 * m].x, r[4 + 2 * m].y, r[4 + 2 * m + 1].x, r[4 + 2 * m + 1].y};
+    }
+}
+
 // Block id -> tile (bi, bj) owns S = X[:, 128 bi .. +128]^T X[:, 128 bj ..
 // +128]; wave w owns the 64 x 64 quarter (w / 2, w % 2) as 2 x 2 matrix-core
-// blocks.  The registers stay few enough for three blocks per CU (at
-// K = 4096, all 528 tiles resident at once), so H is read only after the
-// token loop, when the other blocks' loops overlap it.
-// Each step stages 64 token rows of X's two column ranges in LDS transposed,
-// [column][token], so that an operand (8 tokens of a column) is one 16-byte
-// read: wave w loads tokens 16 w .. 16 w + 15, lanes 0-31 four columns of the
-// I range and lanes 32-63 four of the J range (8-byte loads, 256 contiguous
-// bytes per token row per half-wave), transposes them in registers with byte
-// permutes and writes two 16-byte runs per column.  The next step's loads are
-// in flight while a step is multiplied; every load is issued whatever the
-// token count (tokens past T reload row 0 and are zeroed when staged), so
-// that the compiler waits for exactly the step it stages.  The decode flags
-// ride with the loads (lane l of a wave fetches its token l % 16) and are
-// read across the wave when staged.  Tokens past T, prefill tokens and
-// columns past K are zero.
-// Off the diagonal, S^T is added into H[J][I] through LDS, 32 rows of a
-// wave's quarter at a time, so that each H row is read and written as 64
+// blocks.
+// X goes from HBM/L2 straight into a three-slot LDS ring of 32-token stages,
+// untransposed ([range][token][128 columns], column units swizzled by row),
+// with global-to-LDS loads: per stage each wave issues four 1 KB loads (four
+// token rows of one range; 16 lanes per row) and one 64-byte load of the
+// stage's decode flags into its own corner of the slot, so every stage costs
+// each wave the same five loads and the waits are fixed counts.  Per stage a
+// wave waits for its own loads, meets the block at a barrier (no memory
+// fence: the wait already covers its loads into LDS), issues the loads of
+// the stage after next into the slot every wave has just finished reading,
+// and multiplies: operands come from transposing LDS reads, no register
+// staging.  Loads are issued whatever T is (tokens past T reload row T - 1;
+// columns past K reload column 0 and only reach entries never stored), and
+// tokens past T or flagged prefill are zeroed in both operands from a
+// wave-uniform bit word, so non-finite prefill rows cannot leak in.
+// Then H[I][J] += S, and off the diagonal H[J][I] += S^T through LDS, 32 rows
+// of a wave's quarter at a time, so that each H row is read and written as 64
 // consecutive floats.
 template <int DT>
 __global__ __launch_bounds__(256, 3) void calib_accumulate_kernel(const uint16_t* __restrict__ X,
-                                                               const uint8_t* __restrict__ decode, int T, int K,
-                                                               float* __restrict__ H)
+                                                                  const uint8_t* __restrict__ decode, int T, int K,
+                                                                  float* __restrict__ H)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kTile * kTPitch];   // [range][column][token]
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // kSlots * kSlotBytes, at LDS offset 0
+    lds_u8_t* const L = (lds_u8_t*)smem;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int bi, bj;
     tile_of(blockIdx.x, bi, bj);
     const int i0 = bi * kTile, j0 = bj * kTile;
     const int wi = (wave >> 1) * 64, wj = (wave & 1) * 64;
+
+    // Load role: instruction q of the wave is n = wave + 4 q: range n / 8,
+    // token rows 4 (n % 8) .. + 3; the lane takes row lane / 16 of them and
+    // LDS position lane % 16, i.e. column unit (lane % 16) ^ swz(row).
+    int scol[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int n = wave + 4 * q, r = n >> 3, t = 4 * (n & 7) + (lane >> 4);
+        const int col = (r == 0 ? i0 : j0) + 8 * ((lane & 15) ^ swz(t));
+        scol[q] = col < K ? col : 0;             // K % 8 == 0: a unit is in or out whole
+    }
+    const uint8_t* flags = decode ? decode : reinterpret_cast<const uint8_t*>(X);   // (read, then ignored)
+    auto issue = [&](int st) {
+        const int t0 = st * kTS;
+        const uint32_t slot = (uint32_t)((st % kSlots) * kSlotBytes);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = wave + 4 * q;
+            const int tok = min(t0 + 4 * (n & 7) + (lane >> 4), T - 1);
+            dma<16>(X + (size_t)tok * K + scol[q], slot + (n >> 3) * kRangeBytes + (n & 7) * 1024);
+        }
+        dma<1>(flags + min(t0 + lane, T - 1), slot + 2 * kRangeBytes + wave * 256);
+    };
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -119,60 +241,28 @@ __global__ __launch_bounds__(256, 3) void calib_accumulate_kernel(const uint16_t
             for (int v = 0; v < 16; ++v)
                 acc[m][n][v] = 0.f;
 
-    // Staging role: range r (0: columns I, 1: J), columns c4 .. c4 + 3 of it,
-    // tokens kTW wave .. kTW wave + kTW - 1 of the step.
-    const int r = lane >> 5, c4 = 4 * (lane & 31);
-    const int col = (r == 0 ? i0 : j0) + c4;
-    const bool col_ok = col < K;                   // K % 4 == 0: four columns in or out together
-    const uint32_t loff = 2u * (uint32_t)(col_ok ? col : 0);   // the lane's byte offset in a token row
-    const uint8_t* flags = decode ? decode : reinterpret_cast<const uint8_t*>(X);   // (read, then ignored)
-    struct Step {
-        u32x2 w[kTW];
-        uint32_t f;                                // decode flag of token (lane % kTW) of the wave's rows
-    };
-    auto load_step = [&](Step& st, int t0) {
+    auto consume = [&](int st) {
+        const int t0 = st * kTS;
+        const uint32_t slot = (uint32_t)((st % kSlots) * kSlotBytes);
+        const uint32_t fd = *(const lds_u32_t*)(L + slot + 2 * kRangeBytes + wave * 256 + (lane & 31) * 4);
+        const bool ok = t0 + (lane & 31) < T && (!decode || fd != 0u);
+        const uint32_t fw = (uint32_t)__builtin_amdgcn_ballot_w64(ok);   // bit e: token t0 + e enters H
 #pragma unroll
-        for (int e = 0; e < kTW; ++e) {
-            const int t = t0 + kTW * wave + e;  // wave-uniform: a scalar row base plus the lane's offset
-            const char* row = reinterpret_cast<const char*>(X) + (size_t)(t < T ? t : 0) * K * 2;
-            st.w[e] = *reinterpret_cast<const u32x2*>(row + loff);
-        }
-        const int tf = t0 + kTW * wave + (lane & (kTW - 1));
-        st.f = flags[tf < T ? tf : 0];
-    };
-    auto store_step = [&](const Step& st, int t0) {
-        uint32_t w[kTW][2];
-#pragma unroll
-        for (int e = 0; e < kTW; ++e) {
-            const int t = t0 + kTW * wave + e;
-            const bool live = col_ok && t < T && (!decode || __builtin_amdgcn_readlane((int)st.f, e) != 0);
-            w[e][0] = live ? st.w[e].x : 0u;
-            w[e][1] = live ? st.w[e].y : 0u;
-        }
-        // Column c4 + u (u = 0..3) takes half u % 2 of word u / 2 of each token.
-#pragma unroll
-        for (int g = 0; g < kTW / 8; ++g)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;   // high or low halves of two words
-                const uint32_t(*wg)[2] = w + 8 * g;
-                u32x4 o;
-                o.x = __builtin_amdgcn_perm(wg[1][u >> 1], wg[0][u >> 1], sel);
-                o.y = __builtin_amdgcn_perm(wg[3][u >> 1], wg[2][u >> 1], sel);
-                o.z = __builtin_amdgcn_perm(wg[5][u >> 1], wg[4][u >> 1], sel);
-                o.w = __builtin_amdgcn_perm(wg[7][u >> 1], wg[6][u >> 1], sel);
-                *reinterpret_cast<u32x4*>(&xs[(r * kTile + c4 + u) * kTPitch + kTW * wave + 8 * g]) = o;
-            }
-    };
-    auto multiply = [&]() {
-#pragma unroll
-        for (int k = 0; k < kTT / 16; ++k) {
-            const int tk = 16 * k + 8 * (lane >> 5);
+        for (int k = 0; k < kTS / 16; ++k) {
             u32x4 a[2], b[2];
+            step_operands(slot, wi, wj, 16 * k, lane, a, b);
+            if (fw != 0xFFFFFFFFu) {
+                const uint32_t bits = (fw >> (16 * k + 8 * (lane >> 5))) & 0xFFu;
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                a[m] = *reinterpret_cast<const u32x4*>(&xs[(wi + 32 * m + (lane & 31)) * kTPitch + tk]);
-                b[m] = *reinterpret_cast<const u32x4*>(&xs[(kTile + wj + 32 * m + (lane & 31)) * kTPitch + tk]);
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t mk = ((bits >> (2 * d)) & 1u ? 0x0000FFFFu : 0u) |
+                                        ((bits >> (2 * d + 1)) & 1u ? 0xFFFF0000u : 0u);
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        a[m][d] &= mk;
+                        b[m][d] &= mk;
+                    }
+                }
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
@@ -182,15 +272,20 @@ __global__ __launch_bounds__(256, 3) void calib_accumulate_kernel(const uint16_t
         }
     };
 
-    Step st;
-    load_step(st, 0);
-    for (int t0 = 0; t0 < T; t0 += kTT) {
-        __syncthreads();                          // the previous step's tiles are no longer read
-        store_step(st, t0);
-        __syncthreads();
-        load_step(st, t0 + kTT);                  // in flight during this step's products
-        multiply();
+    const int nst = (T + kTS - 1) / kTS;
+    issue(0);
+    issue(1);
+    for (int st = 0; st < nst; ++st) {
+        wait_vmcnt<5>();                          // this wave's loads of stage st have landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();             // every wave's have; all finished reading stage st - 1
+        asm volatile("" ::: "memory");
+        issue(st + 2);                            // into stage st - 1's slot
+        consume(st);
     }
+    wait_vmcnt<0>();                              // the ring's last loads (past T) have landed
+    __syncthreads();                              // and every wave is done with the ring
+
     // H[I][J] += the block's sums, one 32-row half of the wave's quarter at a
     // time (its 32 values read, then written: 32 consecutive columns per
     // half-wave), addressed from the tile's corner.
@@ -222,12 +317,12 @@ __global__ __launch_bounds__(256, 3) void calib_accumulate_kernel(const uint16_t
         return;
     // H[J][I] += S^T: rows j = 32 n + (lane % 32) of the wave's quarter go to
     // LDS as tq[j][i], then each of those 32 H rows is updated by all 64 lanes.
-    float* tq = reinterpret_cast<float*>(xs) + wave * 32 * kMPitch;
+    float* tq = reinterpret_cast<float*>(smem) + wave * 32 * kMPitch;
     float* const Hm = H + (size_t)j0 * K + i0;   // the mirror tile's corner
     const int ci = i0 + wi + lane;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-        __syncthreads();                          // xs (or the previous half) is no longer read
+        __syncthreads();                          // the previous half is no longer read
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -331,10 +426,10 @@ int nm_calib_accumulate(const void* X, const uint8_t* decode, int64_t T, int64_t
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (dtype == NM_FP16)
-        hipLaunchKernelGGL(calib_accumulate_kernel<NM_FP16>, dim3(tiles), dim3(256), 0, s,
+        hipLaunchKernelGGL(calib_accumulate_kernel<NM_FP16>, dim3(tiles), dim3(256), kSlots * kSlotBytes, s,
                            static_cast<const uint16_t*>(X), decode, (int)T, (int)K, H);
     else
-        hipLaunchKernelGGL(calib_accumulate_kernel<NM_BF16>, dim3(tiles), dim3(256), 0, s,
+        hipLaunchKernelGGL(calib_accumulate_kernel<NM_BF16>, dim3(tiles), dim3(256), kSlots * kSlotBytes, s,
                            static_cast<const uint16_t*>(X), decode, (int)T, (int)K, H);
     return launched();
 }
