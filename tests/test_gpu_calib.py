@@ -72,6 +72,27 @@ def test_calib_accumulate_onto_unsymmetric_h(nm, dt, T, K):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_calib_accumulate_nonfinite_prefill_rows_excluded(nm, dt):
+    """Prefill rows holding Inf and NaN do not reach H: rows flagged as
+    prefill contribute nothing, not 0 * Inf.  T = 100 puts flagged rows in
+    every 32-token stage, the partial last one included."""
+    T, K = 100, 264
+    X = I.activation_normal(T, K, TD[dt], I.seed_of("calNF", dt))
+    d = np.ones(T, np.uint8)
+    bad = [0, 5, 31, 32, 63, 70, 99]
+    d[bad] = 0
+    Xb = X.clone()
+    Xb[bad[0::2], :] = float("inf")
+    Xb[bad[1::2], 7] = float("nan")
+    Xb[bad[1::2], 100] = -float("inf")
+    H = nm.calib_accumulate(Xb.cuda(), torch.from_numpy(d).cuda()).cpu().numpy()
+    assert np.isfinite(H).all()
+    Href, A = oracle.calib_accumulate(bits(X), dt, decode=d)
+    ok, worst, idx = oracle.check_calib(H, Href, A)
+    assert ok, (worst, idx)
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
 def test_calib_accumulate_integer_exact(nm, dt):
     """Integer-valued rows: every partial sum is an integer below 2^24, so H
     must equal the exact sums in any order."""
