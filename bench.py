@@ -603,6 +603,7 @@ def main():
         "mlp_shapes": mlp,
         "extras": extras,
         "read_ceiling_gbs": round(ceiling, 1),
+        "pct_of_read_ceiling": round(100.0 * gbs / ceiling, 2) if ceiling else None,
         "copy_calibration_bytes": copy_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
