@@ -21,6 +21,7 @@
 // Its traffic is H's read and write (8 K^2 bytes).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "nm_decode.h"
@@ -424,14 +425,26 @@ int nm_calib_accumulate(const void* X, const uint8_t* decode, int64_t T, int64_t
     const unsigned nb = (unsigned)((K + kTile - 1) / kTile);
     const unsigned tiles = nb * (nb + 1) / 2;     // upper triangle, diagonal included
     hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    if (dtype == NM_FP16)
-        hipLaunchKernelGGL(calib_accumulate_kernel<NM_FP16>, dim3(tiles), dim3(256), kSlots * kSlotBytes, s,
-                           static_cast<const uint16_t*>(X), decode, (int)T, (int)K, H);
-    else
-        hipLaunchKernelGGL(calib_accumulate_kernel<NM_BF16>, dim3(tiles), dim3(256), kSlots * kSlotBytes, s,
-                           static_cast<const uint16_t*>(X), decode, (int)T, (int)K, H);
-    return launched();
+    // At most 2^30 rows per launch, so that the kernel's token arithmetic
+    // (which runs two 32-row stages past its rows) stays in 32 bits; the
+    // launches add into H one after another.
+    constexpr int64_t kMaxRows = int64_t(1) << 30;
+    for (int64_t t0 = 0; t0 < T; t0 += kMaxRows) {
+        const int Tc = (int)std::min<int64_t>(kMaxRows, T - t0);
+        const uint16_t* Xc = static_cast<const uint16_t*>(X) + t0 * K;
+        const uint8_t* dc = decode ? decode + t0 : nullptr;
+        (void)hipGetLastError();
+        if (dtype == NM_FP16)
+            hipLaunchKernelGGL(calib_accumulate_kernel<NM_FP16>, dim3(tiles), dim3(256), kSlots * kSlotBytes, s, Xc,
+                               dc, Tc, (int)K, H);
+        else
+            hipLaunchKernelGGL(calib_accumulate_kernel<NM_BF16>, dim3(tiles), dim3(256), kSlots * kSlotBytes, s, Xc,
+                               dc, Tc, (int)K, H);
+        const int st = launched();
+        if (st != NM_OK)
+            return st;
+    }
+    return NM_OK;
 }
 
 int nm_calib_keep_mask(const void* W, const float* h, int64_t h_stride, int64_t R, int64_t K, int N, int M, int dtype,
