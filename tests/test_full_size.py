@@ -112,8 +112,12 @@ def test_llama33_70b_layer(nm, name):
     check_rows(W, v, mk, x, y, 2, 4, "bf16", sample_rows(R, 4, k=12), yd)
 
 
-@pytest.mark.parametrize("B", [1, 2, 4, 8])
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32])
 def test_qwen3_32b_small_batch(nm, B):
+    """Each batch size bench.py times at the Qwen3-32B MLP shapes; 16 and 32
+    run the matrix-core kernels in their large-batch shapes (gate/up: two
+    waves of two tiles sharing x, two batch tiles; down: the staged kernel
+    above 16)."""
     for name, (R, K) in I.QWEN3_32B_MLP.items():
         W, x = make(R, K, "bf16", ("qwen3_32b_batch", name, B), B=B)
         v, mk = nm.pack(W, None, 2, 4)
