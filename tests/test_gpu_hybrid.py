@@ -53,6 +53,28 @@ def test_row_loss_and_choice_bitexact(nm, dt, n, m, mode):
         assert np.array_equal(flags.cpu().numpy(), oracle.hybrid_select(want, nd))
 
 
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("with_keep", [False, True])
+def test_row_loss_unaligned_inputs(nm, dt, with_keep):
+    """W 2 bytes and keep 1 byte past an aligned address (the call accepts
+    both): rows are then staged element by element, with the same sums."""
+    R, K, n, m = 300, 1040, 2, 4
+    W = I.weight(R, K, TD[dt], I.seed_of("hyU", dt))
+    buf = torch.empty(R * K + 8, dtype=TD[dt], device="cuda")
+    Wu = buf[1:1 + R * K].view(R, K)
+    Wu.copy_(W.cuda())
+    keep = kp = None
+    if with_keep:
+        keep = random_keep(R, K, n, m, I.seed_of("hyUk"))
+        kbuf = torch.empty(R * K + 16, dtype=torch.uint8, device="cuda")
+        kp = kbuf[1:1 + R * K].view(R, K)
+        kp.copy_(keep.cuda())
+    assert Wu.data_ptr() % 16 != 0 and (kp is None or kp.data_ptr() % 8 != 0)
+    loss = nm.hybrid_row_loss(Wu, n, m, keep=kp)
+    want = oracle.hybrid_row_loss(bits(W), n, m, dt, keep=None if keep is None else keep.numpy())
+    assert np.array_equal(loss.cpu().numpy(), want)
+
+
 def test_row_choice_ties_and_nan(nm):
     loss = torch.tensor([3.0, 1.0, 3.0, float("nan"), 0.0, 7.0, 1.0, 3.0], dtype=torch.float64)
     for nd in range(loss.numel() + 1):
