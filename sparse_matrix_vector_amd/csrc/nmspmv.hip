@@ -1554,62 +1554,101 @@ __global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, 
 // The Spense abstract (fifth page) splits a matrix into a 2:4-sparse and a
 // dense region; here the dense region is a set of whole rows, those whose
 // pruning loses most.  L_r = sum over the row's pruned columns of w^2 h[c],
-// one thread per row: groups in column order, pruned columns ascending, each
-// term (w*w)*h exact in double and one rounding per added term (explicit
-// round-to-nearest operations, no contraction), so the sum is the same
-// number the oracle forms.  The pruned columns are those the keep-mask drops,
+// added in column order (groups in column order, pruned columns ascending),
+// each term (w*w)*h exact in double and one rounding per added term
+// (explicit round-to-nearest operations, no contraction), so the sum is the
+// same number the oracle forms.  The pruned columns are those the keep-mask drops,
 // or those the top-N magnitude rule (nm_pack's) drops.  Keep-mask groups
 // without N kept, or NaN weights under the magnitude rule, set the status
 // word (as nm_pack's check does).
+constexpr int kLossRows = 64;    // rows per block
+constexpr int kLossCols = 64;    // columns per chunk
+
+// Block of 256 threads, 64 rows.  Per 64-column chunk, every thread computes
+// the terms of 16 columns (whole groups: M divides 16) of one row -- thread t
+// takes row t / 4, columns 16 (t % 4) .. + 15 -- into LDS with a mask of the
+// pruned ones; then thread t < 64 adds its row's pruned terms in column
+// order.  Only the adds form a dependent chain; the decoding, the top-N rule
+// and the products run in parallel over the chunk (one thread per row and
+// column run would leave the chip almost idle: R / 64 waves in all).
 template <int DT>
 __global__ __launch_bounds__(256) void hybrid_loss_kernel(const uint16_t* __restrict__ W, const uint8_t* __restrict__ keep,
                                                           const float* __restrict__ h, int64_t h_stride, int R, int K,
                                                           int N, int M, double* __restrict__ loss,
                                                           uint32_t* __restrict__ status)
 {
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= R)
-        return;
-    const uint16_t* w = W + (size_t)r * K;
-    const uint8_t* kp = keep ? keep + (size_t)r * K : nullptr;
+    __shared__ double terms[kLossRows][kLossCols + 1];   // +1: the fold's column reads fall in distinct banks
+    __shared__ __attribute__((aligned(8))) uint16_t pruned[kLossRows][4];   // bit j of [row][q]: column 16 q + j is pruned
+    __shared__ double hs[kLossCols];
+    const int t = threadIdx.x;
+    const int r0 = blockIdx.x * kLossRows;
+    const int lr = t >> 2, q = t & 3, r = r0 + lr;
     double l = 0.0;
     uint32_t bad = 0;
-    for (int g = 0; g < K / M; ++g) {
-        uint32_t wv[8];
-        for (int j = 0; j < M; ++j)
-            wv[j] = w[g * M + j];
-        uint32_t kept = 0;
-        if (kp) {
-            int cnt = 0;
-            for (int j = 0; j < M; ++j) {
-                const uint32_t k = kp[g * M + j] != 0;
-                kept |= k << j;
-                cnt += (int)k;
-            }
-            if (cnt != N)
-                bad |= kStatusBadMask;
-        } else {
-            for (int j = 0; j < M; ++j) {
-                const uint32_t mj = wv[j] & 0x7FFFu;
-                if (mj > (DT == NM_FP16 ? 0x7C00u : 0x7F80u))
-                    bad |= kStatusNaN;
-                int beats = 0;
-                for (int k = 0; k < M; ++k) {
-                    const uint32_t mk = wv[k] & 0x7FFFu;
-                    beats += (mk > mj) || (mk == mj && k < j);
+    for (int c0 = 0; c0 < K; c0 += kLossCols) {
+        const int cw = min(kLossCols, K - c0);           // a multiple of 8 (K % 8 == 0)
+        __syncthreads();                                 // the previous chunk is folded
+        if (t < cw)
+            hs[t] = h ? nm_decode::f32_to_f64(h[(int64_t)(c0 + t) * h_stride]) : 1.0;
+        __syncthreads();
+        uint32_t pm = 0;
+        if (r < R) {
+            const uint16_t* w = W + (size_t)r * K + c0;
+            const uint8_t* kp = keep ? keep + (size_t)r * K + c0 : nullptr;
+            for (int g = 16 * q; g < 16 * q + 16 && g < cw; g += M) {
+                uint32_t wv[8];
+                for (int j = 0; j < M; ++j)
+                    wv[j] = w[g + j];
+                uint32_t kept = 0;
+                if (kp) {
+                    int cnt = 0;
+                    for (int j = 0; j < M; ++j) {
+                        const uint32_t k = kp[g + j] != 0;
+                        kept |= k << j;
+                        cnt += (int)k;
+                    }
+                    if (cnt != N)
+                        bad |= kStatusBadMask;
+                } else {
+                    for (int j = 0; j < M; ++j) {
+                        const uint32_t mj = wv[j] & 0x7FFFu;
+                        if (mj > (DT == NM_FP16 ? 0x7C00u : 0x7F80u))
+                            bad |= kStatusNaN;
+                        int beats = 0;
+                        for (int k = 0; k < M; ++k) {
+                            const uint32_t mk = wv[k] & 0x7FFFu;
+                            beats += (mk > mj) || (mk == mj && k < j);
+                        }
+                        kept |= (uint32_t)(beats < N) << j;
+                    }
                 }
-                kept |= (uint32_t)(beats < N) << j;
+                for (int j = 0; j < M; ++j) {
+                    if ((kept >> j) & 1u)
+                        continue;
+                    const double v = nm_decode::w_to_f64<DT>(wv[j]);
+                    terms[lr][g + j] = __dmul_rn(__dmul_rn(v, v), hs[g + j]);
+                    pm |= 1u << (g + j - 16 * q);
+                }
             }
         }
-        for (int j = 0; j < M; ++j) {
-            if ((kept >> j) & 1u)
-                continue;
-            const double v = nm_decode::w_to_f64<DT>(wv[j]);
-            const double hv = h ? nm_decode::f32_to_f64(h[(int64_t)(g * M + j) * h_stride]) : 1.0;
-            l = __dadd_rn(l, __dmul_rn(__dmul_rn(v, v), hv));
+        pruned[lr][q] = (uint16_t)pm;
+        __syncthreads();
+        if (t < kLossRows && r0 + t < R) {
+            const uint64_t pmask = *reinterpret_cast<const uint64_t*>(&pruned[t][0]);   // bit c: column c pruned
+            for (int cb = 0; cb < cw; cb += 16) {    // 16 terms read together, then added in order
+                double tv[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    tv[j] = terms[t][cb + j];
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if ((pmask >> (cb + j)) & 1u)
+                        l = __dadd_rn(l, tv[j]);
+            }
         }
     }
-    loss[r] = l;
+    if (t < kLossRows && r0 + t < R)
+        loss[r0 + t] = l;
     if (bad)
         atomicOr(status, bad);
 }
@@ -2712,7 +2751,7 @@ int nm_hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int64
     if (R == 0)
         return NM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const unsigned grid = (unsigned)((R + 255) / 256);
+    const unsigned grid = (unsigned)((R + kLossRows - 1) / kLossRows);
     return with_status(s, [&](uint32_t* status) {
         if (dtype == NM_FP16)
             hipLaunchKernelGGL(hybrid_loss_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const uint16_t*)W, keep, h,
