@@ -441,7 +441,7 @@ int orc_calib_keep(const uint16_t* W, const double* h, int64_t R, int64_t K, int
                 int64_t c = g * M + j;
                 double w = orc_to_double(W[r * K + c], dtype);
                 double s = w * w * h[c];
-                sal[j] = isnan(s) ? -1.0 : s;
+                sal[j] = isnan(s) ? -INFINITY : s;
                 taken[j] = 0;
                 keep[r * K + c] = 0;
             }
@@ -510,10 +510,10 @@ int orc_hybrid_select(const double* loss, int64_t R, int64_t n_dense, uint8_t* f
     if (R < 0 || n_dense < 0 || n_dense > R)
         return ORC_BAD_SHAPE;
     for (int64_t r = 0; r < R; ++r) {
-        double lr = isnan(loss[r]) ? -1.0 : loss[r];
+        double lr = isnan(loss[r]) ? -INFINITY : loss[r];
         int64_t above = 0;
         for (int64_t s = 0; s < R; ++s) {
-            double ls = isnan(loss[s]) ? -1.0 : loss[s];
+            double ls = isnan(loss[s]) ? -INFINITY : loss[s];
             if (ls > lr || (ls == lr && s < r))
                 ++above;
         }

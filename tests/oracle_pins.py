@@ -529,6 +529,10 @@ def pin_calib_keep(seed=8):
     assert keep.tolist() == [[0, 1, 0, 1, 0, 1, 0, 1]]
     keep = oracle.calib_keep(W, np.ones(8, np.float32), 3, 4, "fp16")
     assert keep.tolist() == [[1, 1, 0, 1, 1, 1, 0, 1]]
+    # ... negative saliencies included: NaN, -2, -3, -1 keep columns 3 and 1 (then a group of equal ones)
+    W = np.array([[0x7E00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00]], np.uint16)
+    keep = oracle.calib_keep(W, np.array([1.0, -2.0, -3.0, -1.0, 1.0, 1.0, 1.0, 1.0], np.float32), 2, 4, "fp16")
+    assert keep.tolist() == [[0, 1, 0, 1, 1, 1, 0, 0]]
 
 
 def pin_hybrid(seed=9):
@@ -563,12 +567,15 @@ def pin_hybrid(seed=9):
                 kept = _bitmap_to_keep(mk, K)[0].astype(bool)
                 assert loss1[r] == math.fsum(Wv[r, c] ** 2 for c in range(K) if not kept[c]) or \
                     abs(loss1[r] - math.fsum(Wv[r, c] ** 2 for c in range(K) if not kept[c])) <= 1e-12 * loss1[r]
-    loss = np.array([3.0, 1.0, 3.0, float("nan"), 0.0, 7.0, 1.0])
-    for nd in range(len(loss) + 1):
-        order = sorted(range(len(loss)), key=lambda r: (-(loss[r] if loss[r] == loss[r] else -1.0), r))
-        want = np.zeros(len(loss), np.uint8)
-        want[order[:nd]] = 1
-        assert np.array_equal(oracle.hybrid_select(loss, nd), want)
+    # NaN ranks below every number, negative and -inf included (lower row first among equals)
+    for loss in (np.array([3.0, 1.0, 3.0, float("nan"), 0.0, 7.0, 1.0]),
+                 np.array([-5.0, float("nan"), -0.5, 2.0, -float("inf"), -5.0, float("nan")])):
+        for nd in range(len(loss) + 1):
+            order = sorted(range(len(loss)), key=lambda r: (-(loss[r] if loss[r] == loss[r] else -math.inf), r))
+            want = np.zeros(len(loss), np.uint8)
+            want[order[:nd]] = 1
+            assert np.array_equal(oracle.hybrid_select(loss, nd), want)
+    assert list(oracle.hybrid_select(np.array([float("nan"), -2.0]), 1)) == [0, 1]
     # the product reduces to the plain ones
     R, K = 6, 64
     W = to_bits(np.round(rng.normal(0, 1, (R, K)) * 16) / 16, "fp16")

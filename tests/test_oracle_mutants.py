@@ -37,7 +37,9 @@ MUTANTS = [
     ("saliency_abs_w", "double s = w * w * h[c];", "double s = fabs(w) * h[c];"),
     ("saliency_ignores_h", "double s = w * w * h[c];", "double s = w * w;"),
     ("saliency_tie_to_highest", "(best < 0 || sal[j] > sal[best])", "(best < 0 || sal[j] >= sal[best])"),
-    ("saliency_nan_ranks_high", "sal[j] = isnan(s) ? -1.0 : s;", "sal[j] = isnan(s) ? 1e300 : s;"),
+    ("saliency_nan_ranks_high", "sal[j] = isnan(s) ? -INFINITY : s;", "sal[j] = isnan(s) ? 1e300 : s;"),
+    ("saliency_nan_at_minus_one", "sal[j] = isnan(s) ? -INFINITY : s;", "sal[j] = isnan(s) ? -1.0 : s;"),
+    ("row_loss_nan_at_minus_one", "double lr = isnan(loss[r]) ? -INFINITY : loss[r];", "double lr = isnan(loss[r]) ? -1.0 : loss[r];"),
     ("hybrid_loss_counts_kept", "                if (chosen[j])\n                    continue;\n                double v",
      "                if (!chosen[j])\n                    continue;\n                double v"),
     ("hybrid_loss_ignores_h", "double hv = h ? h[g * M + j] : 1.0;", "double hv = 1.0;"),
