@@ -222,8 +222,8 @@ int nm_hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int64
                        int M, int dtype, double* loss, void* stream);
 
 /* nm_hybrid_select_rows -- flags[r] = 1 for the n_dense (0..R) rows of largest
- * loss, 0 elsewhere; a NaN loss ranks lowest, the lower row first among
- * equals.  loss [R] double (8-byte aligned), flags [R] bytes.  Enqueues. */
+ * loss, 0 elsewhere; a NaN loss ranks below every number (-inf included),
+ * the lower row first among equals.  loss [R] double (8-byte aligned), flags [R] bytes.  Enqueues. */
 int nm_hybrid_select_rows(const double* loss, int64_t R, int64_t n_dense, uint8_t* flags, void* stream);
 
 /*

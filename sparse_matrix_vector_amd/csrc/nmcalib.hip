@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, 3) void calib_accumulate_kernel(const uint16_t
 
 // One thread per (row, 8 columns): two 4-groups or one 8-group.  Saliency
 // w^2 h is exact in double (w^2 has at most 22 significant bits, h 24); a NaN
-// saliency ranks below every other.  Column j is kept when fewer than N group
+// saliency ranks below every number.  Column j is kept when fewer than N group
 // members beat it: larger saliency, or equal saliency at a lower column.
 template <int DT>
 __global__ __launch_bounds__(256) void calib_keep_kernel(const u32x4* __restrict__ W, const float* __restrict__ h,
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void calib_keep_kernel(const u32x4* __restrict
         const double w = nm_decode::w_to_f64<DT>((words[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
         const double hv = nm_decode::f32_to_f64(h[(c0 + e) * h_stride]);
         const double v = w * w * hv;
-        s[e] = v != v ? -1.0 : v;
+        s[e] = v != v ? -__builtin_inf() : v;
     }
     uint32_t lo = 0, hi = 0;
 #pragma unroll

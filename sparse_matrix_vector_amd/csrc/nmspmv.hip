@@ -1653,32 +1653,38 @@ __global__ __launch_bounds__(256) void hybrid_loss_kernel(const uint16_t* __rest
         atomicOr(status, bad);
 }
 
-// flags[r] = 1 for the n_dense rows of largest loss (a NaN loss ranks lowest,
-// the lower row first among equals): row r's rank counts the rows ahead of
-// it, against 256-row tiles of the losses staged in LDS.
+// flags[r] = 1 for the n_dense rows of largest loss (a NaN loss ranks below
+// every number, the lower row first among equals): row r's rank counts the
+// rows ahead of it, against 256-row tiles of the losses staged in LDS.  A
+// block takes 64 rows, four threads per row, each counting a quarter of every
+// tile; the four counts add up exactly in any order.
 __global__ __launch_bounds__(256) void hybrid_select_kernel(const double* __restrict__ loss, int R, int n_dense,
                                                             uint8_t* __restrict__ flags)
 {
     __shared__ double tile[256];
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    __shared__ int part[256];
+    const int t = threadIdx.x, q = t & 3;
+    const int r = blockIdx.x * 64 + (t >> 2);
     const double lr0 = r < R ? loss[r] : 0.0;
-    const double lr = lr0 != lr0 ? -1.0 : lr0;
+    const double lr = lr0 != lr0 ? -__builtin_inf() : lr0;
     int above = 0;
     for (int s0 = 0; s0 < R; s0 += 256) {
         __syncthreads();
-        if (s0 + (int)threadIdx.x < R) {
-            const double v = loss[s0 + threadIdx.x];
-            tile[threadIdx.x] = v != v ? -1.0 : v;
+        if (s0 + t < R) {
+            const double v = loss[s0 + t];
+            tile[t] = v != v ? -__builtin_inf() : v;
         }
         __syncthreads();
         const int ns = min(256, R - s0);
-        for (int k = 0; k < ns; ++k) {
+        for (int k = q; k < ns; k += 4) {
             const double ls = tile[k];
             above += (ls > lr) || (ls == lr && s0 + k < r);
         }
     }
-    if (r < R)
-        flags[r] = above < n_dense ? 1 : 0;
+    part[t] = above;
+    __syncthreads();
+    if (q == 0 && r < R)
+        flags[r] = part[t] + part[t + 1] + part[t + 2] + part[t + 3] < n_dense ? 1 : 0;
 }
 
 // One block: the rows flagged dense, in order, to rows_dense (at most n_dense
@@ -2772,7 +2778,7 @@ int nm_hybrid_select_rows(const double* loss, int64_t R, int64_t n_dense, uint8_
         return NM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(hybrid_select_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, loss, (int)R,
+    hipLaunchKernelGGL(hybrid_select_kernel, dim3((unsigned)((R + 63) / 64)), dim3(256), 0, s, loss, (int)R,
                        (int)n_dense, flags);
     return hip_status(hipGetLastError());
 }

@@ -175,6 +175,20 @@ def test_calib_keep_mask_nan_and_full_h(nm):
     assert keep[0, 0] == 0 and keep[1, 4:8].tolist() == [1, 1, 0, 0]
 
 
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+def test_calib_keep_mask_negative_saliency_and_nan(nm, n, m):
+    """A caller's h may hold negative values: NaN saliencies still rank below
+    every number, negative ones included."""
+    R, K = 6, 64
+    W = I.weight(R, K, torch.bfloat16, I.seed_of("ckNeg", n, m))
+    W[0, 0] = float("nan")
+    W[2, 8:12] = float("nan")
+    h = (np.random.default_rng(17).random(K) * 4 - 3).astype(np.float32)   # mostly negative
+    keep = nm.calib_keep_mask(W.cuda(), torch.from_numpy(h).cuda(), n, m).cpu().numpy()
+    assert np.array_equal(keep, oracle.calib_keep(bits(W), h, n, m, "bf16"))
+    assert keep[0, 0] == 0
+
+
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
 def test_calibrated_pack_and_spmv(nm, dt):
     """The offline flow end to end on a Llama-3.1-8B-shaped layer slice:

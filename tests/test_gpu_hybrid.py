@@ -75,11 +75,27 @@ def test_row_loss_unaligned_inputs(nm, dt, with_keep):
     assert np.array_equal(loss.cpu().numpy(), want)
 
 
-def test_row_choice_ties_and_nan(nm):
-    loss = torch.tensor([3.0, 1.0, 3.0, float("nan"), 0.0, 7.0, 1.0, 3.0], dtype=torch.float64)
+@pytest.mark.parametrize("values", [
+    [3.0, 1.0, 3.0, float("nan"), 0.0, 7.0, 1.0, 3.0],
+    [-5.0, float("nan"), -0.5, 2.0, -float("inf"), -5.0, float("nan"), -1.0],   # NaN below negatives and -inf
+])
+def test_row_choice_ties_and_nan(nm, values):
+    loss = torch.tensor(values, dtype=torch.float64)
     for nd in range(loss.numel() + 1):
         got = nm.hybrid_select_rows(loss.cuda(), nd).cpu().numpy()
         assert np.array_equal(got, oracle.hybrid_select(loss.numpy(), nd)), nd
+
+
+def test_row_choice_many_rows_all_partitions(nm):
+    """1000 rows (16 blocks, the last partial), many equal losses, NaNs and
+    negatives: every count of dense rows matches the oracle."""
+    g = np.random.default_rng(21)
+    loss = np.round(g.normal(0, 2, 1000), 1)
+    loss[g.random(1000) < 0.05] = np.nan
+    lt = torch.from_numpy(loss).cuda()
+    for nd in (0, 1, 63, 64, 65, 500, 999, 1000):
+        got = nm.hybrid_select_rows(lt, nd).cpu().numpy()
+        assert np.array_equal(got, oracle.hybrid_select(loss, nd)), nd
 
 
 def test_row_loss_errors(nm):
