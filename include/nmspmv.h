@@ -246,8 +246,8 @@ int nm_hybrid_pack(const void* W, const uint8_t* keep, const uint8_t* flags, int
  * does.  The lists must partition 0..R-1 (as nm_hybrid_pack writes them);
  * otherwise y is unspecified, but entries are clamped into 0..R-1, never
  * written out of bounds.  Rules as for nm_spmv (x [B][K], y [B][R], B <= 32).
- * With one vector and 2:4 or 4:8 rows (K % 16 == 0) both parts usually run
- * in a single launch.  Enqueues.
+ * With one to three vectors and 2:4 or 4:8 rows (K % 16 == 0) both parts
+ * usually run in a single launch.  Enqueues.
  */
 int nm_spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows_sparse, const void* W_dense,
                    const int32_t* rows_dense, int64_t n_dense, int64_t R, int64_t K, int N, int M, int dtype,

@@ -2171,18 +2171,18 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
     return hip_status(hipGetLastError());
 }
 
-// A hybrid matrix's sparse rows (PS, RS of them) and dense rows (PD, RD) at a
-// single x vector in one hybrid_rowslice_kernel launch.  It applies when the
-// sparse rows get a row-slice plan (taken with at least two rows per block)
-// with an even number of rows per block (the dense rows take half as many,
-// over twice the slices); *launched is false, and nothing is launched,
-// otherwise.
-template <int F, int DT>
+// A hybrid matrix's sparse rows (PS, RS of them) and dense rows (PD, RD) at NB
+// x vectors (1 to 3: where both parts run on the row-slice kernel) in one
+// hybrid_rowslice_kernel launch.  It applies when the sparse rows get a
+// row-slice plan (taken with at least two rows per block) with an even number
+// of rows per block (the dense rows take half as many, over twice the
+// slices); *launched is false, and nothing is launched, otherwise.
+template <int F, int DT, int NB>
 int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS, int RD, int K, hipStream_t s,
                         bool* launched)
 {
     *launched = false;
-    Plan P = plan_for<F>(RS, K, 1, false);
+    Plan P = plan_for<F>(RS, K, NB, false);
     if (P.kind == 1 && P.rpb == 1 && g_env.rpb == 0 && P.S <= 8) {
         // Few sparse rows: the plan went to one row per block to keep two
         // blocks per CU; here the dense rows add blocks of their own, so take
@@ -2190,7 +2190,7 @@ int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS,
         P.rpb = 2;
         P.threads = 2 * P.S * kWave;
         P.grid = (unsigned)((RS + 1) / 2);
-        P.lds = (size_t)table_units<F>() * sizeof(u32x4) + (size_t)K * 2 + (size_t)P.rpb * P.S * 4;
+        P.lds = (size_t)table_units<F>() * sizeof(u32x4) + (size_t)NB * K * 2 + (size_t)P.rpb * P.S * NB * 4;
     }
     if (P.kind != 1 || P.rpb < 2 || P.rpb % 2 != 0)
         return NM_OK;
@@ -2198,17 +2198,21 @@ int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS,
     const int64_t sblocks = P.grid, blocks = sblocks + (RD + dense_rpb - 1) / dense_rpb;
     const u32x4* x4 = static_cast<const u32x4*>(x);
     (void)hipGetLastError();
-#define NM_HYB_XU(CPL, XU)                                                                                      \
-    hipLaunchKernelGGL((hybrid_rowslice_kernel<F, DT, 1, CPL, XU>), dim3((unsigned)blocks), dim3(P.threads), P.lds, \
+#define NM_HYB_XU(CPL, XU)                                                                                       \
+    hipLaunchKernelGGL((hybrid_rowslice_kernel<F, DT, NB, CPL, XU>), dim3((unsigned)blocks), dim3(P.threads), P.lds, \
                        s, PS, PD, x4, RS, RD, K, P.S, P.rpb, (int)sblocks)
-#define NM_HYB(CPL)                 \
-    do {                            \
-        if (P.xu == 1)              \
-            NM_HYB_XU(CPL, 1);      \
-        else if (P.xu == 2)         \
-            NM_HYB_XU(CPL, 2);      \
-        else                        \
-            NM_HYB_XU(CPL, 4);      \
+#define NM_HYB(CPL)                             \
+    do {                                        \
+        if constexpr (NB == 1) {                \
+            if (P.xu == 1)                      \
+                NM_HYB_XU(CPL, 1);              \
+            else if (P.xu == 2)                 \
+                NM_HYB_XU(CPL, 2);              \
+            else                                \
+                NM_HYB_XU(CPL, 4);              \
+        } else {                                \
+            NM_HYB_XU(CPL, 4);                  \
+        }                                       \
     } while (0)
     switch (P.cpl) {
     case 1: NM_HYB(1); break;
@@ -2226,12 +2230,24 @@ int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS,
     return hip_status(hipGetLastError());
 }
 
-template <int F>
-int launch_hybrid_fused_dt(int dtype, const Parts& PS, const Parts& PD, const void* x, int RS, int RD, int K,
+template <int F, int DT>
+int launch_hybrid_fused_nb(int B, const Parts& PS, const Parts& PD, const void* x, int RS, int RD, int K,
                            hipStream_t s, bool* launched)
 {
-    return dtype == NM_FP16 ? launch_hybrid_fused<F, NM_FP16>(PS, PD, x, RS, RD, K, s, launched)
-                            : launch_hybrid_fused<F, NM_BF16>(PS, PD, x, RS, RD, K, s, launched);
+    switch (B) {
+    case 1: return launch_hybrid_fused<F, DT, 1>(PS, PD, x, RS, RD, K, s, launched);
+    case 2: return launch_hybrid_fused<F, DT, 2>(PS, PD, x, RS, RD, K, s, launched);
+    case 3: return launch_hybrid_fused<F, DT, 3>(PS, PD, x, RS, RD, K, s, launched);
+    default: *launched = false; return NM_OK;
+    }
+}
+
+template <int F>
+int launch_hybrid_fused_dt(int dtype, int B, const Parts& PS, const Parts& PD, const void* x, int RS, int RD, int K,
+                           hipStream_t s, bool* launched)
+{
+    return dtype == NM_FP16 ? launch_hybrid_fused_nb<F, NM_FP16>(B, PS, PD, x, RS, RD, K, s, launched)
+                            : launch_hybrid_fused_nb<F, NM_BF16>(B, PS, PD, x, RS, RD, K, s, launched);
 }
 
 // ---- host: argument rules ------------------------------------------------------
@@ -2866,14 +2882,15 @@ int nm_spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows
     if (K == 0)
         return launch_zero(y, (int64_t)B * R, s);
     const bool tuned = K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8));
-    if (B == 1 && Rs > 0 && n_dense > 0 && tuned) {
+    if (B <= 3 && Rs > 0 && n_dense > 0 && tuned) {
         std::call_once(g_env_once, read_env);
         if (g_env.hybrid_split != 1) {
             const Parts PS = mapped_part(values, masks, rows_sparse, Rs, R, y);
             const Parts PD = mapped_part(W_dense, nullptr, rows_dense, n_dense, R, y);
             bool launched = false;
-            st = M == 4 ? launch_hybrid_fused_dt<kNM24>(dtype, PS, PD, x, (int)Rs, (int)n_dense, (int)K, s, &launched)
-                        : launch_hybrid_fused_dt<kNM48>(dtype, PS, PD, x, (int)Rs, (int)n_dense, (int)K, s, &launched);
+            st = M == 4 ? launch_hybrid_fused_dt<kNM24>(dtype, B, PS, PD, x, (int)Rs, (int)n_dense, (int)K, s, &launched)
+                        : launch_hybrid_fused_dt<kNM48>(dtype, B, PS, PD, x, (int)Rs, (int)n_dense, (int)K, s,
+                                                        &launched);
             if (launched || st != NM_OK)
                 return st;
         }

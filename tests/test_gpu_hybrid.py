@@ -136,7 +136,7 @@ def test_hybrid_pack_and_spmv(nm, dt, n, m, K, B, frac):
     assert ok, (worst, idx)
 
 
-# Single-vector shapes whose sparse and dense rows run in one launch: one
+# Shapes (at one to three vectors) whose sparse and dense rows run in one launch: one
 # slice (K = 1040, 4096), two (K = 8192; dense rows at four), four (K = 18432,
 # or few rows; dense rows at eight, one per block); few sparse rows (taken two
 # per block); ragged row counts on both sides.
@@ -149,10 +149,11 @@ def test_hybrid_pack_and_spmv(nm, dt, n, m, K, B, frac):
     ("fp16", 2, 4, 4096, 1024, 0.05),           # few sparse rows: two per block in the one launch
     ("bf16", 4, 8, 1040, 600, 0.2),
 ])
-def test_hybrid_one_launch_shapes(nm, dt, n, m, K, R, frac):
+@pytest.mark.parametrize("B", [1, 2, 3])
+def test_hybrid_one_launch_shapes(nm, dt, n, m, K, R, frac, B):
     tdt = TD[dt]
     W = I.weight(R, K, tdt, I.seed_of("h1W", dt, n, m, K, R), device="cuda")
-    x = I.activation_normal(1, K, tdt, I.seed_of("h1x", dt, K), device="cuda", outlier_frac=0.01)
+    x = I.activation_normal(B, K, tdt, I.seed_of("h1x", dt, K, B), device="cuda", outlier_frac=0.01)
     nd = int(round(frac * R))
     flags = nm.hybrid_select_rows(nm.hybrid_row_loss(W, n, m), nd)
     hyb = nm.hybrid_pack(W, flags, nd, n, m)
