@@ -1787,6 +1787,22 @@ int cu_count()
     return g_cu_count[dev];
 }
 
+// Lets `kernel` take up to the CU's LDS as dynamic shared memory, once per
+// kernel and device (the attribute is set for the current device);
+// `raised` is the kernel's own array of per-device flags.
+int allow_full_lds(const void* kernel, bool* raised)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return NM_ERR_HIP;
+    if (!raised[dev]) {
+        if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
+            return NM_ERR_HIP;
+        raised[dev] = true;
+    }
+    return NM_OK;
+}
+
 struct Plan {
     int kind = 0;            // 1 row-slice, 3 stream
     int S = 1, rpb = 1, cpl = 1, xu = 4, threads = 256, tile_cols = 0;
@@ -1981,13 +1997,9 @@ int launch_mfma_nt(const Parts& parts, const void* x, int R, int K, int B, hipSt
 {
     const Plan P = plan_mfma_stage<F>(R, K, NT);
     if (P.lds > 64 * 1024) {
-        static bool raised = false;              // once per instantiation
-        if (!raised) {
-            if (hipFuncSetAttribute((const void*)mfma_stage_kernel<F, DT, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    kLdsMax) != hipSuccess)
-                return NM_ERR_HIP;
-            raised = true;
-        }
+        static bool raised[64] = {};             // per device, once per instantiation
+        if (allow_full_lds((const void*)mfma_stage_kernel<F, DT, NT>, raised) != NM_OK)
+            return NM_ERR_HIP;
     }
     (void)hipGetLastError();
     hipLaunchKernelGGL((mfma_stage_kernel<F, DT, NT>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
@@ -2059,13 +2071,9 @@ template <int F, int DT, int TW, int NT, bool SHX>
 int launch_mfma_ring_k(const Plan& P, const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
     if (P.lds > 64 * 1024) {
-        static bool raised = false;              // once per instantiation
-        if (!raised) {
-            if (hipFuncSetAttribute((const void*)mfma_ring_kernel<F, DT, TW, NT, SHX>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
-                return NM_ERR_HIP;
-            raised = true;
-        }
+        static bool raised[64] = {};             // per device, once per instantiation
+        if (allow_full_lds((const void*)mfma_ring_kernel<F, DT, TW, NT, SHX>, raised) != NM_OK)
+            return NM_ERR_HIP;
     }
     (void)hipGetLastError();
     hipLaunchKernelGGL((mfma_ring_kernel<F, DT, TW, NT, SHX>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
@@ -2157,13 +2165,9 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
 #undef NM_SLICE_XU
     } else {
         if (P.lds > 64 * 1024) {
-            static bool raised = false;          // once per instantiation
-            if (!raised) {
-                if (hipFuncSetAttribute((const void*)stream_kernel<F, DT, NB, 4>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
-                    return NM_ERR_HIP;
-                raised = true;
-            }
+            static bool raised[64] = {};         // per device, once per instantiation
+            if (allow_full_lds((const void*)stream_kernel<F, DT, NB, 4>, raised) != NM_OK)
+                return NM_ERR_HIP;
         }
         hipLaunchKernelGGL((stream_kernel<F, DT, NB, 4>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K,
                            P.tile_cols);
