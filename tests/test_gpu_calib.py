@@ -138,6 +138,30 @@ def test_calib_accumulate_full_size_sampled(nm):
     assert ok, (worst, idx)
 
 
+def test_calib_accumulate_largest_k(nm):
+    """K = 65536, the largest the call accepts: a 16 GB H, 131328 upper-
+    triangle tiles; entries H[S][S] for sampled columns S (both sides of the
+    diagonal, the last tile included) against the oracle on X[:, S]."""
+    T, K = 40, 65536
+    X = I.activation_normal(T, K, torch.bfloat16, I.seed_of("calK"), device="cuda")
+    d = np.ones(T, np.uint8)
+    d[:3] = 0
+    H = torch.zeros((K, K), dtype=torch.float32, device="cuda")
+    H[0, K - 1] = 2.0                              # prior contents, off the diagonal
+    H[K - 1, 0] = -3.0
+    nm.calib_accumulate(X, torch.from_numpy(d).cuda(), H=H)
+    S = np.sort(np.random.default_rng(31).choice(K, size=48, replace=False))
+    S[0], S[-1] = 0, K - 1
+    Hs = H[torch.from_numpy(S).cuda()][:, torch.from_numpy(S).cuda()].cpu().numpy()
+    del H
+    torch.cuda.empty_cache()
+    H0 = np.zeros((len(S), len(S)), np.float64)
+    H0[0, -1], H0[-1, 0] = 2.0, -3.0
+    Href, A = oracle.calib_accumulate(bits(X)[:, S], "bf16", decode=d, H=H0)
+    ok, worst, idx = oracle.check_calib(Hs, Href, A, H0=H0)
+    assert ok, (worst, idx)
+
+
 def test_calib_accumulate_empty(nm):
     H = torch.full((16, 16), 3.0, device="cuda")
     nm.calib_accumulate(torch.empty((0, 16), dtype=torch.float16, device="cuda"), None, H=H)

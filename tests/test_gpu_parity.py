@@ -332,6 +332,12 @@ def test_gemv_dense_multi(nm, dt, Rs, K, B):
         assert ok, (worst, idx)
 
 
+def test_spmv_very_long_rows(nm):
+    """K = 2^20: x (2 MB) runs through the stream kernel in many K-tiles;
+    the packed rows and every product against the oracle."""
+    run_case(nm, 64, 1 << 20, 2, 4, "bf16", 1, seed=15)
+
+
 @pytest.mark.parametrize("B", [2, 8])
 def test_spmv_multi_tile_many_rows(nm, B):
     """Several x tiles with more rows than one pass of the grid's waves: the
