@@ -1965,7 +1965,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
 // Staged matrix-core launch shape: 16-row tiles; 1, 2, 4 or 8 K-slices (each
 // at least one 32-chunk stage) until the launch has ~12 waves per CU (the
 // kernel's register use allows 3 per SIMD); the slices of a tile, or 4 tiles,
-// share a block of at most 8 waves.
+// share a block of at most 8 waves.  With two batch tiles (17 to 32 vectors)
+// at most 2 slices: measured with bf16 2:4 rows from 1024 x 4096 to
+// 8192 x 28672 at 17 and 32 vectors, 2 slices beat 4 and 8 on every shape
+// (by 4-30%; 4096 x 4096 at 32 vectors: 16.0 against 22.8 us with 8).
 template <int F>
 Plan plan_mfma_stage(int64_t R, int64_t K, int NT)
 {
@@ -1974,7 +1977,8 @@ Plan plan_mfma_stage(int64_t R, int64_t K, int NT)
     const int cus = cu_count();
     const int64_t C = K / COLS, tiles = (R + 15) / 16;
     int S = 1;
-    while (S < 8 && tiles * S < 12LL * cus && C / (2 * S) >= kStageChunks)
+    const int smax = NT == 2 ? 2 : 8;
+    while (S < smax && tiles * S < 12LL * cus && C / (2 * S) >= kStageChunks)
         S *= 2;
     if (g_env.mfma_slices > 0 && g_env.mfma_slices <= 8)
         S = g_env.mfma_slices;
