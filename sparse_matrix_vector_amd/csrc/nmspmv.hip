@@ -1966,18 +1966,22 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
 // at least one 32-chunk stage) until the launch has ~12 waves per CU (the
 // kernel's register use allows 3 per SIMD); the slices of a tile, or 4 tiles,
 // share a block of at most 8 waves.  With two batch tiles (17 to 32 vectors)
-// at most 2 slices: measured with bf16 2:4 rows from 1024 x 4096 to
-// 8192 x 28672 at 17 and 32 vectors, 2 slices beat 4 and 8 on every shape
-// (by 4-30%; 4096 x 4096 at 32 vectors: 16.0 against 22.8 us with 8).
+// at most 2 slices, and 1 from 24 vectors when there are more tiles than
+// CUs.  Measured with bf16 2:4 rows on shapes from 1024 x 4096 to
+// 8192 x 28672: 2 slices beat 4 and 8 on every shape at 17 and 32 vectors
+// (by 4-30%; 4096 x 4096 at 32: 16.0 against 22.8 us with 8); at 24-32
+// vectors 1 slice beat 2 by 6-11% on every shape of more than 256 tiles
+// (5120 x 25600 at 32: 104.6 against 117.3 us) and lost by 16-42% on those
+// of 256 or fewer; at 17 vectors it lost on all.
 template <int F>
-Plan plan_mfma_stage(int64_t R, int64_t K, int NT)
+Plan plan_mfma_stage(int64_t R, int64_t K, int NT, int B)
 {
     std::call_once(g_env_once, read_env);
     constexpr int COLS = chunk_cols<F>();
     const int cus = cu_count();
     const int64_t C = K / COLS, tiles = (R + 15) / 16;
     int S = 1;
-    const int smax = NT == 2 ? 2 : 8;
+    const int smax = NT == 2 ? (B >= 24 && tiles > cus ? 1 : 2) : 8;
     while (S < smax && tiles * S < 12LL * cus && C / (2 * S) >= kStageChunks)
         S *= 2;
     if (g_env.mfma_slices > 0 && g_env.mfma_slices <= 8)
@@ -1999,7 +2003,7 @@ Plan plan_mfma_stage(int64_t R, int64_t K, int NT)
 template <int F, int DT, int NT>
 int launch_mfma_nt(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
-    const Plan P = plan_mfma_stage<F>(R, K, NT);
+    const Plan P = plan_mfma_stage<F>(R, K, NT, B);
     if (P.lds > 64 * 1024) {
         static bool raised[64] = {};             // per device, once per instantiation
         if (allow_full_lds((const void*)mfma_stage_kernel<F, DT, NT>, raised) != NM_OK)
