@@ -57,6 +57,17 @@ def test_spmv_batched(nm, dt, n, m, R, K, B):
     run_sparse(nm, R, K, n, m, dt, B, seed=1)
 
 
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("R,B", [(4096, 24), (4112, 24), (4112, 32), (5000, 20)])
+def test_spmv_batched_slice_rule(nm, n, m, R, B):
+    """Above 16 vectors, rows too few for the LDS ring go to the staged
+    kernel, which splits K in 2 slices, or keeps it whole from 24 vectors
+    when the 16-row tiles outnumber the CUs (on 256 CUs: 4112 rows = 257
+    tiles whole; 4096 rows at 24 and 5000 rows at 20 in 2 slices).  Every
+    output is compared."""
+    run_sparse(nm, R, 2048, n, m, "bf16", B, seed=7)
+
+
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
 @pytest.mark.parametrize("B", [5, 16, 32])
