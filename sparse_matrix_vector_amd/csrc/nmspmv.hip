@@ -851,10 +851,10 @@ __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u3
     constexpr int RPL = kWave / kStageChunks;    // rows per load instruction
     constexpr int NL = 16 / RPL;                 // load instructions per stage
     const int lrow = lane / kStageChunks, lc = lane % kStageChunks;  // load layout: row RPL rr + lrow, chunk c0 + lc
-    int xrow[NT];
+    const u32x4* xrow[NT];                       // the lane's x row (B K / 8 units can pass 2^31)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-        xrow[nt] = min(16 * nt + i, B - 1) * (K / 8);
+        xrow[nt] = x4 + (size_t)min(16 * nt + i, B - 1) * (K / 8);
     const u32x4* wp[NL];
     const uint16_t* mp[NL];
 #pragma unroll
@@ -893,7 +893,7 @@ __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u3
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int h = 0; h < XC; ++h)
-                    xv[nt][t][h] = x4[xrow[nt] + cc * XC + h];
+                    xv[nt][t][h] = xrow[nt][cc * XC + h];
         }
     };
     auto stash = [&](const u32x4* v, const uint32_t* m) {

@@ -136,3 +136,36 @@ def test_tiny_1024_seed0_full(nm):
     v, mk = nm.pack(W.cuda(), None, 2, 4)
     y = nm.spmv(v, mk, x.cuda(), 2, 4)
     check_rows(W, v.cpu(), mk.cpu(), x, y.cpu(), 2, 4, "fp16", list(range(1024)))
+
+
+def test_spmv_x_past_2g_units(nm):
+    """32 vectors of K = 671088640 (x is 43 GB; the last row starts
+    31 K / 8 > 2^31 16-byte units in) over 16 rows, which the staged
+    matrix-core kernel takes.  Too large for the oracle, so the packed
+    operands are built on the GPU (columns 0 and 1 of every group kept,
+    seeded values) and every x row is the same seeded row; properties that
+    hold at any size: all 32 outputs of a row bit-identical, finite and not
+    all zero, and a second call bit-identical to the first."""
+    R, K, B = 16, 671088640, 32
+    need = B * K * 2 + R * (K // 2) * 6 + R * (K // 8) + (2 << 30)
+    if torch.cuda.mem_get_info()[0] < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(I.seed_of("xbig", R, K, B))
+    values = torch.empty((R, K // 2), dtype=torch.bfloat16, device="cuda")
+    for r in range(R):                        # one row at a time keeps the fp32 draw small
+        values[r] = (torch.randn(K // 2, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    masks = torch.full((R, K // 8), 0x33, dtype=torch.uint8, device="cuda")
+    x0 = torch.randn(K, device="cuda", generator=g).to(torch.bfloat16)
+    x = x0.expand(B, K).contiguous()
+    del x0
+    y = nm.spmv(values, masks, x, 2, 4)
+    y2 = nm.spmv(values, masks, x, 2, 4)
+    torch.cuda.synchronize()
+    assert y.shape == (B, R)
+    yb = y.view(torch.int16)
+    assert torch.equal(yb, yb[:1].expand(B, R)), "batch columns differ"
+    assert torch.isfinite(y.float()).all() and (y[0] != 0).any()
+    assert torch.equal(yb, y2.view(torch.int16))
+    del values, masks, x, y, y2
+    torch.cuda.empty_cache()
