@@ -32,7 +32,8 @@
  * - dtype is NM_FP16 (IEEE binary16) or NM_BF16 (bfloat16); W, values, x and y
  *   all use it.
  * - Shapes: R >= 0, K >= 0, K % 8 == 0, M in {4, 8}, 1 <= N < M, K % M == 0,
- *   1 <= B <= 32, and R, K below 2^31.  Anything else returns NM_ERR_BAD_SHAPE
+ *   1 <= B <= 32, R below 2^31 - 1024 (2 R for the gated calls) and K
+ *   below 2^31.  Anything else returns NM_ERR_BAD_SHAPE
  *   (or NM_ERR_UNSUPPORTED for a dtype that is not one of the two) before
  *   any work is queued; outputs are then untouched.
  * - Alignment: W, values, masks and x must be 16-byte aligned; y 2-byte
@@ -122,7 +123,7 @@ int nm_gemv_dense(const void* W, int64_t R, int64_t K, int dtype, const void* x,
  * Each y[i] equals what nm_spmv would give for part i alone up to fp32
  * summation order (the row split across lanes may differ); rules as for
  * nm_spmv, applied per part, plus: no y[i] may overlap another y[j], and the
- * total row count must stay below 2^31.  count outside 1..4 is
+ * total row count must stay below 2^31 - 1024.  count outside 1..4 is
  * NM_ERR_BAD_SHAPE; NULL array arguments are NM_ERR_INVALID_ARG.
  */
 int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,

@@ -2284,9 +2284,14 @@ bool ptr_ok(const void* p, size_t bytes, uintptr_t align)
 
 int check_dtype(int dtype) { return (dtype == NM_FP16 || dtype == NM_BF16) ? NM_OK : NM_ERR_UNSUPPORTED; }
 
+// Row indices are 32-bit in the kernels, and a launch rounds its rows up to
+// whole tiles and blocks (at most a few hundred rows past R): R, and a fused
+// launch's total, stay below kRowLimit.
+constexpr int64_t kRowLimit = (int64_t(1) << 31) - 1024;
+
 int check_rk(int64_t R, int64_t K)
 {
-    if (R < 0 || K < 0 || R > INT32_MAX || K > INT32_MAX || K % 8 != 0)
+    if (R < 0 || K < 0 || R >= kRowLimit || K > INT32_MAX || K % 8 != 0)
         return NM_ERR_BAD_SHAPE;
     return NM_OK;
 }
@@ -2535,7 +2540,7 @@ int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* ma
             return st;
         total += R[i];
     }
-    if (total > INT32_MAX)
+    if (total >= kRowLimit)
         return NM_ERR_BAD_SHAPE;
     if (!values || !masks || !y)
         return NM_ERR_INVALID_ARG;
@@ -2618,7 +2623,7 @@ int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64
             return st;
         total += R[i];
     }
-    if (total > INT32_MAX)
+    if (total >= kRowLimit)
         return NM_ERR_BAD_SHAPE;
     if (!W || !y)
         return NM_ERR_INVALID_ARG;
@@ -2675,7 +2680,7 @@ int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const voi
         return st;
     if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
         return st;
-    if (B < 1 || B > kMaxBatch || 2 * R > INT32_MAX)
+    if (B < 1 || B > kMaxBatch || 2 * R >= kRowLimit)
         return NM_ERR_BAD_SHAPE;
     const size_t xbytes = (size_t)B * (size_t)K * 2, hbytes = (size_t)B * (size_t)R * 2;
     const size_t vb = (size_t)R * (size_t)(K / M * N) * 2, mb = (size_t)R * (size_t)(K / 8);
@@ -2719,7 +2724,7 @@ int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_
         return st;
     if ((st = check_rk(R, K)) != NM_OK)
         return st;
-    if (B < 1 || B > kMaxBatch || 2 * R > INT32_MAX)
+    if (B < 1 || B > kMaxBatch || 2 * R >= kRowLimit)
         return NM_ERR_BAD_SHAPE;
     const size_t xbytes = (size_t)B * (size_t)K * 2, hbytes = (size_t)B * (size_t)R * 2;
     const size_t wb = (size_t)R * (size_t)K * 2;
@@ -2798,7 +2803,7 @@ int nm_hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int64
 
 int nm_hybrid_select_rows(const double* loss, int64_t R, int64_t n_dense, uint8_t* flags, void* stream)
 {
-    if (R < 0 || R > INT32_MAX || n_dense < 0 || n_dense > R)
+    if (R < 0 || R >= kRowLimit || n_dense < 0 || n_dense > R)
         return NM_ERR_BAD_SHAPE;
     if (!ptr_ok(loss, (size_t)R * 8, 8) || !ptr_ok(flags, (size_t)R, 1) || overlaps(flags, (size_t)R, loss, (size_t)R * 8))
         return NM_ERR_INVALID_ARG;

@@ -58,7 +58,7 @@ def pack(W=FAKE, keep=None, R=16, K=64, N=2, M=4, dt=0, values=FAKE2, masks=FAKE
 
 @pytest.mark.parametrize("kw", [dict(K=12), dict(K=-8), dict(R=-1), dict(M=3), dict(M=16), dict(N=0), dict(N=4),
                                 dict(N=8, M=8), dict(K=8 * 3, M=8, N=4) | dict(K=20), dict(B=0), dict(B=33),
-                                dict(R=2 ** 31), dict(K=2 ** 31 + 8)])
+                                dict(R=2 ** 31), dict(R=2 ** 31 - 1024), dict(K=2 ** 31 + 8)])
 def test_spmv_bad_shape(kw):
     assert spmv(**kw) == L.NM_ERR_BAD_SHAPE
 
@@ -80,7 +80,7 @@ def test_spmv_empty_is_ok_without_gpu():
     assert L.lib().nm_spmv(None, None, 0, 64, 2, 4, 0, FAKE2, 1, None, None) == L.NM_OK
 
 
-@pytest.mark.parametrize("kw", [dict(K=12), dict(R=-1), dict(B=0), dict(B=33)])
+@pytest.mark.parametrize("kw", [dict(K=12), dict(R=-1), dict(B=0), dict(B=33), dict(R=2 ** 31 - 1024)])
 def test_gemv_bad_shape(kw):
     assert gemv(**kw) == L.NM_ERR_BAD_SHAPE
 
@@ -145,7 +145,7 @@ def test_multi_rejects_bad_count_and_null_arrays():
     # all parts empty: nothing to do
     R0 = _arr(ctypes.c_int64, [0, 0])
     assert lib.nm_spmv_multi(2, v, m, R0, 64, 2, 4, 0, FAKE2, 1, y, None) == L.NM_OK
-    Rbig = _arr(ctypes.c_int64, [2 ** 30, 2 ** 30])
+    Rbig = _arr(ctypes.c_int64, [2 ** 30, 2 ** 30 - 1024])          # rows stay 1024 below 2^31
     assert lib.nm_spmv_multi(2, v, m, Rbig, 64, 2, 4, 0, FAKE2, 1, y, None) == L.NM_ERR_BAD_SHAPE
 
 
@@ -168,7 +168,7 @@ def swiglu(vg=FAKE, mg=FAKE + 0x1000, vu=FAKE + 0x2000, mu=FAKE + 0x3000, R=16, 
 
 
 @pytest.mark.parametrize("kw", [dict(K=12), dict(R=-1), dict(M=3), dict(N=0), dict(N=4), dict(B=0), dict(B=33),
-                                dict(R=2 ** 30 + 1)])
+                                dict(R=2 ** 30 + 1), dict(R=2 ** 30 - 512)])
 def test_swiglu_bad_shape(kw):
     assert swiglu(**kw) == L.NM_ERR_BAD_SHAPE
 
