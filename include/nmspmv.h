@@ -106,8 +106,14 @@ int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int 
             const void* x, int B, void* y, void* stream);
 
 /*
- * nm_gemv_dense -- the dense baseline y = W * x (the unpruned decode
- * projection the SparseDecoding speedup is measured against).
+ * nm_gemv_dense -- the dense baseline y = W * x: the same decode projection
+ * with the weight left unpruned, i.e. the comparison path that a sparse
+ * speedup has to be read against.  The eucax.ai insights page on
+ * SparseDecoding names that baseline as the missing piece of the published
+ * speedup (section 3, "Reading the 1.48x result correctly") and asks for it to
+ * be fixed and measured at the same operating point (section 6, "A
+ * validation plan before adoption"); this call is that baseline, built on the
+ * same kernel skeleton and fused the same way as nm_spmv.
  *   W [R][K], x [B][K], y [B][R], all dtype; fp32 accumulation, one rounding.
  * Same shape rules as nm_spmv without N and M (K % 8 == 0).
  */
@@ -187,7 +193,8 @@ int nm_calib_accumulate(const void* X, const uint8_t* decode, int64_t T, int64_t
  * nm_calib_keep_mask -- the N:M keep-mask from a calibration Hessian: per
  * M-group of each row keep the N columns of largest saliency w^2 * H_jj (the
  * optimal-brain-surgeon saliency with H taken diagonal), the lower column on
- * equal saliency; a NaN saliency ranks below every other.  The saliency is
+ * equal saliency; a NaN saliency ranks below every number (-inf included),
+ * NaNs among themselves the lower column first.  The saliency is
  * formed exactly (double), so the mask is fully determined by W and H's
  * diagonal.
  *   W [R][K] 16-bit (dtype); h: H_jj = h[j * h_stride] (h_stride = K + 1 on a
@@ -223,8 +230,8 @@ int nm_hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int64
                        int M, int dtype, double* loss, void* stream);
 
 /* nm_hybrid_select_rows -- flags[r] = 1 for the n_dense (0..R) rows of largest
- * loss, 0 elsewhere; a NaN loss ranks below every number (-inf included),
- * the lower row first among equals.  loss [R] double (8-byte aligned), flags [R] bytes.  Enqueues. */
+ * loss, 0 elsewhere; a NaN loss ranks below every number (-inf included) and
+ * equal to another NaN, the lower row first among equals.  loss [R] double (8-byte aligned), flags [R] bytes.  Enqueues. */
 int nm_hybrid_select_rows(const double* loss, int64_t R, int64_t n_dense, uint8_t* flags, void* stream);
 
 /*

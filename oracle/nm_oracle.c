@@ -421,11 +421,28 @@ int orc_calib_accumulate(const uint16_t* X, const uint8_t* decode, int64_t T, in
     return ORC_OK;
 }
 
+/* The order used to rank saliencies and row losses: every number above NaN
+ * (-inf included), numbers by value (-0 equal to +0), all NaNs equal. */
+static int rank_above(double a, double b)
+{
+    if (isnan(a))
+        return 0;
+    return isnan(b) || a > b;
+}
+
+static int rank_equal(double a, double b)
+{
+    if (isnan(a) || isnan(b))
+        return isnan(a) && isnan(b);
+    return a == b;
+}
+
 /* keep[r][c] = 1 for the N columns of each M-group of row r with the largest
  * saliency w^2 * h[c], 0 elsewhere; equal saliencies go to the lower column.
  * h holds the Hessian diagonal (fp32 values, passed exactly as doubles).  The
  * saliency is formed exactly in double (w^2 has at most 22 significant bits,
- * h 24).  A NaN saliency ranks below every other. */
+ * h 24).  A NaN saliency ranks below every number, -inf included; NaNs
+ * rank equal among themselves (lower column first). */
 int orc_calib_keep(const uint16_t* W, const double* h, int64_t R, int64_t K, int N, int M, int dtype, uint8_t* keep)
 {
     int st = check_nm(R, K, N, M);
@@ -441,14 +458,14 @@ int orc_calib_keep(const uint16_t* W, const double* h, int64_t R, int64_t K, int
                 int64_t c = g * M + j;
                 double w = orc_to_double(W[r * K + c], dtype);
                 double s = w * w * h[c];
-                sal[j] = isnan(s) ? -INFINITY : s;
+                sal[j] = s;
                 taken[j] = 0;
                 keep[r * K + c] = 0;
             }
             for (int k = 0; k < N; ++k) {
                 int best = -1;
                 for (int j = 0; j < M; ++j)
-                    if (!taken[j] && (best < 0 || sal[j] > sal[best]))
+                    if (!taken[j] && (best < 0 || rank_above(sal[j], sal[best])))
                         best = j;
                 taken[best] = 1;
                 keep[r * K + g * M + best] = 1;
@@ -503,20 +520,17 @@ int orc_hybrid_row_loss(const uint16_t* W, const uint8_t* keep, const double* h,
     return ORC_OK;
 }
 
-/* flags[r] = 1 for the n_dense rows of largest loss (a NaN loss lowest),
- * the lower row first among equals; 0 for the others. */
+/* flags[r] = 1 for the n_dense rows of largest loss (a NaN loss below every
+ * number, -inf included), the lower row first among equals; 0 for the others. */
 int orc_hybrid_select(const double* loss, int64_t R, int64_t n_dense, uint8_t* flags)
 {
     if (R < 0 || n_dense < 0 || n_dense > R)
         return ORC_BAD_SHAPE;
     for (int64_t r = 0; r < R; ++r) {
-        double lr = isnan(loss[r]) ? -INFINITY : loss[r];
         int64_t above = 0;
-        for (int64_t s = 0; s < R; ++s) {
-            double ls = isnan(loss[s]) ? -INFINITY : loss[s];
-            if (ls > lr || (ls == lr && s < r))
+        for (int64_t s = 0; s < R; ++s)
+            if (rank_above(loss[s], loss[r]) || (rank_equal(loss[s], loss[r]) && s < r))
                 ++above;
-        }
         flags[r] = above < n_dense ? 1 : 0;
     }
     return ORC_OK;

@@ -349,8 +349,9 @@ __global__ __launch_bounds__(256, 3) void calib_accumulate_kernel(const uint16_t
 
 // One thread per (row, 8 columns): two 4-groups or one 8-group.  Saliency
 // w^2 h is exact in double (w^2 has at most 22 significant bits, h 24); a NaN
-// saliency ranks below every number.  Column j is kept when fewer than N group
-// members beat it: larger saliency, or equal saliency at a lower column.
+// saliency ranks below every number, -inf included, and NaNs rank equal.
+// Column j is kept when fewer than N group members beat it: a higher rank,
+// or an equal one at a lower column.
 template <int DT>
 __global__ __launch_bounds__(256) void calib_keep_kernel(const u32x4* __restrict__ W, const float* __restrict__ h,
                                                          int64_t h_stride, int64_t nunits, int64_t units_per_row, int N,
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(256) void calib_keep_kernel(const u32x4* __restrict
         const double w = nm_decode::w_to_f64<DT>((words[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
         const double hv = nm_decode::f32_to_f64(h[(c0 + e) * h_stride]);
         const double v = w * w * hv;
-        s[e] = v != v ? -__builtin_inf() : v;
+        s[e] = v;
     }
     uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -378,7 +379,8 @@ __global__ __launch_bounds__(256) void calib_keep_kernel(const u32x4* __restrict
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             if (k >= g && k < g + M)
-                beats += (s[k] > s[e]) || (s[k] == s[e] && k < e);
+                beats += (s[k] == s[k] && (s[e] != s[e] || s[k] > s[e])) ||
+                         (((s[k] != s[k]) ? (s[e] != s[e]) : (s[k] == s[e])) && k < e);
         const uint32_t bit = beats < N ? 1u : 0u;
         if (e < 4)
             lo |= bit << (8 * e);

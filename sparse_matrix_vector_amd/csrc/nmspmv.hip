@@ -1653,11 +1653,23 @@ __global__ __launch_bounds__(256) void hybrid_loss_kernel(const uint16_t* __rest
         atomicOr(status, bad);
 }
 
+// The ranking order of row losses: every number above NaN (-inf included),
+// numbers by value, all NaNs equal.
+__device__ __forceinline__ bool loss_above(double a, double b)
+{
+    return a == a && (b != b || a > b);
+}
+
+__device__ __forceinline__ bool loss_equal(double a, double b)
+{
+    return (a != a) ? (b != b) : (a == b);
+}
+
 // flags[r] = 1 for the n_dense rows of largest loss (a NaN loss ranks below
-// every number, the lower row first among equals): row r's rank counts the
-// rows ahead of it, against 256-row tiles of the losses staged in LDS.  A
-// block takes 64 rows, four threads per row, each counting a quarter of every
-// tile; the four counts add up exactly in any order.
+// every number, -inf included; the lower row first among equals): row r's
+// rank counts the rows ahead of it, against 256-row tiles of the losses
+// staged in LDS.  A block takes 64 rows, four threads per row, each counting
+// a quarter of every tile; the four counts add up exactly in any order.
 __global__ __launch_bounds__(256) void hybrid_select_kernel(const double* __restrict__ loss, int R, int n_dense,
                                                             uint8_t* __restrict__ flags)
 {
@@ -1665,20 +1677,17 @@ __global__ __launch_bounds__(256) void hybrid_select_kernel(const double* __rest
     __shared__ int part[256];
     const int t = threadIdx.x, q = t & 3;
     const int r = blockIdx.x * 64 + (t >> 2);
-    const double lr0 = r < R ? loss[r] : 0.0;
-    const double lr = lr0 != lr0 ? -__builtin_inf() : lr0;
+    const double lr = r < R ? loss[r] : 0.0;
     int above = 0;
     for (int s0 = 0; s0 < R; s0 += 256) {
         __syncthreads();
-        if (s0 + t < R) {
-            const double v = loss[s0 + t];
-            tile[t] = v != v ? -__builtin_inf() : v;
-        }
+        if (s0 + t < R)
+            tile[t] = loss[s0 + t];
         __syncthreads();
         const int ns = min(256, R - s0);
         for (int k = q; k < ns; k += 4) {
             const double ls = tile[k];
-            above += (ls > lr) || (ls == lr && s0 + k < r);
+            above += loss_above(ls, lr) || (loss_equal(ls, lr) && s0 + k < r);
         }
     }
     part[t] = above;

@@ -498,8 +498,8 @@ def _keep_brute(Wv, h, n, m):
 def pin_calib_keep(seed=8):
     """Saliency keep-mask: equals the magnitude rule when h is constant (a
     reduction to the pinned top-n by |w|), the top-n of h when |w| is
-    constant, exact-rational brute force on random inputs, and NaN ranks
-    lowest."""
+    constant, exact-rational brute force on random inputs, and a NaN saliency
+    ranks below every number, -inf included."""
     rng = np.random.default_rng(seed)
     for dt in ("fp16", "bf16"):
         for n, m in ((2, 4), (4, 8), (1, 4), (3, 8)):
@@ -533,6 +533,16 @@ def pin_calib_keep(seed=8):
     W = np.array([[0x7E00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00]], np.uint16)
     keep = oracle.calib_keep(W, np.array([1.0, -2.0, -3.0, -1.0, 1.0, 1.0, 1.0, 1.0], np.float32), 2, 4, "fp16")
     assert keep.tolist() == [[0, 1, 0, 1, 1, 1, 0, 0]]
+    # ... and below -inf: saliencies NaN, -inf, 2, 3 | -inf, NaN, 2, 3 keep -inf over NaN in either order
+    inf = float("inf")
+    W = np.array([[0x7E00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x7E00, 0x3C00, 0x3C00]], np.uint16)
+    h = np.array([1.0, -inf, 2.0, 3.0, -inf, 1.0, 2.0, 3.0], np.float32)
+    assert oracle.calib_keep(W, h, 3, 4, "fp16").tolist() == [[0, 1, 1, 1, 1, 0, 1, 1]]
+    assert oracle.calib_keep(W, h, 1, 4, "fp16").tolist() == [[0, 0, 0, 1, 0, 0, 0, 1]]
+    # a zero weight under h = -inf gives 0 * -inf = NaN, which also ranks last
+    W = np.array([[0x0000, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x0000]], np.uint16)
+    h = np.array([-inf, -inf, 1.0, 1.0, 1.0, 1.0, -inf, -inf], np.float32)
+    assert oracle.calib_keep(W, h, 3, 4, "fp16").tolist() == [[0, 1, 1, 1, 1, 1, 1, 0]]
 
 
 def pin_hybrid(seed=9):
@@ -567,15 +577,21 @@ def pin_hybrid(seed=9):
                 kept = _bitmap_to_keep(mk, K)[0].astype(bool)
                 assert loss1[r] == math.fsum(Wv[r, c] ** 2 for c in range(K) if not kept[c]) or \
                     abs(loss1[r] - math.fsum(Wv[r, c] ** 2 for c in range(K) if not kept[c])) <= 1e-12 * loss1[r]
-    # NaN ranks below every number, negative and -inf included (lower row first among equals)
-    for loss in (np.array([3.0, 1.0, 3.0, float("nan"), 0.0, 7.0, 1.0]),
-                 np.array([-5.0, float("nan"), -0.5, 2.0, -float("inf"), -5.0, float("nan")])):
+    # NaN ranks below every number, negative and -inf included; NaNs tie among
+    # themselves (lower row first among equals, as for numbers)
+    nan, inf = float("nan"), float("inf")
+    for loss in (np.array([3.0, 1.0, 3.0, nan, 0.0, 7.0, 1.0]),
+                 np.array([-5.0, nan, -0.5, 2.0, -inf, -5.0, nan]),
+                 np.array([nan, -inf, nan, -inf, inf, nan, -0.0, 0.0])):
         for nd in range(len(loss) + 1):
-            order = sorted(range(len(loss)), key=lambda r: (-(loss[r] if loss[r] == loss[r] else -math.inf), r))
+            order = sorted(range(len(loss)), key=lambda r: (math.isnan(loss[r]), 0.0 if math.isnan(loss[r]) else -loss[r], r))
             want = np.zeros(len(loss), np.uint8)
             want[order[:nd]] = 1
             assert np.array_equal(oracle.hybrid_select(loss, nd), want)
-    assert list(oracle.hybrid_select(np.array([float("nan"), -2.0]), 1)) == [0, 1]
+    assert list(oracle.hybrid_select(np.array([nan, -2.0]), 1)) == [0, 1]
+    assert list(oracle.hybrid_select(np.array([nan, -inf]), 1)) == [0, 1]
+    assert list(oracle.hybrid_select(np.array([-inf, nan]), 1)) == [1, 0]
+    assert list(oracle.hybrid_select(np.array([nan, nan, -inf]), 2)) == [1, 0, 1]
     # the product reduces to the plain ones
     R, K = 6, 64
     W = to_bits(np.round(rng.normal(0, 1, (R, K)) * 16) / 16, "fp16")

@@ -214,6 +214,21 @@ def test_calib_keep_mask_negative_saliency_and_nan(nm, n, m):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_calib_keep_mask_nan_below_minus_inf(nm, dt):
+    """A NaN saliency ranks below -inf: groups holding both (NaN first or
+    -inf first, and 0 * -inf = NaN) keep the -inf column before the NaN one."""
+    tdt = TD[dt]
+    inf, nan = float("inf"), float("nan")
+    W = torch.tensor([[nan, 1.0, 1.0, 1.0, 1.0, nan, 1.0, 1.0, 0.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 0.0]], dtype=tdt)
+    h = np.array([1.0, -inf, 2.0, 3.0, -inf, 1.0, 2.0, 3.0, -inf, -inf, 1.0, 1.0, 1.0, 1.0, -inf, -inf], np.float32)
+    for n in (1, 2, 3):
+        keep = nm.calib_keep_mask(W.cuda(), torch.from_numpy(h).cuda(), n, 4).cpu().numpy()
+        assert np.array_equal(keep, oracle.calib_keep(bits(W), h, n, 4, dt)), n
+    keep = nm.calib_keep_mask(W.cuda(), torch.from_numpy(h).cuda(), 3, 4).cpu().numpy()
+    assert keep[0].tolist() == [0, 1, 1, 1, 1, 0, 1, 1, 0, 1, 1, 1, 1, 1, 1, 0]
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
 def test_calibrated_pack_and_spmv(nm, dt):
     """The offline flow end to end on a Llama-3.1-8B-shaped layer slice:
     decode-step activations -> H -> keep-mask -> nm_pack -> nm_spmv, each

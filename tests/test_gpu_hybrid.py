@@ -78,6 +78,9 @@ def test_row_loss_unaligned_inputs(nm, dt, with_keep):
 @pytest.mark.parametrize("values", [
     [3.0, 1.0, 3.0, float("nan"), 0.0, 7.0, 1.0, 3.0],
     [-5.0, float("nan"), -0.5, 2.0, -float("inf"), -5.0, float("nan"), -1.0],   # NaN below negatives and -inf
+    [float("nan"), -float("inf")],                                                 # -inf chosen before NaN ...
+    [-float("inf"), float("nan")],                                                 # ... in either order
+    [float("nan"), -float("inf"), float("nan"), -float("inf"), float("inf"), -0.0, 0.0, float("nan")],
 ])
 def test_row_choice_ties_and_nan(nm, values):
     loss = torch.tensor(values, dtype=torch.float64)

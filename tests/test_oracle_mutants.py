@@ -12,6 +12,10 @@ import oracle_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "nm_oracle.c")
 
+# The ranking helpers of the saliency keep-mask and the hybrid row choice, as
+# they stand in nm_oracle.c (replaced whole by the NaN-placement mutants).
+RANK_HELPERS = "static int rank_above(double a, double b)\n{\n    if (isnan(a))\n        return 0;\n    return isnan(b) || a > b;\n}\n\nstatic int rank_equal(double a, double b)\n{\n    if (isnan(a) || isnan(b))\n        return isnan(a) && isnan(b);\n    return a == b;\n}"
+
 # (name, text in nm_oracle.c, replacement) -- each is a mistake someone could make.
 MUTANTS = [
     ("tie_goes_to_highest_index", "mag[j] > mag[best]", "mag[j] >= mag[best]"),
@@ -36,15 +40,17 @@ MUTANTS = [
     ("calib_diagonal_only", "double p = row[i] * row[j];", "double p = row[i] * row[i];"),
     ("saliency_abs_w", "double s = w * w * h[c];", "double s = fabs(w) * h[c];"),
     ("saliency_ignores_h", "double s = w * w * h[c];", "double s = w * w;"),
-    ("saliency_tie_to_highest", "(best < 0 || sal[j] > sal[best])", "(best < 0 || sal[j] >= sal[best])"),
-    ("saliency_nan_ranks_high", "sal[j] = isnan(s) ? -INFINITY : s;", "sal[j] = isnan(s) ? 1e300 : s;"),
-    ("saliency_nan_at_minus_one", "sal[j] = isnan(s) ? -INFINITY : s;", "sal[j] = isnan(s) ? -1.0 : s;"),
-    ("row_loss_nan_at_minus_one", "double lr = isnan(loss[r]) ? -INFINITY : loss[r];", "double lr = isnan(loss[r]) ? -1.0 : loss[r];"),
+    ("saliency_tie_to_highest", "(best < 0 || rank_above(sal[j], sal[best]))", "(best < 0 || !rank_above(sal[best], sal[j]))"),
+    # NaN placed elsewhere in the ranking order: above every number, at -1, and
+    # equal to -inf (the reading not taken: NaN then ties with -inf)
+    ("nan_ranks_high", "        return 0;\n    return isnan(b) || a > b;", "        return !isnan(b);\n    return a > b;"),
+    ("nan_at_minus_one", RANK_HELPERS, "static int rank_above(double a, double b)\n{\n    return (isnan(a) ? -1.0 : a) > (isnan(b) ? -1.0 : b);\n}\n\nstatic int rank_equal(double a, double b)\n{\n    return (isnan(a) ? -1.0 : a) == (isnan(b) ? -1.0 : b);\n}"),
+    ("nan_equals_minus_inf", RANK_HELPERS, "static int rank_above(double a, double b)\n{\n    return (isnan(a) ? -INFINITY : a) > (isnan(b) ? -INFINITY : b);\n}\n\nstatic int rank_equal(double a, double b)\n{\n    return (isnan(a) ? -INFINITY : a) == (isnan(b) ? -INFINITY : b);\n}"),
     ("hybrid_loss_counts_kept", "                if (chosen[j])\n                    continue;\n                double v",
      "                if (!chosen[j])\n                    continue;\n                double v"),
     ("hybrid_loss_ignores_h", "double hv = h ? h[g * M + j] : 1.0;", "double hv = 1.0;"),
-    ("hybrid_select_ascending", "if (ls > lr || (ls == lr && s < r))", "if (ls < lr || (ls == lr && s < r))"),
-    ("hybrid_select_ties_to_higher", "if (ls > lr || (ls == lr && s < r))", "if (ls > lr || (ls == lr && s > r))"),
+    ("hybrid_select_ascending", "if (rank_above(loss[s], loss[r]) ||", "if (rank_above(loss[r], loss[s]) ||"),
+    ("hybrid_select_ties_to_higher", "(rank_equal(loss[s], loss[r]) && s < r)", "(rank_equal(loss[s], loss[r]) && s > r)"),
 ]
 
 
