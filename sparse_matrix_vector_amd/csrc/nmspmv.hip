@@ -194,60 +194,114 @@ __device__ __forceinline__ void build_table(u32x4* tab)
     }
 }
 
-// x in LDS: [NB][bstride] 16-byte units.  Sparse formats split each 32-byte
-// column range of a chunk into two planes (first 16 bytes at unit c, second
-// at unit bstride/2 + c) so that lanes reading consecutive chunks touch
-// consecutive LDS addresses.
-// The LDS slot of staged x unit j of batch row b.
+// Global-to-LDS loads (gfx950): a load instruction's LDS destination is its
+// base (M0) + 16 bytes x lane; the kernels that use them declare no static
+// LDS, so dynamic LDS starts at offset 0.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+template <int BYTES>
+__device__ __forceinline__ void load_to_lds(const void* g, uint32_t lds_offset)
+{
+    static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte lanes");
+#if defined(__HIP_DEVICE_COMPILE__)
+    lds_void_t* dst = (lds_void_t*)((lds_u8_t*)nullptr + lds_offset);
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_global_load_lds(g, dst, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(g, dst, 4, 0, 0);
+#else
+    (void)g;
+    (void)lds_offset;
+#endif
+}
+
+// s_waitcnt with vmcnt <= N (N < 64) and the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt with vmcnt <= N and lgkmcnt 0.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// x in LDS: [NB][bstride] 16-byte units, bstride a multiple of 64.  Sparse
+// formats keep each 64-unit run of a batch row as two 32-slot halves, its
+// even units first (unit 64 q + 2 i at slot 64 q + i, unit 64 q + 2 i + 1 at
+// slot 64 q + 32 + i), so that lanes reading the two units of consecutive
+// chunks touch consecutive LDS addresses, and one 64-lane global-to-LDS load
+// (1 KB, lane l at slot 64 q + l) fills a whole run.  Dense rows keep unit
+// order.
 template <int F>
 __device__ __forceinline__ int x_slot(int b, int j, int bstride)
 {
     if constexpr (F == kDense)
         return b * bstride + j;
     else
-        return b * bstride + (j & 1) * (bstride / 2) + (j >> 1);
+        return b * bstride + (j & ~63) + ((j & 1) << 5) + ((j >> 1) & 31);
 }
 
-// x staging in two halves around the weight loads: x_fetch issues this
-// thread's first XU units of x (all of it when x has at most XU * blockDim
-// units) into registers before the weight loads are issued; x_store writes
-// them to LDS, and the rest, if any, straight through.  Loads retire in issue
-// order, so a wave can store its x and reach the block barrier while its
-// weight loads are still in flight.  The loads are branch-free (lanes past
-// the end of x reload unit 0, one cache line per wave) so that the compiler
-// can count them exactly; only the LDS stores are predicated.  The launch
-// sizes XU to cover x, so few such reloads happen.
+// Slot of the first unit of sparse chunk c (its second unit is 32 slots on).
+__device__ __forceinline__ int x_chunk_slot(int c)
+{
+    return ((c >> 5) << 6) + (c & 31);
+}
+
+// LDS units per batch row of x for K staged columns: K/8 rounded up to whole
+// 64-unit runs.
+__host__ __device__ constexpr int x_row_units(int64_t K)
+{
+    return (int)(((K / 8) + 63) / 64 * 64);
+}
+
+// The byte offset of a dynamic-LDS pointer (dynamic LDS starts at 0 in these
+// kernels, which declare no static LDS).
+__device__ __forceinline__ uint32_t lds_offset_of(const void* p)
+{
+    return (uint32_t)(uintptr_t)p;
+}
+
+// x [NB][K] into LDS at byte offset x_base, laid out by x_slot<F> with
+// bstride units per batch row: one 64-lane global-to-LDS load per 64-unit
+// run (lanes past the end of a row reload the row's unit 0 into slots no
+// chunk reads), the runs dealt round-robin over the block's waves.  x takes
+// no registers on the way; a wave's loads count in vmcnt like any other, so
+// a wave that has issued n loads after these knows them complete at
+// vmcnt <= n, and the block meets at a barrier before reading x.
+template <int F, int NB>
+__device__ __forceinline__ void x_dma(const u32x4* __restrict__ x4, int K, int bstride, uint32_t x_base, int wave,
+                                      int nwaves, int lane)
+{
+    const int units = K >> 3;
+    const int per_row = (units + 63) >> 6;
+    const int lj = F == kDense ? lane : 2 * (lane & 31) + (lane >> 5);
+    for (int g = wave; g < NB * per_row; g += nwaves) {
+        const int b = NB == 1 ? 0 : g / per_row;
+        const int q = g - b * per_row;
+        const int j = 64 * q + lj;
+        load_to_lds<16>(x4 + (size_t)b * units + (j < units ? j : 0), x_base + (uint32_t)(b * bstride + 64 * q) * 16);
+    }
+}
+
+// The stream kernel stages x in tiles, in two halves around its first weight
+// loads: x_fetch_tile issues this thread's first kXU units of a tile (all of
+// it when the tile has at most kXU * blockDim units) into registers before
+// the weight loads are issued; x_store_tile writes them to LDS, and the
+// rest, if any, straight through.  Loads retire in issue order, so a wave
+// can store its x and reach the block barrier while its weight loads are
+// still in flight.  The loads are branch-free (lanes past the end of the
+// tile reload unit 0) so that the compiler can count them exactly; only the
+// LDS stores are predicated.
 constexpr int kXU = 4;    // x registers of the stream kernel (per tile)
 
-template <int NB, int XU>
-__device__ __forceinline__ void x_fetch(const u32x4* __restrict__ x4, int K, u32x4* xr)
-{
-    const int n = NB * (K / 8);
-#pragma unroll
-    for (int u = 0; u < XU; ++u) {
-        const int i = threadIdx.x + u * blockDim.x;
-        xr[u] = x4[i < n ? i : 0];               // x [NB][K] is contiguous: unit i = batch i/q, unit i%q
-    }
-}
-
-template <int F, int NB, int XU>
-__device__ __forceinline__ void x_store(u32x4* xs, const u32x4* __restrict__ x4, int K, int bstride, const u32x4* xr)
-{
-    const int q = K / 8;
-#pragma unroll
-    for (int u = 0; u < XU; ++u) {
-        const int i = threadIdx.x + u * blockDim.x;
-        const int b = NB == 1 ? 0 : i / q;      // (NB == 1: i < q whenever it is used)
-        if (i < NB * q)
-            xs[x_slot<F>(b, i - b * q, bstride)] = xr[u];
-    }
-    for (int i = threadIdx.x + XU * blockDim.x; i < NB * q; i += blockDim.x) {
-        const int b = NB == 1 ? 0 : i / q;      // (NB == 1: i < q whenever it is used)
-        xs[x_slot<F>(b, i - b * q, bstride)] = x4[i];
-    }
-}
-
-// The same for a tile of `cols` columns starting at column c0.
+// A tile of `cols` columns starting at column c0.
 template <int NB>
 __device__ __forceinline__ void x_fetch_tile(const u32x4* __restrict__ x4, int K, int c0, int cols, u32x4* xr)
 {
@@ -281,16 +335,34 @@ __device__ __forceinline__ void x_store_tile(u32x4* xs, const u32x4* __restrict_
 
 // ---- one 16-byte chunk -------------------------------------------------------
 
-// acc[b] += (chunk . x[b][chunk columns]).  xs: staged x, c: the chunk's index
-// within the staged columns, bstride: units per batch row.
+// The LDS slot of staged x that chunk c (of the staged columns) starts at:
+// its unit (dense) or its first unit (sparse; the second is 32 slots on).
+template <int F>
+__device__ __forceinline__ int chunk_xslot(int c)
+{
+    if constexpr (F == kDense)
+        return c;
+    else
+        return x_chunk_slot(c);
+}
+
+// The slot step between chunks c and c + 64 (same lane, next load slot).
+template <int F>
+constexpr int xslot_step()
+{
+    return F == kDense ? 64 : 128;
+}
+
+// acc[b] += (chunk . x[b][chunk columns]).  xs: staged x, xslot: the chunk's
+// x slot (chunk_xslot), bstride: units per batch row.
 template <int F, int DT, int NB>
 __device__ __forceinline__ void chunk_dot(const u32x4 v, const uint32_t mk, const u32x4* __restrict__ tab,
-                                          const u32x4* __restrict__ xs, const int c, const int bstride, float* acc)
+                                          const u32x4* __restrict__ xs, const int xslot, const int bstride, float* acc)
 {
     if constexpr (F == kDense) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const u32x4 xa = xs[b * bstride + c];
+            const u32x4 xa = xs[b * bstride + xslot];
             float a = acc[b];
             a = dot2<DT>(v.x, xa.x, a);
             a = dot2<DT>(v.y, xa.y, a);
@@ -303,8 +375,8 @@ __device__ __forceinline__ void chunk_dot(const u32x4 v, const uint32_t mk, cons
         const uint32_t s0 = t[mk & 0xF], s1 = t[(mk >> 4) & 0xF], s2 = t[(mk >> 8) & 0xF], s3 = t[(mk >> 12) & 0xF];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const u32x4 xa = xs[b * bstride + c];
-            const u32x4 xb = xs[b * bstride + bstride / 2 + c];
+            const u32x4 xa = xs[b * bstride + xslot];
+            const u32x4 xb = xs[b * bstride + xslot + 32];
             float a = acc[b];
             a = dot2<DT>(v.x, __builtin_amdgcn_perm(xa.y, xa.x, s0), a);
             a = dot2<DT>(v.y, __builtin_amdgcn_perm(xa.w, xa.z, s1), a);
@@ -326,8 +398,8 @@ __device__ __forceinline__ void chunk_dot(const u32x4 v, const uint32_t mk, cons
         w[7] = __builtin_amdgcn_perm(v.w, v.z, s1.w);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const u32x4 xa = xs[b * bstride + c];
-            const u32x4 xb = xs[b * bstride + bstride / 2 + c];
+            const u32x4 xa = xs[b * bstride + xslot];
+            const u32x4 xb = xs[b * bstride + xslot + 32];
             float a = acc[b];
             a = dot2<DT>(w[0], xa.x, a);
             a = dot2<DT>(w[1], xa.y, a);
@@ -379,35 +451,44 @@ struct RowRef {
     int R;               // rows of its part
 };
 
-__device__ __forceinline__ RowRef locate(const Parts& P, int r, int C)
-{
-    int p = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxParts; ++i)
-        if (i < P.count && r >= P.begin[i])
-            p = i;
-    const int rl = r - P.begin[p];
-    RowRef o;
-    o.w = P.w[p] + (size_t)rl * C;
-    o.m = P.m[p] + (size_t)rl * C;
-    o.R = P.ymap[p] ? P.ystride[p] : P.begin[p + 1] - P.begin[p];
-    o.y = P.y[p] + mapped_row(P.ymap[p], o.R, rl);
-    return o;
-}
-
-// Launch row r (see Parts for the gated interleave).
+// Launch row r (wave-uniform; see Parts for the gated interleave).  The part
+// holding r is chosen by selects over the part table, never by an indexed
+// read of the kernel arguments.  Only a part with an output-row map reads
+// memory here (its map entry).
 __device__ __forceinline__ RowRef row_ref(const Parts& P, int r, int C)
 {
+    RowRef o;
     if (P.glu) {
-        const int i = r >> 1, p = r & 1;
-        RowRef o;
-        o.w = P.w[p] + (size_t)i * C;
-        o.m = P.m[p] + (size_t)i * C;
+        const int i = r >> 1;
+        const bool up = (r & 1) != 0;
+        o.w = (up ? P.w[1] : P.w[0]) + (size_t)i * C;
+        o.m = (up ? P.m[1] : P.m[0]) + (size_t)i * C;
         o.y = P.y[0] + i;
         o.R = P.begin[1];
         return o;
     }
-    return locate(P, r, C);
+    // Parts are in increasing row order, so the last boundary passed names the part.
+    const bool p1 = 1 < P.count && r >= P.begin[1];
+    const bool p2 = 2 < P.count && r >= P.begin[2];
+    const bool p3 = 3 < P.count && r >= P.begin[3];
+    const u32x4* w = p3 ? P.w[3] : p2 ? P.w[2] : p1 ? P.w[1] : P.w[0];
+    const uint16_t* m = p3 ? P.m[3] : p2 ? P.m[2] : p1 ? P.m[1] : P.m[0];
+    uint16_t* y = p3 ? P.y[3] : p2 ? P.y[2] : p1 ? P.y[1] : P.y[0];
+    const int32_t* ymap = p3 ? P.ymap[3] : p2 ? P.ymap[2] : p1 ? P.ymap[1] : P.ymap[0];
+    const int b0 = p3 ? P.begin[3] : p2 ? P.begin[2] : p1 ? P.begin[1] : 0;
+    const int b1 = p3 ? P.begin[4] : p2 ? P.begin[3] : p1 ? P.begin[2] : P.begin[1];
+    const int rl = r - b0;
+    o.w = w + (size_t)rl * C;
+    o.m = m + (size_t)rl * C;
+    if (ymap) {
+        const int stride = p3 ? P.ystride[3] : p2 ? P.ystride[2] : p1 ? P.ystride[1] : P.ystride[0];
+        o.R = stride;
+        o.y = y + mapped_row(ymap, stride, rl);
+    } else {
+        o.R = b1 - b0;
+        o.y = y + rl;
+    }
+    return o;
 }
 
 // Weight pointers of launch row r for a row index that differs across lanes:
@@ -456,17 +537,25 @@ __device__ __forceinline__ uint16_t glu_out(float g, float u)
 // loads -- lanes past cend reload chunk 0, and the consumer zeroes them with
 // chunk_live() -- so the code is branch-free and the compiler can wait for
 // exactly the loads each use needs (loads retire in issue order).
+// The row pointers are cast to the global address space so that the loads
+// are global (not flat) loads whatever the compiler can prove about where
+// the pointers came from.
+typedef __attribute__((address_space(1))) const u32x4 gu32x4_t;
+typedef __attribute__((address_space(1))) const uint16_t gu16_t;
+
 template <int F, int U>
 __device__ __forceinline__ void load_chunks(const u32x4* __restrict__ wrow, const uint16_t* __restrict__ mrow,
                                             int c0, int cend, int lane, u32x4* v, uint32_t* mk)
 {
+    gu32x4_t* gw = (gu32x4_t*)wrow;
+    gu16_t* gm = (gu16_t*)mrow;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = c0 + lane + u * kWave;
         const int cc = c < cend ? c : 0;
-        v[u] = __builtin_nontemporal_load(wrow + cc);
+        v[u] = __builtin_nontemporal_load(gw + cc);
         if constexpr (F != kDense)
-            mk[u] = __builtin_nontemporal_load(mrow + cc);
+            mk[u] = __builtin_nontemporal_load(gm + cc);
         else
             mk[u] = 0;
     }
@@ -485,54 +574,99 @@ __device__ __forceinline__ void chunk_live(bool live, u32x4& v, uint32_t& mk)
 
 // ---- row-slice kernel ------------------------------------------------------
 
-// A block holds rows_per_block rows x S K-slices, one wave per (row, slice).
-// A lane issues all of its chunk loads (at most CPL) first, then the block
-// stages the selector table and x in LDS, computes, reduces each wave across
-// lanes, and adds a row's S slice sums in slice order.
+// A block holds rows_per_block rows x S = 2^ls K-slices, one wave per (row,
+// slice).  A wave issues its share of the block's x loads -- one 16-byte
+// unit per thread into a register when that covers x (xreg), else
+// global-to-LDS loads, which hold no registers -- and then all of its chunk
+// loads (at most CPL), builds the selector table, waits for its own x loads
+// (storing a register unit), meets the block, computes chunk by chunk as the
+// weights land, reduces across lanes, and a row's S slice sums are added in
+// slice order.  With xfirst, every wave of the block issues its x loads
+// before any wave issues weight loads (an issue-order barrier; nothing is
+// waited for): a CU serves its loads roughly in issue order, and a block
+// cannot compute until all of its x is in LDS, so x queued behind the
+// block's own weights would hold every wave of the block until nearly all of
+// its data had arrived.
 // The body takes its block index as an argument so that one launch can run
 // two plans side by side (hybrid_rowslice_kernel).
 template <int F, int DT, int NB, int CPL, int XU>
-__device__ __forceinline__ void rowslice_body(const Parts& P, const u32x4* __restrict__ x4, int R, int K, int S,
-                                              int rows_per_block, unsigned blk)
+__device__ __forceinline__ void rowslice_body(const Parts& P, const u32x4* __restrict__ x4, int R, int K, int ls,
+                                              int rows_per_block, int xfirst, int xreg, unsigned blk)
 {
     extern __shared__ u32x4 smem[];
     constexpr int COLS = chunk_cols<F>();
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int lr = wave / S, sl = wave - lr * S;
+    const int nwaves = blockDim.x / kWave;
+    const int S = 1 << ls;
+    const int lr = wave >> ls, sl = wave & (S - 1);
     const int r = blk * rows_per_block + lr;
     const bool active = r < R;
-    const int C = K / COLS;
-    const int cps = (C + S - 1) / S;
+    const int C = (int)((unsigned)K / COLS);
+    // Slices start on 32-chunk boundaries, so that a lane's x slots are one
+    // base plus a fixed step per load slot (the last slice may be shorter).
+    const int cps = (((C + S - 1) >> ls) + 31) & ~31;
     const int cbeg = sl * cps, cend = active ? min(C, cbeg + cps) : cbeg;
     const RowRef row = row_ref(P, active ? r : 0, C);
 
+    u32x4* tab = smem;
+    u32x4* xs = smem + table_units<F>();
+    const int bstride = x_row_units(K);
+    float* part = reinterpret_cast<float*>(xs + NB * bstride);
+    const int xunits = NB * (K >> 3);
     u32x4 xr[XU];
-    x_fetch<NB, XU>(x4, K, xr);
+    if (xreg) {                                  // XU x units per thread cover x
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int i = threadIdx.x + u * blockDim.x;
+            xr[u] = x4[i < xunits ? i : 0];
+        }
+    } else {
+        x_dma<F, NB>(x4, K, bstride, lds_offset_of(xs), wave, nwaves, lane);
+    }
+    if (xfirst)
+        __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 v[CPL];
     uint32_t mk[CPL];
     load_chunks<F, CPL>(row.w, row.m, cbeg, cend, lane, v, mk);
-
-    u32x4* tab = smem;
-    u32x4* xs = smem + table_units<F>();
-    const int bstride = K / 8;
-    float* part = reinterpret_cast<float*>(xs + NB * bstride);
     build_table<F>(tab);
-    x_store<F, NB, XU>(xs, x4, K, bstride, xr);
-    __syncthreads();
+    constexpr int NW = F == kDense ? CPL : 2 * CPL;   // weight loads issued after x
+    if (xreg) {
+        wait_vmcnt<NW>();
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int i = threadIdx.x + u * blockDim.x;
+            if (i < xunits) {
+                const int b = NB == 1 ? 0 : i / (K >> 3);
+                xs[x_slot<F>(b, i - b * (K >> 3), bstride)] = xr[u];
+            }
+        }
+    }
+    // This wave's x loads, issued before its weight loads, have landed and its
+    // LDS stores are done; then the block meets at a barrier with no memory
+    // fence (a fence would wait for the weight loads too).
+    wait_vmcnt_lgkm0<NW>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
     float acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
         acc[b] = 0.f;
+    const int xl = chunk_xslot<F>(cbeg + lane);      // cbeg % 32 == 0: slot u is xl + u * step
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
         if (u * kWave >= cend - cbeg)          // wave-uniform: nothing left in this slot for any lane
             break;
-        const int c = cbeg + lane + u * kWave;
-        const bool live = c < cend;
-        chunk_live(live, v[u], mk[u]);
-        chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, live ? c : 0, bstride, acc);
+        if ((u + 1) * kWave <= cend - cbeg) {  // wave-uniform: every lane holds a chunk
+            chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, xl + u * xslot_step<F>(), bstride, acc);
+        } else {
+            const bool live = cbeg + lane + u * kWave < cend;
+            chunk_live(live, v[u], mk[u]);
+            chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, live ? xl + u * xslot_step<F>() : 0, bstride, acc);
+        }
     }
     float sum[NB];
 #pragma unroll
@@ -578,10 +712,10 @@ __device__ __forceinline__ void rowslice_body(const Parts& P, const u32x4* __res
 }
 
 template <int F, int DT, int NB, int CPL, int XU>
-__global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K, int S,
-                                                        int rows_per_block)
+__global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
+                                                        int ls, int rows_per_block, int xfirst, int xreg)
 {
-    rowslice_body<F, DT, NB, CPL, XU>(P, x4, R, K, S, rows_per_block, blockIdx.x);
+    rowslice_body<F, DT, NB, CPL, XU>(P, x4, R, K, ls, rows_per_block, xfirst, xreg, blockIdx.x);
 }
 
 // A hybrid matrix (sparse rows PS plus dense rows PD, both scattered into one
@@ -590,17 +724,19 @@ __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32
 // plan, the rest the dense rows' plan with twice the slices and half the rows
 // per block -- a dense row has twice the chunks of a sparse one at the same
 // K, so both plans give a lane the same CPL chunks and a block the same
-// waves and x registers.
+// waves.
 template <int F, int DT, int NB, int CPL, int XU>
 __global__ __launch_bounds__(1024) void hybrid_rowslice_kernel(const Parts PS, const Parts PD,
                                                                const u32x4* __restrict__ x4, int RS, int RD, int K,
-                                                               int S, int rows_per_block, int sparse_blocks)
+                                                               int ls, int rows_per_block, int xfirst, int xreg,
+                                                               int sparse_blocks)
 {
     const unsigned blk = blockIdx.x;
     if (blk < (unsigned)sparse_blocks)
-        rowslice_body<F, DT, NB, CPL, XU>(PS, x4, RS, K, S, rows_per_block, blk);
+        rowslice_body<F, DT, NB, CPL, XU>(PS, x4, RS, K, ls, rows_per_block, xfirst, xreg, blk);
     else
-        rowslice_body<kDense, DT, NB, CPL, XU>(PD, x4, RD, K, 2 * S, rows_per_block / 2, blk - sparse_blocks);
+        rowslice_body<kDense, DT, NB, CPL, XU>(PD, x4, RD, K, ls + 1, rows_per_block / 2, xfirst, xreg,
+                                               blk - sparse_blocks);
 }
 
 // ---- streaming kernel --------------------------------------------------------
@@ -637,7 +773,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
 #pragma unroll
     for (int b = 0; b < NB; ++b)
         gs[b] = 0.f;
-    const int bstride = tile_cols / 8;
+    const int bstride = x_row_units(tile_cols);
 
     u32x4* tab = smem;
     u32x4* xs = smem + table_units<F>();
@@ -684,7 +820,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
                 u32x4 vv = v[u];
                 uint32_t mm = mk[u];
                 chunk_live(live, vv, mm);
-                chunk_dot<F, DT, NB>(vv, mm, tab, xs, live ? c - cb : 0, bstride, acc);
+                chunk_dot<F, DT, NB>(vv, mm, tab, xs, live ? chunk_xslot<F>(c - cb) : 0, bstride, acc);
             }
             if (q == gpr - 1) {
                 const RowRef row = row_ref(P, lrow(t), C);
@@ -1056,35 +1192,6 @@ __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u3
 //  * masks: 16 rows x 32 bytes; position p of a row holds mask dword
 //    2 (p % 4) + p / 4, so that dwords 0, 2, 4, 6 (chunks 4 t + q, q < 2) and
 //    1, 3, 5, 7 (q >= 2) each form one 16-byte read.
-// A load instruction's LDS destination is its base (M0) + 16 bytes x lane;
-// these kernels declare no static LDS, so dynamic LDS starts at offset 0.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-
-template <int BYTES>
-__device__ __forceinline__ void load_to_lds(const void* g, uint32_t lds_offset)
-{
-    static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte lanes");
-#if defined(__HIP_DEVICE_COMPILE__)
-    lds_void_t* dst = (lds_void_t*)((lds_u8_t*)nullptr + lds_offset);
-    if constexpr (BYTES == 16)
-        __builtin_amdgcn_global_load_lds(g, dst, 16, 0, 0);
-    else
-        __builtin_amdgcn_global_load_lds(g, dst, 4, 0, 0);
-#else
-    (void)g;
-    (void)lds_offset;
-#endif
-}
-
-// s_waitcnt with vmcnt <= N (N < 64) and the other counters left alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 constexpr int kRingValues = 16 * kStageChunks * 16;               // 4 KB
 constexpr int kRingMasks = 16 * kStageChunks * 2;                 // 512 B
 
@@ -1753,10 +1860,14 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 // NMSPMV_BLOCKS, NMSPMV_THREADS, NMSPMV_TILE_BYTES (stream);
 // NMSPMV_MFMA_MIN_B (smallest batch sent to the matrix-core kernels),
 // NMSPMV_MFMA_SLICES; NMSPMV_HYBRID_SPLIT=1 runs a hybrid matrix's sparse and
-// dense rows as two launches.
+// dense rows as two launches; NMSPMV_XFIRST=0/1 turns the row-slice kernel's
+// x-first issue order off/on (default: on where a row is cut into slices);
+// NMSPMV_BLOCKS_PER_CU (2 to 8) caps a row-slice launch's resident blocks
+// per CU by padding its LDS; NMSPMV_XDMA=1 stages x by global-to-LDS loads
+// wherever one register per thread does not cover it.
 struct Env {
     int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0,
-        ring_tiles = 0, ring_share = 0, hybrid_split = 0;
+        ring_tiles = 0, ring_share = 0, hybrid_split = 0, xfirst = -1, blocks_per_cu = 0, xdma = 0;
 };
 Env g_env;
 std::once_flag g_env_once;
@@ -1778,6 +1889,10 @@ void read_env()
     g_env.ring_tiles = get("NMSPMV_RING_TILES");
     g_env.ring_share = get("NMSPMV_RING_SHARE");
     g_env.hybrid_split = get("NMSPMV_HYBRID_SPLIT");
+    g_env.blocks_per_cu = get("NMSPMV_BLOCKS_PER_CU");
+    g_env.xdma = get("NMSPMV_XDMA");
+    const char* xf = std::getenv("NMSPMV_XFIRST");
+    g_env.xfirst = xf ? std::atoi(xf) : -1;
 }
 
 int g_cu_count[64] = {};
@@ -1814,10 +1929,20 @@ int allow_full_lds(const void* kernel, bool* raised)
 
 struct Plan {
     int kind = 0;            // 1 row-slice, 3 stream
-    int S = 1, rpb = 1, cpl = 1, xu = 4, threads = 256, tile_cols = 0;
+    int S = 1, rpb = 1, cpl = 1, threads = 256, tile_cols = 0;
+    int ls = 0;              // log2(S) (row-slice: S is a power of two)
+    int xf = 0;              // row-slice: x loads issued by the whole block before any weight load
     size_t lds = 0;
     unsigned grid = 1;
 };
+
+int log2_exact(int v)
+{
+    int l = 0;
+    while ((1 << (l + 1)) <= v)
+        ++l;
+    return l;
+}
 
 // Row-slice shape (rules from timing sweeps on MI355X over the Llama-3.1-8B,
 // Llama-3.3-70B and Qwen3 projection shapes, sparse and dense):
@@ -1828,10 +1953,13 @@ struct Plan {
 //    longer: the fewest slices that keep a lane at <= 7 chunks, 8 / S rows;
 //  * few rows (under ~16 waves per CU): more slices, down to 64 chunks each;
 //  * at least two blocks per CU;
-//  * a single x vector is staged from as few registers as cover it (1, 2 or
-//    4 units per thread); sparse rows cut into slices go in 16-wave blocks
-//    when that lets 2 units cover x (fewer registers, full occupancy).
-bool plan_rowslice(int64_t R, int64_t C, int64_t xunits, bool dense, bool glu, Plan* P)
+//  * blocks of at most 8 waves: 16-wave blocks (tried for the Llama-3.1-8B
+//    down projection, 4096 x 14336) timed 12.5 us on some MI355X GPUs and
+//    13.7-14.9 us, with a wide spread between launches, on others, where
+//    8-wave blocks held 12.4-12.5 us on all of them;
+//  * rows cut into slices issue x first (x-first issue order; the same
+//    sweep: 12.7-12.8 us without it).
+bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, Plan* P)
 {
     const int cus = cu_count();
     int S = 1, rpb = dense ? 4 : 8;
@@ -1847,7 +1975,7 @@ bool plan_rowslice(int64_t R, int64_t C, int64_t xunits, bool dense, bool glu, P
         rpb = std::max(1, 8 / S);
     }
     if (g_env.slices > 0)
-        S = g_env.slices;
+        S = 1 << log2_exact(std::min(g_env.slices, 16));
     if (glu && S > 8)                            // gated rows come in pairs: at least 2 rows per block
         S = 8;
     const int64_t cps = (C + S - 1) / S;
@@ -1856,8 +1984,6 @@ bool plan_rowslice(int64_t R, int64_t C, int64_t xunits, bool dense, bool glu, P
         return false;
     while (rpb > 1 && (R + rpb - 1) / rpb < 2 * cus)
         rpb /= 2;
-    if (xunits <= 2048 && !dense && S >= 2 && rpb * S == 8 && xunits > 2 * 8 * kWave && (R + 2 * rpb - 1) / (2 * rpb) >= 2 * cus)
-        rpb *= 2;
     if (g_env.rpb > 0)
         rpb = g_env.rpb;
     if (glu)
@@ -1865,12 +1991,12 @@ bool plan_rowslice(int64_t R, int64_t C, int64_t xunits, bool dense, bool glu, P
     if (rpb * S > 16)
         return false;
     const int64_t threads = (int64_t)rpb * S * kWave;
-    const int64_t per_thread = (xunits + threads - 1) / threads;
     P->kind = 1;
     P->S = S;
+    P->ls = log2_exact(S);
+    P->xf = g_env.xfirst >= 0 ? (g_env.xfirst != 0) : (S >= 2);
     P->rpb = rpb;
     P->cpl = cpl;
-    P->xu = per_thread <= 1 ? 1 : per_thread <= 2 ? 2 : 4;
     P->threads = (int)threads;
     P->grid = (unsigned)((R + rpb - 1) / rpb);
     return true;
@@ -1887,16 +2013,16 @@ Plan plan_for(int64_t R, int64_t K, int B, bool glu)
     constexpr int COLS = chunk_cols<F>();
     const int64_t C = K / COLS;
     const size_t tab = (size_t)table_units<F>() * sizeof(u32x4);
-    const size_t xbytes = (size_t)B * (size_t)K * 2;
+    const size_t xbytes = (size_t)B * (size_t)x_row_units(K) * 16;   // x as staged (rows rounded to 64 units)
     const bool fits = xbytes <= (size_t)kXTileBudget;
     Plan P;
     int kind = g_env.kernel;
     if (kind != 1 && kind != 3)
         kind = (fits && C <= (F == kDense ? 32 : 18) * kWave) ? 1 : 3;
-    if (kind == 1 && fits && plan_rowslice(R, C, (int64_t)B * K / 8, F == kDense, glu, &P)) {
-        if (B > 1)
-            P.xu = 4;                            // batched launches: one x register count
+    if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, glu, &P)) {
         P.lds = tab + xbytes + (size_t)P.rpb * P.S * B * 4;
+        if (g_env.blocks_per_cu >= 2 && g_env.blocks_per_cu <= 8)
+            P.lds = std::max(P.lds, (size_t)kLdsMax / (g_env.blocks_per_cu + 1) + 256);
         return P;
     }
     const int cus = cu_count();
@@ -1933,12 +2059,12 @@ Plan plan_for(int64_t R, int64_t K, int B, bool glu)
             blocks = (Ru + nw * (rpw_max / per) - 1) / (nw * (rpw_max / per));
             rpw = per * ((Ru + blocks * nw - 1) / (blocks * nw));
         }
-        while (tile > 1024 && tab + (size_t)B * tile * 2 + (size_t)nw * rpw * B * 4 > (size_t)kLdsMax)
+        while (tile > 1024 && tab + (size_t)B * x_row_units(tile) * 16 + (size_t)nw * rpw * B * 4 > (size_t)kLdsMax)
             tile -= 1024;
     }
     P.tile_cols = (int)tile;
     P.grid = (unsigned)blocks;
-    P.lds = tab + (size_t)B * (size_t)tile * 2 + (tile < K ? (size_t)nw * rpw * B * 4 : 0);
+    P.lds = tab + (size_t)B * (size_t)x_row_units(tile) * 16 + (tile < K ? (size_t)nw * rpw * B * 4 : 0);
     return P;
 }
 
@@ -2149,24 +2275,23 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
     const u32x4* x4 = static_cast<const u32x4*>(x);
     (void)hipGetLastError();
     if (P.kind == 1) {
-        // Single-vector launches pick 1, 2 or 4 x registers per thread;
-        // batched ones always use 4 (fewer instantiations).
-        const int xu = NB == 1 ? P.xu : 4;
-#define NM_SLICE_XU(CPL, XU) \
-    hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, CPL, XU>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, K, \
-                       P.S, P.rpb)
-#define NM_SLICE(CPL)                                            \
-    do {                                                         \
-        if constexpr (NB == 1) {                                 \
-            if (xu == 1)                                         \
-                NM_SLICE_XU(CPL, 1);                             \
-            else if (xu == 2)                                    \
-                NM_SLICE_XU(CPL, 2);                             \
-            else                                                 \
-                NM_SLICE_XU(CPL, 4);                             \
-        } else {                                                 \
-            NM_SLICE_XU(CPL, 4);                                 \
-        }                                                        \
+        // x staging: one register per thread where that covers x; four for a
+        // single vector that they cover; else global-to-LDS loads.
+        const int64_t xunits = (int64_t)NB * (K / 8);
+        const int xu = xunits <= P.threads ? 1 : (NB == 1 && xunits <= 4LL * P.threads && g_env.xdma != 1) ? 4 : 0;
+#define NM_SLICE_XU(CPL, XU)                                                                                         \
+    hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, CPL, XU>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, \
+                       K, P.ls, P.rpb, P.xf, (int)(xu != 0))
+#define NM_SLICE(CPL)                  \
+    do {                               \
+        if constexpr (NB == 1) {       \
+            if (xu == 4)               \
+                NM_SLICE_XU(CPL, 4);   \
+            else                       \
+                NM_SLICE_XU(CPL, 1);   \
+        } else {                       \
+            NM_SLICE_XU(CPL, 1);       \
+        }                              \
     } while (0)
         switch (P.cpl) {
         case 1: NM_SLICE(1); break;
@@ -2211,7 +2336,7 @@ int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS,
         P.rpb = 2;
         P.threads = 2 * P.S * kWave;
         P.grid = (unsigned)((RS + 1) / 2);
-        P.lds = (size_t)table_units<F>() * sizeof(u32x4) + (size_t)NB * K * 2 + (size_t)P.rpb * P.S * NB * 4;
+        P.lds = (size_t)table_units<F>() * sizeof(u32x4) + (size_t)NB * x_row_units(K) * 16 + (size_t)P.rpb * P.S * NB * 4;
     }
     if (P.kind != 1 || P.rpb < 2 || P.rpb % 2 != 0)
         return NM_OK;
@@ -2219,22 +2344,9 @@ int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS,
     const int64_t sblocks = P.grid, blocks = sblocks + (RD + dense_rpb - 1) / dense_rpb;
     const u32x4* x4 = static_cast<const u32x4*>(x);
     (void)hipGetLastError();
-#define NM_HYB_XU(CPL, XU)                                                                                       \
-    hipLaunchKernelGGL((hybrid_rowslice_kernel<F, DT, NB, CPL, XU>), dim3((unsigned)blocks), dim3(P.threads), P.lds, \
-                       s, PS, PD, x4, RS, RD, K, P.S, P.rpb, (int)sblocks)
-#define NM_HYB(CPL)                             \
-    do {                                        \
-        if constexpr (NB == 1) {                \
-            if (P.xu == 1)                      \
-                NM_HYB_XU(CPL, 1);              \
-            else if (P.xu == 2)                 \
-                NM_HYB_XU(CPL, 2);              \
-            else                                \
-                NM_HYB_XU(CPL, 4);              \
-        } else {                                \
-            NM_HYB_XU(CPL, 4);                  \
-        }                                       \
-    } while (0)
+#define NM_HYB(CPL)                                                                                             \
+    hipLaunchKernelGGL((hybrid_rowslice_kernel<F, DT, NB, CPL, 1>), dim3((unsigned)blocks), dim3(P.threads), P.lds, s, \
+                       PS, PD, x4, RS, RD, K, P.ls, P.rpb, P.xf, (int)(NB * (K / 8) <= P.threads), (int)sblocks)
     switch (P.cpl) {
     case 1: NM_HYB(1); break;
     case 2: NM_HYB(2); break;
@@ -2246,7 +2358,6 @@ int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS,
     default: NM_HYB(8); break;
     }
 #undef NM_HYB
-#undef NM_HYB_XU
     *launched = true;
     return hip_status(hipGetLastError());
 }
