@@ -73,6 +73,8 @@ def parse():
     p.add_argument("--crossover", action="store_true",
                    help="batch crossover study instead of the step: Qwen3-32B MLP shapes (2:4 bf16) at B = 1..32, "
                         "sparse vs the dense kernel vs torch's matmul; prints one JSON line")
+    p.add_argument("--no-configs", action="store_true",
+                   help="leave out the other workloads' step figures (extras.configs) from the default run")
     p.add_argument("--no-glu", action="store_true",
                    help="skip the gated gate+up launch (its grid equals the plain gate+up launch's, which would mix "
                         "the two in a kernel trace keyed by kernel and grid)")
@@ -190,7 +192,7 @@ def capture(torch, fn, args_for_stream):
 
 def read_ceiling(torch, cur):
     """Plain 16-byte streaming read of 1 GB regions rotated over 4 GB."""
-    from sparse_matrix_vector_amd import probe
+    from measure import probe
     lib = probe.lib()
     buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
@@ -212,7 +214,7 @@ def read_ceiling(torch, cur):
 def copy_calibration(torch, cur, nbytes=256 << 20):
     """One plain 16-byte copy of known size: its FETCH_SIZE / WRITE_SIZE
     counter readings calibrate the counters' units in profiling runs."""
-    from sparse_matrix_vector_amd import probe
+    from measure import probe
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     if probe.lib().nmp_copy(P(src.data_ptr()), P(dst.data_ptr()), nbytes, 1024, P(cur)) != 0:
@@ -220,6 +222,15 @@ def copy_calibration(torch, cur, nbytes=256 << 20):
     torch.cuda.synchronize()
     del src, dst
     return nbytes
+
+
+def burst(torch, fn, args_for_stream, trials):
+    """(min, median, max) per-launch microseconds of a back-to-back burst of
+    fn(*args) launches, captured once into a HIP graph and replayed (a
+    launch from Python can take longer than a small kernel runs)."""
+    g = capture(torch, fn, args_for_stream)
+    n = len(args_for_stream(0))
+    return trials_us(torch, g.replay, trials, n)
 
 
 def trials_us(torch, body, trials, launches):
@@ -232,31 +243,36 @@ def trials_us(torch, body, trials, launches):
 
 def mlp_single(torch, lib, launches, cur, reps=10, trials=20):
     """MLP projections (gate, up, down) as single nm_spmv / nm_gemv_dense
-    launches, back to back over every layer's weights; per-launch time is the
-    median over `trials` bursts (min and max beside it)."""
+    launches, back to back over every layer's weights (HIP-graph bursts);
+    per-launch time is the median over `trials` bursts (min and max beside
+    it)."""
     out = {}
     for name in ("gate", "up", "down"):
-        sargs, dargs, nbytes, dbytes = [], [], 0, 0
-        for L in launches:
-            if name not in L.names:
-                continue
-            i = L.names.index(name)
-            R, K = L.R[i], L.K
-            sargs.append((P(L.values[i].data_ptr()), P(L.masks[i].data_ptr()), I64(R), I64(K), I32(L.n), I32(L.m),
-                          I32(L.dtc), P(L.x.data_ptr()), I32(L.B), P(L.y[i].data_ptr()), P(cur)))
-            dargs.append((P(L.W[i].data_ptr()), I64(R), I64(K), I32(L.dtc), P(L.x.data_ptr()), I32(L.B),
-                          P(L.yd[i].data_ptr()), P(cur)))
-            nbytes = L.part_bytes(i) + L.B * K * 2
-            dbytes = R * K * 2 + L.B * (K + R) * 2
-        if not sargs:
+        group = [L for L in launches if name in L.names]
+        if not group:
             continue
-        run(lib.nm_spmv, sargs)
-        ts = trials_us(torch, lambda: run(lib.nm_spmv, sargs), trials, len(sargs))
-        run(lib.nm_gemv_dense, dargs)
-        td = trials_us(torch, lambda: run(lib.nm_gemv_dense, dargs), trials, len(dargs))
+        L0 = group[0]
+        i0 = L0.names.index(name)
+        R, K, B = L0.R[i0], L0.K, L0.B
+
+        def sargs(st):
+            out_ = []
+            for L in group:
+                i = L.names.index(name)
+                out_.append((P(L.values[i].data_ptr()), P(L.masks[i].data_ptr()), I64(R), I64(K), I32(L.n),
+                             I32(L.m), I32(L.dtc), P(L.x.data_ptr()), I32(L.B), P(L.y[i].data_ptr()), P(st)))
+            return out_
+
+        def dargs(st):
+            return [(P(L.W[L.names.index(name)].data_ptr()), I64(R), I64(K), I32(L.dtc), P(L.x.data_ptr()),
+                     I32(L.B), P(L.yd[L.names.index(name)].data_ptr()), P(st)) for L in group]
+        nbytes = L0.part_bytes(i0) + B * K * 2
+        dbytes = R * K * 2 + B * (K + R) * 2
+        ts = burst(torch, lib.nm_spmv, sargs, trials)
+        td = burst(torch, lib.nm_gemv_dense, dargs, trials)
         us, usd = ts[1], td[1]
         # torch's own dense product (hipBLASLt / rocBLAS) on the same weights, as context
-        pairs = [(L.W[L.names.index(name)], L.x, L.yd[L.names.index(name)]) for L in launches if name in L.names]
+        pairs = [(L.W[L.names.index(name)], L.x, L.yd[L.names.index(name)]) for L in group]
 
         def torch_linear():
             for W, x, yd in pairs:
@@ -292,17 +308,18 @@ def hybrid_gate(torch, nm, lib, launches, cur, fracs=(0.05, 0.10), reps=5):
             flags = nm.hybrid_select_rows(nm.hybrid_row_loss(W, L.n, L.m), nd)
             hybs.append((nm.hybrid_pack(W, flags, nd, L.n, L.m), L))
         ys = [torch.empty_like(L.y[i]) for _, L in hybs]     # own outputs: L.y is checked against the oracle later
-        args = [(P(h.values.data_ptr()), P(h.masks.data_ptr()), P(h.rows_sparse.data_ptr()), P(h.W_dense.data_ptr()),
-                 P(h.rows_dense.data_ptr()), I64(nd), I64(R), I64(K), I32(h.n), I32(h.m), I32(L.dtc),
-                 P(L.x.data_ptr()), I32(B), P(y.data_ptr()), P(cur)) for (h, L), y in zip(hybs, ys)]
-        run(lib.nm_spmv_hybrid, args)
-        us = time_ms(torch, lambda: run(lib.nm_spmv_hybrid, args), reps) / len(args) * 1e3
+
+        def args(st):
+            return [(P(h.values.data_ptr()), P(h.masks.data_ptr()), P(h.rows_sparse.data_ptr()),
+                     P(h.W_dense.data_ptr()), P(h.rows_dense.data_ptr()), I64(nd), I64(R), I64(K), I32(h.n), I32(h.m),
+                     I32(L.dtc), P(L.x.data_ptr()), I32(B), P(y.data_ptr()), P(st)) for (h, L), y in zip(hybs, ys)]
+        us = burst(torch, lib.nm_spmv_hybrid, args, reps)[1]
         h0, L0 = hybs[0]
         Rs = R - nd
         nbytes = Rs * K * h0.n // h0.m * 2 + Rs * K // 8 + nd * K * 2 + R * 4 + B * (K + R) * 2
         out[f"{int(frac * 100)}pct_dense_rows"] = {"shape": [R, K], "dense_rows": nd, "us": round(us, 3),
                                                    "gbs": round(nbytes / us / 1e3, 1), "bytes": nbytes}
-        del hybs, args, ys
+        del hybs, ys
         torch.cuda.empty_cache()
     return out
 
@@ -427,6 +444,51 @@ def measured_traffic():
     return rec["traffic_bytes_per_launch"] if rec.get("source_sha256") == sha else None
 
 
+# The other workloads, each as a decode step over its own weight instances
+# (more than the 256 MB last-level cache holds), in the default run's line.
+CONFIG_STEPS = [("qwen3_14b_4of8", 8), ("qwen3_14b_2of4", 8), ("qwen3_32b_4of8", 8), ("qwen3_32b_2of4", 8),
+                ("llama33_70b", 8), ("qwen3_32b_b1", 8), ("qwen3_32b_b2", 8), ("qwen3_32b_b4", 8),
+                ("qwen3_32b_b8", 8)]
+
+
+def config_steps(torch, nm, I, specs, steps=10):
+    """Each workload of CONFIG_STEPS as a HIP-graph step over `layers` layer
+    instances of its projections: GB/s (algorithmic bytes per step / step
+    time), share of the 8 TB/s peak, speedup over the same step on the dense
+    weights (nm_gemv_dense_multi), us per layer, and per launch kind the
+    median us of back-to-back bursts."""
+    lib = nm.lib()
+    out = {}
+    for name, layers in CONFIG_STEPS:
+        spec = specs[name]
+        launches = build_step(spec, name, layers, torch, nm, I)
+        sparse_bytes = sum(L.sparse_bytes() for L in launches)
+        dense_bytes = sum(L.dense_bytes() for L in launches)
+        gs = capture(torch, lib.nm_spmv_multi, lambda st: [L.sparse_args(st) for L in launches])
+        gd = capture(torch, lib.nm_gemv_dense_multi, lambda st: [L.dense_args(st) for L in launches])
+        for _ in range(3):
+            gs.replay()
+        ms = time_ms(torch, gs.replay, steps)
+        for _ in range(3):
+            gd.replay()
+        msd = time_ms(torch, gd.replay, steps)
+        kinds = {}
+        for names, _ in spec[7]:
+            kind = "+".join(names)
+            group = [L for L in launches if L.kind == kind]
+            kinds[kind] = round(burst(torch, lib.nm_spmv_multi, lambda st: [L.sparse_args(st) for L in group], 5)[1], 3)
+        gbs = sparse_bytes / (ms * 1e-3) / 1e9
+        out[name] = {"workload": spec[0], "layers": layers, "n_m": f"{spec[4]}:{spec[5]}", "batch": spec[6],
+                     "gbs": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
+                     "speedup_vs_dense": round(msd / ms, 4), "us_per_layer": round(ms * 1e3 / layers, 2),
+                     "ms_per_step": round(ms, 4), "dense_ms_per_step": round(msd, 4),
+                     "packed_bytes_per_step": sparse_bytes, "per_launch_us": kinds}
+        del launches, gs, gd
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def crossover(torch, nm, I, batches=(1, 2, 4, 8, 16, 32)):
     """Sparse 2:4 (nm_spmv), dense (nm_gemv_dense) and torch.matmul (hipBLASLt)
     on the Qwen3-32B MLP shapes over a range of batch sizes, each timed over
@@ -497,6 +559,7 @@ def main():
     cur = torch.cuda.current_stream().cuda_stream
 
     launches = build_step(spec, a.workload, layers, torch, nm, I)
+    n_launches = len(launches)
     sparse_bytes = sum(L.sparse_bytes() for L in launches)
     dense_bytes = sum(L.dense_bytes() for L in launches)
 
@@ -525,32 +588,29 @@ def main():
     for names, _ in spec[7]:
         kind = "+".join(names)
         group = [L for L in launches if L.kind == kind]
-        sl = [L.sparse_args(cur) for L in group]
-        dl = [L.dense_args(cur) for L in group]
-        run(lib.nm_spmv_multi, sl)
-        us = time_ms(torch, lambda: run(lib.nm_spmv_multi, sl), 5) / len(sl) * 1e3
-        run(lib.nm_gemv_dense_multi, dl)
-        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense_multi, dl), 5) / len(dl) * 1e3
+        ts = burst(torch, lib.nm_spmv_multi, lambda st: [L.sparse_args(st) for L in group], 10)
+        td = burst(torch, lib.nm_gemv_dense_multi, lambda st: [L.dense_args(st) for L in group], 10)
+        us, usd = ts[1], td[1]
         sb, db = group[0].sparse_bytes(), group[0].dense_bytes()
-        per[kind] = {"rows": sum(group[0].R), "K": group[0].K, "us": round(us, 3), "gbs": round(sb / us / 1e3, 1),
-                     "dense_us": round(usd, 3), "dense_gbs": round(db / usd / 1e3, 1), "speedup": round(usd / us, 4),
-                     "bytes": sb}
+        per[kind] = {"rows": sum(group[0].R), "K": group[0].K, "us": round(us, 3), "us_min": round(ts[0], 3),
+                     "us_max": round(ts[2], 3), "trials": 10, "gbs": round(sb / us / 1e3, 1),
+                     "pct_of_peak": round(100 * sb / us / 1e3 / PEAK_GBS, 2), "dense_us": round(usd, 3),
+                     "dense_us_min": round(td[0], 3), "dense_us_max": round(td[2], 3),
+                     "dense_gbs": round(db / usd / 1e3, 1), "speedup": round(usd / us, 4), "bytes": sb}
 
     # ---- gated MLP input as one launch: h = SiLU(gate x) * (up x) ----
     group = [L for L in launches if L.names == ("gate", "up")]
     if group and not a.no_glu:
-        sl = [L.glu_args(cur) for L in group]
-        dl = [L.glu_args(cur, dense=True) for L in group]
-        run(lib.nm_spmv_swiglu, sl)
-        us = time_ms(torch, lambda: run(lib.nm_spmv_swiglu, sl), 5) / len(sl) * 1e3
-        run(lib.nm_gemv_dense_swiglu, dl)
-        usd = time_ms(torch, lambda: run(lib.nm_gemv_dense_swiglu, dl), 5) / len(dl) * 1e3
+        ts = burst(torch, lib.nm_spmv_swiglu, lambda st: [L.glu_args(st) for L in group], 10)
+        td = burst(torch, lib.nm_gemv_dense_swiglu, lambda st: [L.glu_args(st, dense=True) for L in group], 10)
+        us, usd = ts[1], td[1]
         L0 = group[0]
         sb = L0.sparse_bytes() - L0.B * L0.R[1] * 2          # one output of R rows instead of two
         db = L0.dense_bytes() - L0.B * L0.R[1] * 2
-        per["gate+up+silu"] = {"rows": L0.R[0], "K": L0.K, "us": round(us, 3), "gbs": round(sb / us / 1e3, 1),
-                               "dense_us": round(usd, 3), "dense_gbs": round(db / usd / 1e3, 1),
-                               "speedup": round(usd / us, 4), "bytes": sb}
+        per["gate+up+silu"] = {"rows": L0.R[0], "K": L0.K, "us": round(us, 3), "us_min": round(ts[0], 3),
+                               "us_max": round(ts[2], 3), "trials": 10, "gbs": round(sb / us / 1e3, 1),
+                               "pct_of_peak": round(100 * sb / us / 1e3 / PEAK_GBS, 2), "dense_us": round(usd, 3),
+                               "dense_gbs": round(db / usd / 1e3, 1), "speedup": round(usd / us, 4), "bytes": sb}
 
     if a.workload == "llama31_8b":
         # roofline kernel: the instantiation shared by the K = 4096 launches (3 per layer)
@@ -575,6 +635,13 @@ def main():
     worst = sampled_parity(launches, torch)
     default_workload = a.workload == "llama31_8b"
     cpu = None if (a.no_cpu or not default_workload) else cpu_baseline(launches, a.cpu_seconds, torch, desc)
+    if default_workload and not a.no_configs:
+        # the step's own weights are no longer needed: free them before the other workloads
+        del launches
+        step_sparse = step_dense = gs = gd = None                 # noqa: F841 -- releases the step's graphs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        extras["configs"] = config_steps(torch, nm, I, specs)
 
     gbs = sparse_bytes / (ms_step * 1e-3) / 1e9
     props = torch.cuda.get_device_properties(0)
@@ -592,7 +659,7 @@ def main():
         "dtype": "f16" if dts == "fp16" else "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "name": a.workload, "layers": layers, "n_m": f"{n}:{m}", "batch": B,
-                   "launches_per_step": len(launches), "mode": "eager" if a.eager else "hip_graph",
+                   "launches_per_step": n_launches, "mode": "eager" if a.eager else "hip_graph",
                    "packed_bytes_per_step": sparse_bytes, "dense_bytes_per_step": dense_bytes},
         "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
         "speedup_vs_dense": round(ms_dense / ms_step, 4),

@@ -1,6 +1,6 @@
 """ctypes binding of libnmprobe (read-stream ceiling, copy, empty launch).
 
-Measurement helpers only; the product calls live in the package root."""
+Measurement helpers only; the product calls live in sparse_matrix_vector_amd."""
 import ctypes
 import os
 
@@ -12,7 +12,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_PATH):
-            raise RuntimeError(f"{_PATH} is missing: run __graft_entry__.build()")
+            raise RuntimeError(f"{_PATH} is missing: run __graft_entry__.build() or python measure/build.py")
         h = ctypes.CDLL(_PATH)
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         h.nmp_read.argtypes = [P, I64, P, I, P]

@@ -1,7 +1,7 @@
 """Summarise rocprofv3 CSV output (kernel trace and counter collection).
 
-    python -m sparse_matrix_vector_amd.profsummary trace <run>_kernel_trace.csv
-    python -m sparse_matrix_vector_amd.profsummary pmc <run>_counter_collection.csv COUNTER [calib_kernel calib_bytes]
+    python -m measure.profsummary trace <run>_kernel_trace.csv
+    python -m measure.profsummary pmc <run>_counter_collection.csv COUNTER [calib_kernel calib_bytes]
 
 `trace` prints, per kernel name and grid size, the dispatch count and the
 mean / min / max duration in microseconds.  `pmc` prints, per kernel name and

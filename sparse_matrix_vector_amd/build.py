@@ -11,8 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = [os.path.join(HERE, "csrc", "nmspmv.hip"), os.path.join(HERE, "csrc", "nmcalib.hip")]
 LIB = os.path.join(HERE, "libnmspmv.so")
-# (sources, library): the product library and the measurement probes beside it
-TARGETS = [(SRC, LIB), ([os.path.join(HERE, "csrc", "nmprobe.hip")], os.path.join(HERE, "libnmprobe.so"))]
+# (sources, library): the product library
+TARGETS = [(SRC, LIB)]
 ARCH = "gfx950"
 
 

@@ -78,3 +78,16 @@ def test_trials_statistics_order():
 
     lo, med, hi = bench.trials_us(_Torch, lambda: None, 3, 1)
     assert (lo, med, hi) == (1000.0, 2000.0, 3000.0)
+
+
+def test_config_steps_cover_every_other_workload():
+    """The default line's extras.configs block covers the Qwen3-14B/32B MLP
+    steps at 4:8 and 2:4, the Llama-3.3-70B layer sweep and the Qwen3-32B
+    batches of 1/2/4/8, each over at least 8 weight instances per shape."""
+    specs = bench.workloads(I)
+    names = [n for n, _ in bench.CONFIG_STEPS]
+    for n, layers in bench.CONFIG_STEPS:
+        assert n in specs and layers >= 8, n
+    for need in ("qwen3_14b_4of8", "qwen3_14b_2of4", "qwen3_32b_4of8", "qwen3_32b_2of4", "llama33_70b",
+                 "qwen3_32b_b1", "qwen3_32b_b2", "qwen3_32b_b4", "qwen3_32b_b8"):
+        assert need in names, need
