@@ -431,14 +431,12 @@ def sampled_parity(launches, torch):
 def measured_traffic():
     """HBM bytes per launch of the roofline kernel from the committed counter
     summary, or None when the kernel source changed since it was taken."""
-    import hashlib
+    from measure.profsummary import kernel_sources_sha256
     path = os.path.join(ROOT, "profiles", "nm_spmv_llama31_8b_decode_traffic.json")
-    src = os.path.join(ROOT, "sparse_matrix_vector_amd", "csrc", "nmspmv.hip")
     try:
         with open(path) as fh:
             rec = json.load(fh)
-        with open(src, "rb") as fh:
-            sha = hashlib.sha256(fh.read()).hexdigest()
+        sha = kernel_sources_sha256()
     except OSError:
         return None
     return rec["traffic_bytes_per_launch"] if rec.get("source_sha256") == sha else None

@@ -2,6 +2,7 @@
 
     python -m measure.profsummary trace <run>_kernel_trace.csv
     python -m measure.profsummary pmc <run>_counter_collection.csv COUNTER [calib_kernel calib_bytes]
+    python -m measure.profsummary sha
 
 `trace` prints, per kernel name and grid size, the dispatch count and the
 mean / min / max duration in microseconds.  `pmc` prints, per kernel name and
@@ -9,11 +10,28 @@ grid size, the mean of COUNTER per dispatch (nominally KiB for FETCH_SIZE and
 WRITE_SIZE) and, given a calibration kernel (a name prefix) of known byte
 count per dispatch, the factor that turns the counter into bytes and the
 scaled bytes per dispatch.  The grid size (work-items) tells the shapes of one
-kernel apart.
+kernel apart.  `sha` prints the hash of the kernel sources that a counter
+summary records (bench.py reports its traffic only while they match).
 """
 import collections
 import csv
+import hashlib
+import os
 import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+# The sources that decide what the SpMV kernels do and how they are launched.
+KERNEL_SOURCES = ["nmspmv.hip", "nm_plan.h", "nm_rules.h", "nm_decode.h"]
+
+
+def kernel_sources_sha256():
+    """sha256 over the kernel sources (in KERNEL_SOURCES order): a counter
+    summary taken from another version of them no longer describes the kernels."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_matrix_vector_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def short(name, width=110):
@@ -66,6 +84,8 @@ if __name__ == "__main__":
         trace(sys.argv[2])
     elif len(sys.argv) >= 4 and sys.argv[1] == "pmc":
         pmc(sys.argv[2], sys.argv[3], *(sys.argv[4:6]))
+    elif len(sys.argv) == 2 and sys.argv[1] == "sha":
+        print(kernel_sources_sha256())
     else:
         print(__doc__)
         sys.exit(2)

@@ -14,7 +14,8 @@
  *     an N:M sparse matrix-vector kernel that indexes kept weights with a
  *     bitmask and walks them with a fixed step.
  *   - "SparseDecoding Makes LLM Pruning Aware of Generation", Key points: the
- *     same N:M SpMV kernel with bitmask indexing and fixed-step traversal.
+ *     same kernel (kept weights located by mask bits, groups at a constant
+ *     stride in the packed values).
  *   - bedrocknews arXiv 2610.12327v1 article: N:M means a fixed count of
  *     zeros inside every small block, and the product is a sparse matrix
  *     times one vector.

@@ -9,7 +9,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = [os.path.join(HERE, "csrc", "nmspmv.hip"), os.path.join(HERE, "csrc", "nmcalib.hip")]
+SRC = [os.path.join(HERE, "csrc", "nmapi.cpp"), os.path.join(HERE, "csrc", "nmspmv.hip"),
+       os.path.join(HERE, "csrc", "nmcalib.hip")]
 LIB = os.path.join(HERE, "libnmspmv.so")
 # (sources, library): the product library
 TARGETS = [(SRC, LIB)]

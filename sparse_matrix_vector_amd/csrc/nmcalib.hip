@@ -25,6 +25,7 @@
 #include <cstdint>
 
 #include "nm_decode.h"
+#include "nm_launch.h"
 #include "nmspmv.h"
 
 namespace {
@@ -390,40 +391,15 @@ __global__ __launch_bounds__(256) void calib_keep_kernel(const u32x4* __restrict
     keep[u] = u32x2{lo, hi};
 }
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb)
-{
-    if (na == 0 || nb == 0 || !a || !b)
-        return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-    return a0 < b0 + nb && b0 < a0 + na;
-}
-
-bool ptr_ok(const void* p, size_t bytes, uintptr_t align)
-{
-    if (bytes == 0)
-        return true;
-    return p != nullptr && (reinterpret_cast<uintptr_t>(p) & (align - 1)) == 0;
-}
-
 int launched() { return hipGetLastError() == hipSuccess ? NM_OK : NM_ERR_HIP; }
 
 }  // namespace
 
-extern "C" {
+// ---- the kernel side of the entry points (arguments checked by nmapi.cpp) --------
 
-int nm_calib_accumulate(const void* X, const uint8_t* decode, int64_t T, int64_t K, int dtype, float* H, void* stream)
+int nmk::calib_accumulate(const void* X, const uint8_t* decode, int64_t T, int64_t K, int dtype, float* H,
+                          void* stream)
 {
-    if (dtype != NM_FP16 && dtype != NM_BF16)
-        return NM_ERR_UNSUPPORTED;
-    if (T < 0 || K < 0 || K % 8 != 0 || T > INT32_MAX || K > 65536)
-        return NM_ERR_BAD_SHAPE;
-    const size_t xbytes = (size_t)T * (size_t)K * 2, hbytes = (size_t)K * (size_t)K * 4;
-    if (!ptr_ok(X, xbytes, 16) || !ptr_ok(H, hbytes, 4))
-        return NM_ERR_INVALID_ARG;
-    if (overlaps(H, hbytes, X, xbytes) || overlaps(H, hbytes, decode, (size_t)T))
-        return NM_ERR_INVALID_ARG;
-    if (T == 0 || K == 0)
-        return NM_OK;
     const unsigned nb = (unsigned)((K + kTile - 1) / kTile);
     const unsigned tiles = nb * (nb + 1) / 2;     // upper triangle, diagonal included
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -449,22 +425,10 @@ int nm_calib_accumulate(const void* X, const uint8_t* decode, int64_t T, int64_t
     return NM_OK;
 }
 
-int nm_calib_keep_mask(const void* W, const float* h, int64_t h_stride, int64_t R, int64_t K, int N, int M, int dtype,
-                       uint8_t* keep, void* stream)
+int nmk::calib_keep_mask(const void* W, const float* h, int64_t h_stride, int64_t R, int64_t K, int N, int M, int dtype,
+                         uint8_t* keep, void* stream)
 {
-    if (dtype != NM_FP16 && dtype != NM_BF16)
-        return NM_ERR_UNSUPPORTED;
-    if (R < 0 || K < 0 || K % 8 != 0 || (M != 4 && M != 8) || N < 1 || N >= M || K % M != 0 || h_stride < 1)
-        return NM_ERR_BAD_SHAPE;
-    const size_t wbytes = (size_t)R * (size_t)K * 2, kbytes = (size_t)R * (size_t)K;
-    const size_t hbytes = K > 0 ? ((size_t)(K - 1) * (size_t)h_stride + 1) * 4 : 0;
-    if (!ptr_ok(W, wbytes, 16) || !ptr_ok(keep, kbytes, 8) || !ptr_ok(h, hbytes, 4))
-        return NM_ERR_INVALID_ARG;
-    if (overlaps(keep, kbytes, W, wbytes) || overlaps(keep, kbytes, h, hbytes))
-        return NM_ERR_INVALID_ARG;
     const int64_t nunits = R * (K / 8);
-    if (nunits == 0)
-        return NM_OK;
     const unsigned grid = (unsigned)((nunits + 255) / 256);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
@@ -476,5 +440,3 @@ int nm_calib_keep_mask(const void* W, const float* h, int64_t h_stride, int64_t 
                            h_stride, nunits, K / 8, N, M, reinterpret_cast<u32x2*>(keep));
     return launched();
 }
-
-}  // extern "C"

@@ -2,8 +2,9 @@
 //
 // The decode-time hot path named by "SparseDecoding: Decoding-Aware Pruning
 // for Accurate and Efficient LLM Inference" (humanity-list story page,
-// "Abstract"): an N:M sparse matrix-vector kernel with bitmask indexing and
-// fixed-step traversal, used because decoding is memory-bound and the weight
+// "Abstract"): a product of an N:M-pruned weight with one activation vector,
+// where a per-column bit marks which weights were kept and each group's kept
+// values sit at a constant offset; decoding is memory-bound, so the weight
 // bytes read per token set the time.  The pages' kernel was written for A100;
 // this one is designed for CDNA4 (wave64, 160 KB LDS per CU, HBM3E) and shares
 // no code with the CPU oracle that the tests compare it against.
@@ -53,6 +54,8 @@
 #include <mutex>
 
 #include "nm_decode.h"
+#include "nm_launch.h"
+#include "nm_plan.h"
 #include "nmspmv.h"
 
 namespace {
@@ -61,27 +64,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWave = 64;
-constexpr int kXTileBudget = 56 * 1024;   // LDS bytes for x in the row-slice / stream kernels
-constexpr int kXTileStream = 64 * 1024;   // LDS bytes per x tile in the stream kernel
-constexpr int kLdsMax = 160 * 1024;       // LDS per CU on gfx950
-constexpr int kMaxBatch = 32;       // activation vectors per call
-constexpr int kVectorMaxBatch = 8;  // the VALU kernels' limit; larger batches use the matrix cores
-
-enum Fmt { kDense = 0, kNM24 = 1, kNM48 = 2 };
-
-// 16-byte units of the selector table each format keeps in LDS.
-template <int F>
-constexpr int table_units()
-{
-    return F == kNM24 ? 4 : (F == kNM48 ? 256 : 0);
-}
-
-template <int F>
-constexpr int chunk_cols()
-{
-    return F == kDense ? 8 : 16;
-}
+using namespace nmh;   // layout constants, formats, launch planning and argument rules
 
 // ---- arithmetic helpers ----------------------------------------------------
 
@@ -254,13 +237,6 @@ __device__ __forceinline__ int x_chunk_slot(int c)
     return ((c >> 5) << 6) + (c & 31);
 }
 
-// LDS units per batch row of x for K staged columns: K/8 rounded up to whole
-// 64-unit runs.
-__host__ __device__ constexpr int x_row_units(int64_t K)
-{
-    return (int)(((K / 8) + 63) / 64 * 64);
-}
-
 // The byte offset of a dynamic-LDS pointer (dynamic LDS starts at 0 in these
 // kernels, which declare no static LDS).
 __device__ __forceinline__ uint32_t lds_offset_of(const void* p)
@@ -421,8 +397,7 @@ __device__ __forceinline__ void chunk_dot(const u32x4 v, const uint32_t mk, cons
 // (part 0) and up (part 1) projections of a gated MLP, and writes one output
 // h = SiLU(gate x) * (up x) to y[0]; its launch rows interleave the parts
 // (row 2i = gate row i, row 2i + 1 = up row i) so that both rows of an output
-// are always reduced by one block.
-constexpr int kMaxParts = 4;
+// are always reduced by one block.  (kMaxParts is one of the argument rules.)
 
 // A part may also scatter its rows into a larger y: with ymap[p] set, its row
 // i goes to y row ymap[p][i] of a y whose batch stride is ystride[p] (the
@@ -926,15 +901,6 @@ __device__ u32x2 expand24(uint32_t n)
     return u32x2{sel[0], sel[1]};
 }
 
-// 16-byte LDS units of the matrix-core kernels' expansion tables.  2:4: one
-// expand24 selector pair per nibble (16 entries of 8 bytes: 64 lanes reading
-// arbitrary entries touch distinct banks or share a word); 4:8: one select48
-// entry per mask byte.
-template <int F>
-constexpr int mfma_table_units()
-{
-    return F == kDense ? 0 : F == kNM24 ? 8 : 256;
-}
 
 template <int F>
 __device__ __forceinline__ void build_mfma_table(u32x4* tab)
@@ -961,10 +927,6 @@ __device__ __forceinline__ void build_mfma_table(u32x4* tab)
 // next stage's weight loads, so it never waits behind them.  Each lane's row
 // pointers are formed once, by selects over the parts (an index into the
 // kernel arguments that varies by lane would become a memory load).
-constexpr int kStageChunks = 16;                                  // chunks per row per stage
-constexpr int kStagePitch = kStageChunks * 16 + 16;               // bytes per values row (rows 4 banks apart)
-constexpr int kStageMPitch = kStageChunks * 2 + 8;                // bytes per mask row (8-byte reads, rows 10 banks apart)
-constexpr int kStageBytes = 16 * kStagePitch + 16 * kStageMPitch; // per wave
 
 template <int F, int DT, int NT>
 __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
@@ -1192,31 +1154,6 @@ __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u3
 //  * masks: 16 rows x 32 bytes; position p of a row holds mask dword
 //    2 (p % 4) + p / 4, so that dwords 0, 2, 4, 6 (chunks 4 t + q, q < 2) and
 //    1, 3, 5, 7 (q >= 2) each form one 16-byte read.
-constexpr int kRingValues = 16 * kStageChunks * 16;               // 4 KB
-constexpr int kRingMasks = 16 * kStageChunks * 2;                 // 512 B
-
-// x units (16 bytes) per batch row per stage.
-template <int F>
-constexpr int ring_x_units()
-{
-    return kStageChunks * chunk_cols<F>() / 8;
-}
-
-// Batch rows of x staged per slot: B rounded up to whole load instructions
-// (64 lanes of 16 bytes).
-template <int F>
-__host__ __device__ constexpr int ring_x_rows(int B)
-{
-    return (B + kWave / ring_x_units<F>() - 1) / (kWave / ring_x_units<F>()) * (kWave / ring_x_units<F>());
-}
-
-// One ring slot: TW tiles' values and masks, then the stage's x.
-template <int F, int TW>
-__host__ __device__ constexpr int ring_slot_bytes(int B)
-{
-    return TW * (kRingValues + (F == kDense ? 0 : kRingMasks)) + ring_x_rows<F>(B) * ring_x_units<F>() * 16;
-}
-
 // A wave multiplies TW 16-row tiles (rows 16 TW w .. 16 TW w + 16 TW - 1) by
 // the same staged x, so each byte of x brought to LDS serves TW tiles; NT
 // batch tiles of 16 vectors share each weight operand.
@@ -1852,64 +1789,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
         out[i] = W[(int64_t)rows[i / upr] * upr + i % upr];
 }
 
-// ---- host: launch planning -------------------------------------------------------
-
-// Launch-shape overrides, read once, for tuning sweeps (0 = built-in choice):
-// NMSPMV_KERNEL 1 = row-slice, 3 = stream, 5 = staged matrix-core (instead of
-// the LDS ring), 6 = the LDS ring wherever K allows it; NMSPMV_SLICES, NMSPMV_ROWS_PER_BLOCK (row-slice);
-// NMSPMV_BLOCKS, NMSPMV_THREADS, NMSPMV_TILE_BYTES (stream);
-// NMSPMV_MFMA_MIN_B (smallest batch sent to the matrix-core kernels),
-// NMSPMV_MFMA_SLICES; NMSPMV_HYBRID_SPLIT=1 runs a hybrid matrix's sparse and
-// dense rows as two launches; NMSPMV_XFIRST=0/1 turns the row-slice kernel's
-// x-first issue order off/on (default: on where a row is cut into slices);
-// NMSPMV_BLOCKS_PER_CU (2 to 8) caps a row-slice launch's resident blocks
-// per CU by padding its LDS; NMSPMV_XDMA=1 stages x by global-to-LDS loads
-// wherever one register per thread does not cover it.
-struct Env {
-    int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0,
-        ring_tiles = 0, ring_share = 0, hybrid_split = 0, xfirst = -1, blocks_per_cu = 0, xdma = 0;
-};
-Env g_env;
-std::once_flag g_env_once;
-
-void read_env()
-{
-    auto get = [](const char* name) {
-        const char* e = std::getenv(name);
-        return e ? std::atoi(e) : 0;
-    };
-    g_env.kernel = get("NMSPMV_KERNEL");
-    g_env.slices = get("NMSPMV_SLICES");
-    g_env.rpb = get("NMSPMV_ROWS_PER_BLOCK");
-    g_env.blocks = get("NMSPMV_BLOCKS");
-    g_env.threads = get("NMSPMV_THREADS");
-    g_env.tile_bytes = get("NMSPMV_TILE_BYTES");
-    g_env.mfma_min_b = get("NMSPMV_MFMA_MIN_B");
-    g_env.mfma_slices = get("NMSPMV_MFMA_SLICES");
-    g_env.ring_tiles = get("NMSPMV_RING_TILES");
-    g_env.ring_share = get("NMSPMV_RING_SHARE");
-    g_env.hybrid_split = get("NMSPMV_HYBRID_SPLIT");
-    g_env.blocks_per_cu = get("NMSPMV_BLOCKS_PER_CU");
-    g_env.xdma = get("NMSPMV_XDMA");
-    const char* xf = std::getenv("NMSPMV_XFIRST");
-    g_env.xfirst = xf ? std::atoi(xf) : -1;
-}
-
-int g_cu_count[64] = {};
-
-int cu_count()
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (!g_cu_count[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        g_cu_count[dev] = n;
-    }
-    return g_cu_count[dev];
-}
+// ---- host: launch helpers ---------------------------------------------------------
 
 // Lets `kernel` take up to the CU's LDS as dynamic shared memory, once per
 // kernel and device (the attribute is set for the current device);
@@ -1927,213 +1807,9 @@ int allow_full_lds(const void* kernel, bool* raised)
     return NM_OK;
 }
 
-struct Plan {
-    int kind = 0;            // 1 row-slice, 3 stream
-    int S = 1, rpb = 1, cpl = 1, threads = 256, tile_cols = 0;
-    int ls = 0;              // log2(S) (row-slice: S is a power of two)
-    int xf = 0;              // row-slice: x loads issued by the whole block before any weight load
-    size_t lds = 0;
-    unsigned grid = 1;
-};
-
-int log2_exact(int v)
-{
-    int l = 0;
-    while ((1 << (l + 1)) <= v)
-        ++l;
-    return l;
-}
-
-// Row-slice shape (rules from timing sweeps on MI355X over the Llama-3.1-8B,
-// Llama-3.3-70B and Qwen3 projection shapes, sparse and dense):
-//  * sparse rows of <= 320 chunks: one wave per row, 8 rows per block;
-//    longer: the fewest slices S >= 2 (a power of two) that keep a lane at
-//    <= 8 chunks, 8 / S rows per block;
-//  * dense rows of <= 512 chunks: one wave per row, 4 rows per block;
-//    longer: the fewest slices that keep a lane at <= 7 chunks, 8 / S rows;
-//  * few rows (under ~16 waves per CU): more slices, down to 64 chunks each;
-//  * at least two blocks per CU;
-//  * blocks of at most 8 waves: 16-wave blocks (tried for the Llama-3.1-8B
-//    down projection, 4096 x 14336) timed 12.5 us on some MI355X GPUs and
-//    13.7-14.9 us, with a wide spread between launches, on others, where
-//    8-wave blocks held 12.4-12.5 us on all of them;
-//  * rows cut into slices issue x first (x-first issue order; the same
-//    sweep: 12.7-12.8 us without it).
-bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, Plan* P)
-{
-    const int cus = cu_count();
-    int S = 1, rpb = dense ? 4 : 8;
-    if (C > (dense ? 8 : 5) * kWave) {
-        const int64_t max_cps = (dense ? 7 : 8) * kWave;
-        S = 2;
-        while (S < 16 && (C + S - 1) / S > max_cps)
-            S *= 2;
-        rpb = std::max(1, 8 / S);
-    }
-    while (S < 16 && R * S < 16LL * cus && (C + 2 * S - 1) / (2 * S) >= kWave) {
-        S *= 2;
-        rpb = std::max(1, 8 / S);
-    }
-    if (g_env.slices > 0)
-        S = 1 << log2_exact(std::min(g_env.slices, 16));
-    if (glu && S > 8)                            // gated rows come in pairs: at least 2 rows per block
-        S = 8;
-    const int64_t cps = (C + S - 1) / S;
-    const int cpl = (int)((cps + kWave - 1) / kWave);
-    if (cpl > 8)
-        return false;
-    while (rpb > 1 && (R + rpb - 1) / rpb < 2 * cus)
-        rpb /= 2;
-    if (g_env.rpb > 0)
-        rpb = g_env.rpb;
-    if (glu)
-        rpb = std::max(2, rpb & ~1);
-    if (rpb * S > 16)
-        return false;
-    const int64_t threads = (int64_t)rpb * S * kWave;
-    P->kind = 1;
-    P->S = S;
-    P->ls = log2_exact(S);
-    P->xf = g_env.xfirst >= 0 ? (g_env.xfirst != 0) : (S >= 2);
-    P->rpb = rpb;
-    P->cpl = cpl;
-    P->threads = (int)threads;
-    P->grid = (unsigned)((R + rpb - 1) / rpb);
-    return true;
-}
-
-// Chooses the kernel for a matrix shape: the row-slice kernel when x fits its
-// LDS budget and rows are at most 1152 chunks (sparse, K <= 18432) or 2048
-// chunks (dense, K <= 16384); otherwise the stream kernel -- whose blocks
-// stage x once for many rows -- with x in K-tiles when it exceeds the budget.
-template <int F>
-Plan plan_for(int64_t R, int64_t K, int B, bool glu)
-{
-    std::call_once(g_env_once, read_env);
-    constexpr int COLS = chunk_cols<F>();
-    const int64_t C = K / COLS;
-    const size_t tab = (size_t)table_units<F>() * sizeof(u32x4);
-    const size_t xbytes = (size_t)B * (size_t)x_row_units(K) * 16;   // x as staged (rows rounded to 64 units)
-    const bool fits = xbytes <= (size_t)kXTileBudget;
-    Plan P;
-    int kind = g_env.kernel;
-    if (kind != 1 && kind != 3)
-        kind = (fits && C <= (F == kDense ? 32 : 18) * kWave) ? 1 : 3;
-    if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, glu, &P)) {
-        P.lds = tab + xbytes + (size_t)P.rpb * P.S * B * 4;
-        if (g_env.blocks_per_cu >= 2 && g_env.blocks_per_cu <= 8)
-            P.lds = std::max(P.lds, (size_t)kLdsMax / (g_env.blocks_per_cu + 1) + 256);
-        return P;
-    }
-    const int cus = cu_count();
-    P.kind = 3;
-    // Two 512-thread blocks per CU; x larger than the tile budget is cut into
-    // equal K-tiles of whole 1024-column units (each tile costs a barrier and
-    // an x restage per block).
-    int threads = 512;
-    if (g_env.threads > 0 && g_env.threads <= 1024 && g_env.threads % kWave == 0)
-        threads = g_env.threads;
-    P.threads = threads;
-    const int nw = P.threads / kWave;
-    // Rows per wave as the kernel counts them (gated rows go to waves in pairs).
-    const int per = glu ? 2 : 1;
-    const int64_t Ru = R / per;
-    int64_t blocks = g_env.blocks > 0 ? g_env.blocks : 2LL * cus;
-    while (blocks > 1 && (blocks - 1) * nw >= Ru)
-        --blocks;
-    const int64_t budget = g_env.tile_bytes > 0 ? g_env.tile_bytes : kXTileStream;
-    int64_t tile = K;
-    if ((int64_t)B * K * 2 > budget) {
-        const int64_t ntiles = ((int64_t)B * K * 2 + budget - 1) / budget;
-        tile = ((K + ntiles - 1) / ntiles + 1023) / 1024 * 1024;
-        if (tile >= K)
-            tile = K;
-    }
-    // With several tiles each wave keeps its rows' partial sums in LDS: more
-    // blocks when that would take more than 16 KB, narrower tiles if the
-    // block would still exceed the CU's LDS.
-    int64_t rpw = per * ((Ru + blocks * nw - 1) / (blocks * nw));
-    if (tile < K) {
-        const int64_t rpw_max = std::max<int64_t>(per, (16 * 1024) / ((int64_t)nw * B * 4));
-        if (rpw > rpw_max) {
-            blocks = (Ru + nw * (rpw_max / per) - 1) / (nw * (rpw_max / per));
-            rpw = per * ((Ru + blocks * nw - 1) / (blocks * nw));
-        }
-        while (tile > 1024 && tab + (size_t)B * x_row_units(tile) * 16 + (size_t)nw * rpw * B * 4 > (size_t)kLdsMax)
-            tile -= 1024;
-    }
-    P.tile_cols = (int)tile;
-    P.grid = (unsigned)blocks;
-    P.lds = tab + (size_t)B * (size_t)x_row_units(tile) * 16 + (tile < K ? (size_t)nw * rpw * B * 4 : 0);
-    return P;
-}
-
-// Whether a batch goes to the matrix-core kernels rather than the VALU ones
-// (timing on MI355X at the Qwen3-32B MLP shapes with weights streamed from
-// HBM).  The LDS-ring kernel wins from 5 vectors (sparse) over the row-slice
-// kernel and from 3 where x is too long for it and the VALU path would be
-// the K-tiled stream kernel; dense from 4 either way; the staged kernel
-// (sparse rows with K % 32 != 0) from 6.  Above 8 vectors only the matrix
-// cores take the batch.  NMSPMV_MFMA_MIN_B overrides the threshold.
-template <int F>
-bool use_mfma(int64_t R, int64_t K, int B, bool glu)
-{
-    std::call_once(g_env_once, read_env);
-    if (B > kVectorMaxBatch)
-        return true;
-    if (g_env.mfma_min_b > 0)
-        return B >= g_env.mfma_min_b;
-    const bool dense = F == kDense;
-    if (!dense && K % 32 != 0)
-        return B >= 6;
-    if (dense)
-        return B >= 4;
-    return B >= (plan_for<F>(R, K, B, glu).kind == 3 ? 3 : 5);
-}
 
 int hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_HIP; }
 
-
-// (The matrix-core choice, use_mfma, follows the launch planning below.)
-
-
-// Staged matrix-core launch shape: 16-row tiles; 1, 2, 4 or 8 K-slices (each
-// at least one 32-chunk stage) until the launch has ~12 waves per CU (the
-// kernel's register use allows 3 per SIMD); the slices of a tile, or 4 tiles,
-// share a block of at most 8 waves.  With two batch tiles (17 to 32 vectors)
-// at most 2 slices, and 1 from 24 vectors when there are more tiles than
-// CUs.  Measured with bf16 2:4 rows on shapes from 1024 x 4096 to
-// 8192 x 28672: 2 slices beat 4 and 8 on every shape at 17 and 32 vectors
-// (by 4-30%; 4096 x 4096 at 32: 16.0 against 22.8 us with 8); at 24-32
-// vectors 1 slice beat 2 by 6-11% on every shape of more than 256 tiles
-// (5120 x 25600 at 32: 104.6 against 117.3 us) and lost by 16-42% on those
-// of 256 or fewer; at 17 vectors it lost on all.
-template <int F>
-Plan plan_mfma_stage(int64_t R, int64_t K, int NT, int B)
-{
-    std::call_once(g_env_once, read_env);
-    constexpr int COLS = chunk_cols<F>();
-    const int cus = cu_count();
-    const int64_t C = K / COLS, tiles = (R + 15) / 16;
-    int S = 1;
-    const int smax = NT == 2 ? (B >= 24 && tiles > cus ? 1 : 2) : 8;
-    while (S < smax && tiles * S < 12LL * cus && C / (2 * S) >= kStageChunks)
-        S *= 2;
-    if (g_env.mfma_slices > 0 && g_env.mfma_slices <= 8)
-        S = g_env.mfma_slices;
-    int tpb = std::max(1, 4 / S);
-    while (tpb > 1 && (tiles + tpb - 1) / tpb < 2 * cus)
-        tpb /= 2;
-    Plan P;
-    P.kind = 5;
-    P.S = S;
-    P.rpb = tpb;
-    P.threads = S * tpb * kWave;
-    P.grid = (unsigned)((tiles + tpb - 1) / tpb);
-    const size_t waves = (size_t)S * tpb;
-    P.lds = (size_t)mfma_table_units<F>() * sizeof(u32x4) + waves * kStageBytes + waves * NT * kWave * 4 * sizeof(float);
-    return P;
-}
 
 template <int F, int DT, int NT>
 int launch_mfma_nt(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
@@ -2150,65 +1826,6 @@ int launch_mfma_nt(const Parts& parts, const void* x, int R, int K, int B, hipSt
     return hip_status(hipGetLastError());
 }
 
-// LDS-ring launch shape (rules from sweeps on MI355X at the Qwen3-32B MLP
-// shapes, weights streamed from HBM): 16-row tiles, one per wave up to 8
-// vectors, two above (x, then 16 rows per stage, serves both; four tiles a
-// wave, tried for sparse rows above 16, double the LDS a wave holds and halve
-// the waves a CU keeps -- slower than two tiles with x shared by two waves);
-// a block holds one wave group, its K split into S
-// stage-interleaved slices (one wave each).  S is the largest power of two
-// (each slice keeping at least four stages, at most 8 waves a block, the
-// kernel's launch bound) whose launch still fits the CUs' LDS in one round:
-// a second, partly filled round costs more than the extra waves gain.
-template <int F>
-Plan plan_mfma_ring(int64_t R, int64_t K, int B)
-{
-    std::call_once(g_env_once, read_env);
-    constexpr int COLS = chunk_cols<F>();
-    const int cus = cu_count();
-    const int64_t C = K / COLS, NS = (C + kStageChunks - 1) / kStageChunks;
-    int TW = B > 8 ? 2 : 1;
-    if (B <= 16 && (g_env.ring_tiles == 1 || g_env.ring_tiles == 2))
-        TW = g_env.ring_tiles;                   // above 16 vectors the tile count is fixed
-    const int64_t tiles = (R + 16 * TW - 1) / (16 * TW);
-    const size_t tab = (size_t)mfma_table_units<F>() * sizeof(u32x4);
-    const size_t ring = 2 * (size_t)(TW == 2 ? ring_slot_bytes<F, 2>(B) : ring_slot_bytes<F, 1>(B));
-    const int wmax = (int)std::min<size_t>(8, (kLdsMax - tab) / ring);
-    // Waves resident at once with S-wave blocks (LDS-bound).
-    auto resident = [&](int S) { return (int64_t)(kLdsMax / (tab + S * ring)) * S * cus; };
-    int S = 1;
-    for (int s2 = 2; s2 <= wmax && NS >= 4LL * s2; s2 *= 2)
-        if (tiles * s2 <= resident(s2))
-            S = s2;
-    if (g_env.mfma_slices > 0 && g_env.mfma_slices <= wmax)
-        S = g_env.mfma_slices;
-    Plan P;
-    P.kind = 6;
-    P.S = S;
-    P.rpb = 1;
-    P.cpl = TW;
-    P.threads = S * kWave;
-    P.grid = (unsigned)tiles;
-    P.lds = tab + (size_t)S * ring;
-    // One slice per tile: up to 4 waves (one tile group each) share a block's
-    // staged x (2 with two tiles per wave), while the launch keeps at least
-    // one block per CU.
-    int W = TW == 1 ? 4 : 2;
-    if (g_env.ring_share > 0)
-        W = std::min(g_env.ring_share, 8);
-    while (W > 1 && (tiles + W - 1) / W < cus)
-        W /= 2;
-    if (S == 1 && W > 1) {
-        const size_t wring = 2 * (size_t)TW * (kRingValues + (F == kDense ? 0 : kRingMasks));
-        const size_t xslot = (size_t)ring_x_rows<F>(B) * ring_x_units<F>() * 16;
-        P.kind = 7;
-        P.rpb = W;
-        P.threads = W * kWave;
-        P.grid = (unsigned)((tiles + W - 1) / W);
-        P.lds = tab + W * wring + 2 * xslot;
-    }
-    return P;
-}
 
 template <int F, int DT, int TW, int NT, bool SHX>
 int launch_mfma_ring_k(const Plan& P, const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
@@ -2242,20 +1859,10 @@ int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hip
                       : launch_mfma_ring_tw<F, DT, 1, 1>(P, parts, x, R, K, B, s);
 }
 
-// The LDS-ring kernel takes dense rows at any batch, and sparse rows whose
-// mask row is a whole number of dwords (K % 32 == 0): up to 16 vectors
-// always, above 16 when there is at least one 64-row block (two waves of two
-// tiles sharing x) per CU (measured: with fewer the ring needs K-slices,
-// whose waves cannot share x, and does no better than the staged kernel).  Other sparse batches run on the staged
-// kernel, where up to 16 vectors are one tile of the matrix cores' batch
-// dimension and 17 to 32 take two, both fed by the same weight loads.
 template <int F, int DT>
 int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
-    std::call_once(g_env_once, read_env);
-    const bool ring_fits = F == kDense || (K % 32 == 0 && (B <= 16 || (int64_t)R >= 64LL * cu_count() ||
-                                                       g_env.kernel == 6));
-    if (ring_fits && g_env.kernel != 5)
+    if (mfma_use_ring<F>(R, K, B))
         return launch_mfma_ring<F, DT>(parts, x, R, K, B, s);
     return B > 16 ? launch_mfma_nt<F, DT, 2>(parts, x, R, K, B, s) : launch_mfma_nt<F, DT, 1>(parts, x, R, K, B, s);
 }
@@ -2275,10 +1882,7 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
     const u32x4* x4 = static_cast<const u32x4*>(x);
     (void)hipGetLastError();
     if (P.kind == 1) {
-        // x staging: one register per thread where that covers x; four for a
-        // single vector that they cover; else global-to-LDS loads.
-        const int64_t xunits = (int64_t)NB * (K / 8);
-        const int xu = xunits <= P.threads ? 1 : (NB == 1 && xunits <= 4LL * P.threads && g_env.xdma != 1) ? 4 : 0;
+        const int xu = rowslice_x_regs(NB, K, P.threads);
 #define NM_SLICE_XU(CPL, XU)                                                                                         \
     hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, CPL, XU>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, \
                        K, P.ls, P.rpb, P.xf, (int)(xu != 0))
@@ -2328,17 +1932,8 @@ int launch_hybrid_fused(const Parts& PS, const Parts& PD, const void* x, int RS,
                         bool* launched)
 {
     *launched = false;
-    Plan P = plan_for<F>(RS, K, NB, false);
-    if (P.kind == 1 && P.rpb == 1 && g_env.rpb == 0 && P.S <= 8) {
-        // Few sparse rows: the plan went to one row per block to keep two
-        // blocks per CU; here the dense rows add blocks of their own, so take
-        // two rows per block (and the LDS for their partial sums).
-        P.rpb = 2;
-        P.threads = 2 * P.S * kWave;
-        P.grid = (unsigned)((RS + 1) / 2);
-        P.lds = (size_t)table_units<F>() * sizeof(u32x4) + (size_t)NB * x_row_units(K) * 16 + (size_t)P.rpb * P.S * NB * 4;
-    }
-    if (P.kind != 1 || P.rpb < 2 || P.rpb % 2 != 0)
+    Plan P;
+    if (!plan_hybrid<F>(RS, K, NB, &P))
         return NM_OK;
     const int64_t dense_rpb = P.rpb / 2;
     const int64_t sblocks = P.grid, blocks = sblocks + (RD + dense_rpb - 1) / dense_rpb;
@@ -2380,47 +1975,6 @@ int launch_hybrid_fused_dt(int dtype, int B, const Parts& PS, const Parts& PD, c
 {
     return dtype == NM_FP16 ? launch_hybrid_fused_nb<F, NM_FP16>(B, PS, PD, x, RS, RD, K, s, launched)
                             : launch_hybrid_fused_nb<F, NM_BF16>(B, PS, PD, x, RS, RD, K, s, launched);
-}
-
-// ---- host: argument rules ------------------------------------------------------
-
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb)
-{
-    if (na == 0 || nb == 0)
-        return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-    return a0 < b0 + nb && b0 < a0 + na;
-}
-
-// A pointer may be NULL only when its buffer is empty.
-bool ptr_ok(const void* p, size_t bytes, uintptr_t align)
-{
-    if (bytes == 0)
-        return true;
-    return p != nullptr && aligned(p, align);
-}
-
-int check_dtype(int dtype) { return (dtype == NM_FP16 || dtype == NM_BF16) ? NM_OK : NM_ERR_UNSUPPORTED; }
-
-// Row indices are 32-bit in the kernels, and a launch rounds its rows up to
-// whole tiles and blocks (at most a few hundred rows past R): R, and a fused
-// launch's total, stay below kRowLimit.
-constexpr int64_t kRowLimit = (int64_t(1) << 31) - 1024;
-
-int check_rk(int64_t R, int64_t K)
-{
-    if (R < 0 || K < 0 || R >= kRowLimit || K > INT32_MAX || K % 8 != 0)
-        return NM_ERR_BAD_SHAPE;
-    return NM_OK;
-}
-
-int check_nm(int64_t K, int N, int M)
-{
-    if ((M != 4 && M != 8) || N < 1 || N >= M || K % M != 0)
-        return NM_ERR_BAD_SHAPE;
-    return NM_OK;
 }
 
 int launch_zero(void* y, int64_t n, hipStream_t s)
@@ -2624,72 +2178,31 @@ Parts mapped_part(const void* w, const uint8_t* m, const int32_t* rows, int64_t 
 
 }  // namespace
 
-extern "C" {
-
-int nm_version(void) { return 101; }
-
-const char* nm_status_string(int status)
+// Compute units of the current device, read once per device (256 if the
+// runtime cannot say).
+int nmh::cu_count()
 {
-    switch (status) {
-    case NM_OK: return "NM_OK";
-    case NM_ERR_INVALID_ARG: return "NM_ERR_INVALID_ARG";
-    case NM_ERR_BAD_SHAPE: return "NM_ERR_BAD_SHAPE";
-    case NM_ERR_UNSUPPORTED: return "NM_ERR_UNSUPPORTED";
-    case NM_ERR_BAD_MASK: return "NM_ERR_BAD_MASK";
-    case NM_ERR_NONFINITE: return "NM_ERR_NONFINITE";
-    case NM_ERR_HIP: return "NM_ERR_HIP";
-    default: return "NM_ERR_UNKNOWN";
+    static int counts[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!counts[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        counts[dev] = n;
     }
+    return counts[dev];
 }
 
-int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
-                  int N, int M, int dtype, const void* x, int B, void* const* y, void* stream)
+// ---- the kernel side of the entry points (arguments checked by nmapi.cpp) --------
+
+int nmk::zero(void* y, int64_t n, void* stream) { return launch_zero(y, n, static_cast<hipStream_t>(stream)); }
+
+int nmk::spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t total,
+                    int64_t K, int N, int M, int dtype, const void* x, int B, void* const* y, void* stream)
 {
-    int st = check_dtype(dtype);
-    if (st != NM_OK)
-        return st;
-    if (count < 1 || count > kMaxParts || !R)
-        return count < 1 || count > kMaxParts ? NM_ERR_BAD_SHAPE : NM_ERR_INVALID_ARG;
-    if ((st = check_rk(0, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
-        return st;
-    if (B < 1 || B > kMaxBatch)
-        return NM_ERR_BAD_SHAPE;
-    int64_t total = 0;
-    for (int i = 0; i < count; ++i) {
-        if ((st = check_rk(R[i], K)) != NM_OK)
-            return st;
-        total += R[i];
-    }
-    if (total >= kRowLimit)
-        return NM_ERR_BAD_SHAPE;
-    if (!values || !masks || !y)
-        return NM_ERR_INVALID_ARG;
-    const size_t xbytes = (size_t)B * (size_t)K * 2;
-    if (!ptr_ok(x, xbytes, 16))
-        return NM_ERR_INVALID_ARG;
-    for (int i = 0; i < count; ++i) {
-        const size_t vb = (size_t)R[i] * (size_t)(K / M * N) * 2, mb = (size_t)R[i] * (size_t)(K / 8);
-        const size_t yb = (size_t)B * (size_t)R[i] * 2;
-        if (!ptr_ok(values[i], vb, 16) || !ptr_ok(masks[i], mb, 16) || !ptr_ok(y[i], yb, 2))
-            return NM_ERR_INVALID_ARG;
-        if (overlaps(y[i], yb, x, xbytes))
-            return NM_ERR_INVALID_ARG;
-        for (int j = 0; j < count; ++j) {
-            const size_t vbj = (size_t)R[j] * (size_t)(K / M * N) * 2, mbj = (size_t)R[j] * (size_t)(K / 8);
-            if (overlaps(y[i], yb, values[j], vbj) || overlaps(y[i], yb, masks[j], mbj) ||
-                (j != i && overlaps(y[i], yb, y[j], (size_t)B * (size_t)R[j] * 2)))
-                return NM_ERR_INVALID_ARG;
-        }
-    }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (total == 0)
-        return NM_OK;
-    if (K == 0) {
-        for (int i = 0; i < count; ++i)
-            if ((st = launch_zero(y[i], (int64_t)B * R[i], s)) != NM_OK)
-                return st;
-        return NM_OK;
-    }
     if (K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8))) {
         Parts P = {};
         P.begin[0] = 0;
@@ -2713,63 +2226,17 @@ int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* ma
     for (int i = 0; i < count; ++i) {
         if (R[i] == 0)
             continue;
-        if ((st = generic_batches(dtype, B, values[i], masks[i], nullptr, nullptr, x, y[i], R[i], K, N, M, s)) != NM_OK)
+        const int st = generic_batches(dtype, B, values[i], masks[i], nullptr, nullptr, x, y[i], R[i], K, N, M, s);
+        if (st != NM_OK)
             return st;
     }
     return NM_OK;
 }
 
-int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int N, int M, int dtype, const void* x,
-            int B, void* y, void* stream)
+int nmk::gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t total, int64_t K, int dtype,
+                          const void* x, int B, void* const* y, void* stream)
 {
-    return nm_spmv_multi(1, &values, &masks, &R, K, N, M, dtype, x, B, &y, stream);
-}
-
-int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t K, int dtype, const void* x, int B,
-                        void* const* y, void* stream)
-{
-    int st = check_dtype(dtype);
-    if (st != NM_OK)
-        return st;
-    if (count < 1 || count > kMaxParts || !R)
-        return count < 1 || count > kMaxParts ? NM_ERR_BAD_SHAPE : NM_ERR_INVALID_ARG;
-    if ((st = check_rk(0, K)) != NM_OK)
-        return st;
-    if (B < 1 || B > kMaxBatch)
-        return NM_ERR_BAD_SHAPE;
-    int64_t total = 0;
-    for (int i = 0; i < count; ++i) {
-        if ((st = check_rk(R[i], K)) != NM_OK)
-            return st;
-        total += R[i];
-    }
-    if (total >= kRowLimit)
-        return NM_ERR_BAD_SHAPE;
-    if (!W || !y)
-        return NM_ERR_INVALID_ARG;
-    const size_t xbytes = (size_t)B * (size_t)K * 2;
-    if (!ptr_ok(x, xbytes, 16))
-        return NM_ERR_INVALID_ARG;
-    for (int i = 0; i < count; ++i) {
-        const size_t wb = (size_t)R[i] * (size_t)K * 2, yb = (size_t)B * (size_t)R[i] * 2;
-        if (!ptr_ok(W[i], wb, 16) || !ptr_ok(y[i], yb, 2))
-            return NM_ERR_INVALID_ARG;
-        if (overlaps(y[i], yb, x, xbytes))
-            return NM_ERR_INVALID_ARG;
-        for (int j = 0; j < count; ++j)
-            if (overlaps(y[i], yb, W[j], (size_t)R[j] * (size_t)K * 2) ||
-                (j != i && overlaps(y[i], yb, y[j], (size_t)B * (size_t)R[j] * 2)))
-                return NM_ERR_INVALID_ARG;
-    }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (total == 0)
-        return NM_OK;
-    if (K == 0) {
-        for (int i = 0; i < count; ++i)
-            if ((st = launch_zero(y[i], (int64_t)B * R[i], s)) != NM_OK)
-                return st;
-        return NM_OK;
-    }
     Parts P = {};
     for (int i = 0; i < count; ++i) {
         if (R[i] == 0)
@@ -2787,34 +2254,11 @@ int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64
     return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s);
 }
 
-int nm_gemv_dense(const void* W, int64_t R, int64_t K, int dtype, const void* x, int B, void* y, void* stream)
+int nmk::spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const void* values_up,
+                     const uint8_t* masks_up, int64_t R, int64_t K, int N, int M, int dtype, const void* x, int B,
+                     void* h, void* stream)
 {
-    return nm_gemv_dense_multi(1, &W, &R, K, dtype, x, B, &y, stream);
-}
-
-int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const void* values_up, const uint8_t* masks_up,
-                   int64_t R, int64_t K, int N, int M, int dtype, const void* x, int B, void* h, void* stream)
-{
-    int st = check_dtype(dtype);
-    if (st != NM_OK)
-        return st;
-    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
-        return st;
-    if (B < 1 || B > kMaxBatch || 2 * R >= kRowLimit)
-        return NM_ERR_BAD_SHAPE;
-    const size_t xbytes = (size_t)B * (size_t)K * 2, hbytes = (size_t)B * (size_t)R * 2;
-    const size_t vb = (size_t)R * (size_t)(K / M * N) * 2, mb = (size_t)R * (size_t)(K / 8);
-    if (!ptr_ok(x, xbytes, 16) || !ptr_ok(h, hbytes, 2) || !ptr_ok(values_gate, vb, 16) ||
-        !ptr_ok(masks_gate, mb, 16) || !ptr_ok(values_up, vb, 16) || !ptr_ok(masks_up, mb, 16))
-        return NM_ERR_INVALID_ARG;
-    if (overlaps(h, hbytes, x, xbytes) || overlaps(h, hbytes, values_gate, vb) || overlaps(h, hbytes, masks_gate, mb) ||
-        overlaps(h, hbytes, values_up, vb) || overlaps(h, hbytes, masks_up, mb))
-        return NM_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (R == 0)
-        return NM_OK;
-    if (K == 0)                                  // SiLU(0) * 0
-        return launch_zero(h, (int64_t)B * R, s);
     if (K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8))) {
         Parts P = {};
         P.w[0] = static_cast<const u32x4*>(values_gate);
@@ -2836,27 +2280,10 @@ int nm_spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const voi
     return generic_batches(dtype, B, values_gate, masks_gate, values_up, masks_up, x, h, R, K, N, M, s);
 }
 
-int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_t K, int dtype, const void* x, int B,
-                         void* h, void* stream)
+int nmk::gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_t K, int dtype, const void* x,
+                           int B, void* h, void* stream)
 {
-    int st = check_dtype(dtype);
-    if (st != NM_OK)
-        return st;
-    if ((st = check_rk(R, K)) != NM_OK)
-        return st;
-    if (B < 1 || B > kMaxBatch || 2 * R >= kRowLimit)
-        return NM_ERR_BAD_SHAPE;
-    const size_t xbytes = (size_t)B * (size_t)K * 2, hbytes = (size_t)B * (size_t)R * 2;
-    const size_t wb = (size_t)R * (size_t)K * 2;
-    if (!ptr_ok(x, xbytes, 16) || !ptr_ok(h, hbytes, 2) || !ptr_ok(W_gate, wb, 16) || !ptr_ok(W_up, wb, 16))
-        return NM_ERR_INVALID_ARG;
-    if (overlaps(h, hbytes, x, xbytes) || overlaps(h, hbytes, W_gate, wb) || overlaps(h, hbytes, W_up, wb))
-        return NM_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (R == 0)
-        return NM_OK;
-    if (K == 0)
-        return launch_zero(h, (int64_t)B * R, s);
     Parts P = {};
     P.w[0] = static_cast<const u32x4*>(W_gate);
     P.w[1] = static_cast<const u32x4*>(W_up);
@@ -2871,44 +2298,15 @@ int nm_gemv_dense_swiglu(const void* W_gate, const void* W_up, int64_t R, int64_
     return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)(2 * R), (int)K, s);
 }
 
-int nm_pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int M, int dtype, void* values,
-            uint8_t* masks, void* stream)
+int nmk::pack(const void* W, const uint8_t* keep, int64_t R, int64_t K, int N, int M, int dtype, void* values,
+              uint8_t* masks, void* stream)
 {
-    int st = check_dtype(dtype);
-    if (st != NM_OK)
-        return st;
-    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
-        return st;
-    const size_t wbytes = (size_t)R * (size_t)K * 2, kbytes = keep ? (size_t)R * (size_t)K : 0;
-    const size_t vbytes = (size_t)R * (size_t)(K / M * N) * 2, mbytes = (size_t)R * (size_t)(K / 8);
-    if (!ptr_ok(W, wbytes, 16) || !ptr_ok(values, vbytes, 16) || !ptr_ok(masks, mbytes, 16))
-        return NM_ERR_INVALID_ARG;
-    if (overlaps(values, vbytes, W, wbytes) || overlaps(values, vbytes, keep, kbytes) ||
-        overlaps(masks, mbytes, W, wbytes) || overlaps(masks, mbytes, keep, kbytes) ||
-        overlaps(values, vbytes, masks, mbytes))
-        return NM_ERR_INVALID_ARG;
     return pack_rows(W, keep, nullptr, R, K, N, M, dtype, values, masks, static_cast<hipStream_t>(stream));
 }
 
-int nm_hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int64_t h_stride, int64_t R, int64_t K, int N,
-                       int M, int dtype, double* loss, void* stream)
+int nmk::hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int64_t h_stride, int64_t R, int64_t K,
+                         int N, int M, int dtype, double* loss, void* stream)
 {
-    int st = check_dtype(dtype);
-    if (st != NM_OK)
-        return st;
-    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
-        return st;
-    if (h && h_stride < 1)
-        return NM_ERR_BAD_SHAPE;
-    const size_t wbytes = (size_t)R * (size_t)K * 2, kbytes = keep ? (size_t)R * (size_t)K : 0;
-    const size_t hbytes = h && K > 0 ? ((size_t)(K - 1) * (size_t)h_stride + 1) * 4 : 0;
-    const size_t lbytes = (size_t)R * 8;
-    if (!ptr_ok(W, wbytes, 2) || !ptr_ok(loss, lbytes, 8) || (h && !ptr_ok(h, hbytes, 4)))
-        return NM_ERR_INVALID_ARG;
-    if (overlaps(loss, lbytes, W, wbytes) || overlaps(loss, lbytes, keep, kbytes) || overlaps(loss, lbytes, h, hbytes))
-        return NM_ERR_INVALID_ARG;
-    if (R == 0)
-        return NM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const unsigned grid = (unsigned)((R + kLossRows - 1) / kLossRows);
     return with_status(s, [&](uint32_t* status) {
@@ -2921,14 +2319,8 @@ int nm_hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int64
     });
 }
 
-int nm_hybrid_select_rows(const double* loss, int64_t R, int64_t n_dense, uint8_t* flags, void* stream)
+int nmk::hybrid_select_rows(const double* loss, int64_t R, int64_t n_dense, uint8_t* flags, void* stream)
 {
-    if (R < 0 || R >= kRowLimit || n_dense < 0 || n_dense > R)
-        return NM_ERR_BAD_SHAPE;
-    if (!ptr_ok(loss, (size_t)R * 8, 8) || !ptr_ok(flags, (size_t)R, 1) || overlaps(flags, (size_t)R, loss, (size_t)R * 8))
-        return NM_ERR_INVALID_ARG;
-    if (R == 0)
-        return NM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     hipLaunchKernelGGL(hybrid_select_kernel, dim3((unsigned)((R + 63) / 64)), dim3(256), 0, s, loss, (int)R,
@@ -2936,40 +2328,13 @@ int nm_hybrid_select_rows(const double* loss, int64_t R, int64_t n_dense, uint8_
     return hip_status(hipGetLastError());
 }
 
-int nm_hybrid_pack(const void* W, const uint8_t* keep, const uint8_t* flags, int64_t n_dense, int64_t R, int64_t K,
-                   int N, int M, int dtype, void* values, uint8_t* masks, void* W_dense, int32_t* rows_sparse,
-                   int32_t* rows_dense, void* stream)
+int nmk::hybrid_pack(const void* W, const uint8_t* keep, const uint8_t* flags, int64_t n_dense, int64_t R, int64_t K,
+                     int N, int M, int dtype, void* values, uint8_t* masks, void* W_dense, int32_t* rows_sparse,
+                     int32_t* rows_dense, void* stream)
 {
-    int st = check_dtype(dtype);
-    if (st != NM_OK)
-        return st;
-    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
-        return st;
-    if (n_dense < 0 || n_dense > R)
-        return NM_ERR_BAD_SHAPE;
-    const int64_t Rs = R - n_dense;
-    const size_t wbytes = (size_t)R * (size_t)K * 2, kbytes = keep ? (size_t)R * (size_t)K : 0;
-    const size_t vbytes = (size_t)Rs * (size_t)(K / M * N) * 2, mbytes = (size_t)Rs * (size_t)(K / 8);
-    const size_t dbytes = (size_t)n_dense * (size_t)K * 2;
-    const size_t sbytes = (size_t)Rs * 4, ibytes = (size_t)n_dense * 4;
-    if (!ptr_ok(W, wbytes, 16) || !ptr_ok(flags, (size_t)R, 1) || !ptr_ok(values, vbytes, 16) ||
-        !ptr_ok(masks, mbytes, 16) || !ptr_ok(W_dense, dbytes, 16) || !ptr_ok(rows_sparse, sbytes, 4) ||
-        !ptr_ok(rows_dense, ibytes, 4))
-        return NM_ERR_INVALID_ARG;
-    const void* outs[5] = {values, masks, W_dense, rows_sparse, rows_dense};
-    const size_t osz[5] = {vbytes, mbytes, dbytes, sbytes, ibytes};
-    for (int i = 0; i < 5; ++i) {
-        if (overlaps(outs[i], osz[i], W, wbytes) || overlaps(outs[i], osz[i], keep, kbytes) ||
-            overlaps(outs[i], osz[i], flags, (size_t)R))
-            return NM_ERR_INVALID_ARG;
-        for (int j = i + 1; j < 5; ++j)
-            if (overlaps(outs[i], osz[i], outs[j], osz[j]))
-                return NM_ERR_INVALID_ARG;
-    }
-    if (R == 0)
-        return NM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = with_status(s, [&](uint32_t* status) {
+    const int64_t Rs = R - n_dense;
+    int st = with_status(s, [&](uint32_t* status) {
         hipLaunchKernelGGL(hybrid_partition_kernel, dim3(1), dim3(1024), 0, s, flags, (int)R, (int)n_dense, rows_sparse,
                            rows_dense, status);
     });
@@ -2990,34 +2355,13 @@ int nm_hybrid_pack(const void* W, const uint8_t* keep, const uint8_t* flags, int
     return hip_status(hipStreamSynchronize(s));
 }
 
-int nm_spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows_sparse, const void* W_dense,
-                   const int32_t* rows_dense, int64_t n_dense, int64_t R, int64_t K, int N, int M, int dtype,
-                   const void* x, int B, void* y, void* stream)
+int nmk::spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows_sparse, const void* W_dense,
+                     const int32_t* rows_dense, int64_t n_dense, int64_t R, int64_t K, int N, int M, int dtype,
+                     const void* x, int B, void* y, void* stream)
 {
-    int st = check_dtype(dtype);
-    if (st != NM_OK)
-        return st;
-    if ((st = check_rk(R, K)) != NM_OK || (st = check_nm(K, N, M)) != NM_OK)
-        return st;
-    if (n_dense < 0 || n_dense > R || B < 1 || B > kMaxBatch)
-        return NM_ERR_BAD_SHAPE;
-    const int64_t Rs = R - n_dense;
-    const size_t vbytes = (size_t)Rs * (size_t)(K / M * N) * 2, mbytes = (size_t)Rs * (size_t)(K / 8);
-    const size_t dbytes = (size_t)n_dense * (size_t)K * 2, sbytes = (size_t)Rs * 4, ibytes = (size_t)n_dense * 4;
-    const size_t xbytes = (size_t)B * (size_t)K * 2, ybytes = (size_t)B * (size_t)R * 2;
-    if (!ptr_ok(values, vbytes, 16) || !ptr_ok(masks, mbytes, 16) || !ptr_ok(rows_sparse, sbytes, 4) ||
-        !ptr_ok(W_dense, dbytes, 16) || !ptr_ok(rows_dense, ibytes, 4) || !ptr_ok(x, xbytes, 16) ||
-        !ptr_ok(y, ybytes, 2))
-        return NM_ERR_INVALID_ARG;
-    if (overlaps(y, ybytes, values, vbytes) || overlaps(y, ybytes, masks, mbytes) || overlaps(y, ybytes, W_dense, dbytes) ||
-        overlaps(y, ybytes, rows_sparse, sbytes) || overlaps(y, ybytes, rows_dense, ibytes) ||
-        overlaps(y, ybytes, x, xbytes))
-        return NM_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (R == 0)
-        return NM_OK;
-    if (K == 0)
-        return launch_zero(y, (int64_t)B * R, s);
+    const int64_t Rs = R - n_dense;
+    int st = NM_OK;
     const bool tuned = K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8));
     if (B <= 3 && Rs > 0 && n_dense > 0 && tuned) {
         std::call_once(g_env_once, read_env);
@@ -3056,4 +2400,3 @@ int nm_spmv_hybrid(const void* values, const uint8_t* masks, const int32_t* rows
     return NM_OK;
 }
 
-}  // extern "C"

@@ -8,7 +8,8 @@ to show that each plausible mistake fails at least one pin.
 
 Sources of the facts pinned here:
   * SparseDecoding abstract (humanity-list story page, "Abstract"): an N:M
-    sparse matrix-vector product, bitmask indexing, fixed-step traversal.
+    sparse matrix-vector product whose kept weights are marked by mask bits
+    and whose groups sit at a constant stride in the packed values.
   * bedrocknews arXiv 2610.12327v1 article: N:M keeps a fixed count in every
     small block; the product is a sparse matrix times one vector.
   * IEEE 754 binary16 and bfloat16 field layouts, round-to-nearest-even.
