@@ -286,8 +286,34 @@ def mlp_single(torch, lib, launches, cur, reps=10, trials=20):
                      "dense_us": round(usd, 3), "dense_us_min": round(td[0], 3), "dense_us_max": round(td[2], 3),
                      "dense_gbs": round(dbytes / usd / 1e3, 1),
                      "torch_matmul_us": round(ust, 3), "speedup": round(usd / us, 4),
-                     "speedup_vs_best_dense": round(best_dense / us, 4)}
+                     "speedup_vs_best_dense": round(best_dense / us, 4), "bytes": nbytes}
     return out
+
+
+def launch_floors(torch, sizes, trials=10):
+    """For each byte count: the median per-launch time of a one-shot streaming
+    read of that many bytes (measure/nmprobe.hip read_shot_kernel: 512-thread
+    blocks, four 16-byte loads per thread, no loop), back to back over regions
+    rotated past the 256 MB MALL -- the floor for one launch that streams
+    those bytes; and the per-launch time of an empty kernel back to back."""
+    from measure import probe
+    plib = probe.lib()
+    region = (max(sizes) + 4095) // 4096 * 4096
+    n_inst = max(8, -(-(512 << 20) // region))
+    buf = torch.empty(region * n_inst, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    floors = {}
+    for nb in sorted(set(sizes)):
+        n16 = nb // 16 * 16
+
+        def args(st):
+            return [(P(buf.data_ptr() + i * region), I64(n16), P(sink.data_ptr()), I32(512), P(st))
+                    for i in range(n_inst)]
+        floors[nb] = burst(torch, plib.nmp_read_shot, args, trials)[1]
+    empty = burst(torch, plib.nmp_empty, lambda st: [(P(st),) for _ in range(64)], trials)[1]
+    del buf, sink
+    torch.cuda.empty_cache()
+    return floors, empty
 
 
 def hybrid_gate(torch, nm, lib, launches, cur, fracs=(0.05, 0.10), reps=5):
@@ -624,6 +650,12 @@ def main():
     achieved = rbytes / rus / 1e3
 
     mlp = mlp_single(torch, lib, launches, cur, reps=10 if layers <= 64 else 3)
+    # What no single launch of these sizes can beat: a one-shot read of the
+    # same bytes, and an empty kernel (both back to back, as in the step).
+    floors, empty_us = launch_floors(torch, [v["bytes"] for v in per.values()] + [v["bytes"] for v in mlp.values()])
+    for v in list(per.values()) + list(mlp.values()):
+        v["read_floor_us"] = round(floors[v["bytes"]], 3)
+        v["above_floor_us"] = round(v["us"] - floors[v["bytes"]], 3)
     extras = {}
     if a.workload == "llama31_8b" and not a.no_glu:
         extras["hybrid_gate"] = hybrid_gate(torch, nm, lib, launches, cur)
@@ -667,6 +699,8 @@ def main():
         "per_launch": per,
         "mlp_shapes": mlp,
         "extras": extras,
+        "launch_floor": {"empty_kernel_us": round(empty_us, 3),
+                         "read_shot": "one-shot read of each launch's bytes (read_floor_us beside each launch)"},
         "read_ceiling_gbs": round(ceiling, 1),
         "pct_of_read_ceiling": round(100.0 * gbs / ceiling, 2) if ceiling else None,
         "copy_calibration_bytes": copy_bytes,

@@ -6,6 +6,9 @@
 //              cache hints as the product kernels) and folds it into one word
 //              per block, so its time is the achievable read-bandwidth ceiling
 //              for a given size;
+//   nmp_read_shot  reads a buffer once with short-lived blocks (one 16-byte
+//              load per thread per unit, four units, no loop), the floor for
+//              one launch that streams that many bytes;
 //   nmp_copy   a plain 16-byte copy of known size, whose FETCH_SIZE and
 //              WRITE_SIZE counter readings calibrate the counters' units;
 //   nmp_empty  an empty kernel, to time launch cost alone.
@@ -45,6 +48,27 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
         dst[i] = src[i];
 }
 
+// One-shot read: each block reads its own contiguous threads x 4 units once
+// (no loop), like the row-slice kernel's short-lived blocks, so that its time
+// is the floor for a single launch that streams this many bytes.
+__global__ __launch_bounds__(512) void read_shot_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                        uint32_t* __restrict__ sink)
+{
+    const int64_t base = (int64_t)blockIdx.x * blockDim.x * 4 + threadIdx.x;
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + (int64_t)u * blockDim.x;
+        v[u] = __builtin_nontemporal_load(src + (i < n16 ? i : 0));
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    if (acc == 0x9E3779B9u)
+        sink[blockIdx.x] = acc;
+}
+
 __global__ void empty_kernel() {}
 
 }  // namespace
@@ -58,6 +82,19 @@ int nmp_read(const void* src, int64_t bytes, void* sink, int blocks, void* strea
         return 1;
     hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, bytes / 16,
                        (uint32_t*)sink);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+// bytes must be a multiple of 16 and src 16-byte aligned; threads in {64, ..., 512}, a multiple of 64; sink holds
+// one word per block (bytes / (64 * threads) rounded up).
+int nmp_read_shot(const void* src, int64_t bytes, void* sink, int threads, void* stream)
+{
+    if (!src || !sink || bytes <= 0 || bytes % 16 || threads < 64 || threads > 512 || threads % 64 ||
+        (reinterpret_cast<uintptr_t>(src) & 15))
+        return 1;
+    const int64_t n16 = bytes / 16, blocks = (n16 + 4LL * threads - 1) / (4LL * threads);
+    hipLaunchKernelGGL(read_shot_kernel, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
+                       (const u32x4*)src, n16, (uint32_t*)sink);
     return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

@@ -1,4 +1,4 @@
-"""ctypes binding of libnmprobe (read-stream ceiling, copy, empty launch).
+"""ctypes binding of libnmprobe (read-stream ceiling, one-shot read floor, copy, empty launch).
 
 Measurement helpers only; the product calls live in sparse_matrix_vector_amd."""
 import ctypes
@@ -18,7 +18,8 @@ def lib():
         h.nmp_read.argtypes = [P, I64, P, I, P]
         h.nmp_copy.argtypes = [P, P, I64, I, P]
         h.nmp_empty.argtypes = [P]
-        for f in (h.nmp_read, h.nmp_copy, h.nmp_empty):
+        h.nmp_read_shot.argtypes = [P, I64, P, I, P]
+        for f in (h.nmp_read, h.nmp_copy, h.nmp_empty, h.nmp_read_shot):
             f.restype = I
         _lib = h
     return _lib

@@ -2,6 +2,7 @@
 
     python -m measure.profsummary trace <run>_kernel_trace.csv
     python -m measure.profsummary pmc <run>_counter_collection.csv COUNTER [calib_kernel calib_bytes]
+    python -m measure.profsummary pmctable NAME_FILTER <pass1>_counter_collection.csv [<pass2>...]
     python -m measure.profsummary sha
 
 `trace` prints, per kernel name and grid size, the dispatch count and the
@@ -10,7 +11,9 @@ grid size, the mean of COUNTER per dispatch (nominally KiB for FETCH_SIZE and
 WRITE_SIZE) and, given a calibration kernel (a name prefix) of known byte
 count per dispatch, the factor that turns the counter into bytes and the
 scaled bytes per dispatch.  The grid size (work-items) tells the shapes of one
-kernel apart.  `sha` prints the hash of the kernel sources that a counter
+kernel apart.  `pmctable` prints the
+mean of every counter per dispatch for the kernels whose name contains
+NAME_FILTER, over several counter passes.  `sha` prints the hash of the kernel sources that a counter
 summary records (bench.py reports its traffic only while they match).
 """
 import collections
@@ -79,11 +82,35 @@ def pmc(path, counter, calib_kernel=None, calib_bytes=None):
         print(f"{len(v):7d} {grid:9d} {mean:16.1f} {scaled}  {short(name)}")
 
 
+def pmc_table(paths, name_filter="", min_calls=1):
+    """Mean of every counter per dispatch, per kernel name and grid size, over
+    one or more counter-collection CSVs (one pass each), for the kernels whose
+    name contains name_filter."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if name_filter in r["Kernel_Name"]:
+                    vals[(r["Kernel_Name"], _grid(r))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    counters = sorted({c for per in vals.values() for c in per})
+    for (name, grid), per in sorted(vals.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        calls = max(len(v) for v in per.values())
+        if calls < min_calls:
+            continue
+        print(f"{short(name, 60)}  grid {grid}  ({calls} dispatches)")
+        for c in counters:
+            if c in per:
+                v = per[c]
+                print(f"    {c:40s} {sum(v) / len(v):16.1f}")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "trace":
         trace(sys.argv[2])
     elif len(sys.argv) >= 4 and sys.argv[1] == "pmc":
         pmc(sys.argv[2], sys.argv[3], *(sys.argv[4:6]))
+    elif len(sys.argv) >= 4 and sys.argv[1] == "pmctable":
+        pmc_table(sys.argv[3:], sys.argv[2])
     elif len(sys.argv) == 2 and sys.argv[1] == "sha":
         print(kernel_sources_sha256())
     else:

@@ -106,10 +106,12 @@ int cu_count();
 // x-first issue order off/on (default: on where a row is cut into slices);
 // NMSPMV_BLOCKS_PER_CU (2 to 8) caps a row-slice launch's resident blocks
 // per CU by padding its LDS; NMSPMV_XDMA=1 stages x by global-to-LDS loads
-// wherever one register per thread does not cover it.
+// wherever one register per thread does not cover it; NMSPMV_MAX_CPL (9 to
+// 16) lets a single-vector sparse row of up to that many chunks per lane run
+// on one wave instead of being cut into slices.
 struct Env {
     int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0,
-        ring_tiles = 0, ring_share = 0, hybrid_split = 0, xfirst = -1, blocks_per_cu = 0, xdma = 0;
+        ring_tiles = 0, ring_share = 0, hybrid_split = 0, xfirst = -1, blocks_per_cu = 0, xdma = 0, max_cpl = 0;
 };
 inline Env g_env;
 inline std::once_flag g_env_once;
@@ -133,6 +135,7 @@ inline void read_env()
     g_env.hybrid_split = get("NMSPMV_HYBRID_SPLIT");
     g_env.blocks_per_cu = get("NMSPMV_BLOCKS_PER_CU");
     g_env.xdma = get("NMSPMV_XDMA");
+    g_env.max_cpl = get("NMSPMV_MAX_CPL");
     const char* xf = std::getenv("NMSPMV_XFIRST");
     g_env.xfirst = xf ? std::atoi(xf) : -1;
 }
@@ -169,11 +172,14 @@ inline int log2_exact(int v)
 //    8-wave blocks held 12.4-12.5 us on all of them;
 //  * rows cut into slices issue x first (x-first issue order; the same
 //    sweep: 12.7-12.8 us without it).
-inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, Plan* P)
+inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, int B, Plan* P)
 {
     const int cus = cu_count();
+    // Long rows on one wave (up to 16 chunks a lane: a single vector,
+    // sparse, not gated), when NMSPMV_MAX_CPL asks for it.
+    const int max_cpl = (B == 1 && !dense && !glu && g_env.max_cpl > 8) ? std::min(g_env.max_cpl, 16) : 8;
     int S = 1, rpb = dense ? 4 : 8;
-    if (C > (dense ? 8 : 5) * kWave) {
+    if (C > (dense ? 8 : 5) * kWave && C > (int64_t)max_cpl * kWave) {
         const int64_t max_cps = (dense ? 7 : 8) * kWave;
         S = 2;
         while (S < 16 && (C + S - 1) / S > max_cps)
@@ -190,7 +196,7 @@ inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, Plan* P)
         S = 8;
     const int64_t cps = (C + S - 1) / S;
     const int cpl = (int)((cps + kWave - 1) / kWave);
-    if (cpl > 8)
+    if (cpl > max_cpl)
         return false;
     while (rpb > 1 && (R + rpb - 1) / rpb < 2 * cus)
         rpb /= 2;
@@ -229,7 +235,7 @@ Plan plan_for(int64_t R, int64_t K, int B, bool glu)
     int kind = g_env.kernel;
     if (kind != 1 && kind != 3)
         kind = (fits && C <= (F == kDense ? 32 : 18) * kWave) ? 1 : 3;
-    if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, glu, &P)) {
+    if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, glu, B, &P)) {
         P.lds = tab + xbytes + (size_t)P.rpb * P.S * B * 4;
         if (g_env.blocks_per_cu >= 2 && g_env.blocks_per_cu <= 8)
             P.lds = std::max(P.lds, (size_t)kLdsMax / (g_env.blocks_per_cu + 1) + 256);
@@ -280,14 +286,16 @@ Plan plan_for(int64_t R, int64_t K, int B, bool glu)
 
 // Row-slice x staging: 1 = one register per thread covers B x K (each thread
 // loads one 16-byte unit and stores it to LDS); 4 = four registers a thread
-// cover a single vector; 0 = global-to-LDS loads, which hold no registers.
-inline int rowslice_x_regs(int B, int64_t K, int threads)
+// cover a single vector (not with more than 8 chunks a lane, whose weights
+// already hold most of the registers); 0 = global-to-LDS loads, which hold no
+// registers.
+inline int rowslice_x_regs(int B, int64_t K, int threads, int cpl)
 {
     std::call_once(g_env_once, read_env);
     const int64_t xunits = (int64_t)B * (K / 8);
     if (xunits <= threads)
         return 1;
-    return (B == 1 && xunits <= 4LL * threads && g_env.xdma != 1) ? 4 : 0;
+    return (B == 1 && xunits <= 4LL * threads && g_env.xdma != 1 && cpl <= 8) ? 4 : 0;
 }
 
 // Fused hybrid launch (a hybrid matrix's RS sparse and its dense rows in one
@@ -307,7 +315,7 @@ bool plan_hybrid(int64_t RS, int64_t K, int B, Plan* out)
         P.grid = (unsigned)((RS + 1) / 2);
         P.lds = (size_t)table_units<F>() * kUnitBytes + (size_t)B * x_row_units(K) * 16 + (size_t)P.rpb * P.S * B * 4;
     }
-    if (P.kind != 1 || P.rpb < 2 || P.rpb % 2 != 0)
+    if (P.kind != 1 || P.rpb < 2 || P.rpb % 2 != 0 || P.cpl > 8)
         return false;
     *out = P;
     return true;

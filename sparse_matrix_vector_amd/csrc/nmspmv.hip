@@ -1882,7 +1882,7 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
     const u32x4* x4 = static_cast<const u32x4*>(x);
     (void)hipGetLastError();
     if (P.kind == 1) {
-        const int xu = rowslice_x_regs(NB, K, P.threads);
+        const int xu = rowslice_x_regs(NB, K, P.threads, P.cpl);
 #define NM_SLICE_XU(CPL, XU)                                                                                         \
     hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, CPL, XU>), dim3(P.grid), dim3(P.threads), P.lds, s, parts, x4, R, \
                        K, P.ls, P.rpb, P.xf, (int)(xu != 0))
@@ -1897,6 +1897,20 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
             NM_SLICE_XU(CPL, 1);       \
         }                              \
     } while (0)
+        if constexpr (NB == 1 && F != kDense) {
+            // long rows on one wave (single vector): the next even slot count
+            if (P.cpl > 8) {
+                if (P.cpl <= 10)
+                    NM_SLICE_XU(10, 1);
+                else if (P.cpl <= 12)
+                    NM_SLICE_XU(12, 1);
+                else if (P.cpl <= 14)
+                    NM_SLICE_XU(14, 1);
+                else
+                    NM_SLICE_XU(16, 1);
+                return hip_status(hipGetLastError());
+            }
+        }
         switch (P.cpl) {
         case 1: NM_SLICE(1); break;
         case 2: NM_SLICE(2); break;

@@ -42,15 +42,15 @@ void check_rowslice(const Plan& P, int64_t R, int64_t K, int B, bool glu)
     const size_t xbytes = (size_t)B * (size_t)x_row_units(K) * 16;
     REQUIRE(pow2(P.S) && P.S <= 16 && (1 << P.ls) == P.S);
     REQUIRE(P.rpb >= 1 && P.rpb * P.S <= 16 && P.threads == P.rpb * P.S * kWave);
-    REQUIRE(P.cpl >= 1 && P.cpl <= 8);
+    REQUIRE(P.cpl >= 1 && P.cpl <= (B == 1 && !glu && F != kDense ? 16 : 8));
     REQUIRE(slice_chunks(C, P.S, P.ls) <= 64LL * P.cpl);
     REQUIRE((int64_t)P.grid * P.rpb >= R && ((int64_t)P.grid - 1) * P.rpb < R);
     REQUIRE(xbytes <= (size_t)kXTileBudget);
     REQUIRE(P.lds >= (size_t)table_units<F>() * kUnitBytes + xbytes + (size_t)P.rpb * P.S * B * 4);
     if (glu)
         REQUIRE(P.rpb % 2 == 0);
-    const int xu = rowslice_x_regs(B, K, P.threads);
-    REQUIRE(xu == 0 || xu == 1 || (xu == 4 && B == 1));
+    const int xu = rowslice_x_regs(B, K, P.threads, P.cpl);
+    REQUIRE(xu == 0 || xu == 1 || (xu == 4 && B == 1 && P.cpl <= 8));
     if (xu != 0)
         REQUIRE((int64_t)xu * P.threads >= (int64_t)B * (K / 8));
 }
@@ -239,7 +239,8 @@ int main()
         {"ring_share=1", &Env::ring_share, 1},  {"ring_share=8", &Env::ring_share, 8},
         {"xfirst=0", &Env::xfirst, 0},          {"xfirst=1", &Env::xfirst, 1},
         {"blocks_per_cu=2", &Env::blocks_per_cu, 2}, {"blocks_per_cu=8", &Env::blocks_per_cu, 8},
-        {"xdma=1", &Env::xdma, 1},
+        {"xdma=1", &Env::xdma, 1},              {"max_cpl=14", &Env::max_cpl, 14},
+        {"max_cpl=16", &Env::max_cpl, 16},      {"max_cpl=100", &Env::max_cpl, 100},
     };
     for (int cus : {256, 80, 1}) {
         g_cus = cus;
