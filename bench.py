@@ -119,6 +119,13 @@ class Launch:
                 (I64 * c)(*self.R), I64(self.K), I32(self.n), I32(self.m), I32(self.dtc), P(self.x.data_ptr()),
                 I32(self.B), (P * c)(*[y.data_ptr() for y in self.y]), P(stream))
 
+    def sparse_args_ws(self, stream, ws):
+        """nm_spmv_multi_ws arguments: the plain call's, with the K-split workspace."""
+        return self.sparse_args(stream)[:-1] + (P(ws.data_ptr()), I64(ws.numel()), P(stream))
+
+    def dense_args_ws(self, stream, ws):
+        return self.dense_args(stream)[:-1] + (P(ws.data_ptr()), I64(ws.numel()), P(stream))
+
     def dense_args(self, stream):
         c = len(self.names)
         return (I32(c), (P * c)(*[W.data_ptr() for W in self.W]), (I64 * c)(*self.R), I64(self.K), I32(self.dtc),
@@ -479,8 +486,9 @@ def config_steps(torch, nm, I, specs, steps=10):
     """Each workload of CONFIG_STEPS as a HIP-graph step over `layers` layer
     instances of its projections: GB/s (algorithmic bytes per step / step
     time), share of the 8 TB/s peak, speedup over the same step on the dense
-    weights (nm_gemv_dense_multi), us per layer, and per launch kind the
-    median us of back-to-back bursts."""
+    weights, us per layer, and per launch kind the median us of back-to-back
+    bursts.  Sparse and dense steps both run through the K-split workspace
+    calls (nm_spmv_multi_ws, nm_gemv_dense_multi_ws), one workspace a step."""
     lib = nm.lib()
     out = {}
     for name, layers in CONFIG_STEPS:
@@ -488,8 +496,9 @@ def config_steps(torch, nm, I, specs, steps=10):
         launches = build_step(spec, name, layers, torch, nm, I)
         sparse_bytes = sum(L.sparse_bytes() for L in launches)
         dense_bytes = sum(L.dense_bytes() for L in launches)
-        gs = capture(torch, lib.nm_spmv_multi, lambda st: [L.sparse_args(st) for L in launches])
-        gd = capture(torch, lib.nm_gemv_dense_multi, lambda st: [L.dense_args(st) for L in launches])
+        ws = nm.workspace()
+        gs = capture(torch, lib.nm_spmv_multi_ws, lambda st: [L.sparse_args_ws(st, ws) for L in launches])
+        gd = capture(torch, lib.nm_gemv_dense_multi_ws, lambda st: [L.dense_args_ws(st, ws) for L in launches])
         for _ in range(3):
             gs.replay()
         ms = time_ms(torch, gs.replay, steps)
@@ -500,14 +509,15 @@ def config_steps(torch, nm, I, specs, steps=10):
         for names, _ in spec[7]:
             kind = "+".join(names)
             group = [L for L in launches if L.kind == kind]
-            kinds[kind] = round(burst(torch, lib.nm_spmv_multi, lambda st: [L.sparse_args(st) for L in group], 5)[1], 3)
+            kinds[kind] = round(burst(torch, lib.nm_spmv_multi_ws, lambda st: [L.sparse_args_ws(st, ws) for L in group],
+                                      5)[1], 3)
         gbs = sparse_bytes / (ms * 1e-3) / 1e9
         out[name] = {"workload": spec[0], "layers": layers, "n_m": f"{spec[4]}:{spec[5]}", "batch": spec[6],
                      "gbs": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
                      "speedup_vs_dense": round(msd / ms, 4), "us_per_layer": round(ms * 1e3 / layers, 2),
                      "ms_per_step": round(ms, 4), "dense_ms_per_step": round(msd, 4),
                      "packed_bytes_per_step": sparse_bytes, "per_launch_us": kinds}
-        del launches, gs, gd
+        del launches, gs, gd, ws
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     return out
@@ -587,14 +597,15 @@ def main():
     sparse_bytes = sum(L.sparse_bytes() for L in launches)
     dense_bytes = sum(L.dense_bytes() for L in launches)
 
+    ws = nm.workspace()        # the K-split workspace (used by batched products on few rows)
     if a.eager:
-        sl = [L.sparse_args(cur) for L in launches]
-        dl = [L.dense_args(cur) for L in launches]
-        step_sparse = lambda: run(lib.nm_spmv_multi, sl)          # noqa: E731
-        step_dense = lambda: run(lib.nm_gemv_dense_multi, dl)     # noqa: E731
+        sl = [L.sparse_args_ws(cur, ws) for L in launches]
+        dl = [L.dense_args_ws(cur, ws) for L in launches]
+        step_sparse = lambda: run(lib.nm_spmv_multi_ws, sl)       # noqa: E731
+        step_dense = lambda: run(lib.nm_gemv_dense_multi_ws, dl)  # noqa: E731
     else:
-        gs = capture(torch, lib.nm_spmv_multi, lambda s: [L.sparse_args(s) for L in launches])
-        gd = capture(torch, lib.nm_gemv_dense_multi, lambda s: [L.dense_args(s) for L in launches])
+        gs = capture(torch, lib.nm_spmv_multi_ws, lambda s: [L.sparse_args_ws(s, ws) for L in launches])
+        gd = capture(torch, lib.nm_gemv_dense_multi_ws, lambda s: [L.dense_args_ws(s, ws) for L in launches])
         step_sparse, step_dense = gs.replay, gd.replay
 
     # ---- the timed region: K sparse steps ----
@@ -612,8 +623,8 @@ def main():
     for names, _ in spec[7]:
         kind = "+".join(names)
         group = [L for L in launches if L.kind == kind]
-        ts = burst(torch, lib.nm_spmv_multi, lambda st: [L.sparse_args(st) for L in group], 10)
-        td = burst(torch, lib.nm_gemv_dense_multi, lambda st: [L.dense_args(st) for L in group], 10)
+        ts = burst(torch, lib.nm_spmv_multi_ws, lambda st: [L.sparse_args_ws(st, ws) for L in group], 10)
+        td = burst(torch, lib.nm_gemv_dense_multi_ws, lambda st: [L.dense_args_ws(st, ws) for L in group], 10)
         us, usd = ts[1], td[1]
         sb, db = group[0].sparse_bytes(), group[0].dense_bytes()
         per[kind] = {"rows": sum(group[0].R), "K": group[0].K, "us": round(us, 3), "us_min": round(ts[0], 3),

@@ -141,6 +141,37 @@ int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64
                         void* const* y, void* stream);
 
 /*
+ * ---- K-split workspace (batched products on few rows) ------------------------
+ * At a few vectors and up the products run on the matrix cores in 16-row
+ * tiles.  A short matrix (the down projections: few rows, long K) then has
+ * too few tiles to fill the GPU unless each tile's K is cut into slices, and
+ * a slice's wave stages its own copy of x: at 8 vectors about as many x bytes
+ * as weight bytes.  With a workspace the library can instead give each block
+ * several tiles sharing one staged x over one range of K, and add the ranges'
+ * fp32 partial sums at the end (the last block of each tile group adds them in
+ * range order, so results are deterministic; they may differ from the
+ * workspace-free call's in the last bit, as another fp32 summation order).
+ *
+ * nm_workspace_bytes -- the workspace size these calls need (a constant of
+ * this library version, about 16 MB).
+ *
+ * nm_spmv_multi_ws, nm_gemv_dense_multi_ws -- nm_spmv_multi and
+ * nm_gemv_dense_multi with a workspace: device memory of at least
+ * nm_workspace_bytes() bytes, 256-byte aligned, zero-filled before its first
+ * use (the library leaves it in a reusable state after every completed call),
+ * not overlapping any input or output; workspace_bytes smaller, misalignment
+ * or overlap give NM_ERR_INVALID_ARG.  workspace NULL = the plain call.  Calls
+ * that may run at the same time (other streams, other threads) need
+ * workspaces of their own; the caller owns and frees it.
+ */
+int64_t nm_workspace_bytes(void);
+int nm_spmv_multi_ws(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
+                     int N, int M, int dtype, const void* x, int B, void* const* y, void* workspace,
+                     int64_t workspace_bytes, void* stream);
+int nm_gemv_dense_multi_ws(int count, const void* const* W, const int64_t* R, int64_t K, int dtype, const void* x,
+                           int B, void* const* y, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * nm_spmv_swiglu -- the gated-MLP input of a decode layer in one launch:
  *   h[b][r] = SiLU(g) * u,  g = (W_gate x_b)[r],  u = (W_up x_b)[r],
  *   SiLU(t) = t / (1 + e^-t).

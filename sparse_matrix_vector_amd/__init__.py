@@ -12,6 +12,7 @@ step of the computation runs in the HIP kernels of ``libnmspmv.so``.
     keep = calib_keep_mask(W, H, n=2, m=4)         # -> pack(W, keep, 2, 4)
     hyb = hybrid_pack(W, hybrid_select_rows(hybrid_row_loss(W), n_dense))
     y = spmv_hybrid(hyb, x)                        # sparse rows + dense rows
+    ys = spmv_multi(parts, x, ws=workspace())      # K-split plan for batches on few rows
 """
 import ctypes
 
@@ -22,7 +23,7 @@ from ._lib import (NM_BF16, NM_ERR_BAD_MASK, NM_ERR_BAD_SHAPE, NM_ERR_HIP, NM_ER
 
 __all__ = ["pack", "spmv", "spmv_multi", "spmv_swiglu", "gemv_dense", "gemv_dense_multi", "gemv_dense_swiglu",
            "calib_accumulate", "calib_keep_mask", "hybrid_row_loss", "hybrid_select_rows", "hybrid_pack", "spmv_hybrid",
-           "Hybrid", "NmError", "dtype_code", "stream_handle"]
+           "Hybrid", "NmError", "dtype_code", "stream_handle", "workspace"]
 
 _DT = {torch.float16: NM_FP16, torch.bfloat16: NM_BF16}
 
@@ -109,10 +110,25 @@ def _ptr_array(ptrs):
     return arr
 
 
-def spmv_multi(parts, x, n=2, m=4, stream=None):
+def workspace(device="cuda"):
+    """A zero-filled K-split workspace (nm_workspace_bytes() bytes) for
+    spmv_multi / gemv_dense_multi on `device`; give each stream its own."""
+    nbytes = int(lib().nm_workspace_bytes())
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ws_args(ws):
+    if ws is None:
+        return None, 0
+    _dev(ws, "workspace")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def spmv_multi(parts, x, n=2, m=4, stream=None, ws=None):
     """One launch for several packed matrices sharing x (e.g. q, k, v).
     ``parts`` is a list of (values, masks); returns a list of y [B][R_i]
-    (or [R_i] for a 1-D x)."""
+    (or [R_i] for a 1-D x).  ``ws``: a workspace() for the K-split plan of
+    batched products on few rows (nm_spmv_multi_ws), or None."""
     if not 1 <= len(parts) <= 4:
         raise ValueError("1 to 4 parts")
     _dev(x, "x")
@@ -127,14 +143,19 @@ def spmv_multi(parts, x, n=2, m=4, stream=None):
             raise ValueError("part shapes do not match x and n:m")
         ys.append(torch.empty((B, R), dtype=x.dtype, device=x.device))
         Rs.append(R)
-    call("nm_spmv_multi", len(parts), _ptr_array([v.data_ptr() for v, _ in parts]),
-         _ptr_array([mk.data_ptr() for _, mk in parts]), (ctypes.c_int64 * len(parts))(*Rs), K, n, m,
-         dtype_code(x.dtype), x2.data_ptr(), B, _ptr_array([y.data_ptr() for y in ys]), stream_handle(stream))
+    args = (len(parts), _ptr_array([v.data_ptr() for v, _ in parts]), _ptr_array([mk.data_ptr() for _, mk in parts]),
+            (ctypes.c_int64 * len(parts))(*Rs), K, n, m, dtype_code(x.dtype), x2.data_ptr(), B,
+            _ptr_array([y.data_ptr() for y in ys]))
+    if ws is None:
+        call("nm_spmv_multi", *args, stream_handle(stream))
+    else:
+        call("nm_spmv_multi_ws", *args, *_ws_args(ws), stream_handle(stream))
     return [y[0] for y in ys] if squeeze else ys
 
 
-def gemv_dense_multi(Ws, x, stream=None):
-    """Dense baseline of spmv_multi: one launch for several W sharing x."""
+def gemv_dense_multi(Ws, x, stream=None, ws=None):
+    """Dense baseline of spmv_multi: one launch for several W sharing x
+    (``ws`` as in spmv_multi)."""
     if not 1 <= len(Ws) <= 4:
         raise ValueError("1 to 4 matrices")
     _dev(x, "x")
@@ -147,9 +168,12 @@ def gemv_dense_multi(Ws, x, stream=None):
         if W.shape[1] != K or W.dtype != x.dtype:
             raise ValueError("W shapes do not match x")
         ys.append(torch.empty((B, W.shape[0]), dtype=x.dtype, device=x.device))
-    call("nm_gemv_dense_multi", len(Ws), _ptr_array([W.data_ptr() for W in Ws]),
-         (ctypes.c_int64 * len(Ws))(*[W.shape[0] for W in Ws]), K, dtype_code(x.dtype), x2.data_ptr(), B,
-         _ptr_array([y.data_ptr() for y in ys]), stream_handle(stream))
+    args = (len(Ws), _ptr_array([W.data_ptr() for W in Ws]), (ctypes.c_int64 * len(Ws))(*[W.shape[0] for W in Ws]), K,
+            dtype_code(x.dtype), x2.data_ptr(), B, _ptr_array([y.data_ptr() for y in ys]))
+    if ws is None:
+        call("nm_gemv_dense_multi", *args, stream_handle(stream))
+    else:
+        call("nm_gemv_dense_multi_ws", *args, *_ws_args(ws), stream_handle(stream))
     return [y[0] for y in ys] if squeeze else ys
 
 

@@ -21,11 +21,15 @@ namespace nmk {
 // y[0 .. n) = +0 (16-bit words); n > 0.
 int zero(void* y, int64_t n, void* stream);
 
-// total = sum of R[i] > 0, K > 0; parts with R[i] == 0 are skipped.
+// total = sum of R[i] > 0, K > 0; parts with R[i] == 0 are skipped.  workspace:
+// NULL, or kSplitWorkspaceBytes (nm_plan.h) of device memory, 256-byte
+// aligned, whose counters are zero, for the K-split plan of batched products
+// on few rows.
 int spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t total,
-               int64_t K, int N, int M, int dtype, const void* x, int B, void* const* y, void* stream);
+               int64_t K, int N, int M, int dtype, const void* x, int B, void* const* y, void* workspace,
+               void* stream);
 int gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t total, int64_t K, int dtype,
-                     const void* x, int B, void* const* y, void* stream);
+                     const void* x, int B, void* const* y, void* workspace, void* stream);
 
 // R > 0, K > 0.
 int spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const void* values_up, const uint8_t* masks_up,

@@ -108,10 +108,13 @@ int cu_count();
 // per CU by padding its LDS; NMSPMV_XDMA=1 stages x by global-to-LDS loads
 // wherever one register per thread does not cover it; NMSPMV_MAX_CPL (9 to
 // 16) lets a single-vector sparse row of up to that many chunks per lane run
-// on one wave instead of being cut into slices.
+// on one wave instead of being cut into slices; NMSPMV_SPLITK=1 turns the
+// K-split ring plan off, 2 uses it wherever it fits (with a workspace);
+// NMSPMV_SPLITK_KS sets its split count (2 to 32).
 struct Env {
     int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0,
-        ring_tiles = 0, ring_share = 0, hybrid_split = 0, xfirst = -1, blocks_per_cu = 0, xdma = 0, max_cpl = 0;
+        ring_tiles = 0, ring_share = 0, hybrid_split = 0, xfirst = -1, blocks_per_cu = 0, xdma = 0, max_cpl = 0,
+        splitk = 0, splitk_ks = 0;
 };
 inline Env g_env;
 inline std::once_flag g_env_once;
@@ -136,6 +139,8 @@ inline void read_env()
     g_env.blocks_per_cu = get("NMSPMV_BLOCKS_PER_CU");
     g_env.xdma = get("NMSPMV_XDMA");
     g_env.max_cpl = get("NMSPMV_MAX_CPL");
+    g_env.splitk = get("NMSPMV_SPLITK");
+    g_env.splitk_ks = get("NMSPMV_SPLITK_KS");
     const char* xf = std::getenv("NMSPMV_XFIRST");
     g_env.xfirst = xf ? std::atoi(xf) : -1;
 }
@@ -145,6 +150,7 @@ struct Plan {
     int S = 1, rpb = 1, cpl = 1, threads = 256, tile_cols = 0;
     int ls = 0;              // log2(S) (row-slice: S is a power of two)
     int xf = 0;              // row-slice: x loads issued by the whole block before any weight load
+    int ks = 0, kstages = 0; // K-split ring (kind 8): splits, stages per split
     size_t lds = 0;
     unsigned grid = 1;
 };
@@ -456,6 +462,71 @@ bool mfma_use_ring(int64_t R, int64_t K, int B)
     std::call_once(g_env_once, read_env);
     const bool ring_fits = F == kDense || (K % 32 == 0 && (B <= 16 || R >= 64LL * cu_count() || g_env.kernel == 6));
     return ring_fits && g_env.kernel != 5;
+}
+
+// Workspace of the K-split ring plan: partial sums, then one counter per tile
+// group (zero between launches).
+constexpr size_t kSplitPartBytes = size_t(16) << 20;
+constexpr int kSplitMaxGroups = 16384;
+constexpr size_t kSplitWorkspaceBytes = kSplitPartBytes + size_t(kSplitMaxGroups) * 4;
+
+// K-split ring plan (kind 8), for the calls that bring a workspace: where the
+// LDS-ring plan would cut each 16-row tile into per-wave K-slices (few tiles
+// for the CUs, so each wave stages its own x: about as many x bytes as
+// weight bytes at 8 vectors), blocks of W waves (one tile group, TW tiles a
+// wave) share each staged x over one of KS contiguous stage ranges instead,
+// and the last block of a group adds the KS partial sums.  KS: the fewest
+// splits (a power of two) that give the launch two blocks a CU, each split at
+// least four stages; W = 2 tile units a block (sweeps at the Qwen3-32B down
+// shape, 5120 x 25600, at 4 / 8 / 16 vectors, us: W = 2 and 4 splits 39.4 /
+// 40.0 / -, 8 splits - / - / 50.0; W = 4 with 8 splits 43.0 at 8 vectors;
+// without the workspace 41.2 / 49.5 / 58.0).  false: keep the ring plan.
+template <int F>
+bool plan_mfma_split(int64_t R, int64_t K, int B, Plan* out)
+{
+    std::call_once(g_env_once, read_env);
+    if (g_env.splitk == 1)
+        return false;
+    const Plan base = plan_mfma_ring<F>(R, K, B);
+    if (g_env.splitk != 2 && !(base.kind == 6 && base.S >= 2))
+        return false;
+    constexpr int COLS = chunk_cols<F>();
+    const int cus = cu_count();
+    const int TW = base.cpl;
+    const int NT = B > 16 ? 2 : 1;
+    const int64_t C = K / COLS, NS = (C + kStageChunks - 1) / kStageChunks;
+    const int64_t tiles = (R + 16 * TW - 1) / (16 * TW);
+    const size_t tab = (size_t)mfma_table_units<F>() * kUnitBytes;
+    const size_t wring = 2 * (size_t)TW * (kRingValues + (F == kDense ? 0 : kRingMasks));
+    const size_t xslot = (size_t)ring_x_rows<F>(B) * ring_x_units<F>() * 16;
+    int W = 2;
+    if (g_env.ring_share > 0)
+        W = std::min(g_env.ring_share, 8);
+    while (W > 1 && tab + W * wring + 2 * xslot > (size_t)kLdsMax / 2)
+        W /= 2;
+    const int64_t groups = (tiles + W - 1) / W;
+    int KS = 1;
+    while (KS < 32 && groups * KS < 2LL * cus && NS / (2 * KS) >= 4)
+        KS *= 2;
+    if (g_env.splitk_ks >= 2 && g_env.splitk_ks <= 32)
+        KS = (int)std::min<int64_t>(g_env.splitk_ks, NS);
+    if (KS < 2 || groups > kSplitMaxGroups)
+        return false;
+    const int64_t stages = (NS + KS - 1) / KS;
+    if ((size_t)KS * (size_t)groups * W * TW * NT * 1024 > kSplitPartBytes)
+        return false;
+    Plan P;
+    P.kind = 8;
+    P.S = 1;
+    P.rpb = W;
+    P.cpl = TW;
+    P.threads = W * kWave;
+    P.grid = (unsigned)(groups * KS);
+    P.ks = KS;
+    P.kstages = (int)stages;
+    P.lds = tab + W * wring + 2 * xslot;
+    *out = P;
+    return true;
 }
 
 }  // namespace nmh

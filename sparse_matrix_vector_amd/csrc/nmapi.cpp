@@ -11,6 +11,7 @@
 #include <cstdint>
 
 #include "nm_launch.h"
+#include "nm_plan.h"
 #include "nm_rules.h"
 #include "nmspmv.h"
 
@@ -32,26 +33,13 @@ int zero_outputs(int count, void* const* y, const int64_t* R, int B, void* strea
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int nm_version(void) { return 101; }
-
-const char* nm_status_string(int status)
-{
-    switch (status) {
-    case NM_OK: return "NM_OK";
-    case NM_ERR_INVALID_ARG: return "NM_ERR_INVALID_ARG";
-    case NM_ERR_BAD_SHAPE: return "NM_ERR_BAD_SHAPE";
-    case NM_ERR_UNSUPPORTED: return "NM_ERR_UNSUPPORTED";
-    case NM_ERR_BAD_MASK: return "NM_ERR_BAD_MASK";
-    case NM_ERR_NONFINITE: return "NM_ERR_NONFINITE";
-    case NM_ERR_HIP: return "NM_ERR_HIP";
-    default: return "NM_ERR_UNKNOWN";
-    }
-}
-
-int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
-                  int N, int M, int dtype, const void* x, int B, void* const* y, void* stream)
+// nm_spmv_multi with an optional K-split workspace (ws, ws_bytes; checked
+// here when given).
+int spmv_multi_with(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
+                    int N, int M, int dtype, const void* x, int B, void* const* y, void* ws, int64_t ws_bytes,
+                    void* stream)
 {
     int st = check_dtype(dtype);
     if (st != NM_OK)
@@ -87,21 +75,27 @@ int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* ma
                 return NM_ERR_INVALID_ARG;
         }
     }
+    if (ws) {
+        if (ws_bytes < (int64_t)kSplitWorkspaceBytes || !aligned(ws, 256))
+            return NM_ERR_INVALID_ARG;
+        if (overlaps(ws, (size_t)ws_bytes, x, xbytes))
+            return NM_ERR_INVALID_ARG;
+        for (int i = 0; i < count; ++i) {
+            const size_t vb = (size_t)R[i] * (size_t)(K / M * N) * 2, mb = (size_t)R[i] * (size_t)(K / 8);
+            if (overlaps(ws, (size_t)ws_bytes, values[i], vb) || overlaps(ws, (size_t)ws_bytes, masks[i], mb) ||
+                overlaps(ws, (size_t)ws_bytes, y[i], (size_t)B * (size_t)R[i] * 2))
+                return NM_ERR_INVALID_ARG;
+        }
+    }
     if (total == 0)
         return NM_OK;
     if (K == 0)
         return zero_outputs(count, y, R, B, stream);
-    return nmk::spmv_multi(count, values, masks, R, total, K, N, M, dtype, x, B, y, stream);
+    return nmk::spmv_multi(count, values, masks, R, total, K, N, M, dtype, x, B, y, ws, stream);
 }
 
-int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int N, int M, int dtype, const void* x,
-            int B, void* y, void* stream)
-{
-    return nm_spmv_multi(1, &values, &masks, &R, K, N, M, dtype, x, B, &y, stream);
-}
-
-int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t K, int dtype, const void* x, int B,
-                        void* const* y, void* stream)
+int gemv_dense_multi_with(int count, const void* const* W, const int64_t* R, int64_t K, int dtype, const void* x,
+                          int B, void* const* y, void* ws, int64_t ws_bytes, void* stream)
 {
     int st = check_dtype(dtype);
     if (st != NM_OK)
@@ -134,11 +128,74 @@ int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64
                 (j != i && overlaps(y[i], yb, y[j], (size_t)B * (size_t)R[j] * 2)))
                 return NM_ERR_INVALID_ARG;
     }
+    if (ws) {
+        if (ws_bytes < (int64_t)kSplitWorkspaceBytes || !aligned(ws, 256))
+            return NM_ERR_INVALID_ARG;
+        if (overlaps(ws, (size_t)ws_bytes, x, xbytes))
+            return NM_ERR_INVALID_ARG;
+        for (int i = 0; i < count; ++i)
+            if (overlaps(ws, (size_t)ws_bytes, W[i], (size_t)R[i] * (size_t)K * 2) ||
+                overlaps(ws, (size_t)ws_bytes, y[i], (size_t)B * (size_t)R[i] * 2))
+                return NM_ERR_INVALID_ARG;
+    }
     if (total == 0)
         return NM_OK;
     if (K == 0)
         return zero_outputs(count, y, R, B, stream);
-    return nmk::gemv_dense_multi(count, W, R, total, K, dtype, x, B, y, stream);
+    return nmk::gemv_dense_multi(count, W, R, total, K, dtype, x, B, y, ws, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int nm_version(void) { return 101; }
+
+const char* nm_status_string(int status)
+{
+    switch (status) {
+    case NM_OK: return "NM_OK";
+    case NM_ERR_INVALID_ARG: return "NM_ERR_INVALID_ARG";
+    case NM_ERR_BAD_SHAPE: return "NM_ERR_BAD_SHAPE";
+    case NM_ERR_UNSUPPORTED: return "NM_ERR_UNSUPPORTED";
+    case NM_ERR_BAD_MASK: return "NM_ERR_BAD_MASK";
+    case NM_ERR_NONFINITE: return "NM_ERR_NONFINITE";
+    case NM_ERR_HIP: return "NM_ERR_HIP";
+    default: return "NM_ERR_UNKNOWN";
+    }
+}
+
+int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
+                  int N, int M, int dtype, const void* x, int B, void* const* y, void* stream)
+{
+    return spmv_multi_with(count, values, masks, R, K, N, M, dtype, x, B, y, nullptr, 0, stream);
+}
+
+int nm_spmv_multi_ws(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
+                     int N, int M, int dtype, const void* x, int B, void* const* y, void* workspace,
+                     int64_t workspace_bytes, void* stream)
+{
+    return spmv_multi_with(count, values, masks, R, K, N, M, dtype, x, B, y, workspace, workspace_bytes, stream);
+}
+
+int64_t nm_workspace_bytes(void) { return (int64_t)kSplitWorkspaceBytes; }
+
+int nm_spmv(const void* values, const uint8_t* masks, int64_t R, int64_t K, int N, int M, int dtype, const void* x,
+            int B, void* y, void* stream)
+{
+    return nm_spmv_multi(1, &values, &masks, &R, K, N, M, dtype, x, B, &y, stream);
+}
+
+int nm_gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t K, int dtype, const void* x, int B,
+                        void* const* y, void* stream)
+{
+    return gemv_dense_multi_with(count, W, R, K, dtype, x, B, y, nullptr, 0, stream);
+}
+
+int nm_gemv_dense_multi_ws(int count, const void* const* W, const int64_t* R, int64_t K, int dtype, const void* x,
+                           int B, void* const* y, void* workspace, int64_t workspace_bytes, void* stream)
+{
+    return gemv_dense_multi_with(count, W, R, K, dtype, x, B, y, workspace, workspace_bytes, stream);
 }
 
 int nm_gemv_dense(const void* W, int64_t R, int64_t K, int dtype, const void* x, int B, void* y, void* stream)

@@ -1167,10 +1167,31 @@ __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u3
 // x issued, into the slot whose last reads every wave finished before that
 // barrier.  Every wave runs all stages (tiles past R read clamped rows and
 // store nothing), so the barrier counts match.
-template <int F, int DT, int TW, int NT, bool SHX>
+//
+// KSPLIT (with SHX): the block's waves take one of KS contiguous ranges of
+// the stages (split ks = blockIdx.x % KS of tile group blockIdx.x / KS), so a
+// short matrix fills the GPU while each staged x still serves several
+// tiles.  Each wave writes its tiles' partial sums to scratch; the block then
+// counts itself in its group's counter, and the block that arrives last adds
+// the KS partials of every tile in split order (fixed, so results do not
+// depend on which block is last), writes y and resets the counter to zero
+// for the next launch.  The partials and the counter are accessed only as
+// agent-scope atomics (coherent across the GPU's L2 caches without cache
+// write-back or invalidation, which cost tens of microseconds here), and
+// each thread waits for its partial stores to complete before the block's
+// counter update, so the last block's reads see them.
+struct SplitK {
+    float* part;         // KS x (tile groups x tiles_per_block x TW x NT) x 256 floats
+    unsigned* cnt;       // one counter per tile group, zero between launches
+    int ks;              // splits (KS)
+    int stages;          // stages per split (the last may have fewer, or none)
+};
+
+template <int F, int DT, int TW, int NT, bool SHX, bool KSPLIT = false>
 __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
-                                                        int B, int S, int tiles_per_block)
+                                                        int B, int S, int tiles_per_block, SplitK sk)
 {
+    static_assert(!KSPLIT || SHX, "K-split blocks share their staged x");
     extern __shared__ u32x4 smem[];
     constexpr int COLS = chunk_cols<F>();
     constexpr int XC = COLS / 8;                 // 16-byte x units per chunk
@@ -1185,12 +1206,17 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lt = wave / S, sl = wave - lt * S;
-    const int r0 = (blockIdx.x * tiles_per_block + lt) * 16 * TW;
+    const int ks = KSPLIT ? (int)(blockIdx.x % (unsigned)sk.ks) : 0;
+    const int grp = KSPLIT ? (int)(blockIdx.x / (unsigned)sk.ks) : (int)blockIdx.x;
+    const int r0 = (grp * tiles_per_block + lt) * 16 * TW;
     // Slice sl takes stages sl, sl + S, sl + 2 S, ... of the row: the waves
     // of a launch move through K together.
     const int C = K / COLS;
     const int NS = (C + kStageChunks - 1) / kStageChunks;
-    const int nst = SHX ? NS : (r0 < R && sl < NS) ? (NS - sl + S - 1) / S : 0;
+    // KSPLIT: stages st0 .. st0 + nst - 1 (uniform over the block: the barrier counts match)
+    const int st0 = KSPLIT ? ks * sk.stages : 0;
+    const int nst = KSPLIT ? max(0, min(sk.stages, NS - st0))
+                           : SHX ? NS : (r0 < R && sl < NS) ? (NS - sl + S - 1) / S : 0;
     const int i = lane & 15, q = lane >> 4;      // operand layout: row / batch column i, k-quarter q
     const int nxi = ring_x_rows<F>(B) / RPX;     // x load instructions per stage (1 .. 16)
     const int nwaves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
@@ -1230,7 +1256,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     // row's end load the stage's first chunk instead (in bounds; never
     // multiplied).
     auto issue_w = [&](int st, int slot) {
-        const int c0 = (sl + st * S) * kStageChunks;
+        const int c0 = (sl + (st0 + st) * S) * kStageChunks;
         const uint32_t base = ring + (uint32_t)(slot * slot_bytes);
 #pragma unroll
         for (int tw = 0; tw < TW; ++tw) {
@@ -1248,7 +1274,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
         }
     };
     auto issue_x = [&](int st, int slot) {
-        const int c0 = (sl + st * S) * kStageChunks;
+        const int c0 = (sl + (st0 + st) * S) * kStageChunks;
         const uint32_t xbase =
             SHX ? xring + (uint32_t)(slot * xslot_bytes) : ring + (uint32_t)(slot * slot_bytes) + (uint32_t)XOFF;
         for (int n = SHX ? wave : 0; n < nxi; n += SHX ? nwaves : 1) {
@@ -1276,7 +1302,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     // (mask cleared: no selector picks a value, and x is finite; dense:
     // values cleared).
     auto consume = [&](int st, int slot) {
-        const int c0 = (sl + st * S) * kStageChunks;
+        const int c0 = (sl + (st0 + st) * S) * kStageChunks;
         const uint8_t* sv0 = ring_p + slot * slot_bytes;
         const uint8_t* sxs = SHX ? reinterpret_cast<const uint8_t*>(smem) + xring + slot * xslot_bytes : sv0 + XOFF;
         u32x4 xx[NT][T][XC];
@@ -1380,6 +1406,64 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
             __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the slot's reads are done before it is refilled
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+
+    if constexpr (KSPLIT) {
+        // This wave's partial sums: KS x units x TW x NT blocks of 64 lanes x 4 floats.
+        const int units = (int)(gridDim.x / (unsigned)sk.ks) * tiles_per_block;
+        const int unit = grp * tiles_per_block + lt;
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                float* dst = sk.part + ((((size_t)ks * units + unit) * TW + tw) * NT + nt) * 256 + lane * 4;
+#pragma unroll
+                for (int vv = 0; vv < 4; ++vv)
+                    __hip_atomic_store(dst + vv, acc[tw][nt][vv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        wait_vmcnt<0>();                         // this thread's partial stores are complete
+        // The flag lives in wave 0's ring, idle once every wave is past its
+        // last stage (static LDS would move the offsets the ring loads use).
+        int* last_block = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(smem) + TAB);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned old = __hip_atomic_fetch_add(sk.cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *last_block = old == (unsigned)sk.ks - 1u;
+        }
+        __syncthreads();
+        if (!*last_block)
+            return;
+        if (threadIdx.x == 0)
+            __hip_atomic_store(sk.cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (r0 >= R)
+            return;
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int b = 16 * nt + i;
+                float sum[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < sk.ks; ++j) {
+                    const float* src = sk.part + ((((size_t)j * units + unit) * TW + tw) * NT + nt) * 256 + lane * 4;
+#pragma unroll
+                    for (int vv = 0; vv < 4; ++vv)
+                        sum[vv] += __hip_atomic_load(src + vv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (b >= B)
+                    continue;
+#pragma unroll
+                for (int vv = 0; vv < 4; ++vv) {
+                    const int r = r0 + 16 * tw + 4 * q + vv;
+                    if (r >= R)
+                        continue;
+                    const RowRef o = row_ref(P, r, C);
+                    if (!P.glu)
+                        o.y[(size_t)b * o.R] = from_f32<DT>(sum[vv]);
+                    else if ((vv & 1) == 0)      // rows r (gate) and r + 1 (up) of one output
+                        o.y[(size_t)b * o.R] = glu_out<DT>(sum[vv], sum[vv + 1]);
+                }
+            }
+        return;
     }
 
     // Slice sums through the wave's own ring (no loads into it are pending):
@@ -1837,7 +1921,25 @@ int launch_mfma_ring_k(const Plan& P, const Parts& parts, const void* x, int R, 
     }
     (void)hipGetLastError();
     hipLaunchKernelGGL((mfma_ring_kernel<F, DT, TW, NT, SHX>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
-                       static_cast<const u32x4*>(x), R, K, B, P.S, P.rpb);
+                       static_cast<const u32x4*>(x), R, K, B, P.S, P.rpb, SplitK{});
+    return hip_status(hipGetLastError());
+}
+
+// K-split ring launch (kind 8) with its workspace: partial sums first, then
+// the groups' counters (zero between launches).
+template <int F, int DT, int TW, int NT>
+int launch_mfma_split(const Plan& P, const Parts& parts, const void* x, int R, int K, int B, hipStream_t s, void* ws)
+{
+    if (P.lds > 64 * 1024) {
+        static bool raised[64] = {};             // per device, once per instantiation
+        if (allow_full_lds((const void*)mfma_ring_kernel<F, DT, TW, NT, true, true>, raised) != NM_OK)
+            return NM_ERR_HIP;
+    }
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    const SplitK sk{reinterpret_cast<float*>(w), reinterpret_cast<unsigned*>(w + kSplitPartBytes), P.ks, P.kstages};
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((mfma_ring_kernel<F, DT, TW, NT, true, true>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
+                       static_cast<const u32x4*>(x), R, K, B, 1, P.rpb, sk);
     return hip_status(hipGetLastError());
 }
 
@@ -1848,10 +1950,18 @@ int launch_mfma_ring_tw(const Plan& P, const Parts& parts, const void* x, int R,
                        : launch_mfma_ring_k<F, DT, TW, NT, false>(P, parts, x, R, K, B, s);
 }
 
-// Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles).
+// Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles).  With
+// a workspace, the K-split plan where it applies.
 template <int F, int DT>
-int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
+int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s, void* ws)
 {
+    Plan SP;
+    if (ws && plan_mfma_split<F>(R, K, B, &SP)) {
+        if (B > 16)
+            return launch_mfma_split<F, DT, 2, 2>(SP, parts, x, R, K, B, s, ws);
+        return SP.cpl == 2 ? launch_mfma_split<F, DT, 2, 1>(SP, parts, x, R, K, B, s, ws)
+                           : launch_mfma_split<F, DT, 1, 1>(SP, parts, x, R, K, B, s, ws);
+    }
     const Plan P = plan_mfma_ring<F>(R, K, B);
     if (B > 16)
         return launch_mfma_ring_tw<F, DT, 2, 2>(P, parts, x, R, K, B, s);
@@ -1860,18 +1970,20 @@ int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hip
 }
 
 template <int F, int DT>
-int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
+int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s, void* ws)
 {
     if (mfma_use_ring<F>(R, K, B))
-        return launch_mfma_ring<F, DT>(parts, x, R, K, B, s);
+        return launch_mfma_ring<F, DT>(parts, x, R, K, B, s, ws);
     return B > 16 ? launch_mfma_nt<F, DT, 2>(parts, x, R, K, B, s) : launch_mfma_nt<F, DT, 1>(parts, x, R, K, B, s);
 }
 
+// ws: the caller's K-split workspace (kSplitWorkspaceBytes, counters zero), or NULL.
 template <int F>
-int launch_mfma_dt(int dtype, const Parts* parts, const void* x, int R, int K, int B, hipStream_t s)
+int launch_mfma_dt(int dtype, const Parts* parts, const void* x, int R, int K, int B, hipStream_t s,
+                   void* ws = nullptr)
 {
-    return dtype == NM_FP16 ? launch_mfma<F, NM_FP16>(*parts, x, R, K, B, s)
-                            : launch_mfma<F, NM_BF16>(*parts, x, R, K, B, s);
+    return dtype == NM_FP16 ? launch_mfma<F, NM_FP16>(*parts, x, R, K, B, s, ws)
+                            : launch_mfma<F, NM_BF16>(*parts, x, R, K, B, s, ws);
 }
 
 // Launches the chosen kernel over the concatenated rows of `parts` (R in total).
@@ -2214,7 +2326,8 @@ int nmh::cu_count()
 int nmk::zero(void* y, int64_t n, void* stream) { return launch_zero(y, n, static_cast<hipStream_t>(stream)); }
 
 int nmk::spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t total,
-                    int64_t K, int N, int M, int dtype, const void* x, int B, void* const* y, void* stream)
+                    int64_t K, int N, int M, int dtype, const void* x, int B, void* const* y, void* workspace,
+                    void* stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K % 16 == 0 && ((N == 2 && M == 4) || (N == 4 && M == 8))) {
@@ -2232,8 +2345,8 @@ int nmk::spmv_multi(int count, const void* const* values, const uint8_t* const* 
         for (int i = P.count + 1; i <= kMaxParts; ++i)
             P.begin[i] = P.begin[P.count];
         if (M == 4 ? use_mfma<kNM24>(total, K, B, false) : use_mfma<kNM48>(total, K, B, false))
-            return M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)total, (int)K, B, s)
-                          : launch_mfma_dt<kNM48>(dtype, &P, x, (int)total, (int)K, B, s);
+            return M == 4 ? launch_mfma_dt<kNM24>(dtype, &P, x, (int)total, (int)K, B, s, workspace)
+                          : launch_mfma_dt<kNM48>(dtype, &P, x, (int)total, (int)K, B, s, workspace);
         return M == 4 ? dispatch<Sparse24>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s)
                       : dispatch<Sparse48>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s);
     }
@@ -2248,7 +2361,7 @@ int nmk::spmv_multi(int count, const void* const* values, const uint8_t* const* 
 }
 
 int nmk::gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t total, int64_t K, int dtype,
-                          const void* x, int B, void* const* y, void* stream)
+                          const void* x, int B, void* const* y, void* workspace, void* stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     Parts P = {};
@@ -2264,7 +2377,7 @@ int nmk::gemv_dense_multi(int count, const void* const* W, const int64_t* R, int
     for (int i = P.count + 1; i <= kMaxParts; ++i)
         P.begin[i] = P.begin[P.count];
     if (use_mfma<kDense>(total, K, B, false))
-        return launch_mfma_dt<kDense>(dtype, &P, x, (int)total, (int)K, B, s);
+        return launch_mfma_dt<kDense>(dtype, &P, x, (int)total, (int)K, B, s, workspace);
     return dispatch<Dense>(dtype, B, (const Parts*)&P, x, (int)total, (int)K, s);
 }
 

@@ -67,11 +67,25 @@ struct Tally {
     long launched;
 };
 
-Tally g_tally[14] = {{"nm_spmv", {}, 0},          {"nm_gemv_dense", {}, 0},     {"nm_spmv_multi", {}, 0},
-                     {"nm_gemv_dense_multi", {}, 0}, {"nm_spmv_swiglu", {}, 0}, {"nm_gemv_dense_swiglu", {}, 0},
-                     {"nm_pack", {}, 0},          {"nm_hybrid_row_loss", {}, 0}, {"nm_hybrid_select_rows", {}, 0},
-                     {"nm_hybrid_pack", {}, 0},   {"nm_spmv_hybrid", {}, 0},   {"nm_calib_accumulate", {}, 0},
-                     {"nm_calib_keep_mask", {}, 0}, {"(unused)", {}, 0}};
+constexpr int kCalls = 15;
+Tally g_tally[kCalls] = {{"nm_spmv", {}, 0},          {"nm_gemv_dense", {}, 0},     {"nm_spmv_multi", {}, 0},
+                         {"nm_gemv_dense_multi", {}, 0}, {"nm_spmv_swiglu", {}, 0}, {"nm_gemv_dense_swiglu", {}, 0},
+                         {"nm_pack", {}, 0},          {"nm_hybrid_row_loss", {}, 0}, {"nm_hybrid_select_rows", {}, 0},
+                         {"nm_hybrid_pack", {}, 0},   {"nm_spmv_hybrid", {}, 0},   {"nm_calib_accumulate", {}, 0},
+                         {"nm_calib_keep_mask", {}, 0}, {"nm_spmv_multi_ws", {}, 0}, {"nm_gemv_dense_multi_ws", {}, 0}};
+
+// A workspace pointer and size: usually the right size (256-aligned, in the crowded window or far), sometimes
+// too small, misaligned, absent, or an absurd size.
+void pick_ws(void** ws, int64_t* bytes)
+{
+    const int64_t need = nm_workspace_bytes();
+    *ws = below(8) ? pick_ptr(256) : nullptr;
+    if (*ws && below(4) == 0)
+        *ws = reinterpret_cast<void*>(reinterpret_cast<uintptr_t>(*ws) | 16);
+    static const int64_t odd[] = {0, 1, -1, INT64_MAX, INT64_MIN};
+    const uint64_t r = below(10);
+    *bytes = r < 6 ? need : r < 8 ? need - 1 - (int64_t)below(1000) : odd[below(5)];
+}
 
 void record(int which, int st, long before)
 {
@@ -95,7 +109,9 @@ void one_call(int which)
         break;
     case 1: st = nm_gemv_dense(pick_ptr(16), R, K, dt, pick_ptr(16), B, pick_ptr(2), nullptr); break;
     case 2:
-    case 3: {
+    case 3:
+    case 13:
+    case 14: {
         const int count = below(8) ? 1 + (int)below(4) : (int)below(7) - 1;
         const void* v[6];
         const uint8_t* m[6];
@@ -107,12 +123,21 @@ void one_call(int which)
             Rs[i] = below(4) ? (int64_t)below(20) : pick_rows();
             y[i] = pick_ptr(2);
         }
+        void* ws = nullptr;
+        int64_t wsb = 0;
+        pick_ws(&ws, &wsb);
         if (which == 2)
             st = nm_spmv_multi(count, below(20) ? v : nullptr, below(20) ? m : nullptr, below(20) ? Rs : nullptr, K, N,
                                M, dt, pick_ptr(16), B, below(20) ? y : nullptr, nullptr);
-        else
+        else if (which == 3)
             st = nm_gemv_dense_multi(count, below(20) ? v : nullptr, below(20) ? Rs : nullptr, K, dt, pick_ptr(16), B,
                                      below(20) ? y : nullptr, nullptr);
+        else if (which == 13)
+            st = nm_spmv_multi_ws(count, below(20) ? v : nullptr, below(20) ? m : nullptr, below(20) ? Rs : nullptr, K,
+                                  N, M, dt, pick_ptr(16), B, below(20) ? y : nullptr, ws, wsb, nullptr);
+        else
+            st = nm_gemv_dense_multi_ws(count, below(20) ? v : nullptr, below(20) ? Rs : nullptr, K, dt, pick_ptr(16),
+                                        B, below(20) ? y : nullptr, ws, wsb, nullptr);
         break;
     }
     case 4:
@@ -168,9 +193,9 @@ int main(int argc, char** argv)
 {
     const long calls = argc > 1 ? std::atol(argv[1]) : 200000;
     for (long i = 0; i < calls; ++i)
-        one_call((int)(i % 13));
+        one_call((int)(i % kCalls));
     int bad = 0;
-    for (int w = 0; w < 13; ++w) {
+    for (int w = 0; w < kCalls; ++w) {
         const Tally& t = g_tally[w];
         std::printf("%-22s ok %6ld  invalid_arg %6ld  bad_shape %6ld  unsupported %6ld  launched %6ld\n", t.name,
                     t.seen[NM_OK], t.seen[NM_ERR_INVALID_ARG], t.seen[NM_ERR_BAD_SHAPE], t.seen[NM_ERR_UNSUPPORTED],

@@ -83,8 +83,22 @@ int nmk::zero(void* y, int64_t n, void*)
     return launched();
 }
 
+// A workspace, when given, is ws_bytes (the library's constant) long, 256-byte aligned and apart from every
+// input and output.
+void workspace(const char* c, const void* ws, const std::vector<Buf>& ins, const std::vector<Buf>& outs)
+{
+    if (!ws)
+        return;
+    promise(reinterpret_cast<uintptr_t>(ws) % 256 == 0, c, "workspace alignment");
+    const Buf w{ws, (uint64_t)nm_workspace_bytes()};
+    for (const Buf& b : ins)
+        promise(apart(w, b), c, "workspace overlaps an input");
+    for (const Buf& b : outs)
+        promise(apart(w, b), c, "workspace overlaps an output");
+}
+
 int nmk::spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t total,
-                    int64_t K, int N, int M, int dtype, const void* x, int B, void* const* y, void*)
+                    int64_t K, int N, int M, int dtype, const void* x, int B, void* const* y, void* ws, void*)
 {
     const char* c = "spmv_multi";
     promise(count >= 1 && count <= 4 && values && masks && R && y, c, "part arrays");
@@ -108,11 +122,12 @@ int nmk::spmv_multi(int count, const void* const* values, const uint8_t* const* 
         outs.push_back({y[i], (uint64_t)B * R[i] * 2});
     }
     outputs_apart(c, outs, ins);
+    workspace(c, ws, ins, outs);
     return launched();
 }
 
 int nmk::gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t total, int64_t K, int dtype,
-                          const void* x, int B, void* const* y, void*)
+                          const void* x, int B, void* const* y, void* ws, void*)
 {
     const char* c = "gemv_dense_multi";
     promise(count >= 1 && count <= 4 && W && R && y, c, "part arrays");
@@ -134,6 +149,7 @@ int nmk::gemv_dense_multi(int count, const void* const* W, const int64_t* R, int
         outs.push_back({y[i], (uint64_t)B * R[i] * 2});
     }
     outputs_apart(c, outs, ins);
+    workspace(c, ws, ins, outs);
     return launched();
 }
 

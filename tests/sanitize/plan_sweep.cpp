@@ -19,7 +19,7 @@ namespace {
 
 int g_cus = 256;
 long g_plans = 0;
-long g_kinds[8] = {};   // plans seen per kernel kind (0: fused hybrid)
+long g_kinds[8] = {};   // plans seen per kernel kind (0: fused hybrid, 2: K-split ring)
 char g_case[256];
 
 #define REQUIRE(c)                                                                         \
@@ -112,6 +112,22 @@ void check_mfma(int64_t R, int64_t K, int B, bool glu)
         } else {
             REQUIRE(P.kind == 7 && P.S == 1 && P.threads == P.rpb * kWave);
             REQUIRE((int64_t)P.grid * P.rpb >= tiles && ((int64_t)P.grid - 1) * P.rpb < tiles);
+        }
+        Plan SP;
+        if (plan_mfma_split<F>(R, K, B, &SP)) {
+            ++g_plans;
+            ++g_kinds[2];
+            const int64_t NS = (K / chunk_cols<F>() + kStageChunks - 1) / kStageChunks;
+            const int W = SP.rpb, TWs = SP.cpl, NTs = B > 16 ? 2 : 1;
+            REQUIRE(SP.kind == 8 && SP.S == 1 && (TWs == 1 || TWs == 2) && (B <= 16 || TWs == 2));
+            REQUIRE(W >= 1 && SP.threads == W * kWave && SP.threads <= 512);
+            REQUIRE(SP.lds <= (size_t)kLdsMax);
+            REQUIRE(SP.ks >= 2 && SP.ks <= 32 && SP.kstages >= 1);
+            REQUIRE((int64_t)SP.ks * SP.kstages >= NS);                      // every stage in some split
+            const int64_t groups = SP.grid / SP.ks;
+            REQUIRE((int64_t)SP.grid == groups * SP.ks && groups <= kSplitMaxGroups);
+            REQUIRE(groups * W * 16 * TWs >= R);                               // every row in some tile
+            REQUIRE((size_t)SP.ks * groups * W * TWs * NTs * 1024 <= kSplitPartBytes);
         }
     } else {
         const int NT = B > 16 ? 2 : 1;
@@ -241,6 +257,8 @@ int main()
         {"blocks_per_cu=2", &Env::blocks_per_cu, 2}, {"blocks_per_cu=8", &Env::blocks_per_cu, 8},
         {"xdma=1", &Env::xdma, 1},              {"max_cpl=14", &Env::max_cpl, 14},
         {"max_cpl=16", &Env::max_cpl, 16},      {"max_cpl=100", &Env::max_cpl, 100},
+        {"splitk=1", &Env::splitk, 1},          {"splitk=2", &Env::splitk, 2},
+        {"splitk_ks=3", &Env::splitk_ks, 3},    {"splitk_ks=32", &Env::splitk_ks, 32},
     };
     for (int cus : {256, 80, 1}) {
         g_cus = cus;
@@ -254,9 +272,10 @@ int main()
         }
     }
     std::printf("plan sweep: %ld plans checked (fused hybrid %ld, row-slice %ld, stream %ld, staged %ld, ring %ld, "
-                "shared-x ring %ld)\n", g_plans, g_kinds[0], g_kinds[1], g_kinds[3], g_kinds[5], g_kinds[6], g_kinds[7]);
+                "shared-x ring %ld, K-split ring %ld)\n", g_plans, g_kinds[0], g_kinds[1], g_kinds[3], g_kinds[5],
+                g_kinds[6], g_kinds[7], g_kinds[2]);
     std::snprintf(g_case, sizeof g_case, "coverage");
-    for (int k : {0, 1, 3, 5, 6, 7})
+    for (int k : {0, 1, 2, 3, 5, 6, 7})
         REQUIRE(g_kinds[k] > 0);            // every kernel's plan was reached
     return 0;
 }

@@ -280,3 +280,30 @@ def test_hybrid_calls_reject_bad_arguments():
     assert spmv(y=P + 0x400004) == L.NM_ERR_INVALID_ARG              # y over rows_dense
     assert spmv(rs=P + 0x200002) == L.NM_ERR_INVALID_ARG
     assert spmv(R=0, nd=0) == L.NM_OK
+
+
+def test_workspace_calls_check_the_workspace():
+    lib = L.lib()
+    P = ctypes.c_void_p
+    need = lib.nm_workspace_bytes()
+    assert need >= 16 << 20
+    v = _arr(P, [FAKE])
+    m = _arr(P, [FAKE + 0x1000])
+    R = _arr(ctypes.c_int64, [4])
+    y = _arr(P, [FAKE2 + 0x100000])
+    WS = 0x40000000                                   # 256-byte aligned, far from every buffer above
+    ws_call = lambda ws, nb, R=R: lib.nm_spmv_multi_ws(1, v, m, R, 64, 2, 4, 0, FAKE2, 8, y, ws, nb, None)  # noqa: E731
+    assert ws_call(WS, need - 1) == L.NM_ERR_INVALID_ARG            # too small
+    assert ws_call(WS + 16, need) == L.NM_ERR_INVALID_ARG           # misaligned
+    assert ws_call(FAKE2 - 256, need) == L.NM_ERR_INVALID_ARG       # over x
+    y_far = _arr(P, [0x50000000])
+    assert lib.nm_spmv_multi_ws(1, v, m, R, 64, 2, 4, 0, FAKE2, 8, y_far, 0x50000000 - need + 256, need,
+                                None) == L.NM_ERR_INVALID_ARG                       # over y
+    assert lib.nm_spmv_multi_ws(1, v, m, R, 64, 2, 4, 0, FAKE2, 8, y, FAKE - 256, need,
+                                None) == L.NM_ERR_INVALID_ARG                       # over the values
+    R0 = _arr(ctypes.c_int64, [0])
+    assert ws_call(WS, need, R0) == L.NM_OK                          # nothing to do
+    assert ws_call(None, 0, R0) == L.NM_OK                           # no workspace: the plain call
+    Wd = _arr(P, [FAKE])
+    assert lib.nm_gemv_dense_multi_ws(1, Wd, R, 64, 0, FAKE2, 8, y, WS, need - 1, None) == L.NM_ERR_INVALID_ARG
+    assert lib.nm_gemv_dense_multi_ws(1, Wd, R0, 64, 0, FAKE2, 8, y, WS, need, None) == L.NM_OK

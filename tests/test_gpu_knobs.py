@@ -54,6 +54,9 @@ SETTINGS = [
     {"NMSPMV_RING_TILES": "2"},
     {"NMSPMV_RING_SHARE": "8"},
     {"NMSPMV_HYBRID_SPLIT": "1"},
+    {"NMSPMV_SPLITK": "2"},
+    {"NMSPMV_SPLITK": "2", "NMSPMV_SPLITK_KS": "3"},
+    {"NMSPMV_SPLITK": "1"},
 ]
 
 
@@ -90,6 +93,18 @@ def child():
         yref, A = oracle.spmv(ov, om, K, 2, 4, "fp16", G.bits(x))
         ok, w, idx = oracle.check(G.bits(y), yref, A, "fp16")
         assert ok, ("multi", w, idx)
+        worst = max(worst, w)
+    # with a K-split workspace: batched, few rows (and, with the plan forced, any ring shape)
+    print(json.dumps({"case": "workspace"}), flush=True)
+    ws = nm.workspace()
+    for R, K, B in ((160, 16384, 8), (1030, 4096, 16), (70, 2080, 32)):
+        Wk = I.weight(R, K, tdt, I.seed_of("knob_ws", R, K))
+        xk = I.activation_normal(B, K, tdt, I.seed_of("knob_ws_x", K, B), outlier_frac=0.01)
+        yk = nm.spmv_multi([nm.pack(Wk.cuda(), None, 2, 4)], xk.cuda(), 2, 4, ws=ws)[0]
+        ov, om = oracle.pack(G.bits(Wk), None, 2, 4, "fp16")
+        yref, A = oracle.spmv(ov, om, K, 2, 4, "fp16", G.bits(xk))
+        ok, w, idx = oracle.check(G.bits(yk), yref, A, "fp16")
+        assert ok, ("workspace", R, K, B, w, idx)
         worst = max(worst, w)
     # hybrid rows, at one vector (one launch) and at three
     print(json.dumps({"case": "hybrid"}), flush=True)
