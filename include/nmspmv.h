@@ -172,6 +172,25 @@ int nm_gemv_dense_multi_ws(int count, const void* const* W, const int64_t* R, in
                            int B, void* const* y, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * nm_spmv_multi_noalloc -- nm_spmv_multi with the K-split workspace taken
+ * from the library itself, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops).  Arguments and rules as
+ * for nm_spmv_multi; it calls no hipMalloc or other allocating routine.  The
+ * workspace is a file-scope device array of nm_workspace_bytes() bytes in the
+ * library's code object, one per GPU, held until the process ends; its
+ * address is taken once per device, on the first call there, which also
+ * clears its counters (a small kernel on the call's stream).  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and give wrong results -- serialize them.  The array
+ * holds 16 MB of partial sums and 16384 tile-group counters: the K-split plan
+ * is chosen only for calls whose partial sums fit it (the same limit as with
+ * a caller's workspace), so no shape that nm_spmv_multi accepts needs more;
+ * the others run without splitting.
+ */
+int nm_spmv_multi_noalloc(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R,
+                          int64_t K, int N, int M, int dtype, const void* x, int B, void* const* y, void* stream);
+
+/*
  * nm_spmv_swiglu -- the gated-MLP input of a decode layer in one launch:
  *   h[b][r] = SiLU(g) * u,  g = (W_gate x_b)[r],  u = (W_up x_b)[r],
  *   SiLU(t) = t / (1 + e^-t).

@@ -24,6 +24,7 @@ SIGNATURES = {
     "nm_workspace_bytes": (_I64, []),
     "nm_spmv_multi_ws": (_I, [_I, _P, _P, _P, _I64, _I, _I, _I, _P, _I, _P, _P, _I64, _P]),
     "nm_gemv_dense_multi_ws": (_I, [_I, _P, _P, _I64, _I, _P, _I, _P, _P, _I64, _P]),
+    "nm_spmv_multi_noalloc": (_I, [_I, _P, _P, _P, _I64, _I, _I, _I, _P, _I, _P, _P]),
     "nm_spmv_swiglu": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _I, _P, _I, _P, _P]),
     "nm_gemv_dense_swiglu": (_I, [_P, _P, _I64, _I64, _I, _P, _I, _P, _P]),
     "nm_calib_accumulate": (_I, [_P, _P, _I64, _I64, _I, _P, _P]),

@@ -31,6 +31,10 @@ int spmv_multi(int count, const void* const* values, const uint8_t* const* masks
 int gemv_dense_multi(int count, const void* const* W, const int64_t* R, int64_t total, int64_t K, int dtype,
                      const void* x, int B, void* const* y, void* workspace, void* stream);
 
+// The library's own workspace for allocation-free calls (one per GPU, shared
+// by every such call on it): its device address for the current device.
+int static_workspace(void** out, void* stream);
+
 // R > 0, K > 0.
 int spmv_swiglu(const void* values_gate, const uint8_t* masks_gate, const void* values_up, const uint8_t* masks_up,
                 int64_t R, int64_t K, int N, int M, int dtype, const void* x, int B, void* h, void* stream);

@@ -36,10 +36,10 @@ int zero_outputs(int count, void* const* y, const int64_t* R, int B, void* strea
 namespace {
 
 // nm_spmv_multi with an optional K-split workspace (ws, ws_bytes; checked
-// here when given).
+// here when given) or, with use_static, the library's own.
 int spmv_multi_with(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
                     int N, int M, int dtype, const void* x, int B, void* const* y, void* ws, int64_t ws_bytes,
-                    void* stream)
+                    bool use_static, void* stream)
 {
     int st = check_dtype(dtype);
     if (st != NM_OK)
@@ -91,6 +91,8 @@ int spmv_multi_with(int count, const void* const* values, const uint8_t* const* 
         return NM_OK;
     if (K == 0)
         return zero_outputs(count, y, R, B, stream);
+    if (use_static && (st = nmk::static_workspace(&ws, stream)) != NM_OK)
+        return st;
     return nmk::spmv_multi(count, values, masks, R, total, K, N, M, dtype, x, B, y, ws, stream);
 }
 
@@ -168,14 +170,21 @@ const char* nm_status_string(int status)
 int nm_spmv_multi(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
                   int N, int M, int dtype, const void* x, int B, void* const* y, void* stream)
 {
-    return spmv_multi_with(count, values, masks, R, K, N, M, dtype, x, B, y, nullptr, 0, stream);
+    return spmv_multi_with(count, values, masks, R, K, N, M, dtype, x, B, y, nullptr, 0, false, stream);
 }
 
 int nm_spmv_multi_ws(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R, int64_t K,
                      int N, int M, int dtype, const void* x, int B, void* const* y, void* workspace,
                      int64_t workspace_bytes, void* stream)
 {
-    return spmv_multi_with(count, values, masks, R, K, N, M, dtype, x, B, y, workspace, workspace_bytes, stream);
+    return spmv_multi_with(count, values, masks, R, K, N, M, dtype, x, B, y, workspace, workspace_bytes, false,
+                           stream);
+}
+
+int nm_spmv_multi_noalloc(int count, const void* const* values, const uint8_t* const* masks, const int64_t* R,
+                          int64_t K, int N, int M, int dtype, const void* x, int B, void* const* y, void* stream)
+{
+    return spmv_multi_with(count, values, masks, R, K, N, M, dtype, x, B, y, nullptr, 0, true, stream);
 }
 
 int64_t nm_workspace_bytes(void) { return (int64_t)kSplitWorkspaceBytes; }

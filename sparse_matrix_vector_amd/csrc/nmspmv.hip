@@ -2321,6 +2321,53 @@ int nmh::cu_count()
     return counts[dev];
 }
 
+// ---- the allocation-free workspace ---------------------------------------------------
+
+namespace {
+
+// The K-split workspace of nm_spmv_multi_noalloc: one array per GPU, in the
+// library's code object (zero when loaded), shared by every such call on that
+// GPU.  Host code never names it as an address: its device address is taken
+// once per device with hipGetSymbolAddress.
+__device__ __align__(256) uint8_t scratch[kSplitWorkspaceBytes];
+
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch_ptr[64] = {};
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
+}  // namespace
+
+int nmk::static_workspace(void** out, void* stream)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return NM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return NM_ERR_HIP;
+        // The counters start at zero (and every completed launch leaves them
+        // there); clear them once more on this device's first call, by a kernel
+        // on the caller's stream (captured with it, if the call is captured).
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(zero_words_kernel, dim3((kSplitMaxGroups + 255) / 256), dim3(256), 0,
+                           static_cast<hipStream_t>(stream),
+                           reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p) + kSplitPartBytes), kSplitMaxGroups);
+        if (hipGetLastError() != hipSuccess)
+            return NM_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return NM_OK;
+}
+
 // ---- the kernel side of the entry points (arguments checked by nmapi.cpp) --------
 
 int nmk::zero(void* y, int64_t n, void* stream) { return launch_zero(y, n, static_cast<hipStream_t>(stream)); }

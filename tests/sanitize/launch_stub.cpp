@@ -77,6 +77,13 @@ int launched()
 
 extern "C" long nmtest_launches(void) { return g_launches; }
 
+// The library's allocation-free workspace: here a fixed, 256-byte aligned stand-in address (never dereferenced).
+int nmk::static_workspace(void** out, void*)
+{
+    *out = reinterpret_cast<void*>(uintptr_t(0x7f0000000000));
+    return NM_OK;
+}
+
 int nmk::zero(void* y, int64_t n, void*)
 {
     promise(n > 0 && al(y, 2), "zero", "y");
