@@ -1,6 +1,6 @@
 """Run chosen launches of a bench.py workload back to back, for profiler runs.
 
-    python -m measure.launches [--workload llama31_8b] [--layers 8] [--kinds gate,down] [--reps 20] [--ws]
+    python -m measure.launches [--workload llama31_8b] [--layers 8] [--kinds gate,down] [--reps 20] [--ws] [--dense]
 
 Kinds are the step's launch kinds (``q+k+v``, ``o``, ``gate+up``, ``down`` for
 the Llama-3.1-8B step) or one projection of a fused kind on its own (``gate``,
@@ -29,6 +29,7 @@ def main():
     p.add_argument("--kinds", default="gate,down")
     p.add_argument("--reps", type=int, default=20)
     p.add_argument("--ws", action="store_true", help="fused kinds through nm_spmv_multi_ws with a K-split workspace")
+    p.add_argument("--dense", action="store_true", help="the dense baseline of the step's kinds (nm_gemv_dense_multi)")
     a = p.parse_args()
 
     import torch
@@ -47,7 +48,9 @@ def main():
     out = {}
     for kind in kinds:
         group = [L for L in launches if L.kind == kind]
-        if group and a.ws:
+        if group and a.dense:
+            fn, args = lib.nm_gemv_dense_multi, (lambda st, g=group: [L.dense_args(st) for L in g])
+        elif group and a.ws:
             ws = nm.workspace()
             wsa = (P(ws.data_ptr()), I64(ws.numel()))
             fn, args = lib.nm_spmv_multi_ws, (lambda st, g=group: [L.sparse_args(st)[:-1] + wsa + (P(st),) for L in g])

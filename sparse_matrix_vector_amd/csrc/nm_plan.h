@@ -225,9 +225,12 @@ inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, int B, Pla
 }
 
 // Chooses the kernel for a matrix shape: the row-slice kernel when x fits its
-// LDS budget and rows are at most 1152 chunks (sparse, K <= 18432) or 2048
-// chunks (dense, K <= 16384); otherwise the stream kernel -- whose blocks
+// LDS budget and rows are at most 1600 chunks (sparse, K <= 25600) or 3200
+// chunks (dense, K <= 25600); otherwise the stream kernel -- whose blocks
 // stage x once for many rows -- with x in K-tiles when it exceeds the budget.
+// (Single-vector timing, us, stream -> row-slice: Qwen3-32B down, 5120 x
+// 25600, 2:4 32.8 -> 28.8 and dense 50.9 -> 44.7; Llama-3.3-70B down, 8192 x
+// 28672, 2:4 47.6 -> 50.4 and dense 78.0 -> 84.7.)
 template <int F>
 Plan plan_for(int64_t R, int64_t K, int B, bool glu)
 {
@@ -240,7 +243,7 @@ Plan plan_for(int64_t R, int64_t K, int B, bool glu)
     Plan P;
     int kind = g_env.kernel;
     if (kind != 1 && kind != 3)
-        kind = (fits && C <= (F == kDense ? 32 : 18) * kWave) ? 1 : 3;
+        kind = (fits && C <= (F == kDense ? 50 : 25) * kWave) ? 1 : 3;
     if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, glu, B, &P)) {
         P.lds = tab + xbytes + (size_t)P.rpb * P.S * B * 4;
         if (g_env.blocks_per_cu >= 2 && g_env.blocks_per_cu <= 8)
@@ -439,6 +442,36 @@ Plan plan_mfma_ring(int64_t R, int64_t K, int B)
         W = std::min(g_env.ring_share, 8);
     while (W > 1 && ((tiles + W - 1) / W < cus || tab + W * wring + 2 * xslot > (size_t)kLdsMax))
         W /= 2;
+    // Blocks past what the CUs hold at once run as a second round, and each
+    // block streams its tiles' whole K, so the launch lasts about as long as
+    // the busiest CU's tiles: ceil(blocks / CUs) blocks of W tiles each.
+    // When the share above leaves such a round, take the share with the
+    // fewest tiles on the busiest CU (the widest on a tie: less x staged),
+    // keeping every CU busy and 12 waves a CU in flight (the kernel's
+    // registers allow about 20 with one tile a wave).  Qwen3-32B gate+up at 8
+    // vectors (51200 x 5120, 3200 tiles), tiles on the busiest CU and time by
+    // share: 3: 15, 73.8 us; 4: 16, 75.1; 5: 15, 72.0; 6: 18, 77.0; 7: 14,
+    // 65.9.  With two tiles a wave (above 8 vectors) the default share stays:
+    // at 16 vectors the same matrix took 89.2 us at two a block (8 tile pairs
+    // on the busiest CU) and 90.3 at seven (7, but one block of 7 waves a CU).
+    if (g_env.ring_share <= 0 && S == 1 && W > 1 && TW == 1) {
+        auto per_cu = [&](int w) -> int64_t {
+            const size_t l = tab + w * wring + 2 * xslot;
+            return l > (size_t)kLdsMax ? 0 : std::min<int64_t>((int64_t)(kLdsMax / l), 20 / w);
+        };
+        auto load = [&](int w) { return ((tiles + w - 1) / w + cus - 1) / cus * w; };
+        if ((tiles + W - 1) / W > per_cu(W) * cus) {
+            int best = W;
+            for (int w = 2; w <= 8; ++w) {
+                const int64_t nb = per_cu(w), blocks = (tiles + w - 1) / w;
+                if (nb == 0 || blocks < cus || std::min<int64_t>(nb, (blocks + cus - 1) / cus) * w < 12)
+                    continue;
+                if (load(w) < load(best) || (load(w) == load(best) && w > best && best != W))
+                    best = w;
+            }
+            W = best;
+        }
+    }
     if (S == 1 && W > 1) {
         P.kind = 7;
         P.rpb = W;

@@ -151,6 +151,7 @@ def test_hybrid_pack_and_spmv(nm, dt, n, m, K, B, frac):
     ("fp16", 2, 4, 18432, 2100, 0.25),
     ("fp16", 2, 4, 4096, 1024, 0.05),           # few sparse rows: two per block in the one launch
     ("bf16", 4, 8, 1040, 600, 0.2),
+    ("bf16", 2, 4, 25600, 700, 0.1),            # the longest rows on the row-slice kernel: 4 slices, 8 for dense
 ])
 @pytest.mark.parametrize("B", [1, 2, 3])
 def test_hybrid_one_launch_shapes(nm, dt, n, m, K, R, frac, B):

@@ -216,3 +216,39 @@ def test_ring_shared_x_swiglu_and_parts(nm, B):
         yref, A = oracle.spmv(ov, om, K, n, m, dt, bits(x))
         ok, worst, idx = oracle.check(bits(y[:, rr]), yref, A, dt)
         assert ok, ("part", i, worst, idx)
+
+
+def _round_R(extra):
+    """More 16-row tiles than four-wave blocks fit on the CUs at once (12 per
+    CU plus 200), so the share is widened to fit every block in one round;
+    `extra` rows end in a partial tile, and the last block is partial too."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return 16 * (12 * cus + 200) + extra
+
+
+@pytest.mark.parametrize("dt,n,m,B", [("fp16", 2, 4, 8), ("bf16", 4, 8, 5), ("bf16", 2, 4, 6), ("fp16", 4, 8, 7)])
+def test_ring_shared_x_one_round(nm, dt, n, m, B):
+    """Blocks of more than four waves sharing x (the share chosen so that no
+    second round of blocks is left); sampled rows, the last 40 included."""
+    R, K = _round_R(9), 1056
+    tdt = TD[dt]
+    W = I.weight(R, K, tdt, I.seed_of("rg1W", n, m, dt), device="cuda")
+    x = I.activation_normal(B, K, tdt, I.seed_of("rg1x", dt, B), device="cuda", outlier_frac=0.01)
+    sparse_case(nm, W, x, n, m, dt, rows=_sample(R, I.seed_of("rg1r", B), k=64))
+
+
+def test_ring_shared_x_one_round_swiglu(nm):
+    """The gated epilogue on the widened share (gate and up rows interleaved)."""
+    dt, tdt, n, m, B = "bf16", torch.bfloat16, 2, 4, 8
+    Rh, K = _round_R(5) // 2, 1056
+    Wg = I.weight(Rh, K, tdt, I.seed_of("rg1gW"), device="cuda")
+    Wu = I.weight(Rh, K, tdt, I.seed_of("rg1uW"), device="cuda")
+    x = I.activation_normal(B, K, tdt, I.seed_of("rg1gx"), device="cuda", outlier_frac=0.01)
+    h = nm.spmv_swiglu(nm.pack(Wg, None, n, m), nm.pack(Wu, None, n, m), x, n, m)
+    rows = _sample(Rh, I.seed_of("rg1gr"), k=48)
+    gv, gm = oracle.pack(bits(Wg[rows]), None, n, m, dt)
+    uv, um = oracle.pack(bits(Wu[rows]), None, n, m, dt)
+    gref, Ag = oracle.spmv(gv, gm, K, n, m, dt, bits(x))
+    uref, Au = oracle.spmv(uv, um, K, n, m, dt, bits(x))
+    ok, worst, idx = oracle.check_swiglu(bits(h[:, rows]), gref, uref, Ag, Au, dt)
+    assert ok, ("swiglu", worst, idx)
