@@ -508,12 +508,17 @@ constexpr size_t kSplitWorkspaceBytes = kSplitPartBytes + size_t(kSplitMaxGroups
 // for the CUs, so each wave stages its own x: about as many x bytes as
 // weight bytes at 8 vectors), blocks of W waves (one tile group, TW tiles a
 // wave) share each staged x over one of KS contiguous stage ranges instead,
-// and the last block of a group adds the KS partial sums.  KS: the fewest
-// splits (a power of two) that give the launch two blocks a CU, each split at
-// least four stages; W = 2 tile units a block (sweeps at the Qwen3-32B down
-// shape, 5120 x 25600, at 4 / 8 / 16 vectors, us: W = 2 and 4 splits 39.4 /
-// 40.0 / -, 8 splits - / - / 50.0; W = 4 with 8 splits 43.0 at 8 vectors;
-// without the workspace 41.2 / 49.5 / 58.0).  false: keep the ring plan.
+// and the last block of a group adds the KS partial sums.  A CU's share of
+// the read bandwidth sets the pace (a block on a CU that holds three streams
+// a third slower than one on a CU that holds two), so W and KS are chosen for
+// the least bytes on the busiest CU: ceil(blocks / CUs) blocks, each staging
+// its W units and one x per stage over ceil(stages / KS) stages, plus two
+// stages' worth for the block's start (every block issues its first loads at
+// once; they land after ~4 us), the widest W on a tie; at least 4 stages a
+// split, 4 waves a CU, and a block's LDS within a CU's.  Qwen3-32B down, 5120 x 25600, 8
+// vectors (W, KS: that figure, us on one GPU): 2, 4: 1078 KB, 42.3; 2, 8:
+// 998 KB, 42.3; 3, 8: 1075 KB, 44.5; 5, 8: 814 KB, 40.5; 5, 4: 733 KB, 40.3
+// (one block a CU).  false: keep the ring plan.
 template <int F>
 bool plan_mfma_split(int64_t R, int64_t K, int B, Plan* out)
 {
@@ -530,21 +535,37 @@ bool plan_mfma_split(int64_t R, int64_t K, int B, Plan* out)
     const int64_t C = K / COLS, NS = (C + kStageChunks - 1) / kStageChunks;
     const int64_t tiles = (R + 16 * TW - 1) / (16 * TW);
     const size_t tab = (size_t)mfma_table_units<F>() * kUnitBytes;
-    const size_t wring = 2 * (size_t)TW * (kRingValues + (F == kDense ? 0 : kRingMasks));
+    const size_t unit = (size_t)TW * (kRingValues + (F == kDense ? 0 : kRingMasks));   // a unit's stage
     const size_t xslot = (size_t)ring_x_rows<F>(B) * ring_x_units<F>() * 16;
-    int W = 2;
-    if (g_env.ring_share > 0)
-        W = std::min(g_env.ring_share, 8);
-    while (W > 1 && tab + W * wring + 2 * xslot > (size_t)kLdsMax / 2)
-        W /= 2;
-    const int64_t groups = (tiles + W - 1) / W;
-    int KS = 1;
-    while (KS < 32 && groups * KS < 2LL * cus && NS / (2 * KS) >= 4)
-        KS *= 2;
-    if (g_env.splitk_ks >= 2 && g_env.splitk_ks <= 32)
-        KS = (int)std::min<int64_t>(g_env.splitk_ks, NS);
-    if (KS < 2 || groups > kSplitMaxGroups)
+    const int ks_env = g_env.splitk_ks >= 2 && g_env.splitk_ks <= 32 ? (int)std::min<int64_t>(g_env.splitk_ks, NS) : 0;
+    int W = 0, KS = 0;
+    double best = 0.0;
+    for (int w = 1; w <= 8; ++w) {
+        if (g_env.ring_share > 0 && w != std::min(g_env.ring_share, 8))
+            continue;
+        const size_t lds = tab + w * 2 * unit + 2 * xslot;
+        if (lds > (size_t)kLdsMax)
+            break;
+        const int64_t groups = (tiles + w - 1) / w;
+        for (int ks = 2; ks <= 32; ++ks) {
+            if (ks_env ? ks != ks_env : NS < 4LL * ks)
+                continue;
+            if (groups > kSplitMaxGroups || (size_t)ks * (size_t)groups * w * TW * NT * 1024 > kSplitPartBytes)
+                continue;
+            const int64_t per_cu = (groups * ks + cus - 1) / cus;
+            if (g_env.ring_share <= 0 && !ks_env && std::min<int64_t>(per_cu, (int64_t)(kLdsMax / lds)) * w < 4)
+                continue;                        // too few waves a CU to cover the loads' latency
+            const double bytes = (double)per_cu * (double)((NS + ks - 1) / ks + 2) * (double)(w * unit + xslot);
+            if (!W || bytes < best || (bytes == best && w > W)) {
+                best = bytes;
+                W = w;
+                KS = ks;
+            }
+        }
+    }
+    if (!W)
         return false;
+    const int64_t groups = (tiles + W - 1) / W;
     const int64_t stages = (NS + KS - 1) / KS;
     if ((size_t)KS * (size_t)groups * W * TW * NT * 1024 > kSplitPartBytes)
         return false;
@@ -557,7 +578,7 @@ bool plan_mfma_split(int64_t R, int64_t K, int B, Plan* out)
     P.grid = (unsigned)(groups * KS);
     P.ks = KS;
     P.kstages = (int)stages;
-    P.lds = tab + W * wring + 2 * xslot;
+    P.lds = tab + W * 2 * unit + 2 * xslot;
     *out = P;
     return true;
 }

@@ -1443,11 +1443,26 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
             for (int nt = 0; nt < NT; ++nt) {
                 const int b = 16 * nt + i;
                 float sum[4] = {0.f, 0.f, 0.f, 0.f};
-                for (int j = 0; j < sk.ks; ++j) {
-                    const float* src = sk.part + ((((size_t)j * units + unit) * TW + tw) * NT + nt) * 256 + lane * 4;
+                // The partials of up to JB splits are loaded at once (one
+                // round trip instead of one per split), then added in split
+                // order.
+                constexpr int JB = 8;
+                for (int j0 = 0; j0 < sk.ks; j0 += JB) {
+                    float pv[JB][4];
 #pragma unroll
-                    for (int vv = 0; vv < 4; ++vv)
-                        sum[vv] += __hip_atomic_load(src + vv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int jj = 0; jj < JB; ++jj) {
+                        const int j = min(j0 + jj, sk.ks - 1);        // past the last split: loaded, not added
+                        const float* src = sk.part + ((((size_t)j * units + unit) * TW + tw) * NT + nt) * 256 + lane * 4;
+#pragma unroll
+                        for (int vv = 0; vv < 4; ++vv)
+                            pv[jj][vv] = __hip_atomic_load(src + vv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < JB; ++jj)
+                        if (j0 + jj < sk.ks)
+#pragma unroll
+                            for (int vv = 0; vv < 4; ++vv)
+                                sum[vv] += pv[jj][vv];
                 }
                 if (b >= B)
                     continue;

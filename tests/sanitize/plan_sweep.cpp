@@ -90,6 +90,18 @@ void check_valu(int64_t R, int64_t K, int B, bool glu)
     }
 }
 
+// LDS the shared-x ring kernel addresses: the selector table, then per wave
+// two slots of TW tiles (values, and masks for sparse rows), then the
+// block's two x slots of the batch rows (padded to whole load instructions)
+// times one stage of x.
+template <int F>
+size_t shared_ring_lds(int waves, int TW, int B)
+{
+    const size_t tile = kRingValues + (F == kDense ? 0 : kRingMasks);
+    const size_t x = (size_t)ring_x_rows<F>(B) * ring_x_units<F>() * 16;
+    return (size_t)mfma_table_units<F>() * kUnitBytes + (size_t)waves * 2 * TW * tile + 2 * x;
+}
+
 template <int F>
 void check_mfma(int64_t R, int64_t K, int B, bool glu)
 {
@@ -112,6 +124,7 @@ void check_mfma(int64_t R, int64_t K, int B, bool glu)
         } else {
             REQUIRE(P.kind == 7 && P.S == 1 && P.threads == P.rpb * kWave);
             REQUIRE((int64_t)P.grid * P.rpb >= tiles && ((int64_t)P.grid - 1) * P.rpb < tiles);
+            REQUIRE(P.lds >= shared_ring_lds<F>(P.rpb, TW, B));
         }
         Plan SP;
         if (plan_mfma_split<F>(R, K, B, &SP)) {
@@ -121,7 +134,7 @@ void check_mfma(int64_t R, int64_t K, int B, bool glu)
             const int W = SP.rpb, TWs = SP.cpl, NTs = B > 16 ? 2 : 1;
             REQUIRE(SP.kind == 8 && SP.S == 1 && (TWs == 1 || TWs == 2) && (B <= 16 || TWs == 2));
             REQUIRE(W >= 1 && SP.threads == W * kWave && SP.threads <= 512);
-            REQUIRE(SP.lds <= (size_t)kLdsMax);
+            REQUIRE(SP.lds <= (size_t)kLdsMax && SP.lds >= shared_ring_lds<F>(W, TWs, B));
             REQUIRE(SP.ks >= 2 && SP.ks <= 32 && SP.kstages >= 1);
             REQUIRE((int64_t)SP.ks * SP.kstages >= NS);                      // every stage in some split
             const int64_t groups = SP.grid / SP.ks;
