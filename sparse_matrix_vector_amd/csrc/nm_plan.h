@@ -583,6 +583,18 @@ bool plan_mfma_split(int64_t R, int64_t K, int B, Plan* out)
     return true;
 }
 
+// The K-split plan (calls with a workspace) takes the ring kernel's rows --
+// dense rows, and sparse rows whose mask row is a whole number of dwords --
+// at any batch, also where the plain call would take the staged kernel
+// (sparse, above 16 vectors, on few rows): its blocks share x across tiles,
+// which the ring's K-slices cannot.
+template <int F>
+bool mfma_use_split(int64_t R, int64_t K, int B, Plan* out)
+{
+    std::call_once(g_env_once, read_env);
+    return (F == kDense || K % 32 == 0) && g_env.kernel != 5 && plan_mfma_split<F>(R, K, B, out);
+}
+
 }  // namespace nmh
 
 #endif  // NM_PLAN_H

@@ -1965,18 +1965,10 @@ int launch_mfma_ring_tw(const Plan& P, const Parts& parts, const void* x, int R,
                        : launch_mfma_ring_k<F, DT, TW, NT, false>(P, parts, x, R, K, B, s);
 }
 
-// Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles).  With
-// a workspace, the K-split plan where it applies.
+// Up to 16 vectors: one batch tile; 17 to 32: two (and two row tiles).
 template <int F, int DT>
-int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s, void* ws)
+int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s)
 {
-    Plan SP;
-    if (ws && plan_mfma_split<F>(R, K, B, &SP)) {
-        if (B > 16)
-            return launch_mfma_split<F, DT, 2, 2>(SP, parts, x, R, K, B, s, ws);
-        return SP.cpl == 2 ? launch_mfma_split<F, DT, 2, 1>(SP, parts, x, R, K, B, s, ws)
-                           : launch_mfma_split<F, DT, 1, 1>(SP, parts, x, R, K, B, s, ws);
-    }
     const Plan P = plan_mfma_ring<F>(R, K, B);
     if (B > 16)
         return launch_mfma_ring_tw<F, DT, 2, 2>(P, parts, x, R, K, B, s);
@@ -1984,11 +1976,20 @@ int launch_mfma_ring(const Parts& parts, const void* x, int R, int K, int B, hip
                       : launch_mfma_ring_tw<F, DT, 1, 1>(P, parts, x, R, K, B, s);
 }
 
+// With a workspace, the K-split plan where it applies; else the ring or the
+// staged kernel.
 template <int F, int DT>
 int launch_mfma(const Parts& parts, const void* x, int R, int K, int B, hipStream_t s, void* ws)
 {
+    Plan SP;
+    if (ws && mfma_use_split<F>(R, K, B, &SP)) {
+        if (B > 16)
+            return launch_mfma_split<F, DT, 2, 2>(SP, parts, x, R, K, B, s, ws);
+        return SP.cpl == 2 ? launch_mfma_split<F, DT, 2, 1>(SP, parts, x, R, K, B, s, ws)
+                           : launch_mfma_split<F, DT, 1, 1>(SP, parts, x, R, K, B, s, ws);
+    }
     if (mfma_use_ring<F>(R, K, B))
-        return launch_mfma_ring<F, DT>(parts, x, R, K, B, s, ws);
+        return launch_mfma_ring<F, DT>(parts, x, R, K, B, s);
     return B > 16 ? launch_mfma_nt<F, DT, 2>(parts, x, R, K, B, s) : launch_mfma_nt<F, DT, 1>(parts, x, R, K, B, s);
 }
 

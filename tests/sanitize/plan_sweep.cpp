@@ -126,22 +126,6 @@ void check_mfma(int64_t R, int64_t K, int B, bool glu)
             REQUIRE((int64_t)P.grid * P.rpb >= tiles && ((int64_t)P.grid - 1) * P.rpb < tiles);
             REQUIRE(P.lds >= shared_ring_lds<F>(P.rpb, TW, B));
         }
-        Plan SP;
-        if (plan_mfma_split<F>(R, K, B, &SP)) {
-            ++g_plans;
-            ++g_kinds[2];
-            const int64_t NS = (K / chunk_cols<F>() + kStageChunks - 1) / kStageChunks;
-            const int W = SP.rpb, TWs = SP.cpl, NTs = B > 16 ? 2 : 1;
-            REQUIRE(SP.kind == 8 && SP.S == 1 && (TWs == 1 || TWs == 2) && (B <= 16 || TWs == 2));
-            REQUIRE(W >= 1 && SP.threads == W * kWave && SP.threads <= 512);
-            REQUIRE(SP.lds <= (size_t)kLdsMax && SP.lds >= shared_ring_lds<F>(W, TWs, B));
-            REQUIRE(SP.ks >= 2 && SP.ks <= 32 && SP.kstages >= 1);
-            REQUIRE((int64_t)SP.ks * SP.kstages >= NS);                      // every stage in some split
-            const int64_t groups = SP.grid / SP.ks;
-            REQUIRE((int64_t)SP.grid == groups * SP.ks && groups <= kSplitMaxGroups);
-            REQUIRE(groups * W * 16 * TWs >= R);                               // every row in some tile
-            REQUIRE((size_t)SP.ks * groups * W * TWs * NTs * 1024 <= kSplitPartBytes);
-        }
     } else {
         const int NT = B > 16 ? 2 : 1;
         const Plan P = plan_mfma_stage<F>(R, K, NT, B);
@@ -151,6 +135,23 @@ void check_mfma(int64_t R, int64_t K, int B, bool glu)
         REQUIRE(P.threads == P.S * P.rpb * kWave && P.threads <= 512);
         REQUIRE(P.lds <= (size_t)kLdsMax);
         REQUIRE((int64_t)P.grid * P.rpb >= tiles16 && ((int64_t)P.grid - 1) * P.rpb < tiles16);
+    }
+    Plan SP;
+    if (mfma_use_split<F>(R, K, B, &SP)) {
+        REQUIRE(F == kDense || K % 32 == 0);
+        ++g_plans;
+        ++g_kinds[2];
+        const int64_t NS = (K / chunk_cols<F>() + kStageChunks - 1) / kStageChunks;
+        const int W = SP.rpb, TWs = SP.cpl, NTs = B > 16 ? 2 : 1;
+        REQUIRE(SP.kind == 8 && SP.S == 1 && (TWs == 1 || TWs == 2) && (B <= 16 || TWs == 2));
+        REQUIRE(W >= 1 && SP.threads == W * kWave && SP.threads <= 512);
+        REQUIRE(SP.lds <= (size_t)kLdsMax && SP.lds >= shared_ring_lds<F>(W, TWs, B));
+        REQUIRE(SP.ks >= 2 && SP.ks <= 32 && SP.kstages >= 1);
+        REQUIRE((int64_t)SP.ks * SP.kstages >= NS);                      // every stage in some split
+        const int64_t groups = SP.grid / SP.ks;
+        REQUIRE((int64_t)SP.grid == groups * SP.ks && groups <= kSplitMaxGroups);
+        REQUIRE(groups * W * 16 * TWs >= R);                               // every row in some tile
+        REQUIRE((size_t)SP.ks * groups * W * TWs * NTs * 1024 <= kSplitPartBytes);
     }
     (void)glu;
 }
