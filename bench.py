@@ -526,10 +526,14 @@ def config_steps(torch, nm, I, specs, steps=10):
 def crossover(torch, nm, I, batches=(1, 2, 4, 8, 16, 32)):
     """Sparse 2:4 (nm_spmv), dense (nm_gemv_dense) and torch.matmul (hipBLASLt)
     on the Qwen3-32B MLP shapes over a range of batch sizes, each timed over
-    enough weight instances to exceed the 256 MB MALL."""
+    enough weight instances to exceed the 256 MB MALL; beside them the same
+    sparse and dense products through the workspace calls (nm_spmv_multi_ws,
+    nm_gemv_dense_multi_ws: the K-split plan where it applies)."""
     lib = nm.lib()
     cur = torch.cuda.current_stream().cuda_stream
     dt = torch.bfloat16
+    ws = nm.workspace()
+    wsa = (P(ws.data_ptr()), I64(ws.numel()))
     out = {}
     for name in ("gate", "down"):
         R, K = I.QWEN3_32B_MLP[name]
@@ -549,6 +553,14 @@ def crossover(torch, nm, I, batches=(1, 2, 4, 8, 16, 32)):
             us = time_ms(torch, lambda: run(lib.nm_spmv, sargs), 5) / n_inst * 1e3
             run(lib.nm_gemv_dense, dargs)
             usd = time_ms(torch, lambda: run(lib.nm_gemv_dense, dargs), 5) / n_inst * 1e3
+            smargs = [(I32(1), (P * 1)(v.data_ptr()), (P * 1)(mk.data_ptr()), (I64 * 1)(R), I64(K), I32(2), I32(4),
+                       I32(1), P(x.data_ptr()), I32(B), (P * 1)(y.data_ptr())) + wsa + (P(cur),) for v, mk in packed]
+            dmargs = [(I32(1), (P * 1)(W.data_ptr()), (I64 * 1)(R), I64(K), I32(1), P(x.data_ptr()), I32(B),
+                       (P * 1)(y.data_ptr())) + wsa + (P(cur),) for W in Ws]
+            run(lib.nm_spmv_multi_ws, smargs)
+            usw = time_ms(torch, lambda: run(lib.nm_spmv_multi_ws, smargs), 5) / n_inst * 1e3
+            run(lib.nm_gemv_dense_multi_ws, dmargs)
+            usdw = time_ms(torch, lambda: run(lib.nm_gemv_dense_multi_ws, dmargs), 5) / n_inst * 1e3
 
             def torch_mm():
                 for W in Ws:
@@ -559,7 +571,9 @@ def crossover(torch, nm, I, batches=(1, 2, 4, 8, 16, 32)):
             db = R * K * 2 + B * (R + K) * 2
             rows.append({"B": B, "sparse_us": round(us, 2), "sparse_gbs": round(sb / us / 1e3, 1),
                          "dense_us": round(usd, 2), "dense_gbs": round(db / usd / 1e3, 1), "torch_us": round(ust, 2),
-                         "speedup_vs_dense": round(usd / us, 3), "speedup_vs_torch": round(ust / us, 3)})
+                         "speedup_vs_dense": round(usd / us, 3), "speedup_vs_torch": round(ust / us, 3),
+                         "ws_sparse_us": round(usw, 2), "ws_dense_us": round(usdw, 2),
+                         "ws_speedup_vs_dense": round(min(usd, usdw) / min(us, usw), 3)})
         out[name] = {"shape": [R, K], "rows": rows}
         del Ws, packed
         torch.cuda.empty_cache()

@@ -526,14 +526,19 @@ bool plan_mfma_split(int64_t R, int64_t K, int B, Plan* out)
     if (g_env.splitk == 1)
         return false;
     const Plan base = plan_mfma_ring<F>(R, K, B);
-    if (g_env.splitk != 2 && !(base.kind == 6 && base.S >= 2))
-        return false;
     constexpr int COLS = chunk_cols<F>();
     const int cus = cu_count();
     const int TW = base.cpl;
     const int NT = B > 16 ? 2 : 1;
     const int64_t C = K / COLS, NS = (C + kStageChunks - 1) / kStageChunks;
     const int64_t tiles = (R + 16 * TW - 1) / (16 * TW);
+    // Only for short matrices: fewer than four tile units a CU, where the
+    // ring plan cuts tiles into K-slices.  With more tiles the ring plan's
+    // blocks fill the CUs (the dense 25600 x 5120 gate at 4 vectors, 1600
+    // tiles: 49.6 us on the ring plan, 65.6 on a K-split of 1280 ten-stage
+    // blocks).
+    if (g_env.splitk != 2 && !(base.kind == 6 && base.S >= 2 && tiles < 4LL * cus))
+        return false;
     const size_t tab = (size_t)mfma_table_units<F>() * kUnitBytes;
     const size_t unit = (size_t)TW * (kRingValues + (F == kDense ? 0 : kRingMasks));   // a unit's stage
     const size_t xslot = (size_t)ring_x_rows<F>(B) * ring_x_units<F>() * 16;

@@ -37,11 +37,15 @@ def bits(t):
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def check_all_rows(W, values, masks, x, y, n, m, dt, yd=None):
+def check_all_rows(W, values, masks, x, y, n, m, dt, yd=None, y_more=(), yd_more=()):
     """Every row of the packed matrix, the sparse product and (given yd) the
-    dense product against the oracle, in row ranges over NTHREADS threads."""
+    dense product against the oracle, in row ranges over NTHREADS threads;
+    y_more / yd_more: further sparse / dense products of the same inputs
+    (other calls), checked against the same oracle results."""
     Wb, vb, mb, xb, yb = bits(W), bits(values), masks.cpu().numpy(), bits(x), bits(y)
     ydb = None if yd is None else bits(yd)
+    ymb = [bits(t) for t in y_more]
+    ydmb = [bits(t) for t in yd_more]
     R, K = Wb.shape
     step = max(1, -(-R // (4 * NTHREADS)))
 
@@ -53,14 +57,16 @@ def check_all_rows(W, values, masks, x, y, n, m, dt, yd=None):
         if not np.array_equal(mb[r0:r1], om):
             return f"masks differ in rows {r0}..{r1 - 1}"
         yref, A = oracle.spmv(ov, om, K, n, m, dt, xb)
-        ok, worst, idx = oracle.check(yb[:, r0:r1], yref, A, dt)
-        if not ok:
-            return f"spmv outside tolerance in rows {r0}..{r1 - 1}: worst {worst:.3f} at {idx}"
-        if ydb is not None:
-            ydref, Ad = oracle.gemv(Wb[r0:r1], dt, xb)
-            ok, worst, idx = oracle.check(ydb[:, r0:r1], ydref, Ad, dt)
+        for j, yy in enumerate([yb] + ymb):
+            ok, worst, idx = oracle.check(yy[:, r0:r1], yref, A, dt)
             if not ok:
-                return f"dense gemv outside tolerance in rows {r0}..{r1 - 1}: worst {worst:.3f} at {idx}"
+                return f"spmv (output {j}) outside tolerance in rows {r0}..{r1 - 1}: worst {worst:.3f} at {idx}"
+        if ydb is not None or ydmb:
+            ydref, Ad = oracle.gemv(Wb[r0:r1], dt, xb)
+            for j, yy in enumerate(([ydb] if ydb is not None else []) + ydmb):
+                ok, worst, idx = oracle.check(yy[:, r0:r1], ydref, Ad, dt)
+                if not ok:
+                    return f"dense gemv (output {j}) outside tolerance in rows {r0}..{r1 - 1}: worst {worst:.3f} at {idx}"
         return None
 
     with ThreadPoolExecutor(NTHREADS) as ex:
@@ -129,18 +135,22 @@ def test_llama33_70b_layer(nm, name):
 
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32])
 def test_qwen3_32b_small_batch(nm, B):
-    """Each batch size bench.py times at the Qwen3-32B MLP shapes; 16 and 32
-    run the matrix-core kernels in their large-batch shapes (gate/up: two
-    waves of two tiles sharing x, two batch tiles; down: the staged kernel
-    above 16)."""
+    """Each batch size bench.py times at the Qwen3-32B MLP shapes, through the
+    plain calls and through the workspace calls the benchmark's steps use
+    (down from 4 vectors: the K-split plan, five tile units a block; 16 and
+    32 two tiles a wave, 32 two batch tiles; plain down above 16: the staged
+    kernel)."""
+    ws = nm.workspace()
     for name, (R, K) in I.QWEN3_32B_MLP.items():
         W, x = make(R, K, "bf16", ("qwen3_32b_batch", name, B), B=B)
         v, mk = nm.pack(W, None, 2, 4)
         y = nm.spmv(v, mk, x, 2, 4)
         yd = nm.gemv_dense(W, x)
+        yw = nm.spmv_multi([(v, mk)], x, 2, 4, ws=ws)[0]
+        ydw = nm.gemv_dense_multi([W], x, ws=ws)[0]
         torch.cuda.synchronize()
-        assert y.shape == (B, R)
-        check_all_rows(W, v, mk, x, y, 2, 4, "bf16", yd)
+        assert y.shape == (B, R) and yw.shape == (B, R)
+        check_all_rows(W, v, mk, x, y, 2, 4, "bf16", yd, y_more=(yw,), yd_more=(ydw,))
         del W, v, mk
 
 

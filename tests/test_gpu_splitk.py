@@ -65,6 +65,9 @@ def check_sparse(nm, ws, Ws, x, n, m, dt):
     (100, 25600, 2, 4, "bf16", 17),
     (250, 8192, 4, 8, "fp16", 32),
     (17, 32768, 2, 4, "fp16", 8),
+    (5113, 4096, 2, 4, "bf16", 8),     # enough tiles for five units a block (one block a CU)
+    (5113, 4096, 4, 8, "fp16", 16),
+    (5113, 4096, 4, 8, "bf16", 32),
 ])
 def test_splitk_sparse(nm, ws, R, K, n, m, dt, B):
     W, x = make(R, K, n, m, dt, B, 1)
