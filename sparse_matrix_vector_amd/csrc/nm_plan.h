@@ -151,6 +151,7 @@ struct Plan {
     int ls = 0;              // log2(S) (row-slice: S is a power of two)
     int xf = 0;              // row-slice: x loads issued by the whole block before any weight load
     int ks = 0, kstages = 0; // K-split ring (kind 8): splits, stages per split
+    int map_k = 0, map_cus = 0; // shared-x ring (kind 7): CU-major tile map, k blocks a CU (0: plain)
     size_t lds = 0;
     unsigned grid = 1;
 };
@@ -454,11 +455,11 @@ Plan plan_mfma_ring(int64_t R, int64_t K, int B)
     // 65.9.  With two tiles a wave (above 8 vectors) the default share stays:
     // at 16 vectors the same matrix took 89.2 us at two a block (8 tile pairs
     // on the busiest CU) and 90.3 at seven (7, but one block of 7 waves a CU).
+    auto per_cu = [&](int w) -> int64_t {
+        const size_t l = tab + w * wring + 2 * xslot;
+        return l > (size_t)kLdsMax ? 0 : std::min<int64_t>((int64_t)(kLdsMax / l), 20 / w);
+    };
     if (g_env.ring_share <= 0 && S == 1 && W > 1 && TW == 1) {
-        auto per_cu = [&](int w) -> int64_t {
-            const size_t l = tab + w * wring + 2 * xslot;
-            return l > (size_t)kLdsMax ? 0 : std::min<int64_t>((int64_t)(kLdsMax / l), 20 / w);
-        };
         auto load = [&](int w) { return ((tiles + w - 1) / w + cus - 1) / cus * w; };
         if ((tiles + W - 1) / W > per_cu(W) * cus) {
             int best = W;
@@ -471,12 +472,30 @@ Plan plan_mfma_ring(int64_t R, int64_t K, int B)
             }
             W = best;
         }
+        // CU-major tile map: k blocks on every CU in one round, CU c's
+        // ceil or floor of tiles / CUs split over them, so the busiest CU
+        // holds ceil(tiles / CUs) tiles instead of ceil(blocks / CUs) full
+        // blocks.  The fewest blocks a CU (fewest idle waves) that keep 8
+        // waves a CU.  Qwen3-32B gate+up at 8 vectors (3200 tiles): two
+        // blocks of 6-7 tiles a CU, 13 tiles on the busiest CU against 14.
+        const int64_t even = (tiles + cus - 1) / cus;
+        for (int k = 1; k <= 4; ++k) {
+            const int64_t wb = (even + k - 1) / k;
+            if (wb < 2 || wb > 8 || per_cu((int)wb) < k || k * wb < 8)
+                continue;
+            if (even < load(W)) {
+                W = (int)wb;
+                P.map_k = k;
+                P.map_cus = cus;
+            }
+            break;
+        }
     }
     if (S == 1 && W > 1) {
         P.kind = 7;
         P.rpb = W;
         P.threads = W * kWave;
-        P.grid = (unsigned)((tiles + W - 1) / W);
+        P.grid = P.map_k ? (unsigned)(P.map_k * cus) : (unsigned)((tiles + W - 1) / W);
         P.lds = tab + W * wring + 2 * xslot;
     }
     return P;

@@ -1187,9 +1187,22 @@ struct SplitK {
     int stages;          // stages per split (the last may have fewer, or none)
 };
 
+// CU-major tile map (SHX without KSPLIT; k = 0: block b takes tiles
+// b * tiles_per_block ..).  A launch of k * cus blocks whose blocks all fit
+// at once puts block b on CU b % cus (the dispatcher deals blocks to the CUs
+// in turn), so CU c's share of the tile units, [c T / cus, (c + 1) T / cus),
+// is split over its k blocks, block b = c + j cus taking part j.  The map
+// covers each unit once whatever the dispatcher does; only the balance
+// depends on it.  Waves past their block's count take no tile.
+struct TileMap {
+    int tiles;           // T: tile units (TW tiles each)
+    int cus;
+    int k;               // blocks a CU, 0 = plain map
+};
+
 template <int F, int DT, int TW, int NT, bool SHX, bool KSPLIT = false>
 __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
-                                                        int B, int S, int tiles_per_block, SplitK sk)
+                                                        int B, int S, int tiles_per_block, SplitK sk, TileMap tm)
 {
     static_assert(!KSPLIT || SHX, "K-split blocks share their staged x");
     extern __shared__ u32x4 smem[];
@@ -1208,7 +1221,18 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     const int lt = wave / S, sl = wave - lt * S;
     const int ks = KSPLIT ? (int)(blockIdx.x % (unsigned)sk.ks) : 0;
     const int grp = KSPLIT ? (int)(blockIdx.x / (unsigned)sk.ks) : (int)blockIdx.x;
-    const int r0 = (grp * tiles_per_block + lt) * 16 * TW;
+    int unit0 = grp * tiles_per_block + lt;
+    if (SHX && !KSPLIT && tm.k > 0) {
+        const int c = grp % tm.cus, j = grp / tm.cus;
+        const int s0 = (int)((int64_t)c * tm.tiles / tm.cus);
+        const int n = (int)((int64_t)(c + 1) * tm.tiles / tm.cus) - s0;
+        const int f = s0 + j * n / tm.k, l = s0 + (j + 1) * n / tm.k;
+        unit0 = f + lt < l ? f + lt : tm.tiles;  // past the block's count: no tile
+    }
+    const int r0 = (int)min((int64_t)unit0 * 16 * TW, (int64_t)R);
+    // SHX: a wave with no rows streams no weights and multiplies nothing, but
+    // still loads its share of x and meets the block at every stage.
+    const bool idle = SHX && r0 >= R;
     // Slice sl takes stages sl, sl + S, sl + 2 S, ... of the row: the waves
     // of a launch move through K together.
     const int C = K / COLS;
@@ -1256,6 +1280,8 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
     // row's end load the stage's first chunk instead (in bounds; never
     // multiplied).
     auto issue_w = [&](int st, int slot) {
+        if (idle)
+            return;
         const int c0 = (sl + (st0 + st) * S) * kStageChunks;
         const uint32_t base = ring + (uint32_t)(slot * slot_bytes);
 #pragma unroll
@@ -1388,12 +1414,12 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
         issue_x(0, 0);
         for (int st = 0; st < nst; ++st) {
             const bool more = st + 1 < nst;
-            if (more) {
+            if (more)
                 issue_w(st + 1, (st + 1) & 1);
+            if (more && !idle)
                 wait_vmcnt<NW>();
-            } else {
-                wait_vmcnt<0>();
-            }
+            else
+                wait_vmcnt<0>();                 // (a wave with no rows has only x loads in flight)
             if constexpr (SHX) {                 // every wave's share of the stage's x has landed
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_barrier();
@@ -1402,7 +1428,8 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
             if (more)
                 issue_x(st + 1, (st + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
-            consume(st, st & 1);
+            if (!idle)
+                consume(st, st & 1);
             __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the slot's reads are done before it is refilled
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1936,7 +1963,8 @@ int launch_mfma_ring_k(const Plan& P, const Parts& parts, const void* x, int R, 
     }
     (void)hipGetLastError();
     hipLaunchKernelGGL((mfma_ring_kernel<F, DT, TW, NT, SHX>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
-                       static_cast<const u32x4*>(x), R, K, B, P.S, P.rpb, SplitK{});
+                       static_cast<const u32x4*>(x), R, K, B, P.S, P.rpb, SplitK{},
+                       TileMap{(R + 16 * TW - 1) / (16 * TW), P.map_cus, P.map_k});
     return hip_status(hipGetLastError());
 }
 
@@ -1954,7 +1982,7 @@ int launch_mfma_split(const Plan& P, const Parts& parts, const void* x, int R, i
     const SplitK sk{reinterpret_cast<float*>(w), reinterpret_cast<unsigned*>(w + kSplitPartBytes), P.ks, P.kstages};
     (void)hipGetLastError();
     hipLaunchKernelGGL((mfma_ring_kernel<F, DT, TW, NT, true, true>), dim3(P.grid), dim3(P.threads), P.lds, s, parts,
-                       static_cast<const u32x4*>(x), R, K, B, 1, P.rpb, sk);
+                       static_cast<const u32x4*>(x), R, K, B, 1, P.rpb, sk, TileMap{});
     return hip_status(hipGetLastError());
 }
 

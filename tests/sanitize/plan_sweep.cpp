@@ -9,7 +9,10 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <set>
+#include <utility>
+#include <vector>
 
 #include "nm_plan.h"
 
@@ -123,8 +126,31 @@ void check_mfma(int64_t R, int64_t K, int B, bool glu)
             REQUIRE((int64_t)P.grid == tiles);
         } else {
             REQUIRE(P.kind == 7 && P.S == 1 && P.threads == P.rpb * kWave);
-            REQUIRE((int64_t)P.grid * P.rpb >= tiles && ((int64_t)P.grid - 1) * P.rpb < tiles);
             REQUIRE(P.lds >= shared_ring_lds<F>(P.rpb, TW, B));
+            if (P.map_k == 0) {
+                REQUIRE((int64_t)P.grid * P.rpb >= tiles && ((int64_t)P.grid - 1) * P.rpb < tiles);
+            } else {
+                // CU-major map, as the kernel computes it: every tile in exactly one
+                // block, no block with more tiles than waves, one round of blocks
+                REQUIRE(TW == 1 && P.map_cus == g_cus && P.map_k >= 1 && (int64_t)P.grid == (int64_t)P.map_k * g_cus);
+                REQUIRE((int64_t)(kLdsMax / P.lds) >= P.map_k && P.map_k * P.rpb <= 20);
+                std::vector<std::pair<int64_t, int64_t>> parts;
+                for (int64_t b = 0; b < P.grid; ++b) {
+                    const int64_t c = b % P.map_cus, j = b / P.map_cus;
+                    const int64_t s0 = c * tiles / P.map_cus, n = (c + 1) * tiles / P.map_cus - s0;
+                    const int64_t f = s0 + j * n / P.map_k, l = s0 + (j + 1) * n / P.map_k;
+                    REQUIRE(f <= l && l - f <= P.rpb);
+                    if (l > f)
+                        parts.emplace_back(f, l);
+                }
+                std::sort(parts.begin(), parts.end());
+                int64_t next = 0;
+                for (const auto& pr : parts) {
+                    REQUIRE(pr.first == next);
+                    next = pr.second;
+                }
+                REQUIRE(next == tiles);
+            }
         }
     } else {
         const int NT = B > 16 ? 2 : 1;
