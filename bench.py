@@ -248,11 +248,12 @@ def trials_us(torch, body, trials, launches):
     return ts[0], statistics.median(ts), ts[-1]
 
 
-def mlp_single(torch, lib, launches, cur, reps=10, trials=20):
-    """MLP projections (gate, up, down) as single nm_spmv / nm_gemv_dense
-    launches, back to back over every layer's weights (HIP-graph bursts);
-    per-launch time is the median over `trials` bursts (min and max beside
-    it)."""
+def mlp_single(torch, lib, launches, cur, ws, reps=10, trials=20):
+    """MLP projections (gate, up, down) as single launches through the
+    workspace calls the step uses (nm_spmv_multi_ws / nm_gemv_dense_multi_ws
+    on one matrix), back to back over every layer's weights (HIP-graph
+    bursts); per-launch time is the median over `trials` bursts (min and max
+    beside it)."""
     out = {}
     for name in ("gate", "up", "down"):
         group = [L for L in launches if name in L.names]
@@ -262,21 +263,25 @@ def mlp_single(torch, lib, launches, cur, reps=10, trials=20):
         i0 = L0.names.index(name)
         R, K, B = L0.R[i0], L0.K, L0.B
 
+        wsa = (P(ws.data_ptr()), I64(ws.numel()))
+
         def sargs(st):
             out_ = []
             for L in group:
                 i = L.names.index(name)
-                out_.append((P(L.values[i].data_ptr()), P(L.masks[i].data_ptr()), I64(R), I64(K), I32(L.n),
-                             I32(L.m), I32(L.dtc), P(L.x.data_ptr()), I32(L.B), P(L.y[i].data_ptr()), P(st)))
+                out_.append((I32(1), (P * 1)(L.values[i].data_ptr()), (P * 1)(L.masks[i].data_ptr()), (I64 * 1)(R),
+                             I64(K), I32(L.n), I32(L.m), I32(L.dtc), P(L.x.data_ptr()), I32(L.B),
+                             (P * 1)(L.y[i].data_ptr())) + wsa + (P(st),))
             return out_
 
         def dargs(st):
-            return [(P(L.W[L.names.index(name)].data_ptr()), I64(R), I64(K), I32(L.dtc), P(L.x.data_ptr()),
-                     I32(L.B), P(L.yd[L.names.index(name)].data_ptr()), P(st)) for L in group]
+            return [(I32(1), (P * 1)(L.W[L.names.index(name)].data_ptr()), (I64 * 1)(R), I64(K), I32(L.dtc),
+                     P(L.x.data_ptr()), I32(L.B), (P * 1)(L.yd[L.names.index(name)].data_ptr())) + wsa + (P(st),)
+                    for L in group]
         nbytes = L0.part_bytes(i0) + B * K * 2
         dbytes = R * K * 2 + B * (K + R) * 2
-        ts = burst(torch, lib.nm_spmv, sargs, trials)
-        td = burst(torch, lib.nm_gemv_dense, dargs, trials)
+        ts = burst(torch, lib.nm_spmv_multi_ws, sargs, trials)
+        td = burst(torch, lib.nm_gemv_dense_multi_ws, dargs, trials)
         us, usd = ts[1], td[1]
         # torch's own dense product (hipBLASLt / rocBLAS) on the same weights, as context
         pairs = [(L.W[L.names.index(name)], L.x, L.yd[L.names.index(name)]) for L in group]
@@ -674,7 +679,7 @@ def main():
     rus = sum(per[k]["us"] for k in rk) / len(rk)
     achieved = rbytes / rus / 1e3
 
-    mlp = mlp_single(torch, lib, launches, cur, reps=10 if layers <= 64 else 3)
+    mlp = mlp_single(torch, lib, launches, cur, ws, reps=10 if layers <= 64 else 3)
     # What no single launch of these sizes can beat: a one-shot read of the
     # same bytes, and an empty kernel (both back to back, as in the step).
     floors, empty_us = launch_floors(torch, [v["bytes"] for v in per.values()] + [v["bytes"] for v in mlp.values()])

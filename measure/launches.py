@@ -28,7 +28,7 @@ def main():
     p.add_argument("--layers", type=int, default=8)
     p.add_argument("--kinds", default="gate,down")
     p.add_argument("--reps", type=int, default=20)
-    p.add_argument("--ws", action="store_true", help="fused kinds through nm_spmv_multi_ws with a K-split workspace")
+    p.add_argument("--ws", action="store_true", help="the step's kinds through the workspace calls (_multi_ws)")
     p.add_argument("--dense", action="store_true", help="the dense baseline of the step's kinds (nm_gemv_dense_multi)")
     a = p.parse_args()
 
@@ -48,7 +48,10 @@ def main():
     out = {}
     for kind in kinds:
         group = [L for L in launches if L.kind == kind]
-        if group and a.dense:
+        if group and a.dense and a.ws:
+            ws = nm.workspace()
+            fn, args = lib.nm_gemv_dense_multi_ws, (lambda st, g=group: [L.dense_args_ws(st, ws) for L in g])
+        elif group and a.dense:
             fn, args = lib.nm_gemv_dense_multi, (lambda st, g=group: [L.dense_args(st) for L in g])
         elif group and a.ws:
             ws = nm.workspace()

@@ -85,15 +85,29 @@ def make(R, K, dt, tag, B=1, xkind="normal"):
     return W, x
 
 
+@pytest.fixture(scope="module")
+def ws(nm):
+    return nm.workspace()
+
+
+def ws_products(nm, ws, W, v, mk, x, n, m, dense=True):
+    """The same products through the workspace calls (the benchmark's steps
+    use them; long rows there take the K-split plans)."""
+    yw = nm.spmv_multi([(v, mk)], x, n, m, ws=ws)[0]
+    ydw = nm.gemv_dense_multi([W], x, ws=ws)[0] if dense else None
+    return (yw,), ((ydw,) if dense else ())
+
+
 @pytest.mark.parametrize("name", list(I.LLAMA31_8B))
-def test_llama31_8b_single(nm, name):
+def test_llama31_8b_single(nm, ws, name):
     R, K = I.LLAMA31_8B[name]
     W, x = make(R, K, "fp16", ("llama31_8b", name), xkind="outliers")
     v, mk = nm.pack(W, None, 2, 4)
     y = nm.spmv(v, mk, x, 2, 4)
     yd = nm.gemv_dense(W, x)
+    ym, ydm = ws_products(nm, ws, W, v, mk, x, 2, 4)
     torch.cuda.synchronize()
-    check_all_rows(W, v, mk, x, y, 2, 4, "fp16", yd)
+    check_all_rows(W, v, mk, x, y, 2, 4, "fp16", yd, y_more=ym, yd_more=ydm)
 
 
 @pytest.mark.parametrize("group", [("q", "k", "v"), ("gate", "up")])
@@ -111,26 +125,28 @@ def test_llama31_8b_fused(nm, group):
 
 @pytest.mark.parametrize("model,shapes", [("qwen3_14b", I.QWEN3_14B_MLP), ("qwen3_32b", I.QWEN3_32B_MLP)])
 @pytest.mark.parametrize("n,m", [(4, 8), (2, 4)])
-def test_qwen3_mlp(nm, model, shapes, n, m):
+def test_qwen3_mlp(nm, ws, model, shapes, n, m):
     for name, (R, K) in shapes.items():
         W, x = make(R, K, "bf16", (model, name, n, m), xkind="laplace")
         v, mk = nm.pack(W, None, n, m)
         y = nm.spmv(v, mk, x, n, m)
         yd = nm.gemv_dense(W, x) if name != "up" else None
+        ym, ydm = ws_products(nm, ws, W, v, mk, x, n, m, dense=name != "up")
         torch.cuda.synchronize()
-        check_all_rows(W, v, mk, x, y, n, m, "bf16", yd)
+        check_all_rows(W, v, mk, x, y, n, m, "bf16", yd, y_more=ym, yd_more=ydm)
         del W, v, mk
 
 
 @pytest.mark.parametrize("name", list(I.LLAMA33_70B))
-def test_llama33_70b_layer(nm, name):
+def test_llama33_70b_layer(nm, ws, name):
     R, K = I.LLAMA33_70B[name]
     W, x = make(R, K, "bf16", ("llama33_70b", 0, name))
     v, mk = nm.pack(W, None, 2, 4)
     y = nm.spmv(v, mk, x, 2, 4)
     yd = nm.gemv_dense(W, x) if name in ("q", "down") else None
+    ym, ydm = ws_products(nm, ws, W, v, mk, x, 2, 4, dense=name in ("q", "down"))
     torch.cuda.synchronize()
-    check_all_rows(W, v, mk, x, y, 2, 4, "bf16", yd)
+    check_all_rows(W, v, mk, x, y, 2, 4, "bf16", yd, y_more=ym, yd_more=ydm)
 
 
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32])
