@@ -110,11 +110,13 @@ int cu_count();
 // 16) lets a single-vector sparse row of up to that many chunks per lane run
 // on one wave instead of being cut into slices; NMSPMV_SPLITK=1 turns the
 // K-split ring plan off, 2 uses it wherever it fits (with a workspace);
-// NMSPMV_SPLITK_KS sets its split count (2 to 32).
+// NMSPMV_SPLITK_KS sets its split count (2 to 32); NMSPMV_RPW=1 turns the
+// row-slice kernel's row pairs (two rows a wave) off, 2 takes them from 2
+// vectors (default: 3 and 4).
 struct Env {
     int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0,
         ring_tiles = 0, ring_share = 0, hybrid_split = 0, xfirst = -1, blocks_per_cu = 0, xdma = 0, max_cpl = 0,
-        splitk = 0, splitk_ks = 0;
+        splitk = 0, splitk_ks = 0, rpw = 0;
 };
 inline Env g_env;
 inline std::once_flag g_env_once;
@@ -141,6 +143,7 @@ inline void read_env()
     g_env.max_cpl = get("NMSPMV_MAX_CPL");
     g_env.splitk = get("NMSPMV_SPLITK");
     g_env.splitk_ks = get("NMSPMV_SPLITK_KS");
+    g_env.rpw = get("NMSPMV_RPW");
     const char* xf = std::getenv("NMSPMV_XFIRST");
     g_env.xfirst = xf ? std::atoi(xf) : -1;
 }
@@ -149,6 +152,7 @@ struct Plan {
     int kind = 0;            // 1 row-slice, 3 stream
     int S = 1, rpb = 1, cpl = 1, threads = 256, tile_cols = 0;
     int ls = 0;              // log2(S) (row-slice: S is a power of two)
+    int rpw = 1;             // row-slice: rows a wave (2: row pairs; rpb counts rows)
     int xf = 0;              // row-slice: x loads issued by the whole block before any weight load
     int ks = 0, kstages = 0; // K-split ring (kind 8): splits, stages per split
     int map_k = 0, map_cus = 0; // shared-x ring (kind 7): CU-major tile map, k blocks a CU (0: plain)
@@ -178,8 +182,15 @@ inline int log2_exact(int v)
 //    13.7-14.9 us, with a wide spread between launches, on others, where
 //    8-wave blocks held 12.4-12.5 us on all of them;
 //  * rows cut into slices issue x first (x-first issue order; the same
-//    sweep: 12.7-12.8 us without it).
-inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, int B, Plan* P)
+//    sweep: 12.7-12.8 us without it);
+//  * sparse rows of 4 or 5 chunks a lane at 3 or 4 vectors, unsliced: two
+//    rows a wave (row pairs), when that still gives two blocks per CU; at
+//    these batch sizes the VALU kernel is bound by instruction issue, and a
+//    pair shares the wave's fixed work and its x reads (Qwen3-32B gate+up at
+//    4 vectors 61.8 -> 53.3 us; at 2 vectors no gain, so not taken there;
+//    NMSPMV_RPW=2 takes them from 2 vectors; pairs: false keeps one row a
+//    wave, for the fused hybrid launch).
+inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, int B, Plan* P, bool pairs = true)
 {
     const int cus = cu_count();
     // Long rows on one wave (up to 16 chunks a lane: a single vector,
@@ -214,14 +225,19 @@ inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, int B, Pla
     if (rpb * S > 16)
         return false;
     const int64_t threads = (int64_t)rpb * S * kWave;
+    int rpw = 1;
+    if (pairs && !dense && S == 1 && B >= (g_env.rpw == 2 ? 2 : 3) && B <= 4 && (cpl == 4 || cpl == 5) &&
+        g_env.rpw != 1 && g_env.rpb == 0 && (R + 2 * rpb - 1) / (2 * rpb) >= 2 * cus)
+        rpw = 2;
     P->kind = 1;
     P->S = S;
     P->ls = log2_exact(S);
     P->xf = g_env.xfirst >= 0 ? (g_env.xfirst != 0) : (S >= 2);
-    P->rpb = rpb;
+    P->rpw = rpw;
+    P->rpb = rpb * rpw;
     P->cpl = cpl;
     P->threads = (int)threads;
-    P->grid = (unsigned)((R + rpb - 1) / rpb);
+    P->grid = (unsigned)((R + P->rpb - 1) / P->rpb);
     return true;
 }
 
@@ -233,7 +249,7 @@ inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, int B, Pla
 // 25600, 2:4 32.8 -> 28.8 and dense 50.9 -> 44.7; Llama-3.3-70B down, 8192 x
 // 28672, 2:4 47.6 -> 50.4 and dense 78.0 -> 84.7.)
 template <int F>
-Plan plan_for(int64_t R, int64_t K, int B, bool glu)
+Plan plan_for(int64_t R, int64_t K, int B, bool glu, bool pairs = true)
 {
     std::call_once(g_env_once, read_env);
     constexpr int COLS = chunk_cols<F>();
@@ -245,7 +261,7 @@ Plan plan_for(int64_t R, int64_t K, int B, bool glu)
     int kind = g_env.kernel;
     if (kind != 1 && kind != 3)
         kind = (fits && C <= (F == kDense ? 50 : 25) * kWave) ? 1 : 3;
-    if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, glu, B, &P)) {
+    if (kind == 1 && fits && plan_rowslice(R, C, F == kDense, glu, B, &P, pairs)) {
         P.lds = tab + xbytes + (size_t)P.rpb * P.S * B * 4;
         if (g_env.blocks_per_cu >= 2 && g_env.blocks_per_cu <= 8)
             P.lds = std::max(P.lds, (size_t)kLdsMax / (g_env.blocks_per_cu + 1) + 256);
@@ -318,7 +334,7 @@ inline int rowslice_x_regs(int B, int64_t K, int threads, int cpl)
 template <int F>
 bool plan_hybrid(int64_t RS, int64_t K, int B, Plan* out)
 {
-    Plan P = plan_for<F>(RS, K, B, false);
+    Plan P = plan_for<F>(RS, K, B, false, false);
     if (P.kind == 1 && P.rpb == 1 && g_env.rpb == 0 && P.S <= 8) {
         P.rpb = 2;
         P.threads = 2 * P.S * kWave;

@@ -547,6 +547,76 @@ __device__ __forceinline__ void chunk_live(bool live, u32x4& v, uint32_t& mk)
     mk = live ? mk : 0u;
 }
 
+// Two rows' chunks at the same columns (a wave holding a pair of rows):
+// acc[b] += (va . x[b]) and acc2[b] += (vb . x[b]), each x unit read from LDS
+// once for both rows.  Sparse formats only.
+template <int F, int DT, int NB>
+__device__ __forceinline__ void chunk_dot_pair(const u32x4 va, const uint32_t ma, const u32x4 vb, const uint32_t mb,
+                                               const u32x4* __restrict__ tab, const u32x4* __restrict__ xs,
+                                               const int xslot, const int bstride, float* acc, float* acc2)
+{
+    static_assert(F != kDense, "row pairs are a sparse-format plan");
+    if constexpr (F == kNM24) {
+        const uint32_t* t = reinterpret_cast<const uint32_t*>(tab);
+        const uint32_t s0 = t[ma & 0xF], s1 = t[(ma >> 4) & 0xF], s2 = t[(ma >> 8) & 0xF], s3 = t[(ma >> 12) & 0xF];
+        const uint32_t q0 = t[mb & 0xF], q1 = t[(mb >> 4) & 0xF], q2 = t[(mb >> 8) & 0xF], q3 = t[(mb >> 12) & 0xF];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const u32x4 xa = xs[b * bstride + xslot];
+            const u32x4 xb = xs[b * bstride + xslot + 32];
+            float a = acc[b], c = acc2[b];
+            a = dot2<DT>(va.x, __builtin_amdgcn_perm(xa.y, xa.x, s0), a);
+            c = dot2<DT>(vb.x, __builtin_amdgcn_perm(xa.y, xa.x, q0), c);
+            a = dot2<DT>(va.y, __builtin_amdgcn_perm(xa.w, xa.z, s1), a);
+            c = dot2<DT>(vb.y, __builtin_amdgcn_perm(xa.w, xa.z, q1), c);
+            a = dot2<DT>(va.z, __builtin_amdgcn_perm(xb.y, xb.x, s2), a);
+            c = dot2<DT>(vb.z, __builtin_amdgcn_perm(xb.y, xb.x, q2), c);
+            a = dot2<DT>(va.w, __builtin_amdgcn_perm(xb.w, xb.z, s3), a);
+            c = dot2<DT>(vb.w, __builtin_amdgcn_perm(xb.w, xb.z, q3), c);
+            acc[b] = a;
+            acc2[b] = c;
+        }
+    } else {
+        uint32_t w[8], u[8];
+        {
+            const u32x4 s0 = tab[ma & 0xFF], s1 = tab[(ma >> 8) & 0xFF];
+            w[0] = __builtin_amdgcn_perm(va.y, va.x, s0.x);
+            w[1] = __builtin_amdgcn_perm(va.y, va.x, s0.y);
+            w[2] = __builtin_amdgcn_perm(va.y, va.x, s0.z);
+            w[3] = __builtin_amdgcn_perm(va.y, va.x, s0.w);
+            w[4] = __builtin_amdgcn_perm(va.w, va.z, s1.x);
+            w[5] = __builtin_amdgcn_perm(va.w, va.z, s1.y);
+            w[6] = __builtin_amdgcn_perm(va.w, va.z, s1.z);
+            w[7] = __builtin_amdgcn_perm(va.w, va.z, s1.w);
+        }
+        {
+            const u32x4 s0 = tab[mb & 0xFF], s1 = tab[(mb >> 8) & 0xFF];
+            u[0] = __builtin_amdgcn_perm(vb.y, vb.x, s0.x);
+            u[1] = __builtin_amdgcn_perm(vb.y, vb.x, s0.y);
+            u[2] = __builtin_amdgcn_perm(vb.y, vb.x, s0.z);
+            u[3] = __builtin_amdgcn_perm(vb.y, vb.x, s0.w);
+            u[4] = __builtin_amdgcn_perm(vb.w, vb.z, s1.x);
+            u[5] = __builtin_amdgcn_perm(vb.w, vb.z, s1.y);
+            u[6] = __builtin_amdgcn_perm(vb.w, vb.z, s1.z);
+            u[7] = __builtin_amdgcn_perm(vb.w, vb.z, s1.w);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const u32x4 xa = xs[b * bstride + xslot];
+            const u32x4 xb = xs[b * bstride + xslot + 32];
+            const uint32_t xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+            float a = acc[b], c = acc2[b];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                a = dot2<DT>(w[k], xv[k], a);
+                c = dot2<DT>(u[k], xv[k], c);
+            }
+            acc[b] = a;
+            acc2[b] = c;
+        }
+    }
+}
+
 // ---- row-slice kernel ------------------------------------------------------
 
 // A block holds rows_per_block rows x S = 2^ls K-slices, one wave per (row,
@@ -564,10 +634,17 @@ __device__ __forceinline__ void chunk_live(bool live, u32x4& v, uint32_t& mk)
 // its data had arrived.
 // The body takes its block index as an argument so that one launch can run
 // two plans side by side (hybrid_rowslice_kernel).
-template <int F, int DT, int NB, int CPL, int XU>
+//
+// RPW = 2 (sparse rows, S = 1): each wave holds two consecutive rows (a
+// gated launch's gate and up rows of one output), loads both rows' chunks,
+// and multiplies them against the same x reads; the block's rows_per_block
+// rows are then two per wave, so a block's x and its per-wave work serve
+// twice the rows.
+template <int F, int DT, int NB, int CPL, int XU, int RPW = 1>
 __device__ __forceinline__ void rowslice_body(const Parts& P, const u32x4* __restrict__ x4, int R, int K, int ls,
                                               int rows_per_block, int xfirst, int xreg, unsigned blk)
 {
+    static_assert(RPW == 1 || (RPW == 2 && F != kDense), "row pairs: sparse formats");
     extern __shared__ u32x4 smem[];
     constexpr int COLS = chunk_cols<F>();
     const int lane = threadIdx.x & (kWave - 1);
@@ -575,14 +652,16 @@ __device__ __forceinline__ void rowslice_body(const Parts& P, const u32x4* __res
     const int nwaves = blockDim.x / kWave;
     const int S = 1 << ls;
     const int lr = wave >> ls, sl = wave & (S - 1);
-    const int r = blk * rows_per_block + lr;
+    const int r = blk * rows_per_block + lr * RPW;
     const bool active = r < R;
+    const bool active2 = RPW == 2 && r + 1 < R;
     const int C = (int)((unsigned)K / COLS);
     // Slices start on 32-chunk boundaries, so that a lane's x slots are one
     // base plus a fixed step per load slot (the last slice may be shorter).
     const int cps = (((C + S - 1) >> ls) + 31) & ~31;
     const int cbeg = sl * cps, cend = active ? min(C, cbeg + cps) : cbeg;
     const RowRef row = row_ref(P, active ? r : 0, C);
+    const RowRef row2 = row_ref(P, active2 ? r + 1 : 0, C);   // (RPW = 2; its rows stay in [cbeg, cend))
 
     u32x4* tab = smem;
     u32x4* xs = smem + table_units<F>();
@@ -602,11 +681,13 @@ __device__ __forceinline__ void rowslice_body(const Parts& P, const u32x4* __res
     if (xfirst)
         __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 v[CPL];
-    uint32_t mk[CPL];
+    u32x4 v[CPL], v2[RPW == 2 ? CPL : 1];
+    uint32_t mk[CPL], mk2[RPW == 2 ? CPL : 1];
     load_chunks<F, CPL>(row.w, row.m, cbeg, cend, lane, v, mk);
+    if constexpr (RPW == 2)
+        load_chunks<F, CPL>(row2.w, row2.m, cbeg, cend, lane, v2, mk2);
     build_table<F>(tab);
-    constexpr int NW = F == kDense ? CPL : 2 * CPL;   // weight loads issued after x
+    constexpr int NW = (F == kDense ? CPL : 2 * CPL) * RPW;   // weight loads issued after x
     if (xreg) {
         wait_vmcnt<NW>();
 #pragma unroll
@@ -626,27 +707,65 @@ __device__ __forceinline__ void rowslice_body(const Parts& P, const u32x4* __res
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
-    float acc[NB];
+    float acc[NB], acc2[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b) {
         acc[b] = 0.f;
+        acc2[b] = 0.f;
+    }
     const int xl = chunk_xslot<F>(cbeg + lane);      // cbeg % 32 == 0: slot u is xl + u * step
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
         if (u * kWave >= cend - cbeg)          // wave-uniform: nothing left in this slot for any lane
             break;
         if ((u + 1) * kWave <= cend - cbeg) {  // wave-uniform: every lane holds a chunk
-            chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, xl + u * xslot_step<F>(), bstride, acc);
+            if constexpr (RPW == 2)
+                chunk_dot_pair<F, DT, NB>(v[u], mk[u], v2[u], mk2[u], tab, xs, xl + u * xslot_step<F>(), bstride, acc,
+                                          acc2);
+            else
+                chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, xl + u * xslot_step<F>(), bstride, acc);
         } else {
             const bool live = cbeg + lane + u * kWave < cend;
             chunk_live(live, v[u], mk[u]);
-            chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, live ? xl + u * xslot_step<F>() : 0, bstride, acc);
+            if constexpr (RPW == 2) {
+                chunk_live(live, v2[u], mk2[u]);
+                chunk_dot_pair<F, DT, NB>(v[u], mk[u], v2[u], mk2[u], tab, xs, live ? xl + u * xslot_step<F>() : 0,
+                                          bstride, acc, acc2);
+            } else {
+                chunk_dot<F, DT, NB>(v[u], mk[u], tab, xs, live ? xl + u * xslot_step<F>() : 0, bstride, acc);
+            }
         }
     }
     float sum[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
         sum[b] = wave_sum(acc[b]);
+    if constexpr (RPW == 2) {
+        // S = 1: the pair's sums go straight to y (gated: rows r and r + 1 are
+        // the gate and up rows of one output).
+        float sum2[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            sum2[b] = wave_sum(acc2[b]);
+        if (lane != 0)
+            return;
+        if (P.glu) {
+            if (active)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    row.y[(size_t)b * row.R] = glu_out<DT>(sum[b], sum2[b]);
+            return;
+        }
+        if (active)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                row.y[(size_t)b * row.R] = from_f32<DT>(sum[b]);
+        if (active2)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                row2.y[(size_t)b * row2.R] = from_f32<DT>(sum2[b]);
+        return;
+    }
     if (S == 1 && !P.glu) {
         if (active && lane == 0)
 #pragma unroll
@@ -686,11 +805,11 @@ __device__ __forceinline__ void rowslice_body(const Parts& P, const u32x4* __res
     }
 }
 
-template <int F, int DT, int NB, int CPL, int XU>
+template <int F, int DT, int NB, int CPL, int XU, int RPW = 1>
 __global__ __launch_bounds__(1024) void rowslice_kernel(const Parts P, const u32x4* __restrict__ x4, int R, int K,
                                                         int ls, int rows_per_block, int xfirst, int xreg)
 {
-    rowslice_body<F, DT, NB, CPL, XU>(P, x4, R, K, ls, rows_per_block, xfirst, xreg, blockIdx.x);
+    rowslice_body<F, DT, NB, CPL, XU, RPW>(P, x4, R, K, ls, rows_per_block, xfirst, xreg, blockIdx.x);
 }
 
 // A hybrid matrix (sparse rows PS plus dense rows PD, both scattered into one
@@ -2053,6 +2172,18 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
             NM_SLICE_XU(CPL, 1);       \
         }                              \
     } while (0)
+        if constexpr (NB >= 2 && NB <= 4 && F != kDense) {
+            // row pairs (two rows a wave; the plan takes them at 4 or 5 chunks a lane)
+            if (P.rpw == 2) {
+                if (P.cpl == 4)
+                    hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 4, 1, 2>), dim3(P.grid), dim3(P.threads), P.lds, s,
+                                       parts, x4, R, K, P.ls, P.rpb, P.xf, (int)(xu != 0));
+                else
+                    hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 5, 1, 2>), dim3(P.grid), dim3(P.threads), P.lds, s,
+                                       parts, x4, R, K, P.ls, P.rpb, P.xf, (int)(xu != 0));
+                return hip_status(hipGetLastError());
+            }
+        }
         if constexpr (NB == 1 && F != kDense) {
             // long rows on one wave (single vector): the next even slot count
             if (P.cpl > 8) {

@@ -44,7 +44,12 @@ void check_rowslice(const Plan& P, int64_t R, int64_t K, int B, bool glu)
     const int64_t C = K / chunk_cols<F>();
     const size_t xbytes = (size_t)B * (size_t)x_row_units(K) * 16;
     REQUIRE(pow2(P.S) && P.S <= 16 && (1 << P.ls) == P.S);
-    REQUIRE(P.rpb >= 1 && P.rpb * P.S <= 16 && P.threads == P.rpb * P.S * kWave);
+    REQUIRE(P.rpw == 1 || P.rpw == 2);
+    const int waves = P.rpb / P.rpw;            // rpb counts rows: rpw a wave
+    REQUIRE(P.rpb % P.rpw == 0 && waves >= 1 && waves * P.S <= 16 && P.threads == waves * P.S * kWave);
+    if (P.rpw == 2)                             // the instantiated row-pair kernels
+        REQUIRE(F != kDense && P.S == 1 && B >= 2 && B <= 4 && (P.cpl == 4 || P.cpl == 5) &&
+                (B >= 3 || g_env.rpw == 2));
     REQUIRE(P.cpl >= 1 && P.cpl <= (B == 1 && !glu && F != kDense ? 16 : 8));
     REQUIRE(slice_chunks(C, P.S, P.ls) <= 64LL * P.cpl);
     REQUIRE((int64_t)P.grid * P.rpb >= R && ((int64_t)P.grid - 1) * P.rpb < R);
@@ -84,7 +89,7 @@ void check_valu(int64_t R, int64_t K, int B, bool glu)
         if (plan_hybrid<F>(R, K, B, &H)) {
             ++g_plans;
             ++g_kinds[0];
-            REQUIRE(H.kind == 1 && H.rpb >= 2 && H.rpb % 2 == 0);
+            REQUIRE(H.kind == 1 && H.rpb >= 2 && H.rpb % 2 == 0 && H.rpw == 1);
             check_rowslice<F>(H, R, K, B, false);
             REQUIRE(H.lds <= (size_t)kLdsMax);
             // the dense rows: half the rows per block over twice the slices, K / 8 chunks a row
@@ -299,6 +304,7 @@ int main()
         {"max_cpl=16", &Env::max_cpl, 16},      {"max_cpl=100", &Env::max_cpl, 100},
         {"splitk=1", &Env::splitk, 1},          {"splitk=2", &Env::splitk, 2},
         {"splitk_ks=3", &Env::splitk_ks, 3},    {"splitk_ks=32", &Env::splitk_ks, 32},
+        {"rpw=1", &Env::rpw, 1},                {"rpw=2", &Env::rpw, 2},
     };
     for (int cus : {256, 80, 1}) {
         g_cus = cus;

@@ -33,7 +33,10 @@ CASES = [
     (300, 5120, 2, 4, "bf16", 8),
     (100, 8192, 4, 8, "fp16", 16),
     (70, 2080, 2, 4, "fp16", 32),
+    (8193, 4096, 2, 4, "bf16", 3),     # row pairs (two rows a wave) by default
 ]
+# run only under the override that changes their plan
+CASES_FOR = {"NMSPMV_RPW": [(8192, 5120, 2, 4, "fp16", 2)]}   # row pairs from 2 vectors
 
 SETTINGS = [
     {"NMSPMV_MAX_CPL": "16"},
@@ -57,6 +60,8 @@ SETTINGS = [
     {"NMSPMV_SPLITK": "2"},
     {"NMSPMV_SPLITK": "2", "NMSPMV_SPLITK_KS": "3"},
     {"NMSPMV_SPLITK": "1"},
+    {"NMSPMV_RPW": "1"},
+    {"NMSPMV_RPW": "2"},
 ]
 
 
@@ -73,7 +78,11 @@ def child():
     from sparse_matrix_vector_amd import inputs as I
     nm.lib()
     worst = 0.0
-    for seed, (R, K, n, m, dt, B) in enumerate(CASES):
+    cases = list(CASES)
+    for var, extra in CASES_FOR.items():
+        if os.environ.get(var) == "2":
+            cases += extra
+    for seed, (R, K, n, m, dt, B) in enumerate(cases):
         print(json.dumps({"case": [R, K, n, m, dt, B]}), flush=True)
         worst = max(worst, G.run_case(nm, R, K, n, m, dt, B, 700 + seed))
     print(json.dumps({"case": "swiglu"}), flush=True)
