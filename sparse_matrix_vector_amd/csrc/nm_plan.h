@@ -111,8 +111,8 @@ int cu_count();
 // on one wave instead of being cut into slices; NMSPMV_SPLITK=1 turns the
 // K-split ring plan off, 2 uses it wherever it fits (with a workspace);
 // NMSPMV_SPLITK_KS sets its split count (2 to 32); NMSPMV_RPW=1 turns the
-// row-slice kernel's row pairs (two rows a wave) off, 2 takes them from 2
-// vectors (default: 3 and 4).
+// row-slice kernel's row pairs (two rows a wave) off, 2 takes them from one
+// vector (default: 3 and 4).
 struct Env {
     int kernel = 0, slices = 0, rpb = 0, blocks = 0, threads = 0, tile_bytes = 0, mfma_min_b = 0, mfma_slices = 0,
         ring_tiles = 0, ring_share = 0, hybrid_split = 0, xfirst = -1, blocks_per_cu = 0, xdma = 0, max_cpl = 0,
@@ -187,9 +187,9 @@ inline int log2_exact(int v)
 //    rows a wave (row pairs), when that still gives two blocks per CU; at
 //    these batch sizes the VALU kernel is bound by instruction issue, and a
 //    pair shares the wave's fixed work and its x reads (Qwen3-32B gate+up at
-//    4 vectors 61.8 -> 53.3 us; at 2 vectors no gain, so not taken there;
-//    NMSPMV_RPW=2 takes them from 2 vectors; pairs: false keeps one row a
-//    wave, for the fused hybrid launch).
+//    4 vectors 61.8 -> 53.3 us; at 2 vectors no gain and at one a loss, so
+//    not taken there; NMSPMV_RPW=2 takes them from one vector; pairs: false
+//    keeps one row a wave, for the fused hybrid launch).
 inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, int B, Plan* P, bool pairs = true)
 {
     const int cus = cu_count();
@@ -226,8 +226,10 @@ inline bool plan_rowslice(int64_t R, int64_t C, bool dense, bool glu, int B, Pla
         return false;
     const int64_t threads = (int64_t)rpb * S * kWave;
     int rpw = 1;
-    if (pairs && !dense && S == 1 && B >= (g_env.rpw == 2 ? 2 : 3) && B <= 4 && (cpl == 4 || cpl == 5) &&
-        g_env.rpw != 1 && g_env.rpb == 0 && (R + 2 * rpb - 1) / (2 * rpb) >= 2 * cus)
+    // (a single vector's x must fit one register unit a thread: the pair kernels are built for that)
+    if (pairs && !dense && S == 1 && B >= (g_env.rpw == 2 ? 1 : 3) && B <= 4 && (cpl == 4 || cpl == 5) &&
+        g_env.rpw != 1 && g_env.rpb == 0 && (R + 2 * rpb - 1) / (2 * rpb) >= 2 * cus &&
+        (B > 1 || 2 * C <= threads))
         rpw = 2;
     P->kind = 1;
     P->S = S;

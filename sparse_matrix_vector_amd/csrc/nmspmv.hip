@@ -2172,9 +2172,11 @@ int launch_rows(const Parts& parts, const void* x, int R, int K, hipStream_t s)
             NM_SLICE_XU(CPL, 1);       \
         }                              \
     } while (0)
-        if constexpr (NB >= 2 && NB <= 4 && F != kDense) {
+        if constexpr (NB <= 4 && F != kDense) {
             // row pairs (two rows a wave; the plan takes them at 4 or 5 chunks a lane)
             if (P.rpw == 2) {
+                if (xu > 1)                      // the plan never pairs rows whose x needs more
+                    return NM_ERR_UNSUPPORTED;
                 if (P.cpl == 4)
                     hipLaunchKernelGGL((rowslice_kernel<F, DT, NB, 4, 1, 2>), dim3(P.grid), dim3(P.threads), P.lds, s,
                                        parts, x4, R, K, P.ls, P.rpb, P.xf, (int)(xu != 0));

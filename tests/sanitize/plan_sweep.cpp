@@ -48,8 +48,8 @@ void check_rowslice(const Plan& P, int64_t R, int64_t K, int B, bool glu)
     const int waves = P.rpb / P.rpw;            // rpb counts rows: rpw a wave
     REQUIRE(P.rpb % P.rpw == 0 && waves >= 1 && waves * P.S <= 16 && P.threads == waves * P.S * kWave);
     if (P.rpw == 2)                             // the instantiated row-pair kernels
-        REQUIRE(F != kDense && P.S == 1 && B >= 2 && B <= 4 && (P.cpl == 4 || P.cpl == 5) &&
-                (B >= 3 || g_env.rpw == 2));
+        REQUIRE(F != kDense && P.S == 1 && B >= 1 && B <= 4 && (P.cpl == 4 || P.cpl == 5) &&
+                (B >= 3 || g_env.rpw == 2) && rowslice_x_regs(B, K, P.threads, P.cpl) <= 1);
     REQUIRE(P.cpl >= 1 && P.cpl <= (B == 1 && !glu && F != kDense ? 16 : 8));
     REQUIRE(slice_chunks(C, P.S, P.ls) <= 64LL * P.cpl);
     REQUIRE((int64_t)P.grid * P.rpb >= R && ((int64_t)P.grid - 1) * P.rpb < R);

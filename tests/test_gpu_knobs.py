@@ -36,7 +36,7 @@ CASES = [
     (8193, 4096, 2, 4, "bf16", 3),     # row pairs (two rows a wave) by default
 ]
 # run only under the override that changes their plan
-CASES_FOR = {"NMSPMV_RPW": [(8192, 5120, 2, 4, "fp16", 2)]}   # row pairs from 2 vectors
+CASES_FOR = {"NMSPMV_RPW": [(8192, 5120, 2, 4, "fp16", 2), (8201, 4096, 4, 8, "bf16", 1)]}   # row pairs from 1 vector
 
 SETTINGS = [
     {"NMSPMV_MAX_CPL": "16"},
