@@ -30,7 +30,7 @@ enum Fmt { kDense = 0, kNM24 = 1, kNM48 = 2 };
 template <int F>
 constexpr int table_units()
 {
-    return F == kNM24 ? 4 : (F == kNM48 ? 256 : 0);
+    return F == kNM24 ? 4 : (F == kNM48 ? 16 : 0);
 }
 
 template <int F>

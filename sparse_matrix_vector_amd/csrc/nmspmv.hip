@@ -61,6 +61,7 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -164,6 +165,35 @@ __device__ u32x4 select48(uint32_t m)
     return u32x4{s[0], s[1], s[2], s[3]};
 }
 
+// 4:8, one nibble of a group's mask byte, for the VALU kernels: the selectors
+// of the nibble's two dense dwords (columns 2d, 2d+1 of its four) over
+// {hi dword : lo dword} of the group's values, the nibble's first kept value
+// being value k0.  The low nibble's values come first (k0 = 0); in a group with
+// exactly four kept columns the high nibble's follow them, so its k0 is
+// 4 - popcount(high nibble) and each nibble's selectors depend on that nibble
+// alone: two 16-entry tables of 8-byte entries (128 bytes each, every entry
+// on its own two LDS banks) instead of one 256-entry table of 16-byte
+// entries, whose look-ups from 64 lanes fell on the same banks.  A malformed
+// mask gives junk selector bytes, never an out-of-range access.
+__device__ u32x2 select48_nibble(uint32_t n, uint32_t k0)
+{
+    uint32_t s[2];
+    uint32_t k = k0;
+    for (int d = 0; d < 2; ++d) {
+        uint32_t sel = 0;
+        for (int h = 0; h < 2; ++h) {
+            uint32_t pair = 0x0C0Cu;
+            if ((n >> (2 * d + h)) & 1u) {
+                pair = (2 * k) | ((2 * k + 1) << 8);
+                ++k;
+            }
+            sel |= pair << (16 * h);
+        }
+        s[d] = sel;
+    }
+    return u32x2{s[0], s[1]};
+}
+
 template <int F>
 __device__ __forceinline__ void build_table(u32x4* tab)
 {
@@ -172,8 +202,10 @@ __device__ __forceinline__ void build_table(u32x4* tab)
             tab[threadIdx.x] = u32x4{select24(4 * threadIdx.x), select24(4 * threadIdx.x + 1),
                                      select24(4 * threadIdx.x + 2), select24(4 * threadIdx.x + 3)};
     } else if constexpr (F == kNM48) {
-        for (unsigned i = threadIdx.x; i < 256; i += blockDim.x)
-            tab[i] = select48(i);
+        // entries 0-15: low nibbles; 16-31: high nibbles
+        u32x2* t2 = reinterpret_cast<u32x2*>(tab);
+        for (unsigned i = threadIdx.x; i < 32; i += blockDim.x)
+            t2[i] = i < 16 ? select48_nibble(i, 0) : select48_nibble(i - 16, 4u - __builtin_popcount(i - 16));
     }
 }
 
@@ -361,8 +393,11 @@ __device__ __forceinline__ void chunk_dot(const u32x4 v, const uint32_t mk, cons
             acc[b] = a;
         }
     } else {
-        const u32x4 s0 = tab[mk & 0xFF];
-        const u32x4 s1 = tab[(mk >> 8) & 0xFF];
+        const u32x2* t2 = reinterpret_cast<const u32x2*>(tab);
+        const u32x2 a0 = t2[mk & 0xF], a1 = t2[16 + ((mk >> 4) & 0xF)];
+        const u32x2 b0 = t2[(mk >> 8) & 0xF], b1 = t2[16 + ((mk >> 12) & 0xF)];
+        const u32x4 s0 = u32x4{a0.x, a0.y, a1.x, a1.y};
+        const u32x4 s1 = u32x4{b0.x, b0.y, b1.x, b1.y};
         uint32_t w[8];
         w[0] = __builtin_amdgcn_perm(v.y, v.x, s0.x);
         w[1] = __builtin_amdgcn_perm(v.y, v.x, s0.y);
@@ -577,9 +612,13 @@ __device__ __forceinline__ void chunk_dot_pair(const u32x4 va, const uint32_t ma
             acc2[b] = c;
         }
     } else {
+        const u32x2* t2 = reinterpret_cast<const u32x2*>(tab);
         uint32_t w[8], u[8];
         {
-            const u32x4 s0 = tab[ma & 0xFF], s1 = tab[(ma >> 8) & 0xFF];
+            const u32x4 s0 = u32x4{t2[ma & 0xF].x, t2[ma & 0xF].y, t2[16 + ((ma >> 4) & 0xF)].x,
+                                   t2[16 + ((ma >> 4) & 0xF)].y};
+            const u32x4 s1 = u32x4{t2[(ma >> 8) & 0xF].x, t2[(ma >> 8) & 0xF].y, t2[16 + ((ma >> 12) & 0xF)].x,
+                                   t2[16 + ((ma >> 12) & 0xF)].y};
             w[0] = __builtin_amdgcn_perm(va.y, va.x, s0.x);
             w[1] = __builtin_amdgcn_perm(va.y, va.x, s0.y);
             w[2] = __builtin_amdgcn_perm(va.y, va.x, s0.z);
@@ -590,7 +629,10 @@ __device__ __forceinline__ void chunk_dot_pair(const u32x4 va, const uint32_t ma
             w[7] = __builtin_amdgcn_perm(va.w, va.z, s1.w);
         }
         {
-            const u32x4 s0 = tab[mb & 0xFF], s1 = tab[(mb >> 8) & 0xFF];
+            const u32x4 s0 = u32x4{t2[mb & 0xF].x, t2[mb & 0xF].y, t2[16 + ((mb >> 4) & 0xF)].x,
+                                   t2[16 + ((mb >> 4) & 0xF)].y};
+            const u32x4 s1 = u32x4{t2[(mb >> 8) & 0xF].x, t2[(mb >> 8) & 0xF].y, t2[16 + ((mb >> 12) & 0xF)].x,
+                                   t2[16 + ((mb >> 12) & 0xF)].y};
             u[0] = __builtin_amdgcn_perm(vb.y, vb.x, s0.x);
             u[1] = __builtin_amdgcn_perm(vb.y, vb.x, s0.y);
             u[2] = __builtin_amdgcn_perm(vb.y, vb.x, s0.z);
@@ -987,7 +1029,6 @@ __global__ __launch_bounds__(1024) void stream_kernel(const Parts P, const u32x4
 // cross-lane reduction is needed: the slices of a tile add up in LDS in slice
 // order.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
