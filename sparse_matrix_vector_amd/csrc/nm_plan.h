@@ -50,12 +50,12 @@ constexpr int x_row_units(int64_t K)
 
 // 16-byte LDS units of the matrix-core kernels' expansion tables.  2:4: one
 // expand24 selector pair per nibble (16 entries of 8 bytes: 64 lanes reading
-// arbitrary entries touch distinct banks or share a word); 4:8: one select48
-// entry per mask byte.
+// arbitrary entries touch distinct banks or share a word); 4:8: the VALU
+// kernels' two 16-entry nibble tables of 8-byte entries.
 template <int F>
 constexpr int mfma_table_units()
 {
-    return F == kDense ? 0 : F == kNM24 ? 8 : 256;
+    return F == kDense ? 0 : F == kNM24 ? 8 : 16;
 }
 
 // Staged matrix-core kernel: per wave, a 16-row tile's values and masks for

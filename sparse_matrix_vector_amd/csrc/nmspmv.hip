@@ -141,34 +141,11 @@ __device__ uint32_t select24(uint32_t n)
     return (2 * j0) | ((2 * j0 + 1) << 8) | ((2 * j1) << 16) | ((2 * j1 + 1) << 24);
 }
 
-// 4:8.  Byte m marks the kept columns of an 8-column group; its four values
-// (in column order) sit in bytes 2k, 2k+1 of {hi dword : lo dword}.  Dense
-// dword d (columns 2d, 2d+1) gets selector bytes that copy value k into the
-// kept column and zero bytes (0x0C) elsewhere.  With more than four bits set
-// the selectors run past 7 and give junk bytes, never an out-of-range access.
-__device__ u32x4 select48(uint32_t m)
-{
-    uint32_t s[4];
-    uint32_t k = 0;
-    for (int d = 0; d < 4; ++d) {
-        uint32_t sel = 0;
-        for (int h = 0; h < 2; ++h) {
-            uint32_t pair = 0x0C0Cu;
-            if ((m >> (2 * d + h)) & 1u) {
-                pair = (2 * k) | ((2 * k + 1) << 8);
-                ++k;
-            }
-            sel |= pair << (16 * h);
-        }
-        s[d] = sel;
-    }
-    return u32x4{s[0], s[1], s[2], s[3]};
-}
-
-// 4:8, one nibble of a group's mask byte, for the VALU kernels: the selectors
-// of the nibble's two dense dwords (columns 2d, 2d+1 of its four) over
-// {hi dword : lo dword} of the group's values, the nibble's first kept value
-// being value k0.  The low nibble's values come first (k0 = 0); in a group with
+// 4:8, one nibble of a group's mask byte (every kernel's 4:8 table): the
+// selectors of the nibble's two dense dwords (columns 2d, 2d+1 of its four)
+// over {hi dword : lo dword} of the group's four values (in column order,
+// value k in bytes 2k, 2k+1), copying value k into a kept column and zero
+// bytes (0x0C) elsewhere, the nibble's first kept value being value k0.  The low nibble's values come first (k0 = 0); in a group with
 // exactly four kept columns the high nibble's follow them, so its k0 is
 // 4 - popcount(high nibble) and each nibble's selectors depend on that nibble
 // alone: two 16-entry tables of 8-byte entries (128 bytes each, every entry
@@ -1070,8 +1047,10 @@ __device__ __forceinline__ void build_mfma_table(u32x4* tab)
         for (unsigned t = threadIdx.x; t < 16; t += blockDim.x)
             t2[t] = expand24(t);
     } else if constexpr (F == kNM48) {
-        for (unsigned t = threadIdx.x; t < 256; t += blockDim.x)
-            tab[t] = select48(t);
+        // the VALU kernels' nibble tables: entries 0-15 low nibbles, 16-31 high
+        u32x2* t2 = reinterpret_cast<u32x2*>(tab);
+        for (unsigned t = threadIdx.x; t < 32; t += blockDim.x)
+            t2[t] = t < 16 ? select48_nibble(t, 0) : select48_nibble(t - 16, 4u - __builtin_popcount(t - 16));
     }
 }
 
@@ -1208,13 +1187,15 @@ __global__ __launch_bounds__(512) void mfma_stage_kernel(const Parts P, const u3
                     a[s] = u32x2{__builtin_amdgcn_perm(w[s], w[s], sel.x), __builtin_amdgcn_perm(w[s], w[s], sel.y)};
                 }
             } else {
+                const u32x2* n2 = reinterpret_cast<const u32x2*>(tab);
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {                // group g: k-blocks 2 g, 2 g + 1
-                    const u32x4 sel = tab[(mk[t] >> (8 * g)) & 0xFFu];
-                    a[2 * g] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.x),
-                                     __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.y)};
-                    a[2 * g + 1] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.z),
-                                         __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.w)};
+                    const uint32_t mg = (mk[t] >> (8 * g)) & 0xFFu;
+                    const u32x2 lo = n2[mg & 0xFu], hi = n2[16 + (mg >> 4)];
+                    a[2 * g] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], lo.x),
+                                     __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], lo.y)};
+                    a[2 * g + 1] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], hi.x),
+                                         __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], hi.y)};
                 }
             }
             // Two 4-column k-blocks (8 columns, one x unit) per matrix-core step.
@@ -1540,13 +1521,15 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(const Parts P, const u32
                         a[s] = u32x2{__builtin_amdgcn_perm(w[s], w[s], sel.x), __builtin_amdgcn_perm(w[s], w[s], sel.y)};
                     }
                 } else {
+                    const u32x2* n2 = reinterpret_cast<const u32x2*>(tab);
 #pragma unroll
                     for (int g = 0; g < 2; ++g) {
-                        const u32x4 sel = tab[(mk[t] >> (8 * g)) & 0xFFu];
-                        a[2 * g] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.x),
-                                         __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.y)};
-                        a[2 * g + 1] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.z),
-                                             __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel.w)};
+                        const uint32_t mg = (mk[t] >> (8 * g)) & 0xFFu;
+                        const u32x2 lo = n2[mg & 0xFu], hi = n2[16 + (mg >> 4)];
+                        a[2 * g] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], lo.x),
+                                         __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], lo.y)};
+                        a[2 * g + 1] = u32x2{__builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], hi.x),
+                                             __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], hi.y)};
                     }
                 }
                 // Two 4-column k-blocks (8 columns of the chunk, one staged x
