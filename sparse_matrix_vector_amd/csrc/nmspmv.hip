@@ -1818,33 +1818,42 @@ __global__ __launch_bounds__(256) void pack_check_kernel(const u32x4* __restrict
         atomicOr(status, bad);
 }
 
-template <int DT>
+// M is a template parameter so that the group loops unroll and the eight
+// words stay in registers (with a run-time M they were indexed dynamically,
+// through scratch memory).  With four values a byte (2:4 and 4:8) the kept
+// words are gathered by selects and written as one 8-byte store.
+template <int DT, int M>
 __global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, const uint8_t* __restrict__ keep,
-                                                   int64_t nbytes, int N, int M, uint16_t* __restrict__ values,
+                                                   int64_t nbytes, int N, uint16_t* __restrict__ values,
                                                    uint8_t* __restrict__ masks, const int32_t* __restrict__ rowmap,
                                                    int64_t bpr)
 {
+    static_assert(M == 4 || M == 8, "groups of 4 or 8 columns");
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nbytes)
         return;
     const int64_t u = source_unit(rowmap, i, bpr);
     const u32x4 wv = W[u];
-    uint16_t w[8];
+    uint32_t w[8];
     w[0] = wv.x & 0xFFFF; w[1] = wv.x >> 16; w[2] = wv.y & 0xFFFF; w[3] = wv.y >> 16;
     w[4] = wv.z & 0xFFFF; w[5] = wv.z >> 16; w[6] = wv.w & 0xFFFF; w[7] = wv.w >> 16;
     uint32_t kb = 0;
     if (keep) {
         const uint8_t* kp = keep + 8 * u;
+#pragma unroll
         for (int j = 0; j < 8; ++j)
             kb |= (uint32_t)(kp[j] != 0) << j;
     } else {
         // Column j is kept when fewer than N group members beat it: larger
         // magnitude, or equal magnitude at a lower column.  For non-NaN words
         // the unsigned order of (bits & 0x7FFF) is the order of |w|.
+#pragma unroll
         for (int g = 0; g < 8; g += M) {
+#pragma unroll
             for (int j = g; j < g + M; ++j) {
                 const uint32_t mj = w[j] & 0x7FFFu;
                 int beats = 0;
+#pragma unroll
                 for (int k = g; k < g + M; ++k) {
                     const uint32_t mk = w[k] & 0x7FFFu;
                     beats += (mk > mj) || (mk == mj && k < j);
@@ -1854,12 +1863,30 @@ __global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, 
         }
     }
     const int vpb = 8 / M * N;
+    masks[i] = (uint8_t)kb;
+    if (vpb == 4) {
+        // the kept words in column order (the check pass guarantees four; the
+        // selects write nothing past the byte's slot whatever the mask holds)
+        uint32_t o[4] = {0u, 0u, 0u, 0u};
+        int k = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool kept = (kb >> j) & 1u;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                o[t] = (kept && k == t) ? w[j] : o[t];
+            k += kept ? 1 : 0;
+        }
+        // rows are whole bytes, so i * 4 is the fixed-step offset (8-byte aligned)
+        *reinterpret_cast<u32x2*>(values + i * 4) = u32x2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+        return;
+    }
     uint16_t* out = values + i * vpb;            // rows are whole bytes, so i * vpb is the fixed-step offset
     int k = 0;
+#pragma unroll
     for (int j = 0; j < 8; ++j)
         if (((kb >> j) & 1u) && k < vpb)         // the check pass guarantees k < vpb; the guard keeps writes in bounds
-            out[k++] = w[j];
-    masks[i] = (uint8_t)kb;
+            out[k++] = (uint16_t)w[j];
 }
 
 // ---- hybrid sparse + dense rows --------------------------------------------------
@@ -2449,12 +2476,21 @@ int pack_rows(const void* W, const uint8_t* keep, const int32_t* rowmap, int64_t
         return NM_ERR_BAD_MASK;
     if (host_status & kStatusNaN)
         return NM_ERR_NONFINITE;
-    if (dtype == NM_FP16)
-        hipLaunchKernelGGL(pack_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
-                           (uint16_t*)values, masks, rowmap, K / 8);
-    else
-        hipLaunchKernelGGL(pack_kernel<NM_BF16>, dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N, M,
-                           (uint16_t*)values, masks, rowmap, K / 8);
+#define NM_PACK(DT, MM)                                                                                          \
+    hipLaunchKernelGGL((pack_kernel<DT, MM>), dim3(grid), dim3(256), 0, s, (const u32x4*)W, keep, nbytes, N,       \
+                       (uint16_t*)values, masks, rowmap, K / 8)
+    if (dtype == NM_FP16) {
+        if (M == 4)
+            NM_PACK(NM_FP16, 4);
+        else
+            NM_PACK(NM_FP16, 8);
+    } else {
+        if (M == 4)
+            NM_PACK(NM_BF16, 4);
+        else
+            NM_PACK(NM_BF16, 8);
+    }
+#undef NM_PACK
     if (hipGetLastError() != hipSuccess)
         return NM_ERR_HIP;
     return hip_status(hipStreamSynchronize(s));
