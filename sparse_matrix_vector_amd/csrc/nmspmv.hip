@@ -1901,47 +1901,70 @@ __global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ W, 
 // or those the top-N magnitude rule (nm_pack's) drops.  Keep-mask groups
 // without N kept, or NaN weights under the magnitude rule, set the status
 // word (as nm_pack's check does).
-constexpr int kLossRows = 64;    // rows per block
+constexpr int kLossRows = 32;    // rows per block
 constexpr int kLossCols = 64;    // columns per chunk
 
-// Block of 256 threads, 64 rows.  Per 64-column chunk, every thread computes
-// the terms of 16 columns (whole groups: M divides 16) of one row -- thread t
-// takes row t / 4, columns 16 (t % 4) .. + 15 -- into LDS with a mask of the
-// pruned ones; then thread t < 64 adds its row's pruned terms in column
+// Block of 256 threads, 32 rows.  Per 64-column chunk, every thread computes
+// the terms of 8 columns (whole groups: M, a template parameter, divides 8) of one row -- thread t
+// takes row t / 8, columns 8 (t % 8) .. + 7 -- into LDS with a mask of the
+// pruned ones; then thread t < 32 adds its row's pruned terms in column
 // order.  Only the adds form a dependent chain; the decoding, the top-N rule
 // and the products run in parallel over the chunk (one thread per row and
-// column run would leave the chip almost idle: R / 64 waves in all).
-template <int DT>
+// column run would leave the chip almost idle: R / 64 waves in all).  32 rows
+// a block give R / 32 blocks (448 at R = 14336, so every CU holds work;
+// with 64 rows a block, 224 blocks left 32 CUs idle and the rest one block
+// each: 0.9 ms for the Llama-3.1-8B gate).
+template <int DT, int M>
 __global__ __launch_bounds__(256) void hybrid_loss_kernel(const uint16_t* __restrict__ W, const uint8_t* __restrict__ keep,
                                                           const float* __restrict__ h, int64_t h_stride, int R, int K,
-                                                          int N, int M, double* __restrict__ loss,
+                                                          int N, double* __restrict__ loss,
                                                           uint32_t* __restrict__ status)
 {
+    static_assert(M == 4 || M == 8, "groups of 4 or 8 columns");
     __shared__ double terms[kLossRows][kLossCols + 1];   // +1: the fold's column reads fall in distinct banks
-    __shared__ __attribute__((aligned(8))) uint16_t pruned[kLossRows][4];   // bit j of [row][q]: column 16 q + j is pruned
+    __shared__ __attribute__((aligned(8))) uint8_t pruned[kLossRows][8];    // bit j of [row][q]: column 8 q + j is pruned
     __shared__ double hs[kLossCols];
     const int t = threadIdx.x;
     const int r0 = blockIdx.x * kLossRows;
-    const int lr = t >> 2, q = t & 3, r = r0 + lr;
+    const int lr = t >> 3, q = t & 7, r = r0 + lr;
+    const uint16_t* wrow = W + (size_t)(r < R ? r : 0) * K;
     double l = 0.0;
     uint32_t bad = 0;
+    // The next chunk's words and h value are loaded while the current one is
+    // processed (each chunk otherwise waits for its loads between barriers).
+    uint32_t wn[8];
+    float hn = 1.f;
+    auto fetch = [&](int c0) {
+        const int cw = min(kLossCols, K - c0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            wn[j] = (r < R && 8 * q + j < cw) ? wrow[c0 + 8 * q + j] : 0u;
+        if (h && t < cw)
+            hn = h[(int64_t)(c0 + t) * h_stride];
+    };
+    fetch(0);
     for (int c0 = 0; c0 < K; c0 += kLossCols) {
         const int cw = min(kLossCols, K - c0);           // a multiple of 8 (K % 8 == 0)
+        uint32_t wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            wv[j] = wn[j];
+        const float hc = hn;
+        if (c0 + kLossCols < K)
+            fetch(c0 + kLossCols);
         __syncthreads();                                 // the previous chunk is folded
         if (t < cw)
-            hs[t] = h ? nm_decode::f32_to_f64(h[(int64_t)(c0 + t) * h_stride]) : 1.0;
+            hs[t] = h ? nm_decode::f32_to_f64(hc) : 1.0;
         __syncthreads();
         uint32_t pm = 0;
-        if (r < R) {
-            const uint16_t* w = W + (size_t)r * K + c0;
-            const uint8_t* kp = keep ? keep + (size_t)r * K + c0 : nullptr;
-            for (int g = 16 * q; g < 16 * q + 16 && g < cw; g += M) {
-                uint32_t wv[8];
-                for (int j = 0; j < M; ++j)
-                    wv[j] = w[g + j];
+        if (r < R && 8 * q < cw) {
+            const uint8_t* kp = keep ? keep + (size_t)r * K + c0 + 8 * q : nullptr;
+#pragma unroll
+            for (int g = 0; g < 8; g += M) {
                 uint32_t kept = 0;
                 if (kp) {
                     int cnt = 0;
+#pragma unroll
                     for (int j = 0; j < M; ++j) {
                         const uint32_t k = kp[g + j] != 0;
                         kept |= k << j;
@@ -1950,28 +1973,31 @@ __global__ __launch_bounds__(256) void hybrid_loss_kernel(const uint16_t* __rest
                     if (cnt != N)
                         bad |= kStatusBadMask;
                 } else {
+#pragma unroll
                     for (int j = 0; j < M; ++j) {
-                        const uint32_t mj = wv[j] & 0x7FFFu;
+                        const uint32_t mj = wv[g + j] & 0x7FFFu;
                         if (mj > (DT == NM_FP16 ? 0x7C00u : 0x7F80u))
                             bad |= kStatusNaN;
                         int beats = 0;
+#pragma unroll
                         for (int k = 0; k < M; ++k) {
-                            const uint32_t mk = wv[k] & 0x7FFFu;
+                            const uint32_t mk = wv[g + k] & 0x7FFFu;
                             beats += (mk > mj) || (mk == mj && k < j);
                         }
                         kept |= (uint32_t)(beats < N) << j;
                     }
                 }
+#pragma unroll
                 for (int j = 0; j < M; ++j) {
                     if ((kept >> j) & 1u)
                         continue;
-                    const double v = nm_decode::w_to_f64<DT>(wv[j]);
-                    terms[lr][g + j] = __dmul_rn(__dmul_rn(v, v), hs[g + j]);
-                    pm |= 1u << (g + j - 16 * q);
+                    const double v = nm_decode::w_to_f64<DT>(wv[g + j]);
+                    terms[lr][8 * q + g + j] = __dmul_rn(__dmul_rn(v, v), hs[8 * q + g + j]);
+                    pm |= 1u << (g + j);
                 }
             }
         }
-        pruned[lr][q] = (uint16_t)pm;
+        pruned[lr][q] = (uint8_t)pm;
         __syncthreads();
         if (t < kLossRows && r0 + t < R) {
             const uint64_t pmask = *reinterpret_cast<const uint64_t*>(&pruned[t][0]);   // bit c: column c pruned
@@ -2721,12 +2747,21 @@ int nmk::hybrid_row_loss(const void* W, const uint8_t* keep, const float* h, int
     hipStream_t s = static_cast<hipStream_t>(stream);
     const unsigned grid = (unsigned)((R + kLossRows - 1) / kLossRows);
     return with_status(s, [&](uint32_t* status) {
-        if (dtype == NM_FP16)
-            hipLaunchKernelGGL(hybrid_loss_kernel<NM_FP16>, dim3(grid), dim3(256), 0, s, (const uint16_t*)W, keep, h,
-                               h_stride, (int)R, (int)K, N, M, loss, status);
-        else
-            hipLaunchKernelGGL(hybrid_loss_kernel<NM_BF16>, dim3(grid), dim3(256), 0, s, (const uint16_t*)W, keep, h,
-                               h_stride, (int)R, (int)K, N, M, loss, status);
+#define NM_LOSS(DT, MM)                                                                                        \
+    hipLaunchKernelGGL((hybrid_loss_kernel<DT, MM>), dim3(grid), dim3(256), 0, s, (const uint16_t*)W, keep, h,  \
+                       h_stride, (int)R, (int)K, N, loss, status)
+        if (dtype == NM_FP16) {
+            if (M == 4)
+                NM_LOSS(NM_FP16, 4);
+            else
+                NM_LOSS(NM_FP16, 8);
+        } else {
+            if (M == 4)
+                NM_LOSS(NM_BF16, 4);
+            else
+                NM_LOSS(NM_BF16, 8);
+        }
+#undef NM_LOSS
     });
 }
 
